@@ -1,0 +1,315 @@
+// The C-ABI: handles, argument checks, variant dispatch and the autotuner.
+//
+// "Unweight: how we compressed an LLM 22% without sacrificing quality": the
+// runtime picks an execution strategy per weight matrix and batch size from
+// measurements on the target hardware, not from heuristics (paragraph on the
+// four pipelines; paragraph on the autotuner).  Here the candidates are the
+// fused decode+product kernel and decompress-to-HBM followed by the bf16
+// product; uw_autotune times both with HIP events and stores the winner.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "uw_internal.h"
+
+using namespace uw;
+
+namespace {
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_matrix(const uw_matrix* m) {
+  if (!m) return fail(UW_ERR_INVALID, "null matrix handle");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(UW_ERR_HIP, "hipGetDevice failed");
+  if (dev != m->device) return fail(UW_ERR_INVALID, "the current device is not the handle's device");
+  return UW_OK;
+}
+
+int check_dtype(int t) { return t == UW_F32 || t == UW_BF16 ? UW_OK : fail(UW_ERR_INVALID, "dtype must be UW_F32 or UW_BF16"); }
+
+size_t esize(int t) { return t == UW_F32 ? 4 : 2; }
+
+int check_products(const void* X, int64_t batch, int64_t ldx, int xt, const void* Y, int64_t ldy, int yt, int64_t rows,
+                   int64_t cols) {
+  if (batch < 0) return fail(UW_ERR_INVALID, "negative batch");
+  if (check_dtype(xt) || check_dtype(yt)) return UW_ERR_INVALID;
+  if (batch == 0) return UW_OK;
+  if (!X || !Y) return fail(UW_ERR_INVALID, "null X or Y");
+  if (!aligned(X, esize(xt)) || !aligned(Y, esize(yt))) return fail(UW_ERR_INVALID, "X or Y not aligned to its element size");
+  if (ldx < cols || (batch > 1 && ldy < rows)) return fail(UW_ERR_INVALID, "ldx < cols or ldy < rows");
+  return UW_OK;
+}
+
+size_t decompress_ws_bytes(const uw_matrix* m) {
+  return (size_t(m->h.rows) * size_t(m->h.cols) * 2 + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+int uw_version(void) { return UW_VERSION; }
+
+const char* uw_status_string(int s) {
+  switch (s) {
+    case UW_OK: return "ok";
+    case UW_ERR_INVALID: return "invalid argument";
+    case UW_ERR_FORMAT: return "invalid blob format";
+    case UW_ERR_NOSPACE: return "buffer too small";
+    case UW_ERR_HIP: return "HIP runtime error";
+    case UW_ERR_UNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+  }
+}
+
+const char* uw_last_error(void);
+
+int uw_blob_info(const void* blob, size_t n, uw_info* info) {
+  if (!blob || !info) return fail(UW_ERR_INVALID, "uw_blob_info: null pointer");
+  BlobHeader h;
+  int rc = validate_blob(static_cast<const uint8_t*>(blob), n, &h);
+  if (rc) return rc;
+  std::memset(info, 0, sizeof(*info));
+  info->rows = h.rows;
+  info->cols = h.cols;
+  info->K = int32_t(h.K);
+  info->L = int32_t(h.L);
+  info->G = int32_t(h.G);
+  info->plain = h.plain() ? 1 : 0;
+  info->n_blocks = h.n_blocks;
+  info->n_raw_groups = int64_t(h.n_raw_groups);
+  info->total_bytes = h.total_bytes;
+  info->max_block_stream_bytes = h.max_block_stream_bytes;
+  std::memcpy(info->palette, h.palette, 32);
+  std::memcpy(info->code_len, h.code_len, 32);
+  const double w = double(h.rows) * double(h.cols);
+  info->ratio = double(h.total_bytes) / (2.0 * w);
+  info->bits_per_weight = 8.0 * double(h.total_bytes) / w;
+  return UW_OK;
+}
+
+int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_matrix** out) {
+  if (!host_blob || !d_blob || !out) return fail(UW_ERR_INVALID, "uw_matrix_create: null pointer");
+  if (!aligned(d_blob, 256)) return fail(UW_ERR_INVALID, "uw_matrix_create: device blob must be 256-byte aligned");
+  BlobHeader h;
+  int rc = validate_blob(static_cast<const uint8_t*>(host_blob), n, &h);
+  if (rc) return rc;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(UW_ERR_HIP, "uw_matrix_create: no current HIP device");
+  uw_matrix* m = new uw_matrix();
+  m->h = h;
+  m->device = dev;
+  m->d_blob = static_cast<const uint8_t*>(d_blob);
+  DevMatrix& d = m->dev;
+  std::memset(&d, 0, sizeof(d));
+  const uint8_t* b = m->d_blob;
+  d.rows = h.rows;
+  d.cols = h.cols;
+  d.n_groups = h.rows * (h.cols / 64);
+  d.gpr = int32_t(h.cols / 64);
+  if (h.plain()) {
+    d.plain = reinterpret_cast<const uint16_t*>(b + h.off_plain);
+  } else {
+    d.start_word = reinterpret_cast<const uint32_t*>(b + h.off_start_word);
+    d.first_raw = reinterpret_cast<const uint32_t*>(b + h.off_first_raw);
+    d.raw_bits = reinterpret_cast<const uint32_t*>(b + h.off_raw_bits);
+    d.lane_bits = reinterpret_cast<const uint16_t*>(b + h.off_lane_bits);
+    d.stream = reinterpret_cast<const uint32_t*>(b + h.off_stream);
+    d.raw = b + h.off_raw;
+    d.sm = b + h.off_sm;
+    d.G = int32_t(h.G);
+    d.n_blocks = int32_t(h.n_blocks);
+    d.rb_words = int32_t((h.G + 31) / 32);
+    d.L = int32_t(h.L);
+    // the decode tables are built on chip from the canonical codes
+    uint32_t code[32], rev[32];
+    canonical_codes(h, code, rev);
+    d.n_sym = int32_t(h.K);
+    for (uint32_t i = 0; i < h.K; ++i)
+      d.sym[i] = rev[i] | (uint32_t(h.code_len[i]) << 16) | (uint32_t(h.palette[i]) << 24);
+    // front pad + stream + back pad (window reads run one word past a lane's end)
+    d.stage_words = int32_t(h.max_block_stream_bytes / 4 + 8);
+    // a work unit covers whole rows: lcm(G, groups per row) groups
+    const int64_t lcm = int64_t(h.G) / gcd64(h.G, d.gpr) * d.gpr;
+    d.unit_blocks = int32_t(lcm / h.G);
+    d.n_units = int32_t((int64_t(h.n_blocks) + d.unit_blocks - 1) / d.unit_blocks);
+  }
+  *out = m;
+  return UW_OK;
+}
+
+void uw_matrix_destroy(uw_matrix* m) { delete m; }
+
+int uw_decompress(const uw_matrix* m, uint16_t* d_out, int64_t ld_out, void* stream) {
+  if (int rc = check_matrix(m)) return rc;
+  if (!d_out || !aligned(d_out, 16)) return fail(UW_ERR_INVALID, "uw_decompress: output must be non-null and 16-byte aligned");
+  if (ld_out < m->h.cols || ld_out % 8) return fail(UW_ERR_INVALID, "uw_decompress: ld_out must be >= cols and a multiple of 8");
+  return launch_decompress(m, d_out, ld_out, stream);
+}
+
+int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt, void* stream) {
+  if (int rc = check_matrix(m)) return rc;
+  if (int rc = check_products(d_x, 1, m->h.cols, xt, d_y, m->h.rows, yt, m->h.rows, m->h.cols)) return rc;
+  std::string why;
+  if (!fused_supported(m, xt, &why)) return fail(UW_ERR_UNSUPPORTED, "uw_gemv_fused: " + why);
+  if (m->h.plain() && !bf16_gemm_supported(m->h.cols, 1, xt, &why)) return fail(UW_ERR_UNSUPPORTED, "uw_gemv_fused: " + why);
+  return launch_fused(m, d_x, 1, m->h.cols, xt, d_y, m->h.rows, yt, stream);
+}
+
+size_t uw_workspace_size(const uw_matrix* m, int64_t batch, int variant) {
+  if (!m || batch < 0) return 0;
+  if (variant == UW_VARIANT_FUSED) return 0;
+  return decompress_ws_bytes(m);
+}
+
+int uw_get_plan(const uw_matrix* m, int64_t batch, uw_plan* out) {
+  if (!m || !out) return fail(UW_ERR_INVALID, "uw_get_plan: null pointer");
+  std::lock_guard<std::mutex> lk(m->mu);
+  auto it = m->plans.find(batch);
+  if (it == m->plans.end()) return fail(UW_ERR_INVALID, "uw_get_plan: no plan for this batch");
+  *out = it->second;
+  return UW_OK;
+}
+
+int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y, int64_t ldy,
+                  int yt, int variant, void* d_ws, size_t ws_bytes, void* stream) {
+  if (int rc = check_matrix(m)) return rc;
+  if (int rc = check_products(d_X, batch, ldx, xt, d_Y, ldy, yt, m->h.rows, m->h.cols)) return rc;
+  if (batch == 0) return UW_OK;
+  if (variant < 0 || variant >= UW_VARIANT_COUNT) return fail(UW_ERR_INVALID, "uw_gemm_fused: unknown variant");
+  std::string why;
+  const bool fused_ok = fused_supported(m, xt, &why) && (!m->h.plain() || bf16_gemm_supported(m->h.cols, batch, xt, &why));
+  if (variant == UW_VARIANT_AUTO) {
+    uw_plan p;
+    bool have = false;
+    {
+      std::lock_guard<std::mutex> lk(m->mu);
+      auto it = m->plans.find(batch);
+      if (it != m->plans.end()) {
+        p = it->second;
+        have = true;
+      }
+    }
+    if (have) variant = p.variant;
+    else variant = (batch <= 8 && fused_ok) || ws_bytes < decompress_ws_bytes(m) ? UW_VARIANT_FUSED : UW_VARIANT_DECOMPRESS_GEMM;
+  }
+  if (variant == UW_VARIANT_FUSED) {
+    if (!fused_ok) return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused: " + why);
+    return launch_fused(m, d_X, batch, ldx, xt, d_Y, ldy, yt, stream);
+  }
+  // decompress into the workspace, then the bf16 product
+  if (!d_ws || ws_bytes < decompress_ws_bytes(m) || !aligned(d_ws, 256))
+    return fail(UW_ERR_NOSPACE, "uw_gemm_fused: workspace missing, too small or not 256-byte aligned");
+  if (!bf16_gemm_supported(m->h.cols, batch, xt, &why)) return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused: " + why);
+  uint16_t* W = static_cast<uint16_t*>(d_ws);
+  if (int rc = launch_decompress(m, W, m->h.cols, stream)) return rc;
+  return launch_bf16_gemm(W, m->h.rows, m->h.cols, m->h.cols, d_X, batch, ldx, xt, d_Y, ldy, yt, stream);
+}
+
+size_t uw_autotune_scratch_size(const uw_matrix* m, int64_t batch) {
+  if (!m || batch < 0) return 0;
+  const size_t xb = (size_t(batch) * size_t(m->h.cols) * 2 + 255) / 256 * 256;
+  const size_t yb = (size_t(batch) * size_t(m->h.rows) * 2 + 255) / 256 * 256;
+  return xb + yb;
+}
+
+int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* stream, uw_plan* out) {
+  if (int rc = check_matrix(m)) return rc;
+  if (batch < 1) return fail(UW_ERR_INVALID, "uw_autotune: batch must be >= 1");
+  const size_t need_ws = uw_workspace_size(m, batch, UW_VARIANT_AUTO);
+  const size_t need = need_ws + uw_autotune_scratch_size(m, batch);
+  if (!d_ws || ws_bytes < need || !aligned(d_ws, 256)) return fail(UW_ERR_NOSPACE, "uw_autotune: workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(d_ws);
+  void* X = base + need_ws;
+  void* Y = base + need_ws + (size_t(batch) * size_t(m->h.cols) * 2 + 255) / 256 * 256;
+  // X = 1.0 everywhere (values do not change the work of either candidate)
+  if (hipMemsetD16Async(reinterpret_cast<hipDeviceptr_t>(X), 0x3F80, size_t(batch) * size_t(m->h.cols), s) != hipSuccess)
+    return fail(UW_ERR_HIP, "uw_autotune: memset failed");
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return fail(UW_ERR_HIP, "uw_autotune: event");
+  uw_plan plan;
+  std::memset(&plan, 0, sizeof(plan));
+  plan.batch = batch;
+  for (int v = 0; v < UW_VARIANT_COUNT; ++v) plan.candidate_us[v] = -1.f;
+  float best = 1e30f;
+  int best_v = -1;
+  const int warm = 3, reps = 15;
+  for (int v = UW_VARIANT_FUSED; v < UW_VARIANT_COUNT; ++v) {
+    std::vector<float> t;
+    int rc = UW_OK;
+    for (int i = 0; i < warm + reps && rc == UW_OK; ++i) {
+      hipEventRecord(e0, s);
+      rc = uw_gemm_fused(m, X, batch, m->h.cols, UW_BF16, Y, m->h.rows, UW_BF16, v, d_ws, need_ws, stream);
+      hipEventRecord(e1, s);
+      if (rc) break;
+      if (hipEventSynchronize(e1) != hipSuccess) {
+        rc = UW_ERR_HIP;
+        break;
+      }
+      float ms = 0;
+      hipEventElapsedTime(&ms, e0, e1);
+      if (i >= warm) t.push_back(ms * 1000.f);
+    }
+    if (rc == UW_ERR_HIP) {
+      hipEventDestroy(e0);
+      hipEventDestroy(e1);
+      return rc;
+    }
+    if (rc || t.empty()) continue;  // not applicable to this matrix/batch
+    std::sort(t.begin(), t.end());
+    const float med = t[t.size() / 2];
+    plan.candidate_us[v] = med;
+    if (med < best) {
+      best = med;
+      best_v = v;
+    }
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  if (best_v < 0) return fail(UW_ERR_UNSUPPORTED, "uw_autotune: no candidate can run this matrix and batch");
+  plan.variant = best_v;
+  plan.time_us = best;
+  {
+    std::lock_guard<std::mutex> lk(m->mu);
+    m->plans[batch] = plan;
+  }
+  if (out) *out = plan;
+  set_error("");
+  return UW_OK;
+}
+
+int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, const void* d_X, int64_t batch,
+                 int64_t ldx, int xt, void* d_Y, int64_t ldy, int yt, void* stream) {
+  if (!d_W || !aligned(d_W, 16)) return fail(UW_ERR_INVALID, "uw_bf16_gemm: W must be non-null and 16-byte aligned");
+  if (rows < 1 || cols < 8 || cols % 8 || ldw < cols || ldw % 8) return fail(UW_ERR_INVALID, "uw_bf16_gemm: bad shape");
+  if (int rc = check_products(d_X, batch, ldx, xt, d_Y, ldy, yt, rows, cols)) return rc;
+  if (batch == 0) return UW_OK;
+  std::string why;
+  if (!bf16_gemm_supported(cols, batch, xt, &why)) return fail(UW_ERR_UNSUPPORTED, "uw_bf16_gemm: " + why);
+  return launch_bf16_gemm(d_W, rows, cols, ldw, d_X, batch, ldx, xt, d_Y, ldy, yt, stream);
+}
+
+size_t uw_read_probe_sink_size(void) { return read_probe_sink_bytes(); }
+
+int uw_read_probe(const void* d_src, size_t bytes, void* d_sink, void* stream) {
+  if (!d_src || !d_sink || !aligned(d_src, 16) || !aligned(d_sink, 4) || bytes % 16 || bytes == 0)
+    return fail(UW_ERR_INVALID, "uw_read_probe: bad arguments");
+  return launch_read_probe(d_src, bytes, d_sink, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal declarations of the uw library (host side and kernel launchers).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <string>
+
+#include "../../include/uw.h"
+
+namespace uw {
+
+constexpr uint32_t kHeaderBytes = 256;
+constexpr uint32_t kSectionAlign = 256;
+constexpr uint32_t kFlagPlain = 1;
+constexpr int kMaxK = 32;
+constexpr int kMaxL = 12;
+constexpr int kPairPeekBits = 12;  // two codes of <= 6 bits always fit in a 12-bit window
+
+// Parsed header of a blob (see the layout in uw.h).
+struct BlobHeader {
+  uint32_t version = 0, flags = 0;
+  int64_t rows = 0, cols = 0;
+  uint32_t K = 0, L = 0, G = 0, n_blocks = 0;
+  uint64_t n_raw_groups = 0, total_bytes = 0;
+  uint32_t crc32 = 0, max_block_stream_bytes = 0;
+  uint8_t palette[32] = {0};
+  uint8_t code_len[32] = {0};
+  uint64_t off_start_word = 0, off_first_raw = 0, off_raw_bits = 0, off_lane_bits = 0;
+  uint64_t off_stream = 0, size_stream = 0, off_raw = 0, size_raw = 0;
+  uint64_t off_sm = 0, size_sm = 0, off_plain = 0, size_plain = 0;
+  bool plain() const { return flags & kFlagPlain; }
+};
+
+// Serialise / parse the fixed 256-byte header (no validation in read).
+void header_write(const BlobHeader& h, uint8_t* dst);
+void header_read(const uint8_t* src, BlobHeader* h);
+
+// CRC-32 (IEEE 802.3, reflected, as in zlib) of a byte range.
+uint32_t crc32(const uint8_t* p, size_t n, uint32_t crc = 0);
+
+// Full validation of a blob; on failure returns UW_ERR_FORMAT and sets the message.
+int validate_blob(const uint8_t* blob, size_t n, BlobHeader* out);
+
+// Canonical codes (RFC 1951 3.2.2) from lengths, ordered by exponent value;
+// code[i] is MSB-first, rev[i] the bit-reversed pattern as stored in streams.
+void canonical_codes(const BlobHeader& h, uint32_t code[32], uint32_t rev[32]);
+
+// Per-thread error message.
+void set_error(const std::string& msg);
+const char* last_error_text();
+int fail(int status, const std::string& msg);
+
+// Kernel-side description of a compressed matrix, passed by value.
+struct DevMatrix {
+  const uint32_t* start_word;
+  const uint32_t* first_raw;
+  const uint32_t* raw_bits;
+  const uint16_t* lane_bits;
+  const uint32_t* stream;
+  const uint8_t* raw;
+  const uint8_t* sm;
+  const uint16_t* plain;
+  int64_t rows, cols;
+  int64_t n_groups;
+  int32_t G, n_blocks, rb_words, gpr;  // gpr = groups per row = cols/64
+  int32_t L, n_sym;
+  int32_t stage_words;                 // LDS words of one wave's stream buffer
+  int32_t unit_blocks;                 // blocks per work unit (a unit covers whole rows)
+  int32_t n_units;
+  uint32_t sym[32];                    // rev code | len << 16 | exponent << 24
+};
+
+}  // namespace uw
+
+struct uw_matrix {
+  uw::BlobHeader h;
+  uw::DevMatrix dev;
+  const uint8_t* d_blob = nullptr;
+  int device = 0;
+  mutable std::mutex mu;
+  std::map<int64_t, uw_plan> plans;
+};
+
+namespace uw {
+
+// Launchers (uw_kernels.hip).  Shapes and pointers are checked by the caller.
+int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* stream);
+int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, int xt, void* Y,
+                 int64_t ldy, int yt, void* stream);
+bool fused_supported(const uw_matrix* m, int xt, std::string* why);
+int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X,
+                     int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream);
+bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why);
+int launch_read_probe(const void* src, size_t bytes, void* sink, void* stream);
+size_t read_probe_sink_bytes();
+
+}  // namespace uw

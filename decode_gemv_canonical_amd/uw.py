@@ -1,0 +1,311 @@
+"""ctypes binding of libuw.so: the same entry points as include/uw.h.
+
+Argument marshalling only: torch tensors supply device memory and the HIP
+stream; every computation runs in the library (host encoder, gfx950 kernels).
+There is no fallback: if libuw.so is missing or fails to load, importing this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libuw.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "uw.h")
+
+UW_OK = 0
+UW_ERR_INVALID = -1
+UW_ERR_FORMAT = -2
+UW_ERR_NOSPACE = -3
+UW_ERR_HIP = -4
+UW_ERR_UNSUPPORTED = -5
+UW_F32 = 0
+UW_BF16 = 1
+UW_VARIANT_AUTO = 0
+UW_VARIANT_FUSED = 1
+UW_VARIANT_DECOMPRESS_GEMM = 2
+UW_VARIANT_COUNT = 3
+UW_ENC_NO_PLAIN = 1
+VARIANT_NAMES = {UW_VARIANT_AUTO: "auto", UW_VARIANT_FUSED: "fused", UW_VARIANT_DECOMPRESS_GEMM: "decompress+gemm"}
+
+
+class UwError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {message} (status {status})")
+        self.status = status
+
+
+class uw_encode_opts(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("L", ctypes.c_int32), ("G", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class uw_info(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("K", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("G", ctypes.c_int32), ("plain", ctypes.c_int32), ("n_blocks", ctypes.c_int64),
+                ("n_raw_groups", ctypes.c_int64), ("total_bytes", ctypes.c_uint64),
+                ("max_block_stream_bytes", ctypes.c_uint32), ("palette", ctypes.c_uint8 * 32),
+                ("code_len", ctypes.c_uint8 * 32), ("ratio", ctypes.c_double), ("bits_per_weight", ctypes.c_double)]
+
+
+class uw_plan(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("variant", ctypes.c_int32), ("time_us", ctypes.c_float),
+                ("candidate_us", ctypes.c_float * UW_VARIANT_COUNT)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m decode_gemv_canonical_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "uw_version": (I, []),
+        "uw_status_string": (ctypes.c_char_p, [I]),
+        "uw_last_error": (ctypes.c_char_p, []),
+        "uw_encode": (I, [P, I64, I64, ctypes.POINTER(uw_encode_opts), P, ctypes.POINTER(SZ)]),
+        "uw_blob_info": (I, [P, SZ, ctypes.POINTER(uw_info)]),
+        "uw_matrix_create": (I, [P, SZ, P, ctypes.POINTER(P)]),
+        "uw_matrix_destroy": (None, [P]),
+        "uw_decompress": (I, [P, P, I64, P]),
+        "uw_gemv_fused": (I, [P, P, I, P, I, P]),
+        "uw_gemm_fused": (I, [P, P, I64, I64, I, P, I64, I, I, P, SZ, P]),
+        "uw_workspace_size": (SZ, [P, I64, I]),
+        "uw_autotune": (I, [P, I64, P, SZ, P, ctypes.POINTER(uw_plan)]),
+        "uw_autotune_scratch_size": (SZ, [P, I64]),
+        "uw_get_plan": (I, [P, I64, ctypes.POINTER(uw_plan)]),
+        "uw_bf16_gemm": (I, [P, I64, I64, I64, P, I64, I64, I, P, I64, I, P]),
+        "uw_read_probe": (I, [P, SZ, P, P]),
+        "uw_read_probe_sink_size": (SZ, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def header_symbols() -> list[str]:
+    """Entry points declared in include/uw.h."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"\b(uw_[a-z0-9_]+)\s*\(", text)))
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != UW_OK:
+        raise UwError(rc, where, (_lib.uw_last_error() or b"").decode())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return UW_F32
+    if t.dtype == torch.bfloat16:
+        return UW_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _as_u16(w) -> np.ndarray:
+    if hasattr(w, "numpy"):  # torch tensor on the CPU
+        w = w.contiguous().view(dtype=__import__("torch").int16).numpy()
+    a = np.ascontiguousarray(np.asarray(w))
+    if a.dtype not in (np.uint16, np.int16):
+        raise TypeError("weights must be 16-bit bf16 bit patterns")
+    return a.view(np.uint16)
+
+
+# -- entry points -----------------------------------------------------------
+
+def uw_version() -> int:
+    return _lib.uw_version()
+
+
+def uw_status_string(status: int) -> str:
+    return _lib.uw_status_string(status).decode()
+
+
+def uw_last_error() -> str:
+    return (_lib.uw_last_error() or b"").decode()
+
+
+def uw_encode(w_bf16, K: int = 0, L: int = 0, G: int = 0, flags: int = 0) -> bytes:
+    """bf16 bit patterns [rows, cols] (numpy uint16/int16 or a CPU torch tensor) -> blob bytes."""
+    a = _as_u16(w_bf16)
+    if a.ndim != 2:
+        raise ValueError("need a 2-D matrix")
+    opts = uw_encode_opts(K, L, G, flags)
+    size = ctypes.c_size_t(0)
+    _check(_lib.uw_encode(a.ctypes.data, a.shape[0], a.shape[1], ctypes.byref(opts), None, ctypes.byref(size)), "uw_encode")
+    buf = np.empty(size.value, dtype=np.uint8)
+    _check(_lib.uw_encode(a.ctypes.data, a.shape[0], a.shape[1], ctypes.byref(opts), buf.ctypes.data, ctypes.byref(size)),
+           "uw_encode")
+    return buf[: size.value].tobytes()
+
+
+def uw_blob_info(blob: bytes) -> dict:
+    info = uw_info()
+    arr = np.frombuffer(blob, dtype=np.uint8)
+    _check(_lib.uw_blob_info(arr.ctypes.data, arr.size, ctypes.byref(info)), "uw_blob_info")
+    out = {f: getattr(info, f) for f, _ in uw_info._fields_}
+    out["palette"] = list(info.palette)[: info.K]
+    out["code_len"] = list(info.code_len)[: info.K]
+    return out
+
+
+def uw_matrix_create(host_blob: bytes, d_blob) -> int:
+    """Handle for a blob already copied into the CUDA uint8 tensor d_blob (256-byte aligned)."""
+    arr = np.frombuffer(host_blob, dtype=np.uint8)
+    if d_blob.numel() != arr.size:
+        raise ValueError("device blob size differs from the host blob")
+    h = ctypes.c_void_p()
+    _check(_lib.uw_matrix_create(arr.ctypes.data, arr.size, d_blob.data_ptr(), ctypes.byref(h)), "uw_matrix_create")
+    return h.value
+
+
+def uw_matrix_destroy(handle: int) -> None:
+    _lib.uw_matrix_destroy(handle)
+
+
+def uw_decompress(handle: int, d_out, ld_out: int | None = None, stream=None) -> None:
+    if ld_out is None:
+        ld_out = d_out.stride(0)
+    _check(_lib.uw_decompress(handle, d_out.data_ptr(), ld_out, _stream(stream)), "uw_decompress")
+
+
+def uw_gemv_fused(handle: int, x, y, stream=None) -> None:
+    _check(_lib.uw_gemv_fused(handle, x.data_ptr(), _dtype_code(x), y.data_ptr(), _dtype_code(y), _stream(stream)),
+           "uw_gemv_fused")
+
+
+def uw_gemm_fused(handle: int, X, Y, variant: int = UW_VARIANT_AUTO, ws=None, stream=None) -> None:
+    batch = X.shape[0]
+    ws_ptr = ws.data_ptr() if ws is not None else None
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib.uw_gemm_fused(handle, X.data_ptr(), batch, X.stride(0), _dtype_code(X), Y.data_ptr(), Y.stride(0),
+                              _dtype_code(Y), variant, ws_ptr, ws_bytes, _stream(stream)), "uw_gemm_fused")
+
+
+def uw_workspace_size(handle: int, batch: int, variant: int = UW_VARIANT_AUTO) -> int:
+    return _lib.uw_workspace_size(handle, batch, variant)
+
+
+def uw_autotune_scratch_size(handle: int, batch: int) -> int:
+    return _lib.uw_autotune_scratch_size(handle, batch)
+
+
+def _plan_dict(p: uw_plan) -> dict:
+    return {"batch": p.batch, "variant": p.variant, "variant_name": VARIANT_NAMES.get(p.variant, "?"),
+            "time_us": p.time_us, "candidate_us": {VARIANT_NAMES[v]: p.candidate_us[v]
+                                                   for v in range(1, UW_VARIANT_COUNT) if p.candidate_us[v] >= 0}}
+
+
+def uw_autotune(handle: int, batch: int, ws, stream=None) -> dict:
+    p = uw_plan()
+    _check(_lib.uw_autotune(handle, batch, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream),
+                            ctypes.byref(p)), "uw_autotune")
+    return _plan_dict(p)
+
+
+def uw_get_plan(handle: int, batch: int) -> dict:
+    p = uw_plan()
+    _check(_lib.uw_get_plan(handle, batch, ctypes.byref(p)), "uw_get_plan")
+    return _plan_dict(p)
+
+
+def uw_bf16_gemm(W, X, Y, stream=None) -> None:
+    rows, cols = W.shape
+    _check(_lib.uw_bf16_gemm(W.data_ptr(), rows, cols, W.stride(0), X.data_ptr(), X.shape[0], X.stride(0),
+                             _dtype_code(X), Y.data_ptr(), Y.stride(0), _dtype_code(Y), _stream(stream)),
+           "uw_bf16_gemm")
+
+
+def uw_read_probe_sink_size() -> int:
+    return _lib.uw_read_probe_sink_size()
+
+
+def uw_read_probe(src, sink, stream=None) -> None:
+    _check(_lib.uw_read_probe(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), _stream(stream)),
+           "uw_read_probe")
+
+
+# -- convenience owner of a device blob + handle -----------------------------
+
+class CompressedMatrix:
+    """A blob copied to the current CUDA device plus its library handle."""
+
+    def __init__(self, blob: bytes, device: str = "cuda"):
+        import torch
+        self.blob = blob
+        self.info = uw_blob_info(blob)
+        host = torch.frombuffer(bytearray(blob), dtype=torch.uint8)
+        self.d_blob = host.to(device)
+        if self.d_blob.data_ptr() % 256:
+            raise RuntimeError("device blob is not 256-byte aligned")
+        self.handle = uw_matrix_create(blob, self.d_blob)
+        self.rows, self.cols = self.info["rows"], self.info["cols"]
+
+    @classmethod
+    def from_weights(cls, w_bf16, device: str = "cuda", **opts) -> "CompressedMatrix":
+        return cls(uw_encode(w_bf16, **opts), device)
+
+    def decompress(self, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(self.rows, self.cols, dtype=torch.bfloat16, device=self.d_blob.device)
+        uw_decompress(self.handle, out, out.stride(0), stream)
+        return out
+
+    def gemv(self, x, y=None, out_dtype=None, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty(self.rows, dtype=out_dtype or torch.float32, device=x.device)
+        uw_gemv_fused(self.handle, x, y, stream)
+        return y
+
+    def gemm(self, X, Y=None, variant: int = UW_VARIANT_AUTO, ws=None, out_dtype=None, stream=None):
+        import torch
+        if Y is None:
+            Y = torch.empty(X.shape[0], self.rows, dtype=out_dtype or torch.float32, device=X.device)
+        uw_gemm_fused(self.handle, X, Y, variant, ws, stream)
+        return Y
+
+    def workspace(self, batch: int, variant: int = UW_VARIANT_AUTO, autotune: bool = False):
+        import torch
+        n = uw_workspace_size(self.handle, batch, variant)
+        if autotune:
+            n += uw_autotune_scratch_size(self.handle, batch)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.d_blob.device)
+
+    def autotune(self, batch: int, ws=None, stream=None) -> dict:
+        if ws is None:
+            ws = self.workspace(batch, autotune=True)
+        return uw_autotune(self.handle, batch, ws, stream)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            uw_matrix_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,245 @@
+/*
+ * uw.h - lossless BF16 weight compression fused into the decode-time matmul,
+ *        for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "Unweight: how we compressed an LLM 22% without
+ * sacrificing quality": every bf16 weight keeps its sign and 7-bit mantissa as
+ * a raw byte, its 8-bit exponent is Huffman coded (paragraph on Huffman coding
+ * of the exponent byte), and a row of 64 weights holding an exponent outside
+ * the top-K palette is stored raw (paragraph on rare exponents).  Decoding
+ * happens on chip and feeds the multiply directly, so the reconstructed
+ * weights never exist in device memory (paragraph on the reconstructive
+ * matmul); a runtime chooses per matrix and batch size between the fused path
+ * and decompress-then-multiply (paragraph on the four pipelines, paragraph on
+ * the autotuner).
+ *
+ * Conventions for every entry point:
+ *  - returns UW_OK (0) or a negative uw_status; nothing aborts, throws or
+ *    prints across this boundary; uw_last_error() gives a message for the
+ *    calling thread;
+ *  - all arguments are checked on the host before anything is launched;
+ *  - device entry points are asynchronous on the given stream (a hipStream_t
+ *    passed as void*, NULL = the null stream), allocate no memory and do not
+ *    synchronise, except uw_autotune, which is blocking;
+ *  - "device pointer" means memory of the device that was current when the
+ *    matrix handle was created; every device entry point runs on that device.
+ *
+ * Blob layout (the exchange format between uw_encode and the device kernels):
+ * a 256-byte header followed by 256-byte aligned sections, all little-endian.
+ *   header: "UWB1", u32 version=1, u32 header_bytes=256, u32 flags (bit 0 =
+ *   plain), i64 rows, i64 cols, u32 K, u32 L, u32 G, u32 n_blocks,
+ *   u64 n_raw_groups, u64 total_bytes, u32 crc32 (of bytes [256,total)),
+ *   u32 max block stream bytes, u8 palette[32], u8 code_len[32], then u64
+ *   offsets: start_word, first_raw, raw_bits, lane_bits, stream (+size),
+ *   raw (+size), sm (+size), plain (+size).
+ *   A group is 64 consecutive weights of the row-major matrix; block b holds
+ *   groups [b*G, min((b+1)*G, rows*cols/64)); lane l of a block owns weight
+ *   64*j + l of each of the block's groups j.
+ *   start_word u32[n_blocks+1]: first 32-bit word of each block's stream;
+ *   first_raw u32[n_blocks+1]: raw groups before each block;
+ *   raw_bits u32[n_blocks*ceil(G/32)]: bit j = group j of the block is raw;
+ *   lane_bits u16[n_blocks*64]: bits in each lane's code stream; a lane's
+ *   stream starts at the exclusive prefix sum of the block's lane_bits;
+ *   stream: per block, the 64 lane streams concatenated in lane order, codes
+ *   of canonical (RFC 1951 3.2.2) length-limited Huffman codes over the
+ *   palette, bit-reversed and packed LSB-first, zero padded to 16 bytes;
+ *   raw: 64 exponent bytes per raw group;
+ *   sm: per block ceil(G_b/16) tiles of 1024 bytes, byte (j>>4)*1024 +
+ *   l*16 + (j&15) = sign+mantissa byte ((s<<7)|m) of weight 64*j + l;
+ *   plain (plain mode): the bf16 bits, row-major.
+ */
+#ifndef UW_H
+#define UW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UW_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+  UW_OK = 0,
+  UW_ERR_INVALID = -1,     /* a null/misaligned pointer, bad size or option      */
+  UW_ERR_FORMAT = -2,      /* the blob is not a valid UWB1 blob                  */
+  UW_ERR_NOSPACE = -3,     /* an output or workspace buffer is too small         */
+  UW_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed         */
+  UW_ERR_UNSUPPORTED = -5  /* valid request that this build cannot run           */
+} uw_status;
+
+typedef enum { UW_F32 = 0, UW_BF16 = 1 } uw_dtype;
+
+/* Execution strategies for uw_gemm_fused ("four pipelines" paragraph: the
+ * runtime picks one per matrix and batch size). */
+typedef enum {
+  UW_VARIANT_AUTO = 0,             /* the tuned plan for this batch, else a heuristic   */
+  UW_VARIANT_FUSED = 1,            /* decode on chip, multiply on VALU, no bf16 in HBM  */
+  UW_VARIANT_DECOMPRESS_GEMM = 2,  /* uw_decompress into the workspace, then bf16 GEMM  */
+  UW_VARIANT_COUNT = 3
+} uw_variant;
+
+#define UW_ENC_NO_PLAIN 1u /* never fall back to plain mode unless nothing can be coded */
+
+typedef struct {
+  int32_t K;      /* palette size, 1..32; 0 = 16 */
+  int32_t L;      /* maximum code length, 1..12 and K <= 2^L; 0 = 6 */
+  int32_t G;      /* groups of 64 weights per block: multiple of 16 in [16,1024]; 0 = automatic */
+  uint32_t flags; /* UW_ENC_* */
+} uw_encode_opts;
+
+typedef struct {
+  int64_t rows, cols;
+  int32_t K, L, G, plain;
+  int64_t n_blocks, n_raw_groups;
+  uint64_t total_bytes;
+  uint32_t max_block_stream_bytes;
+  uint8_t palette[32];
+  uint8_t code_len[32];
+  double ratio;           /* total_bytes / (2*rows*cols) */
+  double bits_per_weight; /* 8*total_bytes / (rows*cols) */
+} uw_info;
+
+typedef struct {
+  int64_t batch;
+  int32_t variant;                        /* the chosen uw_variant */
+  float time_us;                          /* its measured time per call */
+  float candidate_us[UW_VARIANT_COUNT];   /* per variant, < 0 = not measured */
+} uw_plan;
+
+typedef struct uw_matrix uw_matrix;
+
+/* Library version (UW_VERSION). */
+int uw_version(void);
+
+/* Static text for a status code. */
+const char* uw_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* uw_last_error(void);
+
+/*
+ * uw_encode (host) - compress a bf16 matrix into a blob.
+ * Exponent histogram and top-K palette (exponent-redundancy paragraph),
+ * raw 64-weight groups (rare-exponents paragraph), package-merge code
+ * lengths <= L and canonical codes (Huffman paragraph), blocks of G groups
+ * with one code stream per wavefront lane.
+ *   w_bf16   host, rows*cols bf16 bit patterns, row-major, not modified.
+ *   rows>=1, cols a positive multiple of 64.
+ *   opts     may be NULL (defaults above).
+ *   out      host buffer of *out_size bytes owned by the caller, or NULL to
+ *            query: then *out_size receives the exact size and UW_OK returns.
+ * The output is deterministic.  The coded form is replaced by plain mode when
+ * it would not be smaller (unless UW_ENC_NO_PLAIN).
+ * Errors: UW_ERR_INVALID (null pointers, bad shape or options),
+ *         UW_ERR_NOSPACE (*out_size too small; *out_size set to the need).
+ */
+int uw_encode(const uint16_t* w_bf16, int64_t rows, int64_t cols, const uw_encode_opts* opts,
+              void* out, size_t* out_size);
+
+/*
+ * uw_blob_info (host) - validate a blob (header, section bounds, CRC32, code
+ * lengths forming a prefix code, per-block stream sizes) and describe it.
+ * Errors: UW_ERR_INVALID (null), UW_ERR_FORMAT (anything inconsistent).
+ */
+int uw_blob_info(const void* blob, size_t n, uw_info* info);
+
+/*
+ * uw_matrix_create (host) - bind a handle to a blob already copied to device
+ * memory.  host_blob/n is validated as by uw_blob_info; d_blob must hold the
+ * same n bytes on the current device, 256-byte aligned.  The handle does not
+ * own d_blob: the caller keeps it alive and unchanged until uw_matrix_destroy.
+ * The handle keeps a copy of the header and the decode tables derived from
+ * the code lengths, plus a per-batch plan cache (internally locked).
+ * Errors: UW_ERR_INVALID, UW_ERR_FORMAT, UW_ERR_HIP (no current device).
+ */
+int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_matrix** out);
+
+/* Release a handle (NULL is ignored).  Work already queued keeps running. */
+void uw_matrix_destroy(uw_matrix* m);
+
+/*
+ * uw_decompress (device) - the "full decode" pipeline's preprocessing:
+ * writes the original bf16 bits, W[r][c] at d_out[r*ld_out + c].
+ *   d_out   device, 16-byte aligned, rows*ld_out elements; ld_out >= cols and
+ *           a multiple of 8.  Bit-exact (NaN payloads and subnormals kept).
+ * Errors: UW_ERR_INVALID, UW_ERR_HIP.
+ */
+int uw_decompress(const uw_matrix* m, uint16_t* d_out, int64_t ld_out, void* stream);
+
+/*
+ * uw_gemv_fused (device) - y = W x with the decode fused into the product
+ * (reconstructive-matmul paragraph; batch-1 decode reads every weight once).
+ *   d_x  device, cols elements of xt (UW_F32 or UW_BF16), 4-byte aligned.
+ *   d_y  device, rows elements of yt (UW_F32 or UW_BF16 rounded to nearest
+ *        even), 4-byte aligned.  fp32 accumulation.
+ * Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED (cols too large for the on-chip
+ *         copy of x: more than 32768 for bf16 x, 16384 for fp32 x), UW_ERR_HIP.
+ */
+int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt, void* stream);
+
+/*
+ * uw_gemm_fused (device) - Y = X W^T for a small batch.
+ *   d_X  device, batch rows of cols elements of xt, row stride ldx >= cols.
+ *   d_Y  device, batch rows of rows elements of yt, row stride ldy >= rows.
+ *   variant  a uw_variant; UW_VARIANT_AUTO uses the plan uw_autotune stored
+ *            for this batch, else a heuristic.
+ *   d_ws/ws_bytes  caller-owned device workspace (uw_workspace_size bytes for
+ *            the chosen variant; may be NULL/0 for UW_VARIANT_FUSED).
+ * batch == 0 is a no-op.  fp32 accumulation.
+ * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE (workspace), UW_ERR_UNSUPPORTED, UW_ERR_HIP.
+ */
+int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ldx, int xt,
+                  void* d_Y, int64_t ldy, int yt, int variant, void* d_ws, size_t ws_bytes,
+                  void* stream);
+
+/* Workspace bytes uw_gemm_fused needs for the given variant and batch
+ * (UW_VARIANT_AUTO: the largest any candidate may need). */
+size_t uw_workspace_size(const uw_matrix* m, int64_t batch, int variant);
+
+/*
+ * uw_autotune (device, BLOCKING) - autotuner paragraph: time every applicable
+ * variant for this matrix and batch on the given stream with HIP events (bf16
+ * X and Y; inputs and outputs inside the workspace) and store the fastest in
+ * the handle's plan cache; *out (may be NULL) gets a copy.
+ *   d_ws/ws_bytes  device workspace of at least
+ *                  uw_workspace_size(m, batch, UW_VARIANT_AUTO) +
+ *                  uw_autotune_scratch_size(m, batch) bytes.
+ * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE, UW_ERR_HIP.
+ */
+int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* stream, uw_plan* out);
+
+/* Extra workspace uw_autotune uses for its own X and Y. */
+size_t uw_autotune_scratch_size(const uw_matrix* m, int64_t batch);
+
+/* The stored plan for a batch; UW_ERR_INVALID if none. */
+int uw_get_plan(const uw_matrix* m, int64_t batch, uw_plan* out);
+
+/*
+ * uw_bf16_gemm (device) - Y = X W^T over an uncompressed bf16 matrix: the
+ * multiply of the "full decode" pipeline and the uncompressed comparator.
+ *   d_W  device, rows x cols bf16, row stride ldw >= cols (multiple of 8),
+ *        16-byte aligned.  Other arguments as for uw_gemm_fused.
+ * Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED, UW_ERR_HIP.
+ */
+int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, const void* d_X,
+                 int64_t batch, int64_t ldx, int xt, void* d_Y, int64_t ldy, int yt, void* stream);
+
+/*
+ * uw_read_probe (device) - streaming read of `bytes` bytes (multiple of 16,
+ * 16-byte aligned) that writes one checksum word per workgroup into d_sink
+ * (uw_read_probe_sink_size bytes): the fastest sustainable read rate the
+ * fused kernels are measured against (the Apple-silicon page's section on
+ * the limits of further optimisation measures kernels against the fastest
+ * weight-read rate for their access pattern).
+ * Errors: UW_ERR_INVALID, UW_ERR_HIP.
+ */
+int uw_read_probe(const void* d_src, size_t bytes, void* d_sink, void* stream);
+size_t uw_read_probe_sink_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UW_H */
