@@ -141,8 +141,19 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
     d.n_sym = int32_t(h.K);
     for (uint32_t i = 0; i < h.K; ++i)
       d.sym[i] = rev[i] | (uint32_t(h.code_len[i]) << 16) | (uint32_t(h.palette[i]) << 24);
-    // front pad + stream + back pad (window reads run one word past a lane's end)
-    d.stage_words = int32_t(h.max_block_stream_bytes / 4 + 8);
+    // stage buffer of one wave: 4 pad words, the block's stream, 4 pad words
+    // (window reads run one word past a lane's end), then the block's raw
+    // exponent bytes (64 per raw group)
+    const uint8_t* hb = static_cast<const uint8_t*>(host_blob);
+    uint32_t max_raw = 0;
+    for (uint32_t blk = 0; blk < h.n_blocks; ++blk) {
+      uint32_t a, z;
+      std::memcpy(&a, hb + h.off_first_raw + 4 * blk, 4);
+      std::memcpy(&z, hb + h.off_first_raw + 4 * (blk + 1), 4);
+      max_raw = std::max(max_raw, z - a);
+    }
+    d.stage_raw_word = int32_t(4 + h.max_block_stream_bytes / 4 + 4);
+    d.stage_words = d.stage_raw_word + int32_t(max_raw * 16);
     // a work unit covers whole rows: lcm(G, groups per row) groups
     const int64_t lcm = int64_t(h.G) / gcd64(h.G, d.gpr) * d.gpr;
     d.unit_blocks = int32_t(lcm / h.G);

@@ -66,7 +66,8 @@ struct DevMatrix {
   int64_t n_groups;
   int32_t G, n_blocks, rb_words, gpr;  // gpr = groups per row = cols/64
   int32_t L, n_sym;
-  int32_t stage_words;                 // LDS words of one wave's stream buffer
+  int32_t stage_words;                 // LDS words of one wave's stage buffer (stream + raw bytes)
+  int32_t stage_raw_word;              // word offset of the raw-byte area inside the stage buffer
   int32_t unit_blocks;                 // blocks per work unit (a unit covers whole rows)
   int32_t n_units;
   uint32_t sym[32];                    // rev code | len << 16 | exponent << 24

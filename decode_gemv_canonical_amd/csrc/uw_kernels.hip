@@ -47,12 +47,10 @@ constexpr int kTableWords = 4096;   // pair table (or 2^L single table)
 constexpr int kT1Words = 64;        // single-code table for L <= 6, used to build the pair table
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kTransposeWords = 512;  // 16 groups x 64 lanes x bf16
+constexpr int kRing = 3;              // sm tiles (1 KB each) in flight per wave
+constexpr int kRingWords = kRing * 256;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ inline uint32_t lds_u32(const uint32_t* base, uint32_t byte_addr) {
-  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_addr);
-}
 
 __device__ inline float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ inline uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -134,51 +132,119 @@ __device__ void build_tables(const DevMatrix& d, uint32_t* T, uint32_t* T1) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-lane cursor over the staged stream.
+// LDS is addressed with absolute byte addresses: the kernels that decode use
+// only dynamic LDS, which starts at address 0.  Layout (bytes):
+//   [0, 16384)        decode table (pair table, or the 2^L single table)
+//   [16384, 16640)    single table for L <= 6 (used to build the pair table)
+//   [16640, ...)      kernel-specific area (x for products), then one stage
+//                     buffer per wave: 16 pad bytes, the block's stream, 16 pad
+//                     bytes, the block's raw exponent bytes.
+constexpr uint32_t kT1Addr = kTableWords * 4;
+constexpr uint32_t kAreaAddr = (kTableWords + kT1Words) * 4;
+
+typedef __attribute__((address_space(3))) uint32_t lds_word;
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_quad;
+typedef __attribute__((address_space(3))) uint16_t lds_half;
+
+__device__ inline uint32_t ld32(uint32_t addr) { return *reinterpret_cast<const lds_word*>(size_t(addr)); }
+__device__ inline void st32(uint32_t addr, uint32_t v) { *reinterpret_cast<lds_word*>(size_t(addr)) = v; }
+__device__ inline uint32_t ld8(uint32_t addr) { return *reinterpret_cast<const lds_byte*>(size_t(addr)); }
+__device__ inline uint4 ld128(uint32_t addr) {
+  const u32x4 v = *reinterpret_cast<const lds_quad*>(size_t(addr));
+  return uint4{v.x, v.y, v.z, v.w};
+}
+__device__ inline void st128(uint32_t addr, uint4 v) {
+  *reinterpret_cast<lds_quad*>(size_t(addr)) = u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ inline void st16(uint32_t addr, uint32_t v) { *reinterpret_cast<lds_half*>(size_t(addr)) = uint16_t(v); }
+
+// Per-lane cursor over the staged stream: a 64-bit window (w0, w1) plus the
+// next stream word w2 (loaded one refill ahead, so a refill never waits on
+// LDS), the LDS byte address of w0 and the bit offset qm of (next code - 2)
+// inside the window.  Between refills qm may carry exponent bits above bit 6
+// (see the pair-table layout); its low 7 bits are exact.
 struct Cursor {
-  uint32_t w0, w1;  // window words
-  uint32_t widx;    // word index (in the wave's stage buffer) of w0
-  uint32_t qm;      // bit offset of (next code - 2) in the window; bits >= 7 may hold garbage
+  uint32_t w0, w1, w2, addr, qm;
 };
 
-__device__ inline void cursor_reload(Cursor& c, const uint32_t* stage) {
-  c.w0 = stage[c.widx];
-  c.w1 = stage[c.widx + 1];
+__device__ inline void cursor_reload(Cursor& c) {
+  c.w0 = ld32(c.addr);
+  c.w1 = ld32(c.addr + 4);
+  c.w2 = ld32(c.addr + 8);
 }
 
-__device__ inline void cursor_refill(Cursor& c, const uint32_t* stage) {
-  c.widx += (c.qm >> 5) & 1u;
+// At most 32 bits were consumed since the last refill (qm < 64): slide the
+// window by one word if qm passed 32, and fetch the word after the window.
+__device__ inline void cursor_refill(Cursor& c) {
+  const uint32_t adv = c.qm & 32u;
+  c.addr += adv >> 3;
+  c.w0 = adv ? c.w1 : c.w0;
+  c.w1 = adv ? c.w2 : c.w1;
   c.qm &= 31u;
-  cursor_reload(c, stage);
+  c.w2 = ld32(c.addr + 8);
 }
 
-__device__ inline uint32_t cursor_peek(const Cursor& c) {
-  return __builtin_amdgcn_alignbit(c.w1, c.w0, c.qm);
+__device__ inline uint32_t cursor_peek(const Cursor& c) { return __builtin_amdgcn_alignbit(c.w1, c.w0, c.qm); }
+
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy n_quads 16-byte words from global memory to LDS with direct
+// global->LDS loads (no registers): lane l of each 64-quad chunk writes
+// dst + 16 * (chunk + l).  Completion is waited for with vmcnt.
+__device__ inline void copy_to_lds_async(const uint4* src, uint32_t dst, uint32_t n_quads, int lane) {
+  for (uint32_t c = 0; c < n_quads; c += kWave) {
+    if (c + lane < n_quads)
+      __builtin_amdgcn_global_load_lds(
+          (global_void*)(const_cast<uint4*>(src + c + lane)),
+          reinterpret_cast<lds_void*>(size_t(dst + 16 * c)), 16, 0, 0);
+  }
 }
 
-// Stage block `blk`'s stream into this wave's buffer and place the lane's cursor.
-__device__ inline void stage_block(const DevMatrix& d, int blk, uint32_t* stage, int lane, Cursor& c) {
-  const uint32_t w_begin = d.start_word[blk];
-  const uint32_t n_words = d.start_word[blk + 1] - w_begin;
-  const uint4* src = reinterpret_cast<const uint4*>(d.stream + w_begin);
-  uint4* dst = reinterpret_cast<uint4*>(stage + kPadWords);
-  for (uint32_t i = lane; i < n_words / 4; i += kWave) dst[i] = src[i];
-  const uint32_t lb = d.lane_bits[int64_t(blk) * kWave + lane];
-  const uint32_t start = wave_exclusive_scan(lb, lane);
+// Issue the loads of block `blk`: its stream words and raw exponent bytes go
+// into this wave's stage buffer; the lane bit count and the raw bitmap word
+// of this lane come back in registers.
+struct BlockHead {
+  uint32_t lane_bits;
+  uint32_t raw_word;  // lane w holds raw-bitmap word w of the block
+};
+
+// Block-table words read by the whole wave go through the constant address
+// space so they become scalar loads (their own counter, no wait on the
+// vector loads in flight).
+typedef __attribute__((address_space(4))) const uint32_t const_word;
+__device__ inline uint32_t scalar_word(const uint32_t* p, int64_t i) {
+  return ((const const_word*)(p))[i];
+}
+
+__device__ inline BlockHead issue_head_loads(const DevMatrix& d, int blk, int lane) {
+  BlockHead h;
+  h.lane_bits = d.lane_bits[int64_t(blk) * kWave + lane];
+  h.raw_word = lane < d.rb_words ? d.raw_bits[int64_t(blk) * d.rb_words + lane] : 0u;
+  return h;
+}
+
+__device__ inline void issue_stage_loads(const DevMatrix& d, int blk, uint32_t stage, int lane) {
+  const uint32_t w_begin = scalar_word(d.start_word, blk);
+  const uint32_t n_quads = (scalar_word(d.start_word, blk + 1) - w_begin) / 4;
+  const uint32_t r0 = scalar_word(d.first_raw, blk), r1 = scalar_word(d.first_raw, blk + 1);
+  copy_to_lds_async(reinterpret_cast<const uint4*>(d.stream + w_begin), stage + 16, n_quads, lane);
+  copy_to_lds_async(reinterpret_cast<const uint4*>(d.raw + int64_t(r0) * 64), stage + d.stage_raw_word * 4,
+                    (r1 - r0) * 4, lane);
+}
+
+// After the block's loads: wait for them, then place the lane's cursor at the
+// exclusive prefix sum of the lane bit counts.
+__device__ inline void start_cursor(const BlockHead& h, uint32_t stage, int lane, Cursor& c) {
+  __builtin_amdgcn_s_waitcnt(0);  // every load of the block, direct-to-LDS ones included
+  const uint32_t start = wave_exclusive_scan(h.lane_bits, lane);
   wave_lds_fence();
-  const uint32_t bit = kPadWords * 32 + start - 2;
-  c.widx = bit >> 5;
+  const uint32_t bit = 4 * 32 + start - 2;
+  c.addr = stage + (bit >> 5) * 4;
   c.qm = bit & 31;
-  cursor_reload(c, stage);
-}
-
-// One code, from either table (the pair table's first half or the single table).
-template <bool PAIR>
-__device__ inline uint32_t decode_one(Cursor& c, const uint32_t* T, const uint32_t* stage, uint32_t idx_mask) {
-  const uint32_t e = lds_u32(T, cursor_peek(c) & idx_mask);
-  c.qm += PAIR ? ((e >> 16) & 0xF) : (e & 0xF);
-  cursor_refill(c, stage);
-  return e;  // exponent at bits 7..14
+  cursor_reload(c);
 }
 
 // Replicated sign+mantissa bytes of groups (2k, 2k+1) of a 16-group tile.
@@ -192,110 +258,217 @@ __device__ inline uint32_t sm_byte(const uint4& v, int j) {
   return (w >> (8 * (j & 3))) & 0xFF;
 }
 
-// Two bf16 weights in one register: bits of sign+mantissa from S, exponents from E.
-__device__ inline uint32_t merge_pair(uint32_t S, uint32_t E) {
-  return (S & 0x807F807Fu) | (E & 0x7F807F80u);
-}
+// Two bf16 weights in one register: sign+mantissa bits from S, exponents from E.
+__device__ inline uint32_t merge_pair(uint32_t S, uint32_t E) { return (S & 0x807F807Fu) | (E & 0x7F807F80u); }
 
 __device__ inline uint32_t merge_one(uint32_t sm, uint32_t E) {
   return ((sm & 0x80u) << 8) | (E & 0x7F80u) | (sm & 0x7Fu);
 }
 
-__device__ inline uint4 load_sm_tile(const DevMatrix& d, int blk, int t, int lane) {
-  const uint8_t* p = d.sm + int64_t(blk) * d.G * 64 + int64_t(t) * 1024 + lane * 16;
-  return *reinterpret_cast<const uint4*>(p);
+// sm tile t of a block (1 KB: 16 groups x 64 lanes) into ring slot `slot`.
+__device__ inline void load_sm_tile_to_lds(const uint4* sm_blk, int t, uint32_t ring, int slot, int lane) {
+  __builtin_amdgcn_global_load_lds((global_void*)(const_cast<uint4*>(sm_blk + t * 64 + lane)),
+                                   (lds_void*)(size_t(ring + slot * 1024)), 16, 0, 0);
 }
 
-__device__ inline uint32_t raw_mask16(const DevMatrix& d, int blk, int j0) {
-  const uint32_t w = d.raw_bits[int64_t(blk) * d.rb_words + (j0 >> 5)];
+// Wait until at most kRing-1 vector-memory operations are in flight.  The
+// decode loop issues no other vector-memory operation, so this means the
+// oldest ring load has landed in LDS.
+__device__ inline void wait_vmcnt_ring() {
+  static_assert(kRing - 1 < 16, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRing - 1) : "memory");
+}
+
+// Raw flags of the 16 groups of the tile starting at group j0 (wave-uniform).
+__device__ inline uint32_t raw_mask16(uint32_t raw_word, int j0) {
+  const uint32_t w = __builtin_amdgcn_readlane(raw_word, j0 >> 5);
   return (w >> (j0 & 31)) & 0xFFFFu;
 }
 
+// One code from the table: returns the entry (exponent in bits 7..14) and
+// advances the cursor (qm) and the running peek p by the code's length.
+template <bool PAIR>
+__device__ inline uint32_t take_single(Cursor& c, uint32_t& p, uint32_t mask) {
+  const uint32_t e = ld32(p & mask);
+  if (PAIR) {
+    const uint32_t n = (e >> 16) & 0xFu;
+    p >>= n;
+    c.qm += n;
+  } else {
+    p >>= (e & 31u);  // length in bits 0..3, bit 4 clear
+    c.qm += e;        // exponent bits land above bit 6
+  }
+  return e;
+}
+
+// Decode one block and hand the weights to `sink`:
+//   sink.tile_begin(row0, c0)   before a tile that lies inside one row, starts
+//                               at an even column group and is complete;
+//   sink.pair(k, D)             D = weights of groups (2k, 2k+1) of that tile;
+//   sink.single(jj, row, cg, w) one weight of group jj of any other tile;
+//   sink.tile_end(t, nt)        after every tile.
+// sm tiles stream through a kRing-slot LDS ring filled by direct-to-LDS
+// loads, so kRing KB per wave are in flight and the waits are explicit.
+template <bool PAIR, class Sink>
+__device__ __forceinline__ void decode_block(const DevMatrix& d, int blk, uint32_t stage, uint32_t ring, int lane,
+                                             Sink& sink) {
+  // per-lane table words, the first sm tiles, then the stream and raw bytes;
+  // one wait covers them all
+  const int64_t g_first = int64_t(blk) * d.G;
+  const int gb = int(std::min<int64_t>(d.G, d.n_groups - g_first));
+  const int ntiles = (gb + 15) / 16;
+  const BlockHead head = issue_head_loads(d, blk, lane);
+  const uint4* sm_blk = reinterpret_cast<const uint4*>(d.sm + int64_t(blk) * d.G * 64);
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) load_sm_tile_to_lds(sm_blk, std::min(i, ntiles - 1), ring, i, lane);
+  issue_stage_loads(d, blk, stage, lane);
+  Cursor c;
+  start_cursor(head, stage, lane, c);
+  const uint32_t raw_area = stage + d.stage_raw_word * 4;
+  const uint32_t pmask = PAIR ? 0x3FFCu : (((1u << d.L) - 1u) << 2);
+  int64_t row0 = g_first / d.gpr;
+  int c0 = int(g_first - row0 * d.gpr);
+  uint32_t raw_rank = 0;
+  for (int t = 0; t < ntiles; ++t) {
+    {
+      {
+        // exactly kRing-1 ring loads were issued after tile t's
+        wait_vmcnt_ring();
+        const int slot = t % kRing;
+        const uint4 cur = ld128(ring + slot * 1024 + lane * 16);
+        const int j0 = t * 16;
+        const int nt = std::min(16, gb - j0);
+        const uint32_t rmask = raw_mask16(head.raw_word, j0);
+        if (nt == 16 && c0 + 16 <= d.gpr && (c0 & 1) == 0) {
+          sink.tile_begin(row0, c0);
+          uint32_t p = cursor_peek(c);
+          if (PAIR && rmask == 0) {
+#pragma unroll
+            for (int k = 0; k < 8; k += 2) {
+              const uint32_t e1 = ld32(p & 0x3FFCu);
+              p >>= (e1 & 31u);
+              const uint32_t e2 = ld32(p & 0x3FFCu);
+              c.qm += e1 + e2;
+              cursor_refill(c);
+              p = cursor_peek(c);
+              sink.pair(k, merge_pair(sm_pair(cur, k), e1));
+              sink.pair(k + 1, merge_pair(sm_pair(cur, k + 1), e2));
+            }
+          } else {
+            uint32_t rank = raw_rank;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const uint32_t two = (rmask >> (2 * k)) & 3u;
+              uint32_t E;
+              if (PAIR && two == 0) {
+                E = ld32(p & 0x3FFCu);
+                p >>= (E & 31u);
+                c.qm += E;
+              } else {
+                uint32_t ea, eb;
+                if (two & 1u) ea = ld8(raw_area + (rank++) * 64 + lane) << 7;
+                else ea = take_single<PAIR>(c, p, pmask) & 0x7F80u;
+                if (two & 2u) eb = ld8(raw_area + (rank++) * 64 + lane) << 23;
+                else eb = (take_single<PAIR>(c, p, pmask) & 0x7F80u) << 16;
+                E = ea | eb;
+              }
+              if (!PAIR || (k & 1)) {
+                cursor_refill(c);
+                p = cursor_peek(c);
+              }
+              sink.pair(k, merge_pair(sm_pair(cur, k), E));
+            }
+          }
+        } else {
+          // tile crossing a row end, starting at an odd column group, or partial
+          int64_t row = row0;
+          int cg = c0;
+          uint32_t rank = raw_rank;
+          for (int jj = 0; jj < nt; ++jj, ++cg) {
+            if (cg >= d.gpr) {
+              cg -= d.gpr;
+              ++row;
+            }
+            uint32_t E;
+            if ((rmask >> jj) & 1u) {
+              E = ld8(raw_area + (rank++) * 64 + lane) << 7;
+            } else {
+              uint32_t p = cursor_peek(c);
+              E = take_single<PAIR>(c, p, pmask);
+              cursor_refill(c);
+            }
+            sink.single(jj, row, cg, merge_one(sm_byte(cur, jj), E));
+          }
+        }
+        raw_rank += __builtin_popcount(rmask);
+        sink.tile_end(t, nt);
+        // refill the consumed slot with tile t+kRing; one load per tile
+        // (index clamped near the end) keeps the count of loads in flight fixed
+        load_sm_tile_to_lds(sm_blk, std::min(t + kRing, ntiles - 1), ring, slot, lane);
+        c0 += 16;
+        while (c0 >= d.gpr) {
+          c0 -= d.gpr;
+          ++row0;
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Decompress: every weight goes through a per-wave LDS tile [16][64] bf16 so
-// that the stores are 2 x 16 bytes per lane of consecutive columns.
+// Decompress: weights pass through a per-wave LDS tile [16][64] bf16 so that
+// each lane stores 2 x 16 bytes of consecutive columns.
+struct DecompressSink {
+  const DevMatrix& d;
+  uint16_t* out;
+  int64_t ld_out;
+  uint32_t tile;    // LDS byte address of the transpose tile
+  int lane;
+  int64_t trow;     // (row, col) of the current tile's first weight
+  int64_t tcol;
+  __device__ void tile_begin(int64_t, int) {}
+  __device__ void pair(int k, uint32_t D) {
+    st16(tile + ((2 * k) * kWave + lane) * 2, D);
+    st16(tile + ((2 * k + 1) * kWave + lane) * 2, D >> 16);
+  }
+  __device__ void single(int jj, int64_t, int, uint32_t w) { st16(tile + (jj * kWave + lane) * 2, w); }
+  __device__ void tile_end(int, int nt) {
+    wave_lds_fence();
+    if (lane * 16 < nt * 64) {
+      const uint4 a = ld128(tile + lane * 32), b = ld128(tile + lane * 32 + 16);
+      int64_t row = trow, col = tcol + lane * 16;
+      while (col >= d.cols) {
+        col -= d.cols;
+        ++row;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(out + row * ld_out + col);
+      dst[0] = a;
+      dst[1] = b;
+    }
+    wave_lds_fence();
+    tcol += 1024;
+    while (tcol >= d.cols) {
+      tcol -= d.cols;
+      ++trow;
+    }
+  }
+};
+
 template <bool PAIR>
 __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t* __restrict__ out, int64_t ld_out) {
   extern __shared__ uint32_t lds[];
-  uint32_t* T = lds;
-  uint32_t* T1 = lds + kTableWords;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int waves = blockDim.x / kWave;
-  uint32_t* stage = lds + kTableWords + kT1Words + wave * (d.stage_words + kTransposeWords);
-  uint16_t* tileh = reinterpret_cast<uint16_t*>(stage + d.stage_words);
-  build_tables<PAIR>(d, T, T1);
+  const uint32_t stage = kAreaAddr + wave * (d.stage_words + kRingWords + kTransposeWords) * 4;
+  const uint32_t ring = stage + d.stage_words * 4;
+  const uint32_t tile = ring + kRingWords * 4;
+  build_tables<PAIR>(d, lds, lds + kTableWords);
   __syncthreads();
-  const uint32_t pair_mask = 0x3FFCu;
-  const uint32_t single_mask = ((1u << d.L) - 1u) << 2;
   const int total_waves = gridDim.x * waves;
   for (int blk = blockIdx.x * waves + wave; blk < d.n_blocks; blk += total_waves) {
-    Cursor c;
-    stage_block(d, blk, stage, lane, c);
-    const int64_t g_first = int64_t(blk) * d.G;
-    const int gb = int(std::min<int64_t>(d.G, d.n_groups - g_first));
-    const int ntiles = (gb + 15) / 16;
-    const uint32_t first_raw = d.first_raw[blk];
-    uint32_t raw_rank = 0;
-    // first weight of the current tile as (row, column); advanced without divisions
-    int64_t trow = (g_first * 64) / d.cols;
-    int64_t tcol = g_first * 64 - trow * d.cols;
-    uint4 smv = load_sm_tile(d, blk, 0, lane);
-    for (int t = 0; t < ntiles; ++t) {
-      const uint4 cur = smv;
-      if (t + 1 < ntiles) smv = load_sm_tile(d, blk, t + 1, lane);
-      const int j0 = t * 16;
-      const int nt = std::min(16, gb - j0);
-      const uint32_t rmask = raw_mask16(d, blk, j0);
-      if (PAIR && nt == 16 && rmask == 0) {
-#pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-          const uint32_t p = cursor_peek(c);
-          const uint32_t e1 = lds_u32(T, p & pair_mask);
-          const uint32_t p2 = p >> (e1 & 31u);
-          const uint32_t e2 = lds_u32(T, p2 & pair_mask);
-          c.qm += e1 + e2;
-          cursor_refill(c, stage);
-          const uint32_t D1 = merge_pair(sm_pair(cur, k), e1);
-          const uint32_t D2 = merge_pair(sm_pair(cur, k + 1), e2);
-          tileh[(2 * k) * kWave + lane] = uint16_t(D1);
-          tileh[(2 * k + 1) * kWave + lane] = uint16_t(D1 >> 16);
-          tileh[(2 * k + 2) * kWave + lane] = uint16_t(D2);
-          tileh[(2 * k + 3) * kWave + lane] = uint16_t(D2 >> 16);
-        }
-      } else {
-        for (int jj = 0; jj < nt; ++jj) {
-          uint32_t E;
-          if ((rmask >> jj) & 1u) {
-            E = uint32_t(d.raw[int64_t(first_raw + raw_rank) * 64 + lane]) << 7;
-            raw_rank++;
-          } else {
-            E = PAIR ? decode_one<true>(c, T, stage, pair_mask) : decode_one<false>(c, T, stage, single_mask);
-          }
-          tileh[jj * kWave + lane] = uint16_t(merge_one(sm_byte(cur, jj), E));
-        }
-      }
-      wave_lds_fence();
-      // lane l writes flattened weights [16 l, 16 l + 16) of the tile
-      if (lane * 16 < nt * 64) {
-        const uint4* src = reinterpret_cast<const uint4*>(tileh + lane * 16);
-        const uint4 a = src[0], b = src[1];
-        int64_t row = trow;
-        int64_t col = tcol + lane * 16;
-        while (col >= d.cols) {
-          col -= d.cols;
-          ++row;
-        }
-        uint4* dst = reinterpret_cast<uint4*>(out + row * ld_out + col);
-        dst[0] = a;
-        dst[1] = b;
-      }
-      wave_lds_fence();
-      tcol += 1024;
-      while (tcol >= d.cols) {
-        tcol -= d.cols;
-        ++trow;
-      }
-    }
+    const int64_t flat = int64_t(blk) * d.G * 64;
+    DecompressSink sink{d, out, ld_out, tile, lane, flat / d.cols, flat % d.cols};
+    decode_block<PAIR>(d, blk, stage, ring, lane, sink);
   }
 }
 
@@ -312,8 +485,9 @@ __global__ void copy_plain_kernel(const uint16_t* __restrict__ src, int64_t rows
 
 // ---------------------------------------------------------------------------
 // Fused product Y[b, n] = sum_k X[b, k] W[n, k] for NBP batch columns per pass.
-// X lives in LDS: bf16 as pairs xp[(p*64 + l)*NBP + b] = X[b][128p+l] | X[b][128p+64+l] << 16
-// (groups 2p, 2p+1 of a row for lane l), fp32 as x[(k)*NBP + b].
+// X lives in LDS at kAreaAddr: bf16 as pairs, word (p*64 + l)*NBP + b =
+// X[b][128p + l] | X[b][128p + 64 + l] << 16 (column groups 2p and 2p+1 at
+// lane l); fp32 as word k*NBP + b = X[b][k].
 template <int NBP, bool XF32>
 __device__ inline void load_x(const DevMatrix& d, const void* X, int64_t ldx, int nb_valid, uint32_t* xl) {
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -343,6 +517,117 @@ __device__ inline void load_x(const DevMatrix& d, const void* X, int64_t ldx, in
   }
 }
 
+template <int NBP, bool XF32, bool YBF16>
+struct ProductSink {
+  const DevMatrix& d;
+  uint32_t xaddr;  // LDS byte address of x
+  int lane;
+  int nb_valid;
+  void* Y;
+  int64_t ldy;
+  int64_t cur_row;
+  int c0;
+  uint32_t xtile;  // x address of this lane for column group c0
+  float acc[NBP];
+  // Finished rows are parked in registers (lane r holds the r-th finished row
+  // of the unit) and written with one store after the unit, so the decode
+  // loop issues no global stores.
+  float rows_done[NBP];
+  int64_t first_row;
+  int n_done;
+
+  __device__ void store_done() {
+#pragma unroll
+    for (int b = 0; b < NBP; ++b) {
+      if (lane < n_done && b < nb_valid) {
+        if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + first_row + lane] = f32_to_bf16(rows_done[b]);
+        else static_cast<float*>(Y)[b * ldy + first_row + lane] = rows_done[b];
+      }
+    }
+    first_row += n_done;
+    n_done = 0;
+  }
+  __device__ void flush() {
+#pragma unroll
+    for (int b = 0; b < NBP; ++b) {
+      const float s = wave_sum(acc[b]);
+      rows_done[b] = lane == n_done ? s : rows_done[b];
+      acc[b] = 0.f;
+    }
+    ++n_done;  // a unit covers at most 64 rows (checked on the host)
+  }
+  __device__ void to_row(int64_t row) {
+    if (row != cur_row) {
+      flush();
+      cur_row = row;
+    }
+  }
+  __device__ void tile_begin(int64_t row0, int c) {
+    to_row(row0);
+    c0 = c;
+    xtile = XF32 ? xaddr + ((uint32_t(c) * 64 + lane) * NBP) * 4 : xaddr + (((uint32_t(c) >> 1) * 64 + lane) * NBP) * 4;
+  }
+  // x of column group cg at this lane
+  __device__ float x_at(int cg, int b) const {
+    if (XF32) return bits_f32(ld32(xaddr + ((uint32_t(cg) * 64 + lane) * NBP + b) * 4));
+    const uint32_t v = ld32(xaddr + (((uint32_t(cg) >> 1) * 64 + lane) * NBP + b) * 4);
+    return bits_f32((cg & 1) ? (v & 0xFFFF0000u) : (v << 16));
+  }
+  // tile_begin() guarantees an even c0, so pair k reads x word (c0/2 + k)*64 + lane
+  __device__ void pair(int k, uint32_t D) {
+    if (XF32) {
+      const float wa = bits_f32(D << 16), wb = bits_f32(D & 0xFFFF0000u);
+      const uint32_t a = xtile + uint32_t(2 * k * 64 * NBP * 4);
+#pragma unroll
+      for (int b = 0; b < NBP; ++b) {
+        acc[b] = __builtin_fmaf(wa, bits_f32(ld32(a + 4 * b)), acc[b]);
+        acc[b] = __builtin_fmaf(wb, bits_f32(ld32(a + 64 * NBP * 4 + 4 * b)), acc[b]);
+      }
+    } else {
+      const uint32_t a = xtile + uint32_t(k * 64 * NBP * 4);
+#pragma unroll
+      for (int b = 0; b < NBP; ++b) acc[b] = dot2_bf16(D, ld32(a + 4 * b), acc[b]);
+    }
+  }
+  __device__ void single(int, int64_t row, int cg, uint32_t w) {
+    to_row(row);
+    const float wf = bits_f32(w << 16);
+#pragma unroll
+    for (int b = 0; b < NBP; ++b) acc[b] = __builtin_fmaf(wf, x_at(cg, b), acc[b]);
+  }
+  __device__ void tile_end(int, int) {}
+};
+
+// Wide batch chunks need more registers per lane: at most 8 waves per workgroup.
+constexpr int fused_max_threads(int nbp) { return nbp >= 4 ? 512 : 1024; }
+
+template <int NBP, bool XF32, bool PAIR, bool YBF16>
+__global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(DevMatrix d, const void* __restrict__ X, int64_t ldx,
+                                                             int nb_valid, void* __restrict__ Y, int64_t ldy) {
+  extern __shared__ uint32_t lds[];
+  const uint32_t x_words = XF32 ? uint32_t(d.cols) * NBP : ((uint32_t(d.gpr) + 1) / 2) * 64 * NBP;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int waves = blockDim.x / kWave;
+  const uint32_t stage = kAreaAddr + (x_words + wave * (d.stage_words + kRingWords)) * 4;
+  const uint32_t ring = stage + d.stage_words * 4;
+  build_tables<PAIR>(d, lds, lds + kTableWords);
+  load_x<NBP, XF32>(d, X, ldx, nb_valid, lds + kTableWords + kT1Words);
+  __syncthreads();
+  const int total_waves = gridDim.x * waves;
+  for (int unit = blockIdx.x * waves + wave; unit < d.n_units; unit += total_waves) {
+    const int blk_begin = unit * d.unit_blocks;
+    const int blk_end = std::min(d.n_blocks, blk_begin + d.unit_blocks);
+    const int64_t row_begin = (int64_t(blk_begin) * d.G) / d.gpr;
+    ProductSink<NBP, XF32, YBF16> sink{d, kAreaAddr, lane, nb_valid, Y, ldy, row_begin, 0, 0u, {}, {}, row_begin, 0};
+#pragma unroll
+    for (int b = 0; b < NBP; ++b) sink.acc[b] = sink.rows_done[b] = 0.f;
+    for (int blk = blk_begin; blk < blk_end; ++blk) decode_block<PAIR>(d, blk, stage, ring, lane, sink);
+    sink.flush();
+    sink.store_done();
+  }
+}
+
+// Wave-sum each accumulator and store it as row `row` of Y (lane 0 writes).
 template <int NBP, bool YBF16>
 __device__ inline void flush_row(float (&acc)[NBP], int64_t row, int nb_valid, void* Y, int64_t ldy, int lane) {
 #pragma unroll
@@ -356,123 +641,6 @@ __device__ inline void flush_row(float (&acc)[NBP], int64_t row, int nb_valid, v
   }
 }
 
-// x value(s) for column group c (of a row) at lane l, as fp32
-template <int NBP, bool XF32>
-__device__ inline float x_at(const uint32_t* xl, int c, int lane, int b) {
-  if (XF32) return bits_f32(xl[(int64_t(c) * 64 + lane) * NBP + b]);
-  const uint32_t v = xl[((int64_t(c) >> 1) * 64 + lane) * NBP + b];
-  return bits_f32((c & 1) ? (v & 0xFFFF0000u) : (v << 16));
-}
-
-template <int NBP, bool XF32>
-__device__ inline void accumulate_pair(float (&acc)[NBP], uint32_t D, const uint32_t* xl, int c, int lane) {
-  // D holds the weights of column groups c (low half) and c+1 (high half)
-  if (XF32) {
-    const float wa = bits_f32(D << 16), wb = bits_f32(D & 0xFFFF0000u);
-#pragma unroll
-    for (int b = 0; b < NBP; ++b) {
-      acc[b] = __builtin_fmaf(wa, bits_f32(xl[(int64_t(c) * 64 + lane) * NBP + b]), acc[b]);
-      acc[b] = __builtin_fmaf(wb, bits_f32(xl[(int64_t(c + 1) * 64 + lane) * NBP + b]), acc[b]);
-    }
-  } else {
-    const uint32_t* xp = xl + ((int64_t(c) >> 1) * 64 + lane) * NBP;
-#pragma unroll
-    for (int b = 0; b < NBP; ++b) acc[b] = dot2_bf16(D, xp[b], acc[b]);
-  }
-}
-
-template <int NBP, bool XF32, bool PAIR, bool YBF16>
-__global__ __launch_bounds__(1024) void fused_product_kernel(DevMatrix d, const void* __restrict__ X, int64_t ldx,
-                                                             int nb_valid, void* __restrict__ Y, int64_t ldy) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* T = lds;
-  uint32_t* T1 = lds + kTableWords;
-  uint32_t* xl = lds + kTableWords + kT1Words;
-  const int64_t x_words = XF32 ? d.cols * NBP : ((int64_t(d.gpr) + 1) / 2) * 64 * NBP;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int waves = blockDim.x / kWave;
-  uint32_t* stage = xl + x_words + wave * d.stage_words;
-  build_tables<PAIR>(d, T, T1);
-  load_x<NBP, XF32>(d, X, ldx, nb_valid, xl);
-  __syncthreads();
-  const uint32_t pair_mask = 0x3FFCu;
-  const uint32_t single_mask = ((1u << d.L) - 1u) << 2;
-  const int total_waves = gridDim.x * waves;
-  for (int unit = blockIdx.x * waves + wave; unit < d.n_units; unit += total_waves) {
-    const int blk_begin = unit * d.unit_blocks;
-    const int blk_end = std::min(d.n_blocks, blk_begin + d.unit_blocks);
-    float acc[NBP];
-#pragma unroll
-    for (int b = 0; b < NBP; ++b) acc[b] = 0.f;
-    int64_t cur_row = (int64_t(blk_begin) * d.G) / d.gpr;
-    for (int blk = blk_begin; blk < blk_end; ++blk) {
-      Cursor c;
-      stage_block(d, blk, stage, lane, c);
-      const int64_t g_first = int64_t(blk) * d.G;
-      const int gb = int(std::min<int64_t>(d.G, d.n_groups - g_first));
-      const int ntiles = (gb + 15) / 16;
-      const uint32_t first_raw = d.first_raw[blk];
-      uint32_t raw_rank = 0;
-      // row and column group of the tile's first group; advanced without divisions
-      int64_t row0 = g_first / d.gpr;
-      int c0 = int(g_first - row0 * d.gpr);
-      uint4 smv = load_sm_tile(d, blk, 0, lane);
-      for (int t = 0; t < ntiles; ++t, c0 += 16) {
-        while (c0 >= d.gpr) {
-          c0 -= d.gpr;
-          ++row0;
-        }
-        const uint4 cur = smv;
-        if (t + 1 < ntiles) smv = load_sm_tile(d, blk, t + 1, lane);
-        const int j0 = t * 16;
-        const int nt = std::min(16, gb - j0);
-        const uint32_t rmask = raw_mask16(d, blk, j0);
-        if (PAIR && nt == 16 && rmask == 0 && c0 + 16 <= d.gpr && (c0 & 1) == 0) {
-          if (row0 != cur_row) {
-            flush_row<NBP, YBF16>(acc, cur_row, nb_valid, Y, ldy, lane);
-            cur_row = row0;
-          }
-#pragma unroll
-          for (int k = 0; k < 8; k += 2) {
-            const uint32_t p = cursor_peek(c);
-            const uint32_t e1 = lds_u32(T, p & pair_mask);
-            const uint32_t p2 = p >> (e1 & 31u);
-            const uint32_t e2 = lds_u32(T, p2 & pair_mask);
-            c.qm += e1 + e2;
-            cursor_refill(c, stage);
-            accumulate_pair<NBP, XF32>(acc, merge_pair(sm_pair(cur, k), e1), xl, c0 + 2 * k, lane);
-            accumulate_pair<NBP, XF32>(acc, merge_pair(sm_pair(cur, k + 1), e2), xl, c0 + 2 * k + 2, lane);
-          }
-        } else {
-          int64_t row = row0;
-          int cg = c0;
-          for (int jj = 0; jj < nt; ++jj, ++cg) {
-            if (cg >= d.gpr) {
-              cg -= d.gpr;
-              ++row;
-            }
-            if (row != cur_row) {
-              flush_row<NBP, YBF16>(acc, cur_row, nb_valid, Y, ldy, lane);
-              cur_row = row;
-            }
-            uint32_t E;
-            if ((rmask >> jj) & 1u) {
-              E = uint32_t(d.raw[int64_t(first_raw + raw_rank) * 64 + lane]) << 7;
-              raw_rank++;
-            } else {
-              E = PAIR ? decode_one<true>(c, T, stage, pair_mask) : decode_one<false>(c, T, stage, single_mask);
-            }
-            const float w = bits_f32(merge_one(sm_byte(cur, jj), E) << 16);
-#pragma unroll
-            for (int b = 0; b < NBP; ++b) acc[b] = __builtin_fmaf(w, x_at<NBP, XF32>(xl, cg, lane, b), acc[b]);
-          }
-        }
-      }
-    }
-    flush_row<NBP, YBF16>(acc, cur_row, nb_valid, Y, ldy, lane);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Uncompressed bf16 product on the vector ALU (small batch): one wave per
 // output row, lanes stride the row in 16-byte chunks, X in LDS as [b][k].
@@ -481,7 +649,7 @@ __global__ __launch_bounds__(256) void bf16_gemv_kernel(const uint16_t* __restri
                                                         int64_t ldw, const void* __restrict__ X, int64_t ldx, int nb_valid,
                                                         void* __restrict__ Y, int64_t ldy) {
   extern __shared__ uint32_t lds[];
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, waves = blockDim.x / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave), waves = blockDim.x / kWave;
   // X staged as fp32 [b][k] (fp32 input) or bf16 pairs [b][k/2]
   const int64_t kp = cols / 2;
   if (XF32) {
@@ -625,9 +793,9 @@ template <int NBP, bool XF32, bool PAIR, bool YBF16>
 int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, void* stream) {
   const DevMatrix& d = m->dev;
   const size_t fixed = tables_bytes() + x_bytes(d, NBP, XF32);
-  const size_t per_wave = size_t(d.stage_words) * 4;
+  const size_t per_wave = (size_t(d.stage_words) + kRingWords) * 4;
   if (fixed + per_wave > size_t(kLdsLimit)) return fail(UW_ERR_UNSUPPORTED, "fused product: x does not fit on chip");
-  const int waves = pick_waves(d.n_units, fixed, per_wave);
+  const int waves = std::min(pick_waves(d.n_units, fixed, per_wave), fused_max_threads(NBP) / kWave);
   const size_t lds = fixed + per_wave * waves;
   const int grid = int(std::max<int64_t>(1, (d.n_units + waves - 1) / waves));
   auto kern = fused_product_kernel<NBP, XF32, PAIR, YBF16>;
@@ -658,7 +826,8 @@ int run_fused_x(const uw_matrix* m, const void* X, int64_t ldx, int xt, int nb, 
 int fused_chunk(const DevMatrix& d, int64_t batch, bool xf32) {
   int nbp = 8;
   while (nbp > 1 && (nbp / 2 >= batch ||
-                     tables_bytes() + x_bytes(d, nbp, xf32) + size_t(d.stage_words) * 4 * 4 > size_t(kLdsLimit)))
+                     tables_bytes() + x_bytes(d, nbp, xf32) + (size_t(d.stage_words) + kRingWords) * 4 * 4 >
+                         size_t(kLdsLimit)))
     nbp /= 2;
   return nbp;
 }
@@ -708,7 +877,7 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
     return hip_check(hipGetLastError(), "copy_plain_kernel launch");
   }
   const size_t fixed = tables_bytes();
-  const size_t per_wave = (size_t(d.stage_words) + kTransposeWords) * 4;
+  const size_t per_wave = (size_t(d.stage_words) + kRingWords + kTransposeWords) * 4;
   const int waves = pick_waves(d.n_blocks, fixed, per_wave);
   const size_t lds = fixed + per_wave * waves;
   const int grid = int(std::max<int64_t>(1, (int64_t(d.n_blocks) + waves - 1) / waves));
@@ -725,7 +894,11 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
 bool fused_supported(const uw_matrix* m, int xt, std::string* why) {
   if (m->h.plain()) return true;  // handled by the bf16 product
   const DevMatrix& d = m->dev;
-  if (tables_bytes() + x_bytes(d, 1, xt == UW_F32) + size_t(d.stage_words) * 4 > size_t(kLdsLimit)) {
+  if (int64_t(d.unit_blocks) * d.G > int64_t(kWave) * d.gpr) {
+    if (why) *why = "a work unit (lcm of G and the groups per row) spans more than 64 rows";
+    return false;
+  }
+  if (tables_bytes() + x_bytes(d, 1, xt == UW_F32) + (size_t(d.stage_words) + kRingWords) * 4 > size_t(kLdsLimit)) {
     if (why) *why = "x of this width does not fit in LDS next to the decode tables";
     return false;
   }
