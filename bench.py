@@ -262,6 +262,21 @@ def main():
                                 "frac_hbm_peak": round(dbytes / (us_d * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del out_w
         torch.cuda.empty_cache()
+        # plain copy of known size (random bits store in plain mode: the
+        # decompress is one read and one write of 128 MiB); its counter
+        # readings calibrate FETCH_SIZE / WRITE_SIZE for the traffic figure
+        log("timing plain-mode copy (counter calibration)")
+        wr = workloads.weights("randbits", rows=8192, cols=8192)
+        mplain = uw.CompressedMatrix(uw.uw_encode(wr), device="cuda:0")
+        del wr
+        assert mplain.info["plain"], "random bits are expected to take plain mode"
+        out_p = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+        us_c, _, _ = time_graph([lambda: uw.uw_decompress(mplain.handle, out_p, 8192)], 16, 4, torch)
+        extras["plain_copy"] = {"bytes_each_way": 2 * 8192 * 8192, "us": round(us_c, 3),
+                                "GBs_read_plus_write": round(4 * 8192 * 8192 / (us_c * 1e-6) / 1e9, 1)}
+        mplain.close()
+        del out_p
+        torch.cuda.empty_cache()
         out["extras"] = extras
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
