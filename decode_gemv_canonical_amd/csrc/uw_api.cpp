@@ -183,7 +183,7 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
 
 size_t uw_workspace_size(const uw_matrix* m, int64_t batch, int variant) {
   if (!m || batch < 0) return 0;
-  if (variant == UW_VARIANT_FUSED) return 0;
+  if (variant == UW_VARIANT_FUSED || variant == UW_VARIANT_FUSED_MFMA) return 0;
   return decompress_ws_bytes(m);
 }
 
@@ -202,8 +202,10 @@ int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ld
   if (int rc = check_products(d_X, batch, ldx, xt, d_Y, ldy, yt, m->h.rows, m->h.cols)) return rc;
   if (batch == 0) return UW_OK;
   if (variant < 0 || variant >= UW_VARIANT_COUNT) return fail(UW_ERR_INVALID, "uw_gemm_fused: unknown variant");
-  std::string why;
+  std::string why, why_mfma;
   const bool fused_ok = fused_supported(m, xt, &why) && (!m->h.plain() || bf16_gemm_supported(m->h.cols, batch, xt, &why));
+  const bool mfma_ok = fused_mfma_supported(m, xt, &why_mfma) && aligned(d_X, 16) && ldx % 8 == 0;
+  if (!mfma_ok && why_mfma.empty()) why_mfma = "X must be 16-byte aligned with ldx a multiple of 8";
   if (variant == UW_VARIANT_AUTO) {
     uw_plan p;
     bool have = false;
@@ -216,7 +218,12 @@ int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ld
       }
     }
     if (have) variant = p.variant;
+    else if (batch > 8 && mfma_ok) variant = UW_VARIANT_FUSED_MFMA;
     else variant = (batch <= 8 && fused_ok) || ws_bytes < decompress_ws_bytes(m) ? UW_VARIANT_FUSED : UW_VARIANT_DECOMPRESS_GEMM;
+  }
+  if (variant == UW_VARIANT_FUSED_MFMA) {
+    if (!mfma_ok) return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused: " + why_mfma);
+    return launch_fused_mfma(m, d_X, batch, ldx, d_Y, ldy, yt, stream);
   }
   if (variant == UW_VARIANT_FUSED) {
     if (!fused_ok) return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused: " + why);

@@ -91,6 +91,9 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
 int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, int xt, void* Y,
                  int64_t ldy, int yt, void* stream);
 bool fused_supported(const uw_matrix* m, int xt, std::string* why);
+int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, void* Y, int64_t ldy, int yt,
+                      void* stream);
+bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why);
 int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X,
                      int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream);
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why);

@@ -301,6 +301,53 @@ __device__ inline uint32_t take_single(Cursor& c, uint32_t& p, uint32_t mask) {
   return e;
 }
 
+// Decode a complete 16-group tile that lies inside one row and starts at an
+// even column group: sink.pair(k, D) receives D = the lane's weights of
+// groups (2k, 2k+1).  rmask holds the tile's raw flags, raw_rank the index
+// (within the block) of its first raw group.
+template <bool PAIR, class Sink>
+__device__ __forceinline__ void decode_tile_pairs(Cursor& c, const uint4& cur, uint32_t rmask, uint32_t raw_area,
+                                                  uint32_t raw_rank, uint32_t pmask, int lane, Sink& sink) {
+  uint32_t p = cursor_peek(c);
+  if (PAIR && rmask == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const uint32_t e1 = ld32(p & 0x3FFCu);
+      p >>= (e1 & 31u);
+      const uint32_t e2 = ld32(p & 0x3FFCu);
+      c.qm += e1 + e2;
+      cursor_refill(c);
+      p = cursor_peek(c);
+      sink.pair(k, merge_pair(sm_pair(cur, k), e1));
+      sink.pair(k + 1, merge_pair(sm_pair(cur, k + 1), e2));
+    }
+  } else {
+    uint32_t rank = raw_rank;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t two = (rmask >> (2 * k)) & 3u;
+      uint32_t E;
+      if (PAIR && two == 0) {
+        E = ld32(p & 0x3FFCu);
+        p >>= (E & 31u);
+        c.qm += E;
+      } else {
+        uint32_t ea, eb;
+        if (two & 1u) ea = ld8(raw_area + (rank++) * 64 + lane) << 7;
+        else ea = take_single<PAIR>(c, p, pmask) & 0x7F80u;
+        if (two & 2u) eb = ld8(raw_area + (rank++) * 64 + lane) << 23;
+        else eb = (take_single<PAIR>(c, p, pmask) & 0x7F80u) << 16;
+        E = ea | eb;
+      }
+      if (!PAIR || (k & 1)) {
+        cursor_refill(c);
+        p = cursor_peek(c);
+      }
+      sink.pair(k, merge_pair(sm_pair(cur, k), E));
+    }
+  }
+}
+
 // Decode one block and hand the weights to `sink`:
 //   sink.tile_begin(row0, c0)   before a tile that lies inside one row, starts
 //                               at an even column group and is complete;
@@ -341,44 +388,7 @@ __device__ __forceinline__ void decode_block(const DevMatrix& d, int blk, uint32
         const uint32_t rmask = raw_mask16(head.raw_word, j0);
         if (nt == 16 && c0 + 16 <= d.gpr && (c0 & 1) == 0) {
           sink.tile_begin(row0, c0);
-          uint32_t p = cursor_peek(c);
-          if (PAIR && rmask == 0) {
-#pragma unroll
-            for (int k = 0; k < 8; k += 2) {
-              const uint32_t e1 = ld32(p & 0x3FFCu);
-              p >>= (e1 & 31u);
-              const uint32_t e2 = ld32(p & 0x3FFCu);
-              c.qm += e1 + e2;
-              cursor_refill(c);
-              p = cursor_peek(c);
-              sink.pair(k, merge_pair(sm_pair(cur, k), e1));
-              sink.pair(k + 1, merge_pair(sm_pair(cur, k + 1), e2));
-            }
-          } else {
-            uint32_t rank = raw_rank;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const uint32_t two = (rmask >> (2 * k)) & 3u;
-              uint32_t E;
-              if (PAIR && two == 0) {
-                E = ld32(p & 0x3FFCu);
-                p >>= (E & 31u);
-                c.qm += E;
-              } else {
-                uint32_t ea, eb;
-                if (two & 1u) ea = ld8(raw_area + (rank++) * 64 + lane) << 7;
-                else ea = take_single<PAIR>(c, p, pmask) & 0x7F80u;
-                if (two & 2u) eb = ld8(raw_area + (rank++) * 64 + lane) << 23;
-                else eb = (take_single<PAIR>(c, p, pmask) & 0x7F80u) << 16;
-                E = ea | eb;
-              }
-              if (!PAIR || (k & 1)) {
-                cursor_refill(c);
-                p = cursor_peek(c);
-              }
-              sink.pair(k, merge_pair(sm_pair(cur, k), E));
-            }
-          }
+          decode_tile_pairs<PAIR>(c, cur, rmask, raw_area, raw_rank, pmask, lane, sink);
         } else {
           // tile crossing a row end, starting at an odd column group, or partial
           int64_t row = row0;
@@ -624,6 +634,229 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
     for (int blk = blk_begin; blk < blk_end; ++blk) decode_block<PAIR>(d, blk, stage, ring, lane, sink);
     sink.flush();
     sink.store_done();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused product on the matrix cores (batch >= 16): Y[b, n] = sum_k X[b, k] W[n, k].
+//
+// A workgroup of nw waves decodes nw blocks (or nw rows of blocks) in
+// lockstep, one 16-group tile per step.  Every wave's tile lies in one row
+// and covers the same 1024 columns, so after a step the workgroup holds an
+// nw x 1024 bf16 slice of W in LDS (one row per wave, in natural column
+// order).  That slice is the A operand of v_mfma_f32_16x16x32_bf16 (rows of
+// the slice = M, padded to 16 with zeros); 16 activation rows are the B
+// operand, read straight from global memory (8 consecutive bf16 per lane, so
+// the k order of A and B agree).  The 32 k-steps of a slice are spread over
+// the waves; each wave accumulates its share for every batch tile, and the
+// partial sums are added across waves in a fixed order when the rows end.
+constexpr int kMfmaRing = 2;               // sm tiles per wave in flight
+constexpr uint32_t kWRowBytes = 2048 + 16;  // one row of a slice; the pad keeps the A reads conflict-free
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// How the workgroups walk the matrix (set on the host).
+struct MfmaGeom {
+  int nw;               // waves per workgroup = W rows per slice
+  int by_block;         // 1: wave w decodes block task*nw + w (G a multiple of the groups per row)
+                        // 0: wave w decodes the blocks of row task*nw + w (G divides the groups per row)
+  int rows_per_block;   // by_block: G / groups per row
+  int seq_blocks;       // blocks per wave and task (1, or groups per row / G)
+  int tiles_per_block;  // G / 16
+  int tiles_per_row;    // groups per row / 16
+  int n_tasks;
+};
+
+__device__ inline floatx4 mfma_bf16(const uint4& a, const uint4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// One wave's tile into its row of the slice: pair k holds columns 64*(2k) + lane
+// and 64*(2k+1) + lane.
+struct SliceSink {
+  uint32_t row_addr;
+  int lane;
+  __device__ void pair(int k, uint32_t D) {
+    st16(row_addr + ((2 * k) * kWave + lane) * 2, D);
+    st16(row_addr + ((2 * k + 1) * kWave + lane) * 2, D >> 16);
+  }
+};
+
+// IPW k-steps per wave and slice go with the wave count (IPW = ceil(32 / nw)):
+// 16 waves (2), 11..15 (3), 8..10 (4); fewer waves leave more registers.
+constexpr int mfma_max_threads(int ipw) { return ipw == 2 ? 1024 : ipw == 3 ? 960 : 640; }
+
+template <int TB, int IPW, bool PAIR, bool YBF16>
+__global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMatrix d, MfmaGeom g, const uint16_t* __restrict__ X,
+                                                          int64_t ldx, int nb_valid, void* __restrict__ Y, int64_t ldy) {
+  extern __shared__ uint32_t lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int nw = g.nw;
+  const uint32_t slice = kAreaAddr;  // nw rows of kWRowBytes; also the reduction area
+  const uint32_t per_wave = d.stage_words * 4 + kMfmaRing * 1024;
+  const uint32_t stage = slice + uint32_t(nw) * kWRowBytes + uint32_t(wave) * per_wave;
+  const uint32_t ring = stage + d.stage_words * 4;
+  const uint32_t my_row = slice + uint32_t(wave) * kWRowBytes;
+  const uint32_t pmask = PAIR ? 0x3FFCu : (((1u << d.L) - 1u) << 2);
+  build_tables<PAIR>(d, lds, lds + kTableWords);
+  __syncthreads();
+
+  // A operand row of this lane (rows >= nw are zero padding)
+  const int a_row = lane % 16, a_quad = lane / 16;
+  const uint32_t a_addr = slice + uint32_t(a_row < nw ? a_row : 0) * kWRowBytes + a_quad * 16;
+  // B operand: activation row b = 16 tb + lane % 16 (clamped for the address), 8 columns at 8 * (lane / 16)
+  const uint16_t* xrow[TB];
+  bool xvalid[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int b = 16 * tb + lane % 16;
+    xvalid[tb] = b < nb_valid;
+    xrow[tb] = X + int64_t(b < nb_valid ? b : 0) * ldx + 8 * a_quad;
+  }
+  const int seq_tiles = g.seq_blocks * g.tiles_per_block;
+
+  for (int task = blockIdx.x; task < g.n_tasks; task += gridDim.x) {
+    floatx4 acc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    uint4 xv[IPW][TB];
+    for (int sb = 0; sb < g.seq_blocks; ++sb) {
+      // this wave's block
+      int blk;
+      bool valid;
+      if (g.by_block) {
+        blk = task * nw + wave;
+        valid = blk < d.n_blocks;
+      } else {
+        const int64_t row = int64_t(task) * nw + wave;
+        valid = row < d.rows;
+        blk = int(row * g.seq_blocks + sb);
+      }
+      int ntiles = 0;
+      BlockHead head{0u, 0u};
+      const uint4* sm_blk = nullptr;
+      // earlier ring loads (clamped repeats of the last tile) land before the slots are reused
+      __builtin_amdgcn_s_waitcnt(0);
+      if (valid) {
+        const int64_t g_first = int64_t(blk) * d.G;
+        ntiles = int((std::min<int64_t>(d.G, d.n_groups - g_first) + 15) / 16);
+        head = issue_head_loads(d, blk, lane);
+        sm_blk = reinterpret_cast<const uint4*>(d.sm + int64_t(blk) * d.G * 64);
+#pragma unroll
+        for (int i = 0; i < kMfmaRing; ++i) load_sm_tile_to_lds(sm_blk, std::min(i, ntiles - 1), ring, i, lane);
+        issue_stage_loads(d, blk, stage, lane);
+      }
+      // activations of the first step
+      {
+        const int64_t col0 = int64_t(((sb * g.tiles_per_block) % g.tiles_per_row)) * 1024;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+          const int kk = (wave + i * nw) & 31;  // distinct per i: a merged load would upset the vmcnt count
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) xv[i][tb] = *reinterpret_cast<const uint4*>(xrow[tb] + col0 + 32 * kk);
+        }
+      }
+      Cursor c{0u, 0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(0);
+      if (valid) {
+        const uint32_t start_bit = wave_exclusive_scan(head.lane_bits, lane);
+        wave_lds_fence();
+        const uint32_t bit = 4 * 32 + start_bit - 2;
+        c.addr = stage + (bit >> 5) * 4;
+        c.qm = bit & 31;
+        cursor_reload(c);
+      }
+      const uint32_t raw_area = stage + d.stage_raw_word * 4;
+      uint32_t raw_rank = 0;
+
+      for (int t = 0; t < g.tiles_per_block; ++t) {
+        const int tau = sb * g.tiles_per_block + t;
+        // decode this wave's tile into its slice row
+        if (valid && t < ntiles) {
+          // newer than ring load t: the activations of this step and ring load t+1
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW * TB + 1) : "memory");
+          const uint4 cur = ld128(ring + (t % kMfmaRing) * 1024 + lane * 16);
+          const uint32_t rmask = raw_mask16(head.raw_word, t * 16);
+          SliceSink sink{my_row, lane};
+          decode_tile_pairs<PAIR>(c, cur, rmask, raw_area, raw_rank, pmask, lane, sink);
+          raw_rank += __builtin_popcount(rmask);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) st32(my_row + (i * kWave + lane) * 4, 0u);
+        }
+        __syncthreads();
+        // matrix cores: k-steps wave, wave + nw, ... of the 32 in this slice
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+          const int kk = wave + i * nw;
+          if (kk < 32) {
+            uint4 a = ld128(a_addr + kk * 64);
+            if (a_row >= nw) a = uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+              const uint4 b = xvalid[tb] ? xv[i][tb] : uint4{0u, 0u, 0u, 0u};
+              acc[tb] = mfma_bf16(a, b, acc[tb]);
+            }
+          }
+        }
+        __syncthreads();
+        // activations of the next step (a fixed count per step keeps the vmcnt arithmetic exact),
+        // then the ring refill
+        if (t + 1 < g.tiles_per_block) {
+          const int64_t col0 = int64_t((tau + 1) % g.tiles_per_row) * 1024;
+#pragma unroll
+          for (int i = 0; i < IPW; ++i) {
+            const int kk = (wave + i * nw) & 31;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) xv[i][tb] = *reinterpret_cast<const uint4*>(xrow[tb] + col0 + 32 * kk);
+          }
+          if (valid && t < ntiles)
+            load_sm_tile_to_lds(sm_blk, std::min(t + kMfmaRing, ntiles - 1), ring, t % kMfmaRing, lane);
+        }
+        // the rows of this slice end here: add the partial sums of all waves
+        if ((tau + 1) % g.tiles_per_row == 0) {
+#pragma unroll
+          for (int r = 0; r < TB; r += 2) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              if (r + q < TB) {
+                const floatx4 v = acc[r + q];
+                st128(slice + ((wave * 2 + q) * kWave + lane) * 16,
+                      uint4{f32_bits(v.x), f32_bits(v.y), f32_bits(v.z), f32_bits(v.w)});
+              }
+            }
+            __syncthreads();
+            const int nvals = (TB - r >= 2 ? 2 : 1) * 256;
+            for (int v = threadIdx.x; v < nvals; v += blockDim.x) {
+              const int q = v / 256, rem = v % 256, l = rem / 4, e = rem % 4;
+              float s = 0.f;
+              for (int w = 0; w < nw; ++w) s += bits_f32(ld32(slice + ((w * 2 + q) * kWave + l) * 16 + e * 4));
+              const int m = 4 * (l / 16) + e;  // slice row
+              const int b = 16 * (r + q) + l % 16;
+              int64_t row;
+              bool ok;
+              if (g.by_block) {
+                const int64_t mb = int64_t(task) * nw + m;
+                row = mb * g.rows_per_block + tau / g.tiles_per_row;
+                ok = mb < d.n_blocks;
+              } else {
+                row = int64_t(task) * nw + m;
+                ok = true;
+              }
+              if (m < nw && ok && row < d.rows && b < nb_valid) {
+                if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + row] = f32_to_bf16(s);
+                else static_cast<float*>(Y)[b * ldy + row] = s;
+              }
+            }
+            __syncthreads();
+          }
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
   }
 }
 
@@ -903,6 +1136,103 @@ bool fused_supported(const uw_matrix* m, int xt, std::string* why) {
     return false;
   }
   return true;
+}
+
+// Walk of the matrix-core kernel: waves per workgroup from the LDS budget,
+// chosen so that the tasks fill whole rounds of 256 workgroups.
+bool mfma_geometry(const DevMatrix& d, MfmaGeom* g, std::string* why) {
+  if (d.gpr % 16) {
+    if (why) *why = "the matrix-core path needs cols to be a multiple of 1024";
+    return false;
+  }
+  if (d.G % d.gpr && d.gpr % d.G) {
+    if (why) *why = "the matrix-core path needs G to divide, or be a multiple of, the groups per row";
+    return false;
+  }
+  const size_t per_wave = kWRowBytes + size_t(d.stage_words) * 4 + kMfmaRing * 1024;
+  const int nw_max = int(std::min<size_t>(16, (size_t(kLdsLimit) - tables_bytes()) / per_wave));
+  if (nw_max < 8) {
+    if (why) *why = "the blocks of this matrix are too large for the matrix-core path's LDS budget";
+    return false;
+  }
+  g->by_block = d.G % d.gpr == 0;
+  g->rows_per_block = g->by_block ? d.G / d.gpr : 0;
+  g->seq_blocks = g->by_block ? 1 : d.gpr / d.G;
+  g->tiles_per_block = d.G / 16;
+  g->tiles_per_row = d.gpr / 16;
+  const int64_t units = g->by_block ? int64_t(d.n_blocks) : d.rows;
+  double best = -1.0;
+  for (int nw = 8; nw <= nw_max; ++nw) {
+    const int64_t tasks = (units + nw - 1) / nw;
+    const int64_t rounds = (tasks + 255) / 256;
+    const double eff = double(units) / double(rounds * 256 * nw);
+    if (eff >= best - 1e-9) {
+      best = eff;
+      g->nw = nw;
+      g->n_tasks = int(tasks);
+    }
+  }
+  return true;
+}
+
+template <int TB, int IPW, bool PAIR>
+int run_mfma(const uw_matrix* m, const MfmaGeom& g, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy,
+             int yt, hipStream_t s) {
+  const DevMatrix& d = m->dev;
+  const size_t lds = tables_bytes() + size_t(g.nw) * (kWRowBytes + size_t(d.stage_words) * 4 + kMfmaRing * 1024);
+  auto kern = yt == UW_BF16 ? fused_mfma_kernel<TB, IPW, PAIR, true> : fused_mfma_kernel<TB, IPW, PAIR, false>;
+  allow_full_lds(kern);
+  hipLaunchKernelGGL(kern, dim3(g.n_tasks), dim3(g.nw * kWave), lds, s, d, g, X, ldx, nb, Y, ldy);
+  return hip_check(hipGetLastError(), "fused_mfma_kernel launch");
+}
+
+template <int TB, bool PAIR>
+int run_mfma_ipw(const uw_matrix* m, const MfmaGeom& g, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy,
+                 int yt, hipStream_t s) {
+  if (g.nw >= 16) return run_mfma<TB, 2, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
+  if (g.nw >= 11) return run_mfma<TB, 3, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
+  return run_mfma<TB, 4, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
+}
+
+template <bool PAIR>
+int run_mfma_tb(const uw_matrix* m, const MfmaGeom& g, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy,
+                int yt, hipStream_t s) {
+  if (nb <= 16) return run_mfma_ipw<1, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
+  if (nb <= 32) return run_mfma_ipw<2, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
+  return run_mfma_ipw<4, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
+}
+
+bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why) {
+  if (m->h.plain()) {
+    if (why) *why = "a plain-mode matrix has nothing to decode";
+    return false;
+  }
+  if (xt != UW_BF16) {
+    if (why) *why = "the matrix-core path takes bf16 activations";
+    return false;
+  }
+  MfmaGeom g;
+  return mfma_geometry(m->dev, &g, why);
+}
+
+int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, void* Y, int64_t ldy, int yt,
+                      void* stream) {
+  const DevMatrix& d = m->dev;
+  MfmaGeom g;
+  std::string why;
+  if (!mfma_geometry(d, &g, &why)) return fail(UW_ERR_UNSUPPORTED, "fused matrix-core product: " + why);
+  if (reinterpret_cast<uintptr_t>(X) % 16 || ldx % 8)
+    return fail(UW_ERR_UNSUPPORTED, "fused matrix-core product: X must be 16-byte aligned with ldx a multiple of 8");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t b0 = 0; b0 < batch; b0 += 64) {
+    const int nb = int(std::min<int64_t>(64, batch - b0));
+    const uint16_t* Xb = static_cast<const uint16_t*>(X) + b0 * ldx;
+    void* Yb = static_cast<char*>(Y) + b0 * ldy * elem_size(yt);
+    const int rc = is_pair(d) ? run_mfma_tb<true>(m, g, Xb, ldx, nb, Yb, ldy, yt, s)
+                              : run_mfma_tb<false>(m, g, Xb, ldx, nb, Yb, ldy, yt, s);
+    if (rc) return rc;
+  }
+  return UW_OK;
 }
 
 int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt,

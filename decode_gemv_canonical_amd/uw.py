@@ -28,9 +28,11 @@ UW_BF16 = 1
 UW_VARIANT_AUTO = 0
 UW_VARIANT_FUSED = 1
 UW_VARIANT_DECOMPRESS_GEMM = 2
-UW_VARIANT_COUNT = 3
+UW_VARIANT_FUSED_MFMA = 3
+UW_VARIANT_COUNT = 4
 UW_ENC_NO_PLAIN = 1
-VARIANT_NAMES = {UW_VARIANT_AUTO: "auto", UW_VARIANT_FUSED: "fused", UW_VARIANT_DECOMPRESS_GEMM: "decompress+gemm"}
+VARIANT_NAMES = {UW_VARIANT_AUTO: "auto", UW_VARIANT_FUSED: "fused", UW_VARIANT_DECOMPRESS_GEMM: "decompress+gemm",
+                 UW_VARIANT_FUSED_MFMA: "fused-mfma"}
 
 
 class UwError(RuntimeError):

@@ -77,7 +77,8 @@ typedef enum {
   UW_VARIANT_AUTO = 0,             /* the tuned plan for this batch, else a heuristic   */
   UW_VARIANT_FUSED = 1,            /* decode on chip, multiply on VALU, no bf16 in HBM  */
   UW_VARIANT_DECOMPRESS_GEMM = 2,  /* uw_decompress into the workspace, then bf16 GEMM  */
-  UW_VARIANT_COUNT = 3
+  UW_VARIANT_FUSED_MFMA = 3,       /* decode on chip, multiply on the matrix cores      */
+  UW_VARIANT_COUNT = 4
 } uw_variant;
 
 #define UW_ENC_NO_PLAIN 1u /* never fall back to plain mode unless nothing can be coded */
@@ -186,7 +187,10 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
  *   variant  a uw_variant; UW_VARIANT_AUTO uses the plan uw_autotune stored
  *            for this batch, else a heuristic.
  *   d_ws/ws_bytes  caller-owned device workspace (uw_workspace_size bytes for
- *            the chosen variant; may be NULL/0 for UW_VARIANT_FUSED).
+ *            the chosen variant; may be NULL/0 for the fused variants).
+ *   UW_VARIANT_FUSED_MFMA needs bf16 X that is 16-byte aligned with ldx a
+ *   multiple of 8, cols a multiple of 1024, and G dividing or a multiple of
+ *   cols/64 (else UW_ERR_UNSUPPORTED); it runs 64 batch rows per pass.
  * batch == 0 is a no-op.  fp32 accumulation.
  * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE (workspace), UW_ERR_UNSUPPORTED, UW_ERR_HIP.
  */

@@ -56,11 +56,22 @@ def check_f32(y, ref64, what):
 
 
 def check_bf16(y, ref64, what):
+    """Within 2 bf16 ulp of RNE(y64), or RNE of a value inside the fp32
+    tolerance band |v - y64| <= TOL * max(|y64|, rms): the fp32 sum's error
+    scales with the row's rms, so an output near zero may sit more than 2 bf16
+    ulp (of its own tiny magnitude) from RNE(y64)."""
     got = y.detach().view(torch.int16).cpu().numpy().view(np.uint16)
     ref = products.round_to_bf16(ref64)
     fin = np.isfinite(ref64)
-    d = products.bf16_ulp_distance(got[fin], ref[fin])
-    assert d.max(initial=0) <= 2, f"{what}: {d.max()} bf16 ulp"
+    r = ref64[fin]
+    k = products.bf16_order_key(got[fin])
+    near = products.bf16_ulp_distance(got[fin], ref[fin]) <= 2
+    rms = float(np.sqrt(np.mean(r ** 2))) if r.size else 1.0
+    eps = TOL * np.maximum(np.abs(r), rms if rms > 0 else 1.0)
+    band = (k >= products.bf16_order_key(products.round_to_bf16(r - eps))) & \
+           (k <= products.bf16_order_key(products.round_to_bf16(r + eps)))
+    bad = ~(near | band)
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs outside 2 bf16 ulp and the fp32 band"
     assert np.array_equal(np.isnan(products.bf16_to_f64(got)), np.isnan(ref64)), what
 
 
@@ -181,11 +192,86 @@ def test_gemm_down_both_variants(batch):
     X = workloads.activations(14336, batch, seed=400 + batch, dtype=torch.bfloat16)
     ref = products.gemm_f64(wb, X.float().numpy())
     ws = m.workspace(batch)
-    for v in (uw.UW_VARIANT_FUSED, uw.UW_VARIANT_DECOMPRESS_GEMM):
+    for v in (uw.UW_VARIANT_FUSED, uw.UW_VARIANT_DECOMPRESS_GEMM, uw.UW_VARIANT_FUSED_MFMA):
         _say(f"gemm down batch={batch} variant={v}")
         Y = m.gemm(X.to(DEV), variant=v, ws=ws)
         torch.cuda.synchronize()
         check_f32(Y, ref, f"gemm down b={batch} v={v}")
+
+
+# Matrix-core path: every way a workgroup can walk the blocks (G a multiple of
+# the groups per row with 1, 2 or 4 rows per block; G dividing a row; a
+# partial last block), raw groups, the single-code table (L > 6), partial
+# batch tiles and more than one 64-row pass.
+MFMA_CASES = [
+    ("small", None, None, None, {}, (16, 17, 64)),
+    ("gate", 64, 4096, 41, {"G": 256}, (32, 48)),
+    ("down", 48, 14336, 42, {"G": 112}, (16, 33)),
+    ("small", 13, 1024, 43, {"G": 64}, (16,)),
+    ("small", 40, 2048, 44, {"K": 32, "L": 8}, (20,)),
+    ("big", 96, 8192, 45, {}, (100,)),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-{c[4]}")
+def test_gemm_fused_mfma(case):
+    name, rows, cols, seed, opts, batches = case
+    wb, m = matrix(name, rows, cols, seed, **opts)
+    C = wb.shape[1]
+    for batch in batches:
+        X = workloads.activations(C, batch, seed=700 + batch, dtype=torch.bfloat16)
+        ref = products.gemm_f64(wb, X.float().numpy())
+        _say(f"gemm mfma {name} {wb.shape} {opts} batch={batch}")
+        Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_FUSED_MFMA)
+        Yb = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_FUSED_MFMA, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        check_f32(Y, ref, f"gemm mfma b={batch}")
+        check_bf16(Yb, ref, f"gemm mfma bf16 b={batch}")
+
+
+def test_gemm_fused_mfma_full_sizes():
+    # the 32-row batch of a gate projection, and the 256-row batch on the 8192 x 8192
+    # matrix with outputs sampled on 384 rows (fp64 oracle per sampled row)
+    wb, m = matrix("gate", None, None, None)
+    X = workloads.activations(4096, 32, seed=801, dtype=torch.bfloat16)
+    _say("gemm mfma gate 14336x4096 batch=32")
+    Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_FUSED_MFMA)
+    torch.cuda.synchronize()
+    check_f32(Y, products.gemm_f64(wb, X.float().numpy()), "gate b=32")
+    wb, m = matrix("big", None, None, None)
+    X = workloads.activations(8192, 256, seed=802, dtype=torch.bfloat16)
+    _say("gemm mfma big 8192x8192 batch=256")
+    Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_FUSED_MFMA)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(5).choice(8192, size=384, replace=False)
+    ref = products.gemm_f64(wb[rows], X.float().numpy())
+    check_f32(Y[:, rows], ref, "big b=256 sampled rows")
+
+
+def test_gemm_fused_mfma_is_deterministic_and_checks_support():
+    wb, m = matrix("down", 48, 14336, 42, G=112)
+    X = workloads.activations(14336, 24, seed=803, dtype=torch.bfloat16).to(DEV)
+    Y1 = m.gemm(X, variant=uw.UW_VARIANT_FUSED_MFMA)
+    Y2 = m.gemm(X, variant=uw.UW_VARIANT_FUSED_MFMA)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
+    # fp32 activations, misaligned rows and cols that are not a multiple of 1024 are refused
+    with pytest.raises(uw.UwError) as e:
+        m.gemm(X.float(), variant=uw.UW_VARIANT_FUSED_MFMA)
+    assert e.value.status == uw.UW_ERR_UNSUPPORTED
+    Xs = torch.zeros(24, 14336 + 4, dtype=torch.bfloat16, device=DEV)[:, :14336]
+    with pytest.raises(uw.UwError) as e:
+        m.gemm(Xs, variant=uw.UW_VARIANT_FUSED_MFMA)
+    assert e.value.status == uw.UW_ERR_UNSUPPORTED
+    wb2, m2 = matrix("small", 37, 1600, 9, K=32, L=8)
+    X2 = workloads.activations(1600, 16, seed=804, dtype=torch.bfloat16)
+    with pytest.raises(uw.UwError) as e:
+        m2.gemm(X2.to(DEV), variant=uw.UW_VARIANT_FUSED_MFMA)
+    assert e.value.status == uw.UW_ERR_UNSUPPORTED
+    # AUTO falls back to a path that can run it
+    Y = m2.gemm(X2.to(DEV), variant=uw.UW_VARIANT_AUTO, ws=m2.workspace(16))
+    torch.cuda.synchronize()
+    check_f32(Y, products.gemm_f64(wb2, X2.float().numpy()), "auto fallback")
 
 
 def test_gemm_fp32_input_strided():
@@ -238,7 +324,7 @@ def test_autotune_plan_and_auto_dispatch():
     for batch in (1, 16):
         _say(f"autotune batch={batch}")
         plan = m.autotune(batch)
-        assert plan["variant"] in (uw.UW_VARIANT_FUSED, uw.UW_VARIANT_DECOMPRESS_GEMM)
+        assert plan["variant"] in (uw.UW_VARIANT_FUSED, uw.UW_VARIANT_DECOMPRESS_GEMM, uw.UW_VARIANT_FUSED_MFMA)
         assert plan["time_us"] == min(plan["candidate_us"].values())
         assert uw.uw_get_plan(m.handle, batch)["variant"] == plan["variant"]
         X = workloads.activations(14336, batch, seed=600 + batch, dtype=torch.bfloat16).to(DEV)
