@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--workload", default="gate", choices=["gate", "down", "big", "small"])
     p.add_argument("--no-extras", action="store_true", help="skip comparators, GEMM sweep and CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--skip-gemm", action="store_true", help="skip the batched-product sweep")
+    p.add_argument("--gemm-only", action="store_true", help="run only the batched-product sweep (prints its JSON)")
     return p.parse_args()
 
 
@@ -124,9 +126,11 @@ def cpu_baseline(workload: str, target_s: float):
     rows = 64
     x = workloads.activations(c, 1, seed=workloads.SEEDS[workload] + 100).float().numpy()[0]
 
+    import decode_gemv_canonical_amd as uw
+
     def run(rows):
         w = workloads.weights(workload, rows=rows).numpy().view(np.uint16)
-        b = oblob.encode(w)
+        b = uw.uw_encode(w)  # byte-identical to the oracle's encoder (CPU tests); only the decode is timed
         t0 = time.perf_counter()
         dec = oblob.decode(b)
         y = products.gemm_f32(dec, x)
@@ -152,6 +156,50 @@ def cpu_baseline(workload: str, target_s: float):
             "seconds": round(dt, 3)}
 
 
+def gemm_sweep(uw, workloads, torch, dev, steps):
+    """Batched products on the scope's batch sizes: down_proj at 1/4/16/64,
+    gate_proj at 32 (one layer of the 32-layer stack), 8192x8192 at 256.
+    Every candidate variant, plus torch.matmul on the uncompressed bf16
+    weights; 4 rotated copies each."""
+    cases = [("down", (1, 4, 16, 64)), ("gate", (32,)), ("big", (256,))]
+    names = {uw.UW_VARIANT_FUSED: "fused_valu", uw.UW_VARIANT_FUSED_MFMA: "fused_mfma",
+             uw.UW_VARIANT_DECOMPRESS_GEMM: "decompress_gemm"}
+    out = {}
+    for name, batches in cases:
+        rows, cols = workloads.SHAPES[name]
+        w = workloads.weights(name)
+        blob = uw.uw_encode(w)
+        mats = [uw.CompressedMatrix(blob, device="cuda:0") for _ in range(4)]
+        Wb = [torch.from_numpy(w.numpy()).to(dev).view(torch.bfloat16) for _ in range(2)]
+        for B in batches:
+            X = workloads.activations(cols, B, seed=workloads.SEEDS[name] + 200 + B, dtype=torch.bfloat16).to(dev)
+            Y = torch.empty(B, rows, dtype=torch.float32, device=dev)
+            rec = {}
+            for v, vn in names.items():
+                if v == uw.UW_VARIANT_FUSED and B > 16:
+                    continue  # one decode pass per 8 rows: not a candidate at this size
+                ws = mats[0].workspace(B, v)
+                try:
+                    us, _, _ = time_graph([(lambda m=m: uw.uw_gemm_fused(m.handle, X, Y, v, ws)) for m in mats],
+                                          steps, 4, torch)
+                except uw.UwError:
+                    continue
+                rec[vn + "_us"] = round(us, 2)
+                del ws
+            Yb = torch.empty(B, rows, dtype=torch.bfloat16, device=dev)
+            us, _, _ = time_graph([(lambda W=W: torch.matmul(X, W.t(), out=Yb)) for W in Wb], steps, 4, torch)
+            rec["torch_bf16_matmul_us"] = round(us, 2)
+            best = min(v for k, v in rec.items() if k.startswith(("fused", "decompress")))
+            rec["blob_GBs_best"] = round(len(blob) / (best * 1e-6) / 1e9, 1)
+            out[f"{name}_{rows}x{cols}_b{B}"] = rec
+            log(f"gemm {name} B={B}: {rec}")
+        for m in mats:
+            m.close()
+        del Wb, mats
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -165,6 +213,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.gemm_only:
+        print(json.dumps({"gemm": gemm_sweep(uw, workloads, torch, dev, 48)}), flush=True)
+        return
     name = args.workload
     rows, cols = workloads.SHAPES[name]
     log(f"encoding {name} {rows}x{cols}")
@@ -277,6 +328,9 @@ def main():
         mplain.close()
         del out_p
         torch.cuda.empty_cache()
+        if not args.skip_gemm:
+            log("gemm sweep")
+            extras["gemm"] = gemm_sweep(uw, workloads, torch, dev, 48)
         out["extras"] = extras
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)

@@ -93,7 +93,7 @@ int uw_blob_info(const void* blob, size_t n, uw_info* info) {
   info->n_blocks = h.n_blocks;
   info->n_raw_groups = int64_t(h.n_raw_groups);
   info->total_bytes = h.total_bytes;
-  info->max_block_stream_bytes = h.max_block_stream_bytes;
+  info->max_segment_bytes = h.max_segment_bytes;
   std::memcpy(info->palette, h.palette, 32);
   std::memcpy(info->code_len, h.code_len, 32);
   const double w = double(h.rows) * double(h.cols);
@@ -124,16 +124,15 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
   if (h.plain()) {
     d.plain = reinterpret_cast<const uint16_t*>(b + h.off_plain);
   } else {
-    d.start_word = reinterpret_cast<const uint32_t*>(b + h.off_start_word);
-    d.first_raw = reinterpret_cast<const uint32_t*>(b + h.off_first_raw);
-    d.raw_bits = reinterpret_cast<const uint32_t*>(b + h.off_raw_bits);
-    d.lane_bits = reinterpret_cast<const uint16_t*>(b + h.off_lane_bits);
-    d.stream = reinterpret_cast<const uint32_t*>(b + h.off_stream);
-    d.raw = b + h.off_raw;
+    d.block_off = reinterpret_cast<const uint32_t*>(b + h.off_block);
+    d.seg = reinterpret_cast<const uint16_t*>(b + h.off_seg);
+    d.queue = b + h.off_queue;
     d.sm = b + h.off_sm;
     d.G = int32_t(h.G);
     d.n_blocks = int32_t(h.n_blocks);
     d.rb_words = int32_t((h.G + 31) / 32);
+    d.T = int32_t((h.G + 15) / 16);
+    d.R = int32_t(h.R);
     d.L = int32_t(h.L);
     // the decode tables are built on chip from the canonical codes
     uint32_t code[32], rev[32];
@@ -141,19 +140,11 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
     d.n_sym = int32_t(h.K);
     for (uint32_t i = 0; i < h.K; ++i)
       d.sym[i] = rev[i] | (uint32_t(h.code_len[i]) << 16) | (uint32_t(h.palette[i]) << 24);
-    // stage buffer of one wave: 4 pad words, the block's stream, 4 pad words
-    // (window reads run one word past a lane's end), then the block's raw
-    // exponent bytes (64 per raw group)
-    const uint8_t* hb = static_cast<const uint8_t*>(host_blob);
-    uint32_t max_raw = 0;
-    for (uint32_t blk = 0; blk < h.n_blocks; ++blk) {
-      uint32_t a, z;
-      std::memcpy(&a, hb + h.off_first_raw + 4 * blk, 4);
-      std::memcpy(&z, hb + h.off_first_raw + 4 * (blk + 1), 4);
-      max_raw = std::max(max_raw, z - a);
-    }
-    d.stage_raw_word = int32_t(4 + h.max_block_stream_bytes / 4 + 4);
-    d.stage_words = d.stage_raw_word + int32_t(max_raw * 16);
+    // an LDS slot holds any segment; it is filled by 1 KB direct loads
+    // (a segment is loaded from its 16-byte aligned floor, up to 12 bytes
+    // before it, and lanes that take no word read the word after its end)
+    d.slot_bytes = int32_t((h.max_segment_bytes + 16 + 15) / 16 * 16);
+    d.seg_loads = std::max(1, (d.slot_bytes + 1023) / 1024);
     // a work unit covers whole rows: lcm(G, groups per row) groups
     const int64_t lcm = int64_t(h.G) / gcd64(h.G, d.gpr) * d.gpr;
     d.unit_blocks = int32_t(lcm / h.G);

@@ -61,10 +61,21 @@ uint32_t crc32(const uint8_t* p, size_t n, uint32_t crc) {
   return ~crc;
 }
 
+// Header, 256 bytes (little-endian):
+//    0 "UWB2"   4 u32 version 2   8 u32 header bytes 256   12 u32 flags (bit 0: plain)
+//   16 i64 rows  24 i64 cols  32 u32 K  36 u32 L  40 u32 G  44 u32 n_blocks
+//   48 u64 raw groups  56 u64 total bytes  64 u32 CRC-32 of [256, total)
+//   68 u32 largest segment (bytes)  72 u8 palette[32]  104 u8 code_len[32]
+//  136 u32 R (groups between refill checks)  140 u32 0
+//  144 u64 off_block  152 off_seg  160 off_queue  168 size_queue  176 off_sm
+//  184 size_sm  192 off_plain  200 size_plain
+// Sections: block u32[n_blocks+1] (byte offset of each block's data in the
+// queue), seg u16[n_blocks*T] (T = ceil(G/16): end of tile t's segment in
+// words from the block start), queue (segments), sm (1 KB tiles), plain.
 void header_write(const BlobHeader& h, uint8_t* d) {
   std::memset(d, 0, kHeaderBytes);
-  std::memcpy(d, "UWB1", 4);
-  put<uint32_t>(d, 4, 1);
+  std::memcpy(d, "UWB2", 4);
+  put<uint32_t>(d, 4, 2);
   put<uint32_t>(d, 8, kHeaderBytes);
   put<uint32_t>(d, 12, h.flags);
   put<int64_t>(d, 16, h.rows);
@@ -76,13 +87,13 @@ void header_write(const BlobHeader& h, uint8_t* d) {
   put<uint64_t>(d, 48, h.n_raw_groups);
   put<uint64_t>(d, 56, h.total_bytes);
   put<uint32_t>(d, 64, h.crc32);
-  put<uint32_t>(d, 68, h.max_block_stream_bytes);
+  put<uint32_t>(d, 68, h.max_segment_bytes);
   std::memcpy(d + 72, h.palette, 32);
   std::memcpy(d + 104, h.code_len, 32);
-  const uint64_t offs[12] = {h.off_start_word, h.off_first_raw, h.off_raw_bits, h.off_lane_bits,
-                             h.off_stream, h.size_stream, h.off_raw, h.size_raw,
-                             h.off_sm, h.size_sm, h.off_plain, h.size_plain};
-  for (int i = 0; i < 12; ++i) put<uint64_t>(d, 136 + 8 * i, offs[i]);
+  put<uint32_t>(d, 136, h.R);
+  const uint64_t offs[8] = {h.off_block, h.off_seg, h.off_queue, h.size_queue,
+                            h.off_sm, h.size_sm, h.off_plain, h.size_plain};
+  for (int i = 0; i < 8; ++i) put<uint64_t>(d, 144 + 8 * i, offs[i]);
 }
 
 void header_read(const uint8_t* s, BlobHeader* h) {
@@ -97,13 +108,13 @@ void header_read(const uint8_t* s, BlobHeader* h) {
   h->n_raw_groups = get<uint64_t>(s, 48);
   h->total_bytes = get<uint64_t>(s, 56);
   h->crc32 = get<uint32_t>(s, 64);
-  h->max_block_stream_bytes = get<uint32_t>(s, 68);
+  h->max_segment_bytes = get<uint32_t>(s, 68);
   std::memcpy(h->palette, s + 72, 32);
   std::memcpy(h->code_len, s + 104, 32);
-  uint64_t* offs[12] = {&h->off_start_word, &h->off_first_raw, &h->off_raw_bits, &h->off_lane_bits,
-                        &h->off_stream, &h->size_stream, &h->off_raw, &h->size_raw,
-                        &h->off_sm, &h->size_sm, &h->off_plain, &h->size_plain};
-  for (int i = 0; i < 12; ++i) *offs[i] = get<uint64_t>(s, 136 + 8 * i);
+  h->R = get<uint32_t>(s, 136);
+  uint64_t* offs[8] = {&h->off_block, &h->off_seg, &h->off_queue, &h->size_queue,
+                       &h->off_sm, &h->size_sm, &h->off_plain, &h->size_plain};
+  for (int i = 0; i < 8; ++i) *offs[i] = get<uint64_t>(s, 144 + 8 * i);
 }
 
 void canonical_codes(const BlobHeader& h, uint32_t code[32], uint32_t rev[32]) {
@@ -142,10 +153,10 @@ bool section_ok(uint64_t off, uint64_t size, size_t n) {
 int validate_blob(const uint8_t* b, size_t n, BlobHeader* out) {
   if (!b) return fail(UW_ERR_INVALID, "null blob");
   if (n < kHeaderBytes) return fail(UW_ERR_FORMAT, "blob shorter than its 256-byte header");
-  if (std::memcmp(b, "UWB1", 4) != 0) return fail(UW_ERR_FORMAT, "bad magic");
+  if (std::memcmp(b, "UWB2", 4) != 0) return fail(UW_ERR_FORMAT, "bad magic");
   BlobHeader h;
   header_read(b, &h);
-  if (h.version != 1) return fail(UW_ERR_FORMAT, "unsupported version");
+  if (h.version != 2) return fail(UW_ERR_FORMAT, "unsupported version");
   if (get<uint32_t>(b, 8) != kHeaderBytes) return fail(UW_ERR_FORMAT, "bad header size");
   if (h.total_bytes != n) return fail(UW_ERR_FORMAT, "total_bytes does not match the blob size");
   if (h.flags & ~kFlagPlain) return fail(UW_ERR_FORMAT, "unknown flags");
@@ -162,6 +173,7 @@ int validate_blob(const uint8_t* b, size_t n, BlobHeader* out) {
   if (h.K < 1 || h.K > kMaxK || h.L < 1 || h.L > kMaxL || h.K > (1u << h.L))
     return fail(UW_ERR_FORMAT, "bad K/L");
   if (h.G < 16 || h.G > 1024 || h.G % 16) return fail(UW_ERR_FORMAT, "bad G");
+  if (h.R != check_groups(h.L)) return fail(UW_ERR_FORMAT, "refill interval does not match L");
   const uint64_t n_groups = weights / 64;
   if (h.n_blocks != (n_groups + h.G - 1) / h.G) return fail(UW_ERR_FORMAT, "bad block count");
   // palette distinct; lengths form a complete prefix code (or one 1-bit code)
@@ -185,52 +197,72 @@ int validate_blob(const uint8_t* b, size_t n, BlobHeader* out) {
   if (coded == 1 ? (maxlen != 1) : (kraft != (uint64_t(1) << h.L)))
     return fail(UW_ERR_FORMAT, "code lengths are not a complete prefix code");
   const uint64_t nb = h.n_blocks;
-  const uint64_t W = (h.G + 31) / 32;
-  if (!section_ok(h.off_start_word, 4 * (nb + 1), n) || !section_ok(h.off_first_raw, 4 * (nb + 1), n) ||
-      !section_ok(h.off_raw_bits, 4 * nb * W, n) || !section_ok(h.off_lane_bits, 128 * nb, n) ||
-      !section_ok(h.off_stream, h.size_stream, n) || !section_ok(h.off_raw, h.size_raw, n) ||
-      !section_ok(h.off_sm, h.size_sm, n) || h.size_stream % 16)
+  const uint64_t W = (h.G + 31) / 32, T = (h.G + 15) / 16;
+  if (!section_ok(h.off_block, 4 * (nb + 1), n) || !section_ok(h.off_seg, 2 * nb * T, n) ||
+      !section_ok(h.off_queue, h.size_queue, n) || !section_ok(h.off_sm, h.size_sm, n) ||
+      h.off_queue + h.size_queue + 16 > n)
     return fail(UW_ERR_FORMAT, "section out of bounds or misaligned");
   const uint64_t g_last = n_groups - (nb - 1) * h.G;
   if (h.size_sm != (nb - 1) * uint64_t(h.G) * 64 + (g_last + 15) / 16 * 1024)
     return fail(UW_ERR_FORMAT, "bad sm section size");
-  if (h.size_raw != 64 * h.n_raw_groups) return fail(UW_ERR_FORMAT, "bad raw section size");
-  std::vector<uint32_t> sw(nb + 1), fr(nb + 1), rb(nb * W);
-  std::memcpy(sw.data(), b + h.off_start_word, 4 * (nb + 1));
-  std::memcpy(fr.data(), b + h.off_first_raw, 4 * (nb + 1));
-  std::memcpy(rb.data(), b + h.off_raw_bits, 4 * nb * W);
-  const uint16_t* lb = reinterpret_cast<const uint16_t*>(b + h.off_lane_bits);
-  if (sw[0] != 0 || fr[0] != 0 || uint64_t(sw[nb]) * 4 != h.size_stream || fr[nb] != h.n_raw_groups)
-    return fail(UW_ERR_FORMAT, "bad block table ends");
-  uint32_t max_stream = 0;
+  if (h.max_segment_bytes > 4064 || h.max_segment_bytes % 4) return fail(UW_ERR_FORMAT, "bad largest segment size");
+  std::vector<uint32_t> bo(nb + 1);
+  std::memcpy(bo.data(), b + h.off_block, 4 * (nb + 1));
+  std::vector<uint16_t> sg(nb * T);
+  std::memcpy(sg.data(), b + h.off_seg, 2 * nb * T);
+  if (bo[0] != 0 || bo[nb] != h.size_queue) return fail(UW_ERR_FORMAT, "bad block table ends");
+  uint32_t max_seg = 0;
+  uint64_t nraw_total = 0;
+  const uint8_t* q = b + h.off_queue;
   for (uint64_t blk = 0; blk < nb; ++blk) {
     const uint64_t gb = (blk + 1 == nb) ? g_last : h.G;
-    if (sw[blk + 1] < sw[blk] || (sw[blk + 1] - sw[blk]) % 4) return fail(UW_ERR_FORMAT, "bad start_word");
-    uint32_t nraw = 0;
+    const uint64_t nt = (gb + 15) / 16;
+    if (bo[blk + 1] < bo[blk] || bo[blk] % 4 || bo[blk + 1] - bo[blk] < 128 + 4 * W)
+      return fail(UW_ERR_FORMAT, "bad block offset");
+    const uint64_t words = (bo[blk + 1] - bo[blk]) / 4;
+    const uint8_t* d = q + bo[blk];
+    uint32_t rb[32];
+    std::memcpy(rb, d + 128, 4 * W);
+    // raw flags only for groups of the block; lane word counts in range; the
+    // words of the segments add up to every word of every lane, once
+    uint32_t nraw = 0, tile_raw[64] = {0};
     for (uint64_t w = 0; w < W; ++w) {
-      uint32_t bits = rb[blk * W + w];
       const uint64_t lo = 32 * w;
       if (lo + 32 > gb) {
-        uint32_t valid = gb > lo ? uint32_t(gb - lo) : 0;
-        if (valid < 32 && (bits >> valid)) return fail(UW_ERR_FORMAT, "raw bit beyond the block");
+        const uint32_t valid = gb > lo ? uint32_t(gb - lo) : 0;
+        if (valid < 32 && (rb[w] >> valid)) return fail(UW_ERR_FORMAT, "raw bit beyond the block");
       }
-      nraw += __builtin_popcount(bits);
+      nraw += __builtin_popcount(rb[w]);
+      for (int k = 0; k < 32; ++k)
+        if (rb[w] >> k & 1) tile_raw[(lo + k) / 16]++;
     }
-    if (fr[blk + 1] != fr[blk] + nraw) return fail(UW_ERR_FORMAT, "first_raw inconsistent with raw bits");
+    nraw_total += nraw;
     const uint64_t coded_groups = gb - nraw;
-    uint64_t total = 0;
+    uint64_t init = 0, later = 0;
     for (int l = 0; l < 64; ++l) {
-      uint64_t bits = lb[blk * 64 + l];
-      if (bits < coded_groups * uint64_t(minlen) || bits > coded_groups * uint64_t(maxlen))
-        return fail(UW_ERR_FORMAT, "lane bit count out of range");
-      total += bits;
+      uint16_t nl;
+      std::memcpy(&nl, d + 2 * l, 2);
+      const uint64_t lo_bits = coded_groups * uint64_t(minlen), hi_bits = coded_groups * uint64_t(maxlen);
+      if (nl < (lo_bits + 31) / 32 || nl > (hi_bits + 31) / 32) return fail(UW_ERR_FORMAT, "lane word count out of range");
+      init += std::min<uint64_t>(nl, 2);
+      later += nl > 2 ? nl - 2 : 0;
     }
-    const uint64_t words = sw[blk + 1] - sw[blk];
-    if (total > 32 * words || words != (total + 127) / 128 * 4)
-      return fail(UW_ERR_FORMAT, "block stream size inconsistent with lane bits");
-    max_stream = std::max<uint32_t>(max_stream, uint32_t(words * 4));
+    uint64_t prev = 0, taken = 0;
+    for (uint64_t t = 0; t < T; ++t) {
+      const uint64_t end = sg[blk * T + t];
+      if (end < prev || end > words || (t >= nt && end != prev)) return fail(UW_ERR_FORMAT, "bad segment table");
+      if (t < nt) {
+        const uint64_t fixed = 16 * tile_raw[t] + (t == 0 ? 32 + W + init : 0);
+        if (end - prev < fixed) return fail(UW_ERR_FORMAT, "segment shorter than its fixed part");
+        taken += end - prev - fixed;
+        max_seg = std::max<uint32_t>(max_seg, uint32_t(4 * (end - prev)));
+      }
+      prev = end;
+    }
+    if (prev != words || taken != later) return fail(UW_ERR_FORMAT, "segments inconsistent with the lane word counts");
   }
-  if (max_stream != h.max_block_stream_bytes) return fail(UW_ERR_FORMAT, "bad max block stream size");
+  if (nraw_total != h.n_raw_groups) return fail(UW_ERR_FORMAT, "raw group count mismatch");
+  if (max_seg != h.max_segment_bytes) return fail(UW_ERR_FORMAT, "bad largest segment size");
   *out = h;
   return UW_OK;
 }

@@ -1,0 +1,227 @@
+// Uncompressed kernels for gfx950: the bf16 product on the vector ALU (the
+// comparator, the product half of decompress-then-multiply and the plain-mode
+// path), the plain-mode copy and a streaming-read probe.
+#include <algorithm>
+
+#include "uw_device.h"
+
+namespace uw {
+namespace {
+
+// Wave-sum each accumulator and store it as row `row` of Y (lane 0 writes).
+template <int NBP, bool YBF16>
+__device__ inline void flush_row(float (&acc)[NBP], int64_t row, int nb_valid, void* Y, int64_t ldy, int lane) {
+#pragma unroll
+  for (int b = 0; b < NBP; ++b) {
+    const float s = wave_sum(acc[b]);
+    if (lane == 0 && b < nb_valid) {
+      if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + row] = f32_to_bf16(s);
+      else static_cast<float*>(Y)[b * ldy + row] = s;
+    }
+    acc[b] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Uncompressed bf16 product on the vector ALU (small batch): one wave per
+// output row, lanes stride the row in 16-byte chunks, X in LDS as [b][k].
+template <int NBP, bool XF32, bool YBF16>
+__global__ __launch_bounds__(256) void bf16_gemv_kernel(const uint16_t* __restrict__ W, int64_t rows, int64_t cols,
+                                                        int64_t ldw, const void* __restrict__ X, int64_t ldx, int nb_valid,
+                                                        void* __restrict__ Y, int64_t ldy) {
+  extern __shared__ uint32_t lds[];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave), waves = blockDim.x / kWave;
+  // X staged as fp32 [b][k] (fp32 input) or bf16 pairs [b][k/2]
+  const int64_t kp = cols / 2;
+  if (XF32) {
+    for (int64_t i = tid; i < cols * NBP; i += blockDim.x) {
+      const int b = int(i / cols);
+      const int64_t k = i - int64_t(b) * cols;
+      lds[i] = b < nb_valid ? f32_bits(static_cast<const float*>(X)[b * ldx + k]) : 0u;
+    }
+  } else {
+    for (int64_t i = tid; i < kp * NBP; i += blockDim.x) {
+      const int b = int(i / kp);
+      const int64_t k2 = i - int64_t(b) * kp;
+      const uint16_t* xr = static_cast<const uint16_t*>(X) + b * ldx + 2 * k2;
+      lds[i] = b < nb_valid ? (uint32_t(xr[0]) | (uint32_t(xr[1]) << 16)) : 0u;
+    }
+  }
+  __syncthreads();
+  const int64_t nchunks = cols / 8;
+  for (int64_t row = int64_t(blockIdx.x) * waves + wave; row < rows; row += int64_t(gridDim.x) * waves) {
+    const uint4* wr = reinterpret_cast<const uint4*>(W + row * ldw);
+    float acc[NBP];
+#pragma unroll
+    for (int b = 0; b < NBP; ++b) acc[b] = 0.f;
+    int64_t ch = lane;
+    for (; ch + 3 * kWave < nchunks; ch += 4 * kWave) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = wr[ch + u * kWave];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t k8 = (ch + u * kWave) * 8;
+        const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int b = 0; b < NBP; ++b) {
+          if (XF32) {
+            const float* xf = reinterpret_cast<const float*>(lds) + int64_t(b) * cols + k8;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[b] = __builtin_fmaf(bits_f32(wv[q] << 16), xf[2 * q], acc[b]);
+              acc[b] = __builtin_fmaf(bits_f32(wv[q] & 0xFFFF0000u), xf[2 * q + 1], acc[b]);
+            }
+          } else {
+            const uint4 xv = *reinterpret_cast<const uint4*>(lds + int64_t(b) * kp + k8 / 2);
+            acc[b] = dot2_bf16(wv[0], xv.x, acc[b]);
+            acc[b] = dot2_bf16(wv[1], xv.y, acc[b]);
+            acc[b] = dot2_bf16(wv[2], xv.z, acc[b]);
+            acc[b] = dot2_bf16(wv[3], xv.w, acc[b]);
+          }
+        }
+      }
+    }
+    for (; ch < nchunks; ch += kWave) {
+      const uint4 v = wr[ch];
+      const int64_t k8 = ch * 8;
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int b = 0; b < NBP; ++b) {
+        if (XF32) {
+          const float* xf = reinterpret_cast<const float*>(lds) + int64_t(b) * cols + k8;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[b] = __builtin_fmaf(bits_f32(wv[q] << 16), xf[2 * q], acc[b]);
+            acc[b] = __builtin_fmaf(bits_f32(wv[q] & 0xFFFF0000u), xf[2 * q + 1], acc[b]);
+          }
+        } else {
+          const uint4 xv = *reinterpret_cast<const uint4*>(lds + int64_t(b) * kp + k8 / 2);
+          acc[b] = dot2_bf16(wv[0], xv.x, acc[b]);
+          acc[b] = dot2_bf16(wv[1], xv.y, acc[b]);
+          acc[b] = dot2_bf16(wv[2], xv.z, acc[b]);
+          acc[b] = dot2_bf16(wv[3], xv.w, acc[b]);
+        }
+      }
+    }
+    flush_row<NBP, YBF16>(acc, row, nb_valid, Y, ldy, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming read: every byte read once with 16-byte loads, xor-folded into
+// one word per workgroup so the loads cannot be removed.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                         uint32_t* __restrict__ sink) {
+  uint32_t x = 0;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], e = src[i + 3 * stride];
+    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ e.x ^ e.y ^ e.z ^ e.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t s = 0;
+    for (int t = 0; t < int(blockDim.x); ++t) s ^= red[t];
+    sink[blockIdx.x] = s;
+  }
+}
+
+constexpr int kProbeBlocks = 2048;
+
+// Plain-mode matrices: a strided copy of the stored bf16 bits.
+__global__ void copy_plain_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
+                                  uint16_t* __restrict__ out, int64_t ld_out) {
+  const int64_t per_row = cols / 8;
+  const int64_t n = rows * per_row;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = i / per_row, c8 = i - r * per_row;
+    reinterpret_cast<uint4*>(out + r * ld_out)[c8] = reinterpret_cast<const uint4*>(src + r * cols)[c8];
+  }
+}
+
+template <int NBP, bool XF32, bool YBF16>
+int run_bf16(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X, int64_t ldx, int nb, void* Y,
+             int64_t ldy, void* stream) {
+  const size_t lds = XF32 ? size_t(cols) * NBP * 4 : size_t(cols / 2) * NBP * 4;
+  const int waves = 4;
+  const int64_t grid = std::min<int64_t>((rows + waves - 1) / waves, 8192);
+  auto kern = bf16_gemv_kernel<NBP, XF32, YBF16>;
+  allow_full_lds(kern);
+  hipLaunchKernelGGL(kern, dim3(int(grid)), dim3(waves * kWave), lds, static_cast<hipStream_t>(stream), W, rows, cols,
+                     ldw, X, ldx, nb, Y, ldy);
+  return hip_check(hipGetLastError(), "bf16_gemv_kernel launch");
+}
+
+template <int NBP>
+int run_bf16_xy(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X, int64_t ldx, int xt, int nb,
+                void* Y, int64_t ldy, int yt, void* stream) {
+  if (xt == UW_F32)
+    return yt == UW_BF16 ? run_bf16<NBP, true, true>(W, rows, cols, ldw, X, ldx, nb, Y, ldy, stream)
+                         : run_bf16<NBP, true, false>(W, rows, cols, ldw, X, ldx, nb, Y, ldy, stream);
+  return yt == UW_BF16 ? run_bf16<NBP, false, true>(W, rows, cols, ldw, X, ldx, nb, Y, ldy, stream)
+                       : run_bf16<NBP, false, false>(W, rows, cols, ldw, X, ldx, nb, Y, ldy, stream);
+}
+
+int bf16_chunk(int64_t cols, int64_t batch, bool xf32) {
+  int nbp = 8;
+  const size_t per = xf32 ? size_t(cols) * 4 : size_t(cols) * 2;
+  while (nbp > 1 && (nbp / 2 >= batch || per * nbp > size_t(kLdsLimit))) nbp /= 2;
+  return nbp;
+}
+
+}  // namespace
+
+int launch_copy_plain(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* out, int64_t ld_out, void* stream) {
+  const int64_t n = rows * (cols / 8);
+  const int grid = int(std::min<int64_t>((n + 255) / 256, 8192));
+  hipLaunchKernelGGL(copy_plain_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), src, rows, cols, out,
+                     ld_out);
+  return hip_check(hipGetLastError(), "copy_plain_kernel launch");
+}
+
+bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why) {
+  (void)batch;
+  const size_t per = xt == UW_F32 ? size_t(cols) * 4 : size_t(cols) * 2;
+  if (per > size_t(kLdsLimit)) {
+    if (why) *why = "x of this width does not fit in LDS";
+    return false;
+  }
+  return true;
+}
+
+int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X, int64_t batch,
+                     int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream) {
+  const int nbp = bf16_chunk(cols, batch, xt == UW_F32);
+  for (int64_t b0 = 0; b0 < batch; b0 += nbp) {
+    const int nb = int(std::min<int64_t>(nbp, batch - b0));
+    const void* Xb = static_cast<const char*>(X) + b0 * ldx * elem_size(xt);
+    void* Yb = static_cast<char*>(Y) + b0 * ldy * elem_size(yt);
+    int rc;
+    switch (nbp) {
+      case 1: rc = run_bf16_xy<1>(W, rows, cols, ldw, Xb, ldx, xt, nb, Yb, ldy, yt, stream); break;
+      case 2: rc = run_bf16_xy<2>(W, rows, cols, ldw, Xb, ldx, xt, nb, Yb, ldy, yt, stream); break;
+      case 4: rc = run_bf16_xy<4>(W, rows, cols, ldw, Xb, ldx, xt, nb, Yb, ldy, yt, stream); break;
+      default: rc = run_bf16_xy<8>(W, rows, cols, ldw, Xb, ldx, xt, nb, Yb, ldy, yt, stream); break;
+    }
+    if (rc) return rc;
+  }
+  return UW_OK;
+}
+
+size_t read_probe_sink_bytes() { return size_t(kProbeBlocks) * 4; }
+
+int launch_read_probe(const void* src, size_t bytes, void* sink, void* stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(kProbeBlocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), int64_t(bytes / 16), static_cast<uint32_t*>(sink));
+  return hip_check(hipGetLastError(), "read_probe_kernel launch");
+}
+
+}  // namespace uw

@@ -10,8 +10,11 @@
 //    stored raw, one decision per row instead of a per-weight branch
 //    (paragraph on rare exponents).
 // The code is length-limited (package-merge, Larmore & Hirschberg 1990) and
-// canonical (RFC 1951 3.2.2); blocks of G groups give every wavefront lane its
-// own bit stream so a wave decodes a block with a prefix sum of lane lengths.
+// canonical (RFC 1951 3.2.2).  Blocks of G groups give every wavefront lane
+// its own code stream, cut into 32-bit words; the words are stored in the
+// order the decoding wave takes them (refill checks every R groups, lanes in
+// order), in one segment per 16-group tile, so a decoder streams a block tile
+// by tile instead of holding all of it.
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -99,19 +102,94 @@ uint64_t align_up(uint64_t v) { return (v + kSectionAlign - 1) / kSectionAlign *
 
 struct Plan {
   int64_t rows, cols, n_groups;
-  int K, L, G;
-  uint32_t nb, W;
+  int K, L, G, R;
+  uint32_t nb, W, T;
   std::vector<uint8_t> pal;        // palette exponents
   std::vector<int> sym_of;         // exponent -> palette index or -1
   std::vector<uint8_t> code_len;   // per palette index
   std::vector<uint32_t> rev;       // bit-reversed code per palette index
   std::vector<uint8_t> raw;        // per group
-  std::vector<uint32_t> start_word, first_raw, raw_bits;
-  std::vector<uint16_t> lane_bits;
-  uint32_t max_stream = 0;
+  std::vector<std::vector<uint8_t>> data;  // per block: its segments back to back
+  std::vector<uint32_t> block_off;
+  std::vector<uint16_t> seg;
+  uint32_t max_seg = 0;
   uint64_t n_raw = 0;
-  uint64_t off_sw, off_fr, off_rb, off_lb, off_stream, size_stream, off_raw, size_raw, off_sm, size_sm, total;
+  uint64_t off_block, off_seg, off_queue, size_queue, off_sm, size_sm, total;
 };
+
+// The segments of one block (layout in uw_blob.cpp): every lane's code stream
+// in words, then the refill checks of the decoder replayed to order the words.
+void build_block(const Plan& p, const uint16_t* w, uint64_t blk, std::vector<uint8_t>& out, uint16_t* seg_out,
+                 uint32_t& nraw_out, uint32_t& max_seg) {
+  const int64_t g0 = int64_t(blk) * p.G, g1 = std::min<int64_t>(g0 + p.G, p.n_groups);
+  const int gb = int(g1 - g0);
+  const int ntiles = (gb + 15) / 16;
+  const int cap = (gb * p.L + 31) / 32 + 1;
+  std::vector<uint32_t> lw(64 * size_t(cap), 0);
+  uint32_t n[64], qm[64], taken[64];
+  uint32_t raw_bits[32] = {0};
+  uint32_t nraw = 0;
+  std::vector<uint8_t> lens(size_t(gb) * 64, 0);
+  for (int j = 0; j < gb; ++j) {
+    if (p.raw[g0 + j]) {
+      raw_bits[j / 32] |= 1u << (j % 32);
+      nraw++;
+      continue;
+    }
+    const uint16_t* q = w + 64 * (g0 + j);
+    for (int l = 0; l < 64; ++l) lens[size_t(j) * 64 + l] = p.code_len[p.sym_of[(q[l] >> 7) & 0xFF]];
+  }
+  for (int l = 0; l < 64; ++l) {
+    uint32_t* words = lw.data() + size_t(l) * cap;
+    uint64_t pos = 0;
+    for (int j = 0; j < gb; ++j) {
+      if (p.raw[g0 + j]) continue;
+      const int s = p.sym_of[(w[64 * (g0 + j) + l] >> 7) & 0xFF];
+      const uint32_t c = p.rev[s], len = p.code_len[s];
+      const uint32_t sh = uint32_t(pos & 31);
+      words[pos >> 5] |= c << sh;
+      if (sh + len > 32) words[(pos >> 5) + 1] |= c >> (32 - sh);
+      pos += len;
+    }
+    n[l] = uint32_t((pos + 31) / 32);
+    qm[l] = 30;
+    taken[l] = std::min<uint32_t>(n[l], 2);
+  }
+  // tile 0 starts with the lane word counts, the raw bitmap and each lane's first two words
+  out.clear();
+  for (int l = 0; l < 64; ++l) {
+    const uint16_t v = uint16_t(n[l]);
+    out.insert(out.end(), reinterpret_cast<const uint8_t*>(&v), reinterpret_cast<const uint8_t*>(&v) + 2);
+  }
+  auto put_word = [&](uint32_t v) {
+    out.insert(out.end(), reinterpret_cast<const uint8_t*>(&v), reinterpret_cast<const uint8_t*>(&v) + 4);
+  };
+  for (uint32_t i = 0; i < p.W; ++i) put_word(raw_bits[i]);
+  for (uint32_t i = 0; i < 2; ++i)
+    for (int l = 0; l < 64; ++l)
+      if (n[l] > i) put_word(lw[size_t(l) * cap + i]);
+  size_t seg_start = 0;
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = 16 * t, j1 = std::min(gb, j0 + 16);
+    for (int j = j0; j < j1; ++j)
+      if (p.raw[g0 + j])
+        for (int l = 0; l < 64; ++l) out.push_back(uint8_t((w[64 * (g0 + j) + l] >> 7) & 0xFF));
+    for (int j = j0; j < j1; ++j) {
+      for (int l = 0; l < 64; ++l) qm[l] += lens[size_t(j) * 64 + l];
+      if ((j + 1) % p.R) continue;
+      for (int l = 0; l < 64; ++l) {
+        if (qm[l] < 32) continue;
+        qm[l] -= 32;
+        if (taken[l] < n[l]) put_word(lw[size_t(l) * cap + taken[l]++]);
+      }
+    }
+    max_seg = std::max<uint32_t>(max_seg, uint32_t(out.size() - seg_start));
+    seg_start = out.size();
+    seg_out[t] = uint16_t(out.size() / 4);
+  }
+  for (uint32_t t = uint32_t(ntiles); t < p.T; ++t) seg_out[t] = uint16_t(out.size() / 4);
+  nraw_out = nraw;
+}
 
 void parallel_for(uint64_t n, const std::function<void(uint64_t, uint64_t)>& fn) {
   unsigned hw = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
@@ -239,54 +317,34 @@ extern "C" int uw_encode(const uint16_t* w, int64_t rows, int64_t cols, const uw
   canonical_codes(hc, code, rev);
   p.rev.assign(rev, rev + p.pal.size());
 
-  // block tables (first pass: sizes)
+  // segments of every block (first pass), then offsets and sizes
   p.nb = uint32_t((p.n_groups + p.G - 1) / p.G);
   p.W = uint32_t((p.G + 31) / 32);
-  p.start_word.assign(p.nb + 1, 0);
-  p.first_raw.assign(p.nb + 1, 0);
-  p.raw_bits.assign(uint64_t(p.nb) * p.W, 0);
-  p.lane_bits.assign(uint64_t(p.nb) * 64, 0);
-  std::vector<uint32_t> block_words(p.nb), block_raw(p.nb);
+  p.T = uint32_t((p.G + 15) / 16);
+  p.R = int(check_groups(uint32_t(p.L)));
+  p.data.assign(p.nb, {});
+  p.seg.assign(uint64_t(p.nb) * p.T, 0);
+  std::vector<uint32_t> block_raw(p.nb), block_max(p.nb);
   parallel_for(p.nb, [&](uint64_t a, uint64_t b) {
     for (uint64_t blk = a; blk < b; ++blk) {
-      const int64_t g0 = int64_t(blk) * p.G, g1 = std::min<int64_t>(g0 + p.G, p.n_groups);
-      uint64_t total = 0;
-      uint32_t nraw = 0;
-      uint32_t lanes[64] = {0};
-      for (int64_t g = g0; g < g1; ++g) {
-        if (p.raw[g]) {
-          p.raw_bits[blk * p.W + (g - g0) / 32] |= 1u << ((g - g0) % 32);
-          nraw++;
-          continue;
-        }
-        const uint16_t* q = w + 64 * g;
-        for (int l = 0; l < 64; ++l) lanes[l] += p.code_len[p.sym_of[(q[l] >> 7) & 0xFF]];
-      }
-      for (int l = 0; l < 64; ++l) {
-        p.lane_bits[blk * 64 + l] = uint16_t(lanes[l]);
-        total += lanes[l];
-      }
-      block_words[blk] = uint32_t((total + 127) / 128 * 4);
-      block_raw[blk] = nraw;
+      uint32_t mx = 0;
+      build_block(p, w, blk, p.data[blk], p.seg.data() + blk * p.T, block_raw[blk], mx);
+      block_max[blk] = mx;
     }
   });
+  p.block_off.assign(p.nb + 1, 0);
   for (uint32_t blk = 0; blk < p.nb; ++blk) {
-    p.start_word[blk + 1] = p.start_word[blk] + block_words[blk];
-    p.first_raw[blk + 1] = p.first_raw[blk] + block_raw[blk];
-    p.max_stream = std::max(p.max_stream, 4 * block_words[blk]);
+    p.block_off[blk + 1] = p.block_off[blk] + uint32_t(p.data[blk].size());
+    p.n_raw += block_raw[blk];
+    p.max_seg = std::max(p.max_seg, block_max[blk]);
   }
-  p.n_raw = p.first_raw[p.nb];
   const uint64_t g_last = uint64_t(p.n_groups) - uint64_t(p.nb - 1) * p.G;
-  p.size_stream = uint64_t(p.start_word[p.nb]) * 4;
-  p.size_raw = 64 * p.n_raw;
+  p.size_queue = p.block_off[p.nb];
   p.size_sm = uint64_t(p.nb - 1) * p.G * 64 + (g_last + 15) / 16 * 1024;
   uint64_t off = kHeaderBytes;
-  off = align_up(off); p.off_sw = off; off += 4 * (uint64_t(p.nb) + 1);
-  off = align_up(off); p.off_fr = off; off += 4 * (uint64_t(p.nb) + 1);
-  off = align_up(off); p.off_rb = off; off += 4 * uint64_t(p.nb) * p.W;
-  off = align_up(off); p.off_lb = off; off += 128 * uint64_t(p.nb);
-  off = align_up(off); p.off_stream = off; off += p.size_stream;
-  off = align_up(off); p.off_raw = off; off += p.size_raw;
+  off = align_up(off); p.off_block = off; off += 4 * (uint64_t(p.nb) + 1);
+  off = align_up(off); p.off_seg = off; off += 2 * uint64_t(p.nb) * p.T;
+  off = align_up(off); p.off_queue = off; off += p.size_queue;
   off = align_up(off); p.off_sm = off; off += p.size_sm;
   p.total = off;
   const bool use_plain = allow_plain && p.total - kHeaderBytes >= 2 * nw;
@@ -302,38 +360,17 @@ extern "C" int uw_encode(const uint16_t* w, int64_t rows, int64_t cols, const uw
 
   // second pass: emit
   std::memset(o, 0, p.total);
-  std::memcpy(o + p.off_sw, p.start_word.data(), 4 * (uint64_t(p.nb) + 1));
-  std::memcpy(o + p.off_fr, p.first_raw.data(), 4 * (uint64_t(p.nb) + 1));
-  std::memcpy(o + p.off_rb, p.raw_bits.data(), 4 * uint64_t(p.nb) * p.W);
-  std::memcpy(o + p.off_lb, p.lane_bits.data(), 128 * uint64_t(p.nb));
-  uint32_t* stream = reinterpret_cast<uint32_t*>(o + p.off_stream);
-  uint8_t* rawsec = o + p.off_raw;
+  std::memcpy(o + p.off_block, p.block_off.data(), 4 * (uint64_t(p.nb) + 1));
+  std::memcpy(o + p.off_seg, p.seg.data(), 2 * uint64_t(p.nb) * p.T);
   uint8_t* smsec = o + p.off_sm;
   parallel_for(p.nb, [&](uint64_t a, uint64_t b) {
     for (uint64_t blk = a; blk < b; ++blk) {
+      std::memcpy(o + p.off_queue + p.block_off[blk], p.data[blk].data(), p.data[blk].size());
       const int64_t g0 = int64_t(blk) * p.G, g1 = std::min<int64_t>(g0 + p.G, p.n_groups);
-      uint32_t* words = stream + p.start_word[blk];
-      uint64_t pos = 0;  // bit position inside the block stream
-      for (int l = 0; l < 64; ++l) {
-        for (int64_t g = g0; g < g1; ++g) {
-          if (p.raw[g]) continue;
-          const int s = p.sym_of[(w[64 * g + l] >> 7) & 0xFF];
-          const uint32_t c = p.rev[s], len = p.code_len[s];
-          const uint32_t sh = uint32_t(pos & 31);
-          words[pos >> 5] |= c << sh;
-          if (sh + len > 32) words[(pos >> 5) + 1] |= c >> (32 - sh);
-          pos += len;
-        }
-      }
-      uint64_t r = p.first_raw[blk];
       uint8_t* smb = smsec + uint64_t(blk) * p.G * 64;
       for (int64_t g = g0; g < g1; ++g) {
         const uint16_t* q = w + 64 * g;
         const int64_t j = g - g0;
-        if (p.raw[g]) {
-          for (int l = 0; l < 64; ++l) rawsec[64 * r + l] = uint8_t((q[l] >> 7) & 0xFF);
-          r++;
-        }
         uint8_t* t = smb + (j >> 4) * 1024 + (j & 15);
         for (int l = 0; l < 64; ++l) t[16 * l] = uint8_t(((q[l] >> 8) & 0x80) | (q[l] & 0x7F));
       }
@@ -348,19 +385,16 @@ extern "C" int uw_encode(const uint16_t* w, int64_t rows, int64_t cols, const uw
   h.n_blocks = p.nb;
   h.n_raw_groups = p.n_raw;
   h.total_bytes = p.total;
-  h.max_block_stream_bytes = p.max_stream;
+  h.max_segment_bytes = p.max_seg;
+  h.R = uint32_t(p.R);
   for (size_t i = 0; i < p.pal.size(); ++i) {
     h.palette[i] = p.pal[i];
     h.code_len[i] = p.code_len[i];
   }
-  h.off_start_word = p.off_sw;
-  h.off_first_raw = p.off_fr;
-  h.off_raw_bits = p.off_rb;
-  h.off_lane_bits = p.off_lb;
-  h.off_stream = p.off_stream;
-  h.size_stream = p.size_stream;
-  h.off_raw = p.off_raw;
-  h.size_raw = p.size_raw;
+  h.off_block = p.off_block;
+  h.off_seg = p.off_seg;
+  h.off_queue = p.off_queue;
+  h.size_queue = p.size_queue;
   h.off_sm = p.off_sm;
   h.size_sm = p.size_sm;
   h.crc32 = crc32(o + kHeaderBytes, p.total - kHeaderBytes);

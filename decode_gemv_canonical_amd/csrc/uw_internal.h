@@ -18,20 +18,24 @@ constexpr int kMaxK = 32;
 constexpr int kMaxL = 12;
 constexpr int kPairPeekBits = 12;  // two codes of <= 6 bits always fit in a 12-bit window
 
-// Parsed header of a blob (see the layout in uw.h).
+// Parsed header of a blob (layout in uw_blob.cpp).
 struct BlobHeader {
   uint32_t version = 0, flags = 0;
   int64_t rows = 0, cols = 0;
   uint32_t K = 0, L = 0, G = 0, n_blocks = 0;
   uint64_t n_raw_groups = 0, total_bytes = 0;
-  uint32_t crc32 = 0, max_block_stream_bytes = 0;
+  uint32_t crc32 = 0, max_segment_bytes = 0;
   uint8_t palette[32] = {0};
   uint8_t code_len[32] = {0};
-  uint64_t off_start_word = 0, off_first_raw = 0, off_raw_bits = 0, off_lane_bits = 0;
-  uint64_t off_stream = 0, size_stream = 0, off_raw = 0, size_raw = 0;
+  uint32_t R = 0;  // groups between two refill checks
+  uint64_t off_block = 0, off_seg = 0, off_queue = 0, size_queue = 0;
   uint64_t off_sm = 0, size_sm = 0, off_plain = 0, size_plain = 0;
   bool plain() const { return flags & kFlagPlain; }
 };
+
+// Groups between refill checks for a maximum code length L: the codes decoded
+// between two checks must fit in the 30 bits a lane always holds.
+inline uint32_t check_groups(uint32_t L) { return L <= 7 ? 4u : 2u; }
 
 // Serialise / parse the fixed 256-byte header (no validation in read).
 void header_write(const BlobHeader& h, uint8_t* dst);
@@ -54,20 +58,19 @@ int fail(int status, const std::string& msg);
 
 // Kernel-side description of a compressed matrix, passed by value.
 struct DevMatrix {
-  const uint32_t* start_word;
-  const uint32_t* first_raw;
-  const uint32_t* raw_bits;
-  const uint16_t* lane_bits;
-  const uint32_t* stream;
-  const uint8_t* raw;
+  const uint32_t* block_off;  // byte offset of each block's data in the queue
+  const uint16_t* seg;        // per block, end of each tile's segment (words)
+  const uint8_t* queue;
   const uint8_t* sm;
   const uint16_t* plain;
   int64_t rows, cols;
   int64_t n_groups;
   int32_t G, n_blocks, rb_words, gpr;  // gpr = groups per row = cols/64
+  int32_t T;                           // tiles (segment entries) per block = ceil(G/16)
+  int32_t R;                           // groups between refill checks
   int32_t L, n_sym;
-  int32_t stage_words;                 // LDS words of one wave's stage buffer (stream + raw bytes)
-  int32_t stage_raw_word;              // word offset of the raw-byte area inside the stage buffer
+  int32_t slot_bytes;                  // LDS bytes of one segment slot (>= the largest segment, multiple of 16)
+  int32_t seg_loads;                   // 1 KB direct loads that fill a slot
   int32_t unit_blocks;                 // blocks per work unit (a unit covers whole rows)
   int32_t n_units;
   uint32_t sym[32];                    // rev code | len << 16 | exponent << 24
@@ -94,6 +97,7 @@ bool fused_supported(const uw_matrix* m, int xt, std::string* why);
 int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, void* Y, int64_t ldy, int yt,
                       void* stream);
 bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why);
+int launch_copy_plain(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* out, int64_t ld_out, void* stream);
 int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X,
                      int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream);
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why);

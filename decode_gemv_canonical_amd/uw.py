@@ -49,7 +49,7 @@ class uw_info(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("K", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("G", ctypes.c_int32), ("plain", ctypes.c_int32), ("n_blocks", ctypes.c_int64),
                 ("n_raw_groups", ctypes.c_int64), ("total_bytes", ctypes.c_uint64),
-                ("max_block_stream_bytes", ctypes.c_uint32), ("palette", ctypes.c_uint8 * 32),
+                ("max_segment_bytes", ctypes.c_uint32), ("palette", ctypes.c_uint8 * 32),
                 ("code_len", ctypes.c_uint8 * 32), ("ratio", ctypes.c_double), ("bits_per_weight", ctypes.c_double)]
 
 

@@ -26,24 +26,29 @@
  *
  * Blob layout (the exchange format between uw_encode and the device kernels):
  * a 256-byte header followed by 256-byte aligned sections, all little-endian.
- *   header: "UWB1", u32 version=1, u32 header_bytes=256, u32 flags (bit 0 =
+ *   header: "UWB2", u32 version=2, u32 header_bytes=256, u32 flags (bit 0 =
  *   plain), i64 rows, i64 cols, u32 K, u32 L, u32 G, u32 n_blocks,
  *   u64 n_raw_groups, u64 total_bytes, u32 crc32 (of bytes [256,total)),
- *   u32 max block stream bytes, u8 palette[32], u8 code_len[32], then u64
- *   offsets: start_word, first_raw, raw_bits, lane_bits, stream (+size),
- *   raw (+size), sm (+size), plain (+size).
+ *   u32 largest segment bytes, u8 palette[32], u8 code_len[32], u32 R, u32 0,
+ *   then u64 offsets: block, seg, queue (+size), sm (+size), plain (+size).
  *   A group is 64 consecutive weights of the row-major matrix; block b holds
- *   groups [b*G, min((b+1)*G, rows*cols/64)); lane l of a block owns weight
- *   64*j + l of each of the block's groups j.
- *   start_word u32[n_blocks+1]: first 32-bit word of each block's stream;
- *   first_raw u32[n_blocks+1]: raw groups before each block;
- *   raw_bits u32[n_blocks*ceil(G/32)]: bit j = group j of the block is raw;
- *   lane_bits u16[n_blocks*64]: bits in each lane's code stream; a lane's
- *   stream starts at the exclusive prefix sum of the block's lane_bits;
- *   stream: per block, the 64 lane streams concatenated in lane order, codes
- *   of canonical (RFC 1951 3.2.2) length-limited Huffman codes over the
- *   palette, bit-reversed and packed LSB-first, zero padded to 16 bytes;
- *   raw: 64 exponent bytes per raw group;
+ *   groups [b*G, min((b+1)*G, rows*cols/64)); tile t of a block is its groups
+ *   [16t, 16t+16); lane l of a block owns weight 64*j + l of each group j.
+ *   Lane l's codes (canonical, RFC 1951 3.2.2, length-limited Huffman codes
+ *   over the palette, bit-reversed and packed LSB-first; raw groups skipped)
+ *   form n_l 32-bit words.  A decoding lane holds three words (w0, w1, w2) =
+ *   words (s-1, s, s+1) and qm, the bit offset in w0 of (next code - 2),
+ *   starting at s = 0, qm = 30.  After every R-th group (R = 4 for L <= 7,
+ *   else 2) each lane with qm >= 32 shifts by one word and, while it has
+ *   words left, takes its next one; the words taken at one check are stored
+ *   in lane order.
+ *   block u32[n_blocks+1]: byte offset of each block's data in the queue;
+ *   seg u16[n_blocks*ceil(G/16)]: end of tile t's segment, in words from the
+ *   block start;
+ *   queue: per block, tile 0's segment = u16 n_l[64], u32 raw bits
+ *   [ceil(G/32)], word 0 of the lanes with n_l >= 1, word 1 of the lanes with
+ *   n_l >= 2; every tile's segment then holds the 64 exponent bytes of each
+ *   of its raw groups and the words taken at its checks;
  *   sm: per block ceil(G_b/16) tiles of 1024 bytes, byte (j>>4)*1024 +
  *   l*16 + (j&15) = sign+mantissa byte ((s<<7)|m) of weight 64*j + l;
  *   plain (plain mode): the bf16 bits, row-major.
@@ -63,7 +68,7 @@ extern "C" {
 typedef enum {
   UW_OK = 0,
   UW_ERR_INVALID = -1,     /* a null/misaligned pointer, bad size or option      */
-  UW_ERR_FORMAT = -2,      /* the blob is not a valid UWB1 blob                  */
+  UW_ERR_FORMAT = -2,      /* the blob is not a valid UWB2 blob                  */
   UW_ERR_NOSPACE = -3,     /* an output or workspace buffer is too small         */
   UW_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed         */
   UW_ERR_UNSUPPORTED = -5  /* valid request that this build cannot run           */
@@ -95,7 +100,7 @@ typedef struct {
   int32_t K, L, G, plain;
   int64_t n_blocks, n_raw_groups;
   uint64_t total_bytes;
-  uint32_t max_block_stream_bytes;
+  uint32_t max_segment_bytes;
   uint8_t palette[32];
   uint8_t code_len[32];
   double ratio;           /* total_bytes / (2*rows*cols) */
@@ -125,7 +130,7 @@ const char* uw_last_error(void);
  * Exponent histogram and top-K palette (exponent-redundancy paragraph),
  * raw 64-weight groups (rare-exponents paragraph), package-merge code
  * lengths <= L and canonical codes (Huffman paragraph), blocks of G groups
- * with one code stream per wavefront lane.
+ * with one code stream per wavefront lane, stored tile by tile.
  *   w_bf16   host, rows*cols bf16 bit patterns, row-major, not modified.
  *   rows>=1, cols a positive multiple of 64.
  *   opts     may be NULL (defaults above).
@@ -141,7 +146,8 @@ int uw_encode(const uint16_t* w_bf16, int64_t rows, int64_t cols, const uw_encod
 
 /*
  * uw_blob_info (host) - validate a blob (header, section bounds, CRC32, code
- * lengths forming a prefix code, per-block stream sizes) and describe it.
+ * lengths forming a prefix code, segment tables consistent with the lane
+ * word counts) and describe it.
  * Errors: UW_ERR_INVALID (null), UW_ERR_FORMAT (anything inconsistent).
  */
 int uw_blob_info(const void* blob, size_t n, uw_info* info);
@@ -190,7 +196,7 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
  *            the chosen variant; may be NULL/0 for the fused variants).
  *   UW_VARIANT_FUSED_MFMA needs bf16 X that is 16-byte aligned with ldx a
  *   multiple of 8, cols a multiple of 1024, and G dividing or a multiple of
- *   cols/64 (else UW_ERR_UNSUPPORTED); it runs 64 batch rows per pass.
+ *   cols/64 (else UW_ERR_UNSUPPORTED); it runs 32 batch rows per pass.
  * batch == 0 is a no-op.  fp32 accumulation.
  * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE (workspace), UW_ERR_UNSUPPORTED, UW_ERR_HIP.
  */

@@ -13,32 +13,51 @@ and the library implement it independently.
 Layout (all integers little-endian; every section starts 256-byte aligned):
 
   header, 256 bytes
-     0 "UWB1"          4 u32 version=1      8 u32 header_bytes=256
+     0 "UWB2"          4 u32 version=2      8 u32 header_bytes=256
     12 u32 flags (bit 0: plain mode)       16 i64 rows   24 i64 cols
     32 u32 K (palette entries)             36 u32 L (max code length)
     40 u32 G (groups of 64 per block)      44 u32 n_blocks
     48 u64 n_raw_groups                    56 u64 total_bytes
-    64 u32 crc32 of bytes [256, total)     68 u32 max block stream bytes
+    64 u32 crc32 of bytes [256, total)     68 u32 largest segment, bytes
     72 u8 palette[32]                     104 u8 code_len[32]
-   136 u64 off_start_word  144 u64 off_first_raw  152 u64 off_raw_bits
-   160 u64 off_lane_bits   168 u64 off_stream     176 u64 size_stream
-   184 u64 off_raw         192 u64 size_raw       200 u64 off_sm
-   208 u64 size_sm         216 u64 off_plain      224 u64 size_plain
-  start_word  u32[n_blocks+1]  first 32-bit word of each block's stream
-  first_raw   u32[n_blocks+1]  raw groups in all earlier blocks
-  raw_bits    u32[n_blocks*W]  W = ceil(G/32); bit j (LSB first) = group j raw
-  lane_bits   u16[n_blocks*64] bits in each lane's stream
-  stream      per block: the 64 lane streams concatenated in lane order,
-              codes bit-reversed and packed LSB-first, zero padded to 16 bytes
-  raw         64 exponent bytes per raw group, groups in order
-  sm          per block, ceil(G_b/16) tiles of 1024 bytes; byte
-              (j>>4)*1024 + lane*16 + (j&15) is the sign+mantissa byte of
-              weight 64*j + lane of the block (missing groups are zero)
-  plain       (plain mode only) the bf16 bits, row-major
+   136 u32 R (groups per refill check)    140 u32 zero
+   144 u64 off_block   152 u64 off_seg     160 u64 off_queue  168 u64 size_queue
+   176 u64 off_sm      184 u64 size_sm     192 u64 off_plain  200 u64 size_plain
+  block   u32[n_blocks+1]  byte offset of each block's data in the queue section
+  seg     u16[n_blocks*T]  T = ceil(G/16); entry t = end of tile t's segment,
+                           in 4-byte words from the block's start (entries past
+                           the block's last tile repeat its end)
+  queue   per block, its segments back to back (each a whole number of words)
+  sm      per block, ceil(G_b/16) tiles of 1024 bytes; byte
+          (j>>4)*1024 + lane*16 + (j&15) is the sign+mantissa byte of weight
+          64*j + lane of the block (missing groups are zero)
+  plain   (plain mode only) the bf16 bits, row-major
 
 A group is 64 consecutive weights of the row-major matrix (cols % 64 == 0, so
-it never straddles rows).  Block b holds groups [b*G, min((b+1)*G, total)).
-Lane l of a block owns weight 64*j + l of each of its groups j.
+it never straddles rows).  Block b holds groups [b*G, min((b+1)*G, total)) =
+G_b groups; tile t of a block is its groups [16t, 16t+16).  Lane l of a block
+owns weight 64*j + l of each of its groups j.
+
+Code streams.  Lane l's codes (groups that are not raw, in increasing j; the
+codes bit-reversed and packed LSB-first) form a bit string of bits_l bits, cut
+into n_l = ceil(bits_l / 32) little-endian 32-bit words.  The decoder of a
+lane holds three words (w0, w1, w2) = words (s-1, s, s+1) after s shifts
+(word -1 reads as 0, so does any word past n_l - 1) and qm, the bit offset of
+(next code - 2) inside w0: at the block start s = 0 and qm = 30.  A code of
+length len is decoded from bits qm+2 ... of (w0, w1) and adds len to qm.
+After every R-th group of the block (group j with (j+1) % R == 0; raw groups
+count) every lane with qm >= 32 shifts: qm -= 32, w0 = w1, w1 = w2, and w2
+becomes the lane's next word, taken from the block's data, if the lane has
+taken fewer than n_l words.  R = 4 for L <= 7 and 2 otherwise, so the codes
+between two checks span at most 28 bits and always lie in (w0, w1).  The
+words taken at one check are stored in lane order; the checks of tile t
+store their words in tile t's segment.
+
+Segments.  Tile t's segment is: (tile 0 only) lane_words u16[64] = n_l,
+raw_bits u32[ceil(G/32)] (bit j, LSB first: group j is raw), word 0 of every
+lane with n_l >= 1 in lane order, word 1 of every lane with n_l >= 2 in lane
+order; then the 64 exponent bytes (lane order) of each raw group of the tile,
+in group order; then the words taken at the tile's checks.
 """
 from __future__ import annotations
 
@@ -50,8 +69,8 @@ import numpy as np
 
 from . import huffman
 
-MAGIC = b"UWB1"
-VERSION = 1
+MAGIC = b"UWB2"
+VERSION = 2
 HEADER_BYTES = 256
 FLAG_PLAIN = 1
 ALIGN = 256
@@ -78,6 +97,12 @@ def choose_groups_per_block(rows: int, cols: int) -> int:
     return max(small) if small else min(pool)
 
 
+def check_groups(L: int) -> int:
+    """R, the groups between two refill checks: the codes in between must fit
+    in the 30 bits a lane can always see (4 codes of <= 7 bits, else 2)."""
+    return 4 if L <= 7 else 2
+
+
 @dataclass
 class Header:
     rows: int
@@ -90,34 +115,30 @@ class Header:
     n_raw_groups: int
     total_bytes: int
     crc32: int
-    max_block_stream_bytes: int
+    max_segment_bytes: int
     palette: list
     code_len: list
-    off_start_word: int
-    off_first_raw: int
-    off_raw_bits: int
-    off_lane_bits: int
-    off_stream: int
-    size_stream: int
-    off_raw: int
-    size_raw: int
+    R: int
+    off_block: int
+    off_seg: int
+    off_queue: int
+    size_queue: int
     off_sm: int
     size_sm: int
     off_plain: int
     size_plain: int
 
 
-_HDR = struct.Struct("<4sIIIqqIIIIQQII32s32sQQQQQQQQQQQQ")
+_HDR = struct.Struct("<4sIIIqqIIIIQQII32s32sIIQQQQQQQQ")
 
 
 def _pack_header(h: Header) -> bytes:
     pal = bytes(h.palette) + bytes(32 - len(h.palette))
     cl = bytes(h.code_len) + bytes(32 - len(h.code_len))
     raw = _HDR.pack(MAGIC, VERSION, HEADER_BYTES, h.flags, h.rows, h.cols, h.K, h.L, h.G,
-                    h.n_blocks, h.n_raw_groups, h.total_bytes, h.crc32, h.max_block_stream_bytes,
-                    pal, cl, h.off_start_word, h.off_first_raw, h.off_raw_bits, h.off_lane_bits,
-                    h.off_stream, h.size_stream, h.off_raw, h.size_raw, h.off_sm, h.size_sm,
-                    h.off_plain, h.size_plain)
+                    h.n_blocks, h.n_raw_groups, h.total_bytes, h.crc32, h.max_segment_bytes,
+                    pal, cl, h.R, 0, h.off_block, h.off_seg, h.off_queue, h.size_queue,
+                    h.off_sm, h.size_sm, h.off_plain, h.size_plain)
     return raw + bytes(HEADER_BYTES - len(raw))
 
 
@@ -129,11 +150,10 @@ def parse_header(blob: bytes) -> Header:
         raise ValueError("bad magic/version")
     K = f[6]
     h = Header(rows=f[4], cols=f[5], flags=f[3], K=K, L=f[7], G=f[8], n_blocks=f[9],
-               n_raw_groups=f[10], total_bytes=f[11], crc32=f[12], max_block_stream_bytes=f[13],
-               palette=list(f[14][:K]), code_len=list(f[15][:K]),
-               off_start_word=f[16], off_first_raw=f[17], off_raw_bits=f[18], off_lane_bits=f[19],
-               off_stream=f[20], size_stream=f[21], off_raw=f[22], size_raw=f[23],
-               off_sm=f[24], size_sm=f[25], off_plain=f[26], size_plain=f[27])
+               n_raw_groups=f[10], total_bytes=f[11], crc32=f[12], max_segment_bytes=f[13],
+               palette=list(f[14][:K]), code_len=list(f[15][:K]), R=f[16],
+               off_block=f[18], off_seg=f[19], off_queue=f[20], size_queue=f[21],
+               off_sm=f[22], size_sm=f[23], off_plain=f[24], size_plain=f[25])
     if h.total_bytes != len(blob):
         raise ValueError("size mismatch")
     if zlib.crc32(blob[HEADER_BYTES:]) != h.crc32:
@@ -141,28 +161,31 @@ def parse_header(blob: bytes) -> Header:
     return h
 
 
-def _emit_lane_streams(codes_rev, lens_of, sym_idx, nonraw):
-    """Bit emission of one block: sym_idx[j, lane] (palette index), nonraw[j].
-
-    Returns (lane_bits[64], stream bytes padded to 16 bytes).  Each lane's codes
-    go LSB-first into its own stream in increasing j; lanes are concatenated in
-    lane order with no padding between them.
-    """
-    codes_rev = np.asarray(codes_rev, dtype=np.int64)
-    lens_of = np.asarray(lens_of, dtype=np.int64)
-    s = sym_idx[np.asarray(nonraw, dtype=bool)].T  # [lane, j] in stream order
-    lens = lens_of[s]
-    lane_bits = lens.sum(axis=1)
-    flat_len = lens.ravel()
-    flat_code = codes_rev[s].ravel()
-    offset = np.cumsum(flat_len) - flat_len  # first bit of each code
-    nbits = int(flat_len.sum())
-    padded = -(-nbits // 128) * 128
-    arr = np.zeros(padded, dtype=np.uint8)
-    for t in range(int(lens_of.max(initial=0))):
-        m = flat_len > t
-        arr[offset[m] + t] = (flat_code[m] >> t) & 1
-    return lane_bits, np.packbits(arr, bitorder="little").tobytes()
+def _lane_streams(codes_rev, code_len, sym, coded):
+    """Code streams of every (block, lane): sym[b, j, lane] palette indices,
+    coded[b, j] (group exists and is not raw).  Each lane's codes go LSB-first
+    into its own stream in increasing j.  Returns (words[b, lane, i] uint32,
+    n[b, lane] = words used, lens[b, j, lane] code lengths, 0 where not coded)."""
+    nb, G, _ = sym.shape
+    lens_of = np.asarray(code_len, dtype=np.int32)
+    rev = np.asarray(codes_rev, dtype=np.int64)
+    lens = lens_of[sym] * coded[:, :, None]
+    start = np.cumsum(lens, axis=1, dtype=np.int32) - lens  # first bit of each code in its lane stream
+    bits = lens.sum(axis=1)  # [nb, 64]
+    maxw = max(1, -(-int(bits.max(initial=0)) // 32)) + 1
+    bi, ji, li = np.nonzero(lens)
+    code = rev[sym[bi, ji, li]]
+    st = start[bi, ji, li].astype(np.int64)
+    # a code at stream bit st lands in word st // 32, its high part (if it
+    # crosses the word end) in the next word; codes never overlap, so the
+    # per-word sums of the shifted parts are the word values (exact in fp64)
+    lo = (code << (st % 32)) & 0xFFFFFFFF
+    hi = code >> (32 - st % 32)
+    slot = (bi * 64 + li) * maxw + st // 32
+    acc = np.bincount(slot, weights=lo.astype(np.float64), minlength=nb * 64 * maxw)
+    acc += np.bincount(slot + 1, weights=hi.astype(np.float64), minlength=nb * 64 * maxw)[: nb * 64 * maxw]
+    words = acc.astype(np.uint64).astype(np.uint32).reshape(nb, 64, maxw)
+    return words, -(-bits // 32), lens
 
 
 def encode(w_bits, K: int = 16, L: int = 6, G: int | None = None, allow_plain: bool = True) -> bytes:
@@ -214,48 +237,87 @@ def encode(w_bits, K: int = 16, L: int = 6, G: int | None = None, allow_plain: b
     for i, s in enumerate(pal):
         lut[s] = i
     sym = lut[eg]
+    R = check_groups(L)
 
     n_blocks = -(-n_groups // G)
     W = -(-G // 32)
-    start_word = np.zeros(n_blocks + 1, dtype=np.uint32)
-    first_raw = np.zeros(n_blocks + 1, dtype=np.uint32)
-    raw_bits = np.zeros(n_blocks * W, dtype=np.uint32)
-    lane_bits = np.zeros(n_blocks * 64, dtype=np.uint16)
-    streams = []
+    T = -(-G // 16)
+    pad = n_blocks * G - n_groups
+    symb = np.concatenate([sym.astype(np.int16), np.zeros((pad, 64), np.int16)]).reshape(n_blocks, G, 64)
+    rawb = np.concatenate([raw, np.zeros(pad, bool)]).reshape(n_blocks, G)
+    live = (np.arange(n_blocks)[:, None] * G + np.arange(G)[None, :]) < n_groups
+    coded_g = live & ~rawb
+    words, lane_n, lens = _lane_streams(codes_rev, code_len, symb, coded_g)
+    gb = np.minimum(G, n_groups - np.arange(n_blocks) * G)
+
+    # the decoder's refill checks, all blocks and lanes at once
+    qm = np.full((n_blocks, 64), 30, dtype=np.int64)
+    taken = np.minimum(lane_n, 2)
+    checks = []  # (tile, need[b, lane], word[b, lane]) per check
+    for j in range(G):
+        qm += lens[:, j, :]
+        if (j + 1) % R == 0:
+            chk = live[:, j][:, None]
+            assert (qm[chk[:, 0]] < 64).all()
+            shift = chk & (qm >= 32)
+            need = shift & (taken < lane_n)
+            idx = np.minimum(taken, words.shape[2] - 1)
+            val = np.take_along_axis(words, idx[:, :, None], axis=2)[:, :, 0]
+            checks.append((j // 16, need, val))
+            qm = np.where(shift, qm - 32, qm)
+            taken = taken + need
+    assert np.array_equal(taken, lane_n), "every word is taken exactly once"
+    c_tile = np.array([c[0] for c in checks], dtype=np.int64)
+    c_need = np.stack([c[1] for c in checks], axis=1) if checks else np.zeros((n_blocks, 0, 64), bool)
+    c_val = np.stack([c[2] for c in checks], axis=1) if checks else np.zeros((n_blocks, 0, 64), np.uint32)
+    raw_bits = np.zeros((n_blocks, W), dtype=np.uint32)
+    for j in range(G):
+        raw_bits[:, j // 32] |= (rawb[:, j].astype(np.uint32) << np.uint32(j % 32))
+    lanes_has = [lane_n >= 1, lane_n >= 2]
+
+    block_off = np.zeros(n_blocks + 1, dtype=np.uint32)
+    seg = np.zeros(n_blocks * T, dtype=np.uint16)
+    datas = []
     sm_tiles = []
-    words = 0
-    nraw = 0
-    max_stream = 0
+    nbytes = 0
+    max_seg = 0
     for b in range(n_blocks):
         g0, g1 = b * G, min((b + 1) * G, n_groups)
-        nonraw = ~raw[g0:g1]
-        lb, sbytes = _emit_lane_streams(codes_rev, code_len, sym[g0:g1], nonraw)
-        lane_bits[b * 64:(b + 1) * 64] = lb
-        start_word[b] = words
-        first_raw[b] = nraw
-        words += len(sbytes) // 4
-        max_stream = max(max_stream, len(sbytes))
-        streams.append(sbytes)
-        for j in range(g1 - g0):
-            if raw[g0 + j]:
-                raw_bits[b * W + j // 32] |= np.uint32(1 << (j % 32))
-                nraw += 1
         ntiles = -(-(g1 - g0) // 16)
+        head = (lane_n[b].astype("<u2").tobytes() + raw_bits[b].astype("<u4").tobytes()
+                + words[b, lanes_has[0][b], 0].astype("<u4").tobytes()
+                + words[b, lanes_has[1][b], 1].astype("<u4").tobytes())
+        taken_vals = c_val[b][c_need[b]]  # (check, lane) order
+        per_check = c_need[b].sum(axis=1)
+        per_tile = np.bincount(c_tile, weights=per_check, minlength=T).astype(np.int64)
+        cut = np.concatenate([[0], np.cumsum(per_tile)])
+        end = 0
+        parts = []
+        for t in range(T):
+            if t < ntiles:
+                rj = [j for j in range(16 * t, min(16 * t + 16, g1 - g0)) if rawb[b, j]]
+                segb = ((head if t == 0 else b"") + b"".join(eg[g0 + j].tobytes() for j in rj)
+                        + taken_vals[cut[t]:cut[t + 1]].astype("<u4").tobytes())
+                parts.append(segb)
+                end += len(segb)
+                max_seg = max(max_seg, len(segb))
+            seg[b * T + t] = end // 4
+        block_off[b] = nbytes
+        data = b"".join(parts)
+        datas.append(data)
+        nbytes += len(data)
         tile = np.zeros((ntiles * 16, 64), dtype=np.uint8)
         tile[: g1 - g0] = smg[g0:g1]
         # (j>>4)*1024 + lane*16 + (j&15): tiles of [lane][16 groups]
         sm_tiles.append(tile.reshape(ntiles, 16, 64).transpose(0, 2, 1).tobytes())
-    start_word[n_blocks] = words
-    first_raw[n_blocks] = nraw
-    raw_bytes = eg[raw].tobytes()
-    stream = b"".join(streams)
+    block_off[n_blocks] = nbytes
+    queue = b"".join(datas)
     smb = b"".join(sm_tiles)
 
     off = HEADER_BYTES
     sections = {}
-    for name, payload in (("start_word", start_word.tobytes()), ("first_raw", first_raw.tobytes()),
-                          ("raw_bits", raw_bits.tobytes()), ("lane_bits", lane_bits.tobytes()),
-                          ("stream", stream), ("raw", raw_bytes), ("sm", smb)):
+    for name, payload in (("block", block_off.tobytes()), ("seg", seg.tobytes()), ("queue", queue),
+                          ("sm", smb)):
         off = _align(off)
         sections[name] = (off, payload)
         off += len(payload)
@@ -267,12 +329,10 @@ def encode(w_bits, K: int = 16, L: int = 6, G: int | None = None, allow_plain: b
     for name, (o, payload) in sections.items():
         body[o:o + len(payload)] = payload
     h = Header(rows=rows, cols=cols, flags=0, K=len(pal), L=L, G=G, n_blocks=n_blocks,
-               n_raw_groups=nraw, total_bytes=total, crc32=0, max_block_stream_bytes=max_stream,
-               palette=pal, code_len=code_len,
-               off_start_word=sections["start_word"][0], off_first_raw=sections["first_raw"][0],
-               off_raw_bits=sections["raw_bits"][0], off_lane_bits=sections["lane_bits"][0],
-               off_stream=sections["stream"][0], size_stream=len(stream),
-               off_raw=sections["raw"][0], size_raw=len(raw_bytes),
+               n_raw_groups=int(raw.sum()), total_bytes=total, crc32=0, max_segment_bytes=max_seg,
+               palette=pal, code_len=code_len, R=R,
+               off_block=sections["block"][0], off_seg=sections["seg"][0],
+               off_queue=sections["queue"][0], size_queue=len(queue),
                off_sm=sections["sm"][0], size_sm=len(smb), off_plain=0, size_plain=0)
     h.crc32 = zlib.crc32(bytes(body[HEADER_BYTES:]))
     body[:HEADER_BYTES] = _pack_header(h)
@@ -287,9 +347,8 @@ def _plain_blob(w, rows, cols) -> bytes:
     body[off:] = payload
     h = Header(rows=rows, cols=cols, flags=FLAG_PLAIN, K=0, L=0, G=0, n_blocks=0, n_raw_groups=0,
                total_bytes=total, crc32=zlib.crc32(bytes(body[HEADER_BYTES:])),
-               max_block_stream_bytes=0, palette=[], code_len=[],
-               off_start_word=0, off_first_raw=0, off_raw_bits=0, off_lane_bits=0,
-               off_stream=0, size_stream=0, off_raw=0, size_raw=0, off_sm=0, size_sm=0,
+               max_segment_bytes=0, palette=[], code_len=[], R=0,
+               off_block=0, off_seg=0, off_queue=0, size_queue=0, off_sm=0, size_sm=0,
                off_plain=off, size_plain=len(payload))
     body[:HEADER_BYTES] = _pack_header(h)
     return bytes(body)
@@ -302,29 +361,33 @@ def _section(blob: bytes, off: int, count: int, dtype) -> np.ndarray:
 def decode(blob: bytes) -> np.ndarray:
     """blob -> bf16 bit patterns [rows, cols] (uint16).
 
-    Lane-lockstep: every (block, lane) stream advances one symbol per group
-    step, all streams at once; the loop runs over the group index j only.  A
-    symbol is found by reading the next L bits of the stream and matching them
-    against each code's bit-reversed pattern of its own length.
+    Lane-lockstep over all blocks at once: every (block, lane) decoder holds
+    its three-word window and advances one group per step; the loop runs over
+    the group index j only.  A code is found by reading the next L window bits
+    and matching them against each code's bit-reversed pattern of its own
+    length.  At each refill check the lanes that shift take their next words
+    from the current tile's segment in lane order.
     """
     h = parse_header(blob)
     rows, cols = h.rows, h.cols
     if h.flags & FLAG_PLAIN:
         return _section(blob, h.off_plain, rows * cols, "<u2").reshape(rows, cols).astype(np.uint16)
     n_groups = rows * cols // 64
-    nb, G, W = h.n_blocks, h.G, -(-h.G // 32)
-    start_word = _section(blob, h.off_start_word, nb + 1, "<u4").astype(np.int64)
-    first_raw = _section(blob, h.off_first_raw, nb + 1, "<u4").astype(np.int64)
-    raw_bits = _section(blob, h.off_raw_bits, nb * W, "<u4").astype(np.int64).reshape(nb, W)
-    lane_bits = _section(blob, h.off_lane_bits, nb * 64, "<u2").astype(np.int64).reshape(nb, 64)
-    stream_bits = np.unpackbits(np.frombuffer(blob, dtype=np.uint8, count=h.size_stream,
-                                              offset=h.off_stream), bitorder="little")
-    stream_bits = np.concatenate([stream_bits, np.zeros(16, dtype=np.uint8)])
-    raw = _section(blob, h.off_raw, h.size_raw, np.uint8)
+    nb, G, R = h.n_blocks, h.G, h.R
+    W, T = -(-G // 32), -(-G // 16)
+    if R != check_groups(h.L):
+        raise ValueError("refill interval does not match L")
+    block_off = _section(blob, h.off_block, nb + 1, "<u4").astype(np.int64)
+    seg = _section(blob, h.off_seg, nb * T, "<u2").astype(np.int64).reshape(nb, T)
+    queue = np.frombuffer(blob, dtype=np.uint8, count=h.size_queue, offset=h.off_queue)
+    qwords = np.concatenate([queue, np.zeros(4, np.uint8)])
     sm_all = _section(blob, h.off_sm, h.size_sm, np.uint8)
 
+    def word_at(byte_off):  # little-endian u32 at byte offsets (array)
+        b = qwords[byte_off[..., None] + np.arange(4)].astype(np.int64)
+        return b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+
     codes = huffman.canonical_codes(h.code_len, h.palette)
-    # table of the next L stream bits (bit t of the index = t-th next stream bit)
     sym_of = np.full(1 << h.L, -1, dtype=np.int64)
     len_of = np.zeros(1 << h.L, dtype=np.int64)
     for s, (c, l) in enumerate(zip(codes, h.code_len)):
@@ -336,40 +399,85 @@ def decode(blob: bytes) -> np.ndarray:
                 sym_of[idx] = s
                 len_of[idx] = l
     pal = np.array(h.palette, dtype=np.uint8)
-
-    # per (block, lane) bit position: block base + exclusive prefix of lane bits
-    lane_start = np.cumsum(lane_bits, axis=1) - lane_bits
-    pos = start_word[:nb, None] * 32 + lane_start  # [nb, 64]
-    out_e = np.zeros((nb * G + 16, 64), dtype=np.uint8)
-    raw_seen = np.zeros(nb, dtype=np.int64)
-    weights_of_bit = (1 << np.arange(h.L, dtype=np.int64))
     lanes = np.arange(64)
+    blocks = np.arange(nb)
+    gb = np.minimum(G, n_groups - blocks * G)  # groups per block
+    base = block_off[:nb]  # byte offset of each block's data
+
+    # tile 0 head of every block
+    lane_n = word_at(base[:, None] + 2 * lanes[None, :]) & 0xFFFF  # two bytes read as part of a word
+    raw_bits = word_at(base[:, None] + 128 + 4 * np.arange(W)[None, :])
+    pos = base + 128 + 4 * W  # byte position of the next word to take / raw bytes
+    w0 = np.zeros((nb, 64), dtype=np.int64)
+    w1 = np.zeros((nb, 64), dtype=np.int64)
+    w2 = np.zeros((nb, 64), dtype=np.int64)
+    for i, wr in ((0, w1), (1, w2)):
+        has = lane_n > i
+        rank = np.cumsum(has, axis=1) - has
+        got = word_at(pos[:, None] + 4 * rank)
+        wr[has] = got[has]
+        pos = pos + 4 * has.sum(axis=1)
+    taken = np.minimum(lane_n, 2)
+    qm = np.full((nb, 64), 30, dtype=np.int64)
+    out_e = np.zeros((nb * G + 16, 64), dtype=np.uint8)
+    mask_l = (1 << h.L) - 1
+    rpos = pos  # raw exponent bytes of the current tile
     for j in range(G):
-        gidx = np.arange(nb) * G + j
-        valid = gidx < n_groups
-        is_raw = ((raw_bits[:, j // 32] >> (j % 32)) & 1).astype(bool) & valid
-        coded = valid & ~is_raw
-        if coded.any():
-            p = pos[coded]
-            peek = (stream_bits[p[:, :, None] + np.arange(h.L)] * weights_of_bit).sum(axis=2)
-            s = sym_of[peek]
-            if (s < 0).any():
-                raise ValueError("invalid code in stream")
-            out_e[gidx[coded]] = pal[s]
-            pos[coded] = p + len_of[peek]
+        live = j < gb
+        t = j // 16
+        if j % 16 == 0:
+            # a tile's segment: (tile 0: the head read above) its raw groups'
+            # exponent bytes, then the words its checks take
+            if j > 0:
+                rpos = np.where(live, base + 4 * seg[:, t - 1], pos)
+            n_raw_t = np.zeros(nb, dtype=np.int64)
+            for jj in range(j, min(j + 16, G)):
+                n_raw_t += ((raw_bits[:, jj // 32] >> (jj % 32)) & 1) * (jj < gb)
+            pos = rpos + 64 * n_raw_t
+        gidx = blocks * G + j
+        is_raw = ((raw_bits[:, j // 32] >> (j % 32)) & 1).astype(bool) & live
+        coded = live & ~is_raw
         if is_raw.any():
-            ridx = first_raw[:nb][is_raw] + raw_seen[is_raw]
-            out_e[gidx[is_raw]] = raw[(ridx[:, None] * 64 + lanes[None, :])]
-            raw_seen[is_raw] += 1
-    # every lane must end exactly where the next lane starts
-    if not np.array_equal(pos - start_word[:nb, None] * 32, lane_start + lane_bits):
-        raise ValueError("lane stream length mismatch")
+            out_e[gidx[is_raw]] = qwords[rpos[is_raw][:, None] + lanes[None, :]]
+            rpos = rpos + 64 * is_raw
+        if coded.any():
+            win = (w0 | (w1 << 32)) >> (qm + 2)
+            idx = win & mask_l
+            s = sym_of[idx]
+            if (s[coded] < 0).any():
+                raise ValueError("invalid code in stream")
+            out_e[gidx[coded]] = pal[s[coded]]
+            qm = np.where(coded[:, None], qm + len_of[idx], qm)
+        if (j + 1) % R == 0:
+            chk = live[:, None]
+            if (qm[live] >= 64).any():
+                raise ValueError("window overrun")
+            shift = chk & (qm >= 32)
+            need = shift & (taken < lane_n)
+            rank = np.cumsum(need, axis=1) - need
+            got = word_at(pos[:, None] + 4 * rank)
+            qm = np.where(shift, qm - 32, qm)
+            w0 = np.where(shift, w1, w0)
+            w1 = np.where(shift, w2, w1)
+            w2 = np.where(shift, np.where(need, got, 0), w2)
+            taken = taken + need
+            pos = pos + 4 * need.sum(axis=1)
+        if (j % 16 == 15) or (j == G - 1):
+            # every tile's segment ends exactly where its words end
+            end_t = base + 4 * seg[:, t]
+            fin = live & ((j == gb - 1) | (j % 16 == 15))
+            if not np.array_equal(pos[fin], end_t[fin]):
+                raise ValueError("segment length mismatch")
+    if not np.array_equal(taken, lane_n):
+        raise ValueError("lane word count mismatch")
+    if not np.array_equal(base + 4 * seg[np.arange(nb), (gb - 1) // 16], block_off[1:]):
+        raise ValueError("block length mismatch")
     e = out_e[:n_groups]
     # sm bytes: block b, group j, lane l at b*G*64 + (j>>4)*1024 + l*16 + (j&15)
     g = np.arange(n_groups)
     b, j = g // G, g % G
-    base = b * G * 64 + (j >> 4) * 1024 + (j & 15)
-    smg = sm_all[base[:, None] + lanes[None, :] * 16]
+    sbase = b * G * 64 + (j >> 4) * 1024 + (j & 15)
+    smg = sm_all[sbase[:, None] + lanes[None, :] * 16]
     return huffman.join_bf16(e, smg).reshape(rows, cols)
 
 

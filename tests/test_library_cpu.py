@@ -91,7 +91,18 @@ def test_validator_rejects_consistent_but_wrong_tables():
         struct.pack_into("<I", x, 64, zlib.crc32(bytes(x[256:])))
 
     bad = bytearray(b)
-    struct.pack_into("<H", bad, h.off_lane_bits, 4000)  # a lane longer than its block
+    struct.pack_into("<H", bad, h.off_queue, 4000)  # lane 0 of block 0: more words than its block can hold
+    refresh(bad)
+    with pytest.raises(uw.UwError):
+        uw.uw_blob_info(bytes(bad))
+    bad = bytearray(b)
+    first = struct.unpack_from("<H", bad, h.off_seg)[0]
+    struct.pack_into("<H", bad, h.off_seg, first + 1)  # tile 0's segment one word longer, tile 1's shorter
+    refresh(bad)
+    with pytest.raises(uw.UwError):
+        uw.uw_blob_info(bytes(bad))
+    bad = bytearray(b)
+    struct.pack_into("<I", bad, h.off_block + 4, struct.unpack_from("<I", bad, h.off_block + 4)[0] + 4)
     refresh(bad)
     with pytest.raises(uw.UwError):
         uw.uw_blob_info(bytes(bad))
