@@ -102,6 +102,70 @@ int uw_blob_info(const void* blob, size_t n, uw_info* info) {
   return UW_OK;
 }
 
+namespace {
+// Flat walk (G and the groups per row multiples of 16, so no tile crosses a
+// row): one descriptor per tile for the loads of its step, two words: the
+// 16-byte aligned floor of the tile's segment (byte offset in the queue) and,
+// in byte i, 64 minus the lanes of the i-th of the nq 1 KB loads from that
+// floor (at least one lane, so every step issues the same number of loads).  A load with nothing
+// to move has lane 0 read 16 bytes at floor + 1024 i, so the blob must
+// extend that far past the queue; where it does not, the walk by blocks is
+// used instead.
+int build_step_table(const uint8_t* hb, size_t n, uw_matrix* m) {
+  const BlobHeader& h = m->h;
+  DevMatrix& d = m->dev;
+  d.flat = 0;
+  d.steps = nullptr;
+  d.n_tiles = 0;
+  if (h.G % 16 || d.gpr % 16) return UW_OK;
+  // the loads address the queue from 1 KB before it and the sign+mantissa
+  // section with 32-bit offsets
+  const uint64_t extent = 1024 + h.size_queue + 1024 * uint64_t(d.nq - 1) + 16;
+  if (h.off_queue + extent - 1024 > n || extent >= (uint64_t(1) << 32) || h.size_sm >= (uint64_t(1) << 32))
+    return UW_OK;
+  const uint64_t nb = h.n_blocks, T = d.T;
+  const int64_t n_tiles = d.n_groups / 16;
+  std::vector<uint32_t> st(2 * size_t(n_tiles + 1), 0u);  // + a spare entry read past the last step
+  const uint8_t* bo = hb + h.off_block;
+  const uint8_t* sg = hb + h.off_seg;
+  int64_t u = 0;
+  for (uint64_t blk = 0; blk < nb; ++blk) {
+    uint32_t b_off, start;
+    std::memcpy(&b_off, bo + 4 * blk, 4);
+    const uint64_t gb = std::min<uint64_t>(h.G, uint64_t(d.n_groups) - blk * h.G);
+    start = b_off;
+    for (uint64_t t = 0; t < gb / 16; ++t, ++u) {
+      uint16_t e;
+      std::memcpy(&e, sg + 2 * (blk * T + t), 2);
+      const uint32_t end = b_off + 4u * e;
+      const uint32_t floor16 = start & ~15u;
+      const int64_t len = int64_t(end) - floor16;
+      uint32_t shifts = 0;  // load i runs on lanes < n_i: its exec mask is ~0 >> (64 - n_i)
+      for (int i = 0; i < d.nq; ++i) {
+        const int64_t k = std::clamp<int64_t>((len - 1024 * i + 15) / 16, 1, 64);
+        shifts |= uint32_t(64 - k) << (8 * i);
+      }
+      st[2 * u] = floor16;
+      st[2 * u + 1] = shifts;
+      start = end;
+    }
+  }
+  if (u != n_tiles) return fail(UW_ERR_FORMAT, "tile count does not match the shape");
+  void* p = nullptr;
+  if (hipMalloc(&p, st.size() * 4) != hipSuccess) return fail(UW_ERR_HIP, "uw_matrix_create: cannot allocate the step table");
+  if (hipMemcpy(p, st.data(), st.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(p);
+    return fail(UW_ERR_HIP, "uw_matrix_create: cannot copy the step table");
+  }
+  m->d_steps = p;
+  d.steps = static_cast<const uint32_t*>(p);
+  d.n_tiles = int32_t(n_tiles);
+  d.q_extent = uint32_t(extent);
+  d.flat = 1;
+  return UW_OK;
+}
+}  // namespace
+
 int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_matrix** out) {
   if (!host_blob || !d_blob || !out) return fail(UW_ERR_INVALID, "uw_matrix_create: null pointer");
   if (!aligned(d_blob, 256)) return fail(UW_ERR_INVALID, "uw_matrix_create: device blob must be 256-byte aligned");
@@ -145,16 +209,36 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
     // before it, and lanes that take no word read the word after its end)
     d.slot_bytes = int32_t((h.max_segment_bytes + 16 + 15) / 16 * 16);
     d.seg_loads = std::max(1, (d.slot_bytes + 1023) / 1024);
+    // every step issues nq loads; a load with no bytes to move still has
+    // lane 0 write 16 bytes at 1024 * i, which the slot must hold
+    d.nq = d.seg_loads <= 2 ? 2 : 4;
+    d.slot_bytes = std::max(d.slot_bytes, 1024 * (d.nq - 1) + 16);
     // a work unit covers whole rows: lcm(G, groups per row) groups
     const int64_t lcm = int64_t(h.G) / gcd64(h.G, d.gpr) * d.gpr;
     d.unit_blocks = int32_t(lcm / h.G);
+    d.rows_per_unit = int32_t(lcm / d.gpr);
     d.n_units = int32_t((int64_t(h.n_blocks) + d.unit_blocks - 1) / d.unit_blocks);
+    rc = build_step_table(static_cast<const uint8_t*>(host_blob), n, m);
+    if (rc) {
+      uw_matrix_destroy(m);
+      return rc;
+    }
   }
   *out = m;
   return UW_OK;
 }
 
-void uw_matrix_destroy(uw_matrix* m) { delete m; }
+void uw_matrix_destroy(uw_matrix* m) {
+  if (!m) return;
+  if (m->d_steps) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != m->device) (void)hipSetDevice(m->device);
+    (void)hipFree(m->d_steps);
+    if (cur != m->device && cur >= 0) (void)hipSetDevice(cur);
+  }
+  delete m;
+}
 
 int uw_decompress(const uw_matrix* m, uint16_t* d_out, int64_t ld_out, void* stream) {
   if (int rc = check_matrix(m)) return rc;

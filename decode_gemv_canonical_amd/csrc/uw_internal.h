@@ -71,6 +71,13 @@ struct DevMatrix {
   int32_t L, n_sym;
   int32_t slot_bytes;                  // LDS bytes of one segment slot (>= the largest segment, multiple of 16)
   int32_t seg_loads;                   // 1 KB direct loads that fill a slot
+  int32_t nq;                          // 1 KB queue loads issued per tile step (2 or 4)
+  int32_t flat;                        // 1: no tile crosses a row and `steps` is set
+  int32_t n_tiles;                     // tiles of the matrix (flat walk)
+  uint32_t q_extent;                   // flat walk: bytes readable from queue - 1 KB on
+  int32_t rows_per_unit;               // rows covered by a work unit
+  const uint32_t* steps;               // flat walk, per tile: {16-byte floor of its segment (queue offset),
+                                       //  byte i: 64 - lanes of 1 KB queue load i (at least 1 lane)}
   int32_t unit_blocks;                 // blocks per work unit (a unit covers whole rows)
   int32_t n_units;
   uint32_t sym[32];                    // rev code | len << 16 | exponent << 24
@@ -82,6 +89,7 @@ struct uw_matrix {
   uw::BlobHeader h;
   uw::DevMatrix dev;
   const uint8_t* d_blob = nullptr;
+  void* d_steps = nullptr;  // device copy of the flat-walk step table (owned)
   int device = 0;
   mutable std::mutex mu;
   std::map<int64_t, uw_plan> plans;

@@ -126,19 +126,28 @@ __device__ inline uint32_t peek(const LaneDec& s) { return __builtin_amdgcn_alig
 // next word of those that still have words.  q = segment base, wp = byte
 // offset of the next word to take (wave-uniform).  A lane that takes nothing
 // reads a word inside the segment or just past its end, which the slot holds.
+// left -= 1 on the lanes of mask m: one subtract with the mask as borrow
+__device__ __forceinline__ uint32_t dec_masked(uint32_t left, uint64_t m) {
+  uint32_t r;
+  asm("v_subb_co_u32_e64 %0, vcc, %1, 0, %2" : "=v"(r) : "v"(left), "s"(m) : "vcc");
+  return r;
+}
+
 template <int PH>
 __device__ __forceinline__ void check(LaneDec& s, uint32_t q, uint32_t& wp) {
   const uint32_t w2 = __builtin_amdgcn_inverse_ballot_w64(s.took[PH ^ 1]) ? s.nw[PH ^ 1] : s.w2;
-  const bool adv = s.qm & 32u;
-  const uint64_t m = __builtin_amdgcn_ballot_w64(adv) & __builtin_amdgcn_ballot_w64(s.left != 0u);
+  const uint64_t ma = __builtin_amdgcn_ballot_w64((s.qm & 32u) != 0u);
+  const uint64_t m = ma & __builtin_amdgcn_ballot_w64(s.left != 0u);
+  const bool adv = __builtin_amdgcn_inverse_ballot_w64(ma);
   s.w0 = adv ? s.w1 : s.w0;
   s.w1 = adv ? w2 : s.w1;
   s.w2 = w2;
   s.nw[PH] = ld32(q + wp + 4 * lanes_below(m));
   s.took[PH] = m;
-  s.left = __builtin_amdgcn_inverse_ballot_w64(m) ? s.left - 1u : s.left;
+  s.left = dec_masked(s.left, m);
   s.qm &= 31u;
   wp += 4 * uint32_t(__builtin_popcountll(m));
+  wp = __builtin_amdgcn_readfirstlane(wp);  // wave-uniform: keeps q + wp a scalar sum
 }
 
 __device__ inline void check_rt(LaneDec& s, int ph, uint32_t q, uint32_t& wp) {
@@ -191,7 +200,7 @@ __device__ inline uint32_t take_single(LaneDec& s, uint32_t& p, uint32_t mask) {
 // Decode one tile of one block.  q = LDS address of the tile's segment, rpos
 // = byte offset of its raw exponent bytes (after the head on tile 0), cur =
 // the lane's 16 sign+mantissa
-// bytes, j0 = first group of the tile in the block, nt = groups in the tile.
+// bytes, rmask = raw flags of the tile's groups, nt = groups in the tile.
 // aligned: nt == 16 and the tile lies inside one row starting at an even
 // column group; then the sink receives sink.tile_begin(row0, c0) and
 // sink.pair(k, D) with D = the lane's weights of groups (2k, 2k+1); otherwise
@@ -199,9 +208,8 @@ __device__ inline uint32_t take_single(LaneDec& s, uint32_t& p, uint32_t mask) {
 // it consumed (head, raw bytes and taken words), which is the segment's length.
 template <bool PAIR, class Sink>
 __device__ __forceinline__ uint32_t decode_tile(const DevMatrix& d, LaneDec& s, uint32_t q, uint32_t rpos,
-                                            const uint4& cur, int j0, int nt, bool aligned, int64_t row0, int c0,
-                                            int lane, Sink& sink) {
-  const uint32_t rmask = raw_mask16(s.raw_word, j0);
+                                            const uint4& cur, uint32_t rmask, int nt, bool aligned, int64_t row0,
+                                            int c0, int lane, Sink& sink) {
   uint32_t wp = rpos + 64 * uint32_t(__builtin_popcount(rmask));
   const uint32_t pmask = PAIR ? 0x3FFCu : (((1u << d.L) - 1u) << 2);
   if (aligned) {
@@ -423,7 +431,7 @@ __device__ __forceinline__ void run_blocks(const DevMatrix& d, int b0, int b1, u
       const uint4 cur = ld128(sm_slot + 16u * uint32_t(lane));
       const int nt = std::min(16, r.gb - 16 * t);
       const bool aligned = nt == 16 && c0 + 16 <= gpr && (c0 & 1) == 0;
-      pos += decode_tile<PAIR>(d, s, q, rpos, cur, 16 * t, nt, aligned, row0, c0, lane, sink);
+      pos += decode_tile<PAIR>(d, s, q, rpos, cur, raw_mask16(s.raw_word, 16 * t), nt, aligned, row0, c0, lane, sink);
       rpos = 0;
       sink.tile_end(t, nt);
       c0 += 16;
@@ -440,6 +448,179 @@ __device__ __forceinline__ void run_blocks(const DevMatrix& d, int b0, int b1, u
   __builtin_amdgcn_s_waitcnt(0);  // the repeated loads past the end land before the ring is reused
 }
 
+// ---------------------------------------------------------------------------
+// Flat walk: when G and the groups per row are multiples of 16 no tile
+// crosses a row, and the tiles of blocks [b0, b1) form one sequence of tile
+// steps.  A slot is [1 KB sign+mantissa | queue part]; one M0 (the slot)
+// serves all loads of a step, the queue loads reaching their part through
+// the immediate offset 1024 (i + 1), which applies to both addresses.  The
+// step table gives each tile's segment floor and the lanes of each load.
+// Buffer resource over [base, base + bytes) for raw byte-offset loads.
+__device__ inline __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), int16_t(0), int(bytes), 0x00020000);
+}
+
+// The 1 + NQ loads of tile step v into a slot, from one M0 (the slot): the
+// sign+mantissa tile v at offset 0 (all lanes), then the queue segment from
+// its 16-byte floor at offsets 1024 (i + 1): rq starts 1 KB before the
+// queue, so the immediate offset moves both addresses together.  Load i
+// runs on the lanes below 64 - shift_i (byte i of `shifts`): exec =
+// ~0 >> shift_i (s_lshr_b64 reads the low 6 bits of the shift).  The wave
+// runs this with all lanes active.  The s_nop 4 covers a vector write of
+// any of the scalar operands just before (the loads read them).
+template <int NQ>
+__device__ __forceinline__ void issue_flat(__amdgpu_buffer_rsrc_t rsm, __amdgpu_buffer_rsrc_t rq, int v,
+                                           uint32_t floor16, uint32_t shifts, uint32_t slot, uint32_t lane16) {
+  static_assert(NQ == 2 || NQ == 4, "queue loads per step");
+  const uint32_t sm_off = uint32_t(v) * 1024u;
+  uint32_t t, f2;
+  if constexpr (NQ == 2) {
+    asm volatile(
+        "s_nop 4\n"
+        "s_mov_b32 m0, %[slot]\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %[l16], %[rsm], %[smo] offen lds\n"
+        "s_lshr_b64 exec, -1, %[sh]\n"
+        "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:1024 lds\n"
+        "s_lshr_b32 %[t], %[sh], 8\n"
+        "s_lshr_b64 exec, -1, %[t]\n"
+        "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:2048 lds\n"
+        "s_mov_b64 exec, -1"
+        : [t] "=&s"(t)
+        : [slot] "s"(slot), [l16] "v"(lane16), [rsm] "s"(rsm), [smo] "s"(sm_off), [rq] "s"(rq), [fl] "s"(floor16),
+          [sh] "s"(shifts)
+        : "memory", "m0", "exec");
+  } else {
+    asm volatile(
+        "s_nop 4\n"
+        "s_mov_b32 m0, %[slot]\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %[l16], %[rsm], %[smo] offen lds\n"
+        "s_lshr_b64 exec, -1, %[sh]\n"
+        "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:1024 lds\n"
+        "s_lshr_b32 %[t], %[sh], 8\n"
+        "s_lshr_b64 exec, -1, %[t]\n"
+        "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:2048 lds\n"
+        // loads 2 and 3 from M0 = slot + 2 KB and the floor + 2 KB (the
+        // immediate offset has 12 bits)
+        "s_add_u32 m0, %[slot], 0x800\n"
+        "s_add_u32 %[f2], %[fl], 0x800\n"
+        "s_lshr_b32 %[t], %[sh], 16\n"
+        "s_lshr_b64 exec, -1, %[t]\n"
+        "buffer_load_dwordx4 %[l16], %[rq], %[f2] offen offset:1024 lds\n"
+        "s_lshr_b32 %[t], %[sh], 24\n"
+        "s_lshr_b64 exec, -1, %[t]\n"
+        "buffer_load_dwordx4 %[l16], %[rq], %[f2] offen offset:2048 lds\n"
+        "s_mov_b64 exec, -1"
+        : [t] "=&s"(t), [f2] "=&s"(f2)
+        : [slot] "s"(slot), [l16] "v"(lane16), [rsm] "s"(rsm), [smo] "s"(sm_off), [rq] "s"(rq), [fl] "s"(floor16),
+          [sh] "s"(shifts)
+        : "memory", "m0", "exec");
+  }
+  (void)f2;
+}
+
+// Wait for tile step v: RS - 1 younger steps are in flight, except for the
+// last steps of the walk, which wait for everything issued.
+template <int RS, int NQ, int XTRA>
+__device__ __forceinline__ void wait_step(int v, int v_full) {
+  if (v < v_full) wait_oldest_step<RS, NQ, XTRA>();
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Resources of the flat walk's loads: the sign+mantissa section, and the
+// queue from 1 KB before it (so one immediate offset moves the global and
+// the LDS address of a queue load together).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t flat_rsm(const DevMatrix& d) {
+  return byte_rsrc(d.sm, uint32_t(d.n_tiles) * 1024u);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t flat_rq(const DevMatrix& d) { return byte_rsrc(d.queue - 1024, d.q_extent); }
+
+// Issue the first RS steps of the tiles of blocks [b0, b1) into the ring;
+// returns the next step to issue.
+template <int RS, int NQ>
+__device__ __forceinline__ int flat_start(const DevMatrix& d, int b0, int b1, uint32_t ring, int lane) {
+  const uint32_t lane16 = 16u * uint32_t(lane);
+  const uint32_t stride = 1024u + uint32_t(d.slot_bytes);
+  const int u1 = std::min(b1 * d.T, d.n_tiles);
+  const __amdgpu_buffer_rsrc_t rsm = flat_rsm(d), rq = flat_rq(d);
+  int fv = b0 * d.T;
+  const const_word* fstep = (const const_word*)(d.steps) + 2u * uint32_t(fv);
+  uint32_t slot = ring;
+#pragma unroll
+  for (int i = 0; i < RS; ++i) {
+    if (fv < u1) {
+      issue_flat<NQ>(rsm, rq, fv, fstep[0], fstep[1], slot, lane16);
+      ++fv;
+      fstep += 2;
+      slot += stride;
+    }
+  }
+  return fv;
+}
+
+// Tiles of blocks [b0, b1) of a unit whose first row is row_base; flat_start
+// has issued the steps before fv0.
+template <int RS, int NQ, int XTRA, bool PAIR, class Sink>
+__device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, int b1, int64_t row_base, uint32_t ring,
+                                         int lane, Sink& sink) {
+  const uint32_t lane16 = 16u * uint32_t(lane);
+  const uint32_t stride = 1024u + uint32_t(d.slot_bytes);
+  const uint32_t ring_last = ring + (RS - 1) * stride;
+  const int T = d.T;
+  const int u0 = b0 * T, u1 = std::min(b1 * T, d.n_tiles);
+  const int v_full = u1 - (RS - 1);  // steps before this one have RS - 1 younger steps
+  const __amdgpu_buffer_rsrc_t rsm = flat_rsm(d), rq = flat_rq(d);
+  // issue side: the descriptor of the next step to issue is read one step
+  // ahead (the table has a spare entry at its end)
+  int fv = __builtin_amdgcn_readfirstlane(fv0);
+  const const_word* fstep = (const const_word*)(d.steps) + 2u * uint32_t(fv);
+  uint32_t f_floor = fstep[0], f_shifts = fstep[1];
+  // consume side
+  uint32_t qpos = scalar_word(d.block_off, b0);  // queue offset of the next segment
+  int64_t row = row_base;
+  int c0 = 0;  // a unit starts a row
+  LaneDec s{};
+  uint32_t slot = ring;
+  for (int v = u0; v < u1;) {
+    // a block: its head (in tile 0's segment) starts the lane decoders
+    wait_step<RS, NQ, XTRA>(v, v_full);
+    uint32_t rpos = lane_dec_start(s, slot + 1024u + (qpos & 15u), d.rb_words, lane);
+    // lane t: raw flags of tile t of the block
+    const uint32_t tile_rm =
+        (ld32(slot + 1024u + (qpos & 15u) + 128 + 4 * uint32_t(lane >> 1)) >> (16 * (lane & 1))) & 0xFFFFu;
+    const int v_end = std::min(v + T, u1);
+    for (int t = 0;;) {
+      const uint32_t q = slot + 1024u + (qpos & 15u);
+      const uint4 cur = ld128(slot + lane16);
+      const uint32_t rmask = __builtin_amdgcn_readlane(tile_rm, t);
+      qpos += __builtin_amdgcn_readfirstlane(decode_tile<PAIR>(d, s, q, rpos, cur, rmask, 16, true, row, c0, lane, sink));
+      rpos = 0;
+      sink.tile_end(t, 16);
+      c0 += 16;
+      if (c0 == d.gpr) {
+        c0 = 0;
+        ++row;
+        sink.row_end();
+      }
+      // every LDS read of the slot is done before it is refilled (the
+      // builtin form, so the compiler knows the reads have completed)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      if (fv < u1) {
+        issue_flat<NQ>(rsm, rq, fv, f_floor, f_shifts, slot, lane16);
+        ++fv;
+        fstep += 2;
+        f_floor = fstep[0];
+        f_shifts = fstep[1];
+      }
+      slot = slot == ring_last ? ring : slot + stride;
+      ++t;
+      if (++v == v_end) break;
+      wait_step<RS, NQ, XTRA>(v, v_full);
+    }
+  }
+}
+
 constexpr int kRS = 4;  // tile steps in flight per wave
 
 __host__ __device__ inline uint32_t ring_bytes(int rs, int slot_bytes) { return uint32_t(rs) * (1024u + uint32_t(slot_bytes)); }
@@ -447,6 +628,7 @@ __host__ __device__ inline uint32_t ring_bytes(int rs, int slot_bytes) { return 
 // ---------------------------------------------------------------------------
 // Decompress: weights pass through a per-wave LDS tile [16][64] bf16 so that
 // each lane stores 2 x 16 bytes of consecutive columns.
+template <bool FLAT>
 struct DecompressSink {
   int64_t cols, G;
   uint16_t* out;
@@ -458,11 +640,17 @@ struct DecompressSink {
   __device__ void unit_begin(int) {}
   __device__ void unit_end() {}
   __device__ void block_begin(int blk) {
+    if (FLAT) return;  // the flat walk gives each tile's place
     const int64_t flat = int64_t(blk) * G * 64;
     trow = flat / cols;
     tcol = flat - trow * cols;
   }
-  __device__ void tile_begin(int64_t, int) {}
+  __device__ void row_end() {}
+  __device__ void tile_begin(int64_t row0, int c0) {
+    if (!FLAT) return;
+    trow = row0;
+    tcol = int64_t(c0) * 64;
+  }
   __device__ void pair(int k, uint32_t D) {
     st16(tile + ((2 * k) * kWave + lane) * 2, D);
     st16(tile + ((2 * k + 1) * kWave + lane) * 2, D >> 16);
@@ -473,7 +661,7 @@ struct DecompressSink {
     if (lane * 16 < nt * 64) {
       const uint4 a = ld128(tile + lane * 32), b = ld128(tile + lane * 32 + 16);
       int64_t row = trow, col = tcol + lane * 16;
-      while (col >= cols) {
+      while (!FLAT && col >= cols) {
         col -= cols;
         ++row;
       }
@@ -482,6 +670,7 @@ struct DecompressSink {
       dst[1] = b;
     }
     wave_lds_fence();
+    if (FLAT) return;
     tcol += 1024;
     while (tcol >= cols) {
       tcol -= cols;
@@ -490,7 +679,7 @@ struct DecompressSink {
   }
 };
 
-template <bool PAIR, int NQ>
+template <bool PAIR, int NQ, bool FLAT>
 __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t* __restrict__ out, int64_t ld_out) {
   extern __shared__ uint32_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -499,13 +688,24 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   const uint32_t sm_ring = kAreaAddr + uint32_t(wave) * per_wave;
   const uint32_t q_ring = sm_ring + kRS * 1024;
   const uint32_t tile = sm_ring + ring_bytes(kRS, d.slot_bytes);
+  const int u_first = blockIdx.x * waves + wave;
+  int fv = 0;
+  // the first unit's loads go out before the tables are built
+  if (FLAT && u_first < d.n_units)
+    fv = flat_start<kRS, NQ>(d, u_first * d.unit_blocks, std::min(d.n_blocks, (u_first + 1) * d.unit_blocks), sm_ring,
+                             lane);
   build_tables<PAIR>(d, lds, lds + kTableWords);
-  __syncthreads();
-  DecompressSink sink{d.cols, d.G, out, ld_out, tile, lane, 0, 0};
-  for (int u = blockIdx.x * waves + wave; u < d.n_units; u += gridDim.x * waves) {
-    const int b0 = u * d.unit_blocks;
+  lds_barrier();
+  DecompressSink<FLAT> sink{d.cols, d.G, out, ld_out, tile, lane, 0, 0};
+  for (int u = u_first; u < d.n_units; u += gridDim.x * waves) {
+    const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
     // the two 16-byte stores per tile only make the ring waits stricter
-    run_blocks<kRS, NQ, 0, PAIR>(d, b0, std::min(d.n_blocks, b0 + d.unit_blocks), sm_ring, q_ring, lane, sink);
+    if (FLAT) {
+      if (u != u_first) fv = flat_start<kRS, NQ>(d, b0, b1, sm_ring, lane);
+      run_flat<kRS, NQ, 0, PAIR>(d, fv, b0, b1, int64_t(u) * d.rows_per_unit, sm_ring, lane, sink);
+    } else {
+      run_blocks<kRS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
+    }
   }
 }
 
@@ -543,7 +743,7 @@ __device__ inline void load_x(const DevMatrix& d, const void* X, int64_t ldx, in
   }
 }
 
-template <int NBP, bool XF32, bool YBF16>
+template <int NBP, bool XF32, bool YBF16, bool FLAT>
 struct ProductSink {
   const DevMatrix& d;
   uint32_t xaddr;  // LDS byte address of x
@@ -551,7 +751,7 @@ struct ProductSink {
   int nb_valid;
   void* Y;
   int64_t ldy;
-  int64_t cur_row;
+  int cur_row;  // row being accumulated, relative to first_row
   int c0;
   uint32_t xtile;  // x address of this lane for column group c0
   float acc[NBP];
@@ -583,13 +783,14 @@ struct ProductSink {
     ++n_done;  // a unit covers at most 64 rows (checked on the host)
   }
   __device__ void to_row(int64_t row) {
-    if (row != cur_row) {
+    const int r = int(row - first_row);  // a unit covers at most 64 rows
+    if (r != cur_row) {
       flush();
-      cur_row = row;
+      cur_row = r;
     }
   }
   __device__ void tile_begin(int64_t row0, int c) {
-    to_row(row0);
+    if (!FLAT) to_row(row0);  // the flat walk ends rows with row_end()
     c0 = c;
     xtile = XF32 ? xaddr + ((uint32_t(c) * 64 + lane) * NBP) * 4 : xaddr + (((uint32_t(c) >> 1) * 64 + lane) * NBP) * 4;
   }
@@ -625,13 +826,15 @@ struct ProductSink {
   __device__ void block_begin(int) {}
   // a unit covers whole rows; finished rows are stored when it ends
   __device__ void unit_begin(int unit) {
-    cur_row = first_row = (int64_t(unit) * d.unit_blocks * d.G) / d.gpr;
+    first_row = int64_t(unit) * d.rows_per_unit;
+    cur_row = 0;
     n_done = 0;
 #pragma unroll
     for (int b = 0; b < NBP; ++b) acc[b] = rows_done[b] = 0.f;
   }
+  __device__ void row_end() { flush(); }
   __device__ void unit_end() {
-    flush();
+    if (!FLAT) flush();  // the flat walk has ended the unit's last row
     store_done();
   }
 };
@@ -639,7 +842,7 @@ struct ProductSink {
 // Wide batch chunks need more registers per lane: at most 8 waves per workgroup.
 constexpr int fused_max_threads(int nbp) { return nbp >= 4 ? 512 : 1024; }
 
-template <int NBP, bool XF32, bool PAIR, bool YBF16, int NQ>
+template <int NBP, bool XF32, bool PAIR, bool YBF16, int NQ, bool FLAT>
 __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(DevMatrix d, const void* __restrict__ X,
                                                                                int64_t ldx, int nb_valid,
                                                                                void* __restrict__ Y, int64_t ldy) {
@@ -649,14 +852,25 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
   const int waves = blockDim.x / kWave;
   const uint32_t sm_ring = kAreaAddr + x_words * 4 + uint32_t(wave) * ring_bytes(kRS, d.slot_bytes);
   const uint32_t q_ring = sm_ring + kRS * 1024;
+  const int u_first = blockIdx.x * waves + wave;
+  int fv = 0;
+  // the first unit's loads go out before the tables and x are set up
+  if (FLAT && u_first < d.n_units)
+    fv = flat_start<kRS, NQ>(d, u_first * d.unit_blocks, std::min(d.n_blocks, (u_first + 1) * d.unit_blocks), sm_ring,
+                             lane);
   build_tables<PAIR>(d, lds, lds + kTableWords);
   load_x<NBP, XF32>(d, X, ldx, nb_valid, lds + kTableWords + kT1Words);
-  __syncthreads();
-  ProductSink<NBP, XF32, YBF16> sink{d, kAreaAddr, lane, nb_valid, Y, ldy, 0, 0, 0u, {}, {}, 0, 0};
-  for (int u = blockIdx.x * waves + wave; u < d.n_units; u += gridDim.x * waves) {
+  lds_barrier();
+  ProductSink<NBP, XF32, YBF16, FLAT> sink{d, kAreaAddr, lane, nb_valid, Y, ldy, 0, 0, 0u, {}, {}, 0, 0};
+  for (int u = u_first; u < d.n_units; u += gridDim.x * waves) {
     sink.unit_begin(u);
-    const int b0 = u * d.unit_blocks;
-    run_blocks<kRS, NQ, 0, PAIR>(d, b0, std::min(d.n_blocks, b0 + d.unit_blocks), sm_ring, q_ring, lane, sink);
+    const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
+    if (FLAT) {
+      if (u != u_first) fv = flat_start<kRS, NQ>(d, b0, b1, sm_ring, lane);
+      run_flat<kRS, NQ, 0, PAIR>(d, fv, b0, b1, int64_t(u) * d.rows_per_unit, sm_ring, lane, sink);
+    } else {
+      run_blocks<kRS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
+    }
     sink.unit_end();
   }
 }
@@ -792,7 +1006,7 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
           rpos = t == 0 ? lane_dec_start(s, q, d.rb_words, lane) : 0u;
           const uint4 cur = ld128(sm_slot + 16u * uint32_t(lane));
           SliceSink sink{my_row, lane};
-          pos += decode_tile<PAIR>(d, s, q, rpos, cur, 16 * t, 16, true, 0, 0, lane, sink);
+          pos += decode_tile<PAIR>(d, s, q, rpos, cur, raw_mask16(s.raw_word, 16 * t), 16, true, 0, 0, lane, sink);
           if (++ct == cr.nt) {
             ct = 0;
             ++cblk;
@@ -905,7 +1119,10 @@ int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, i
   const int waves = std::min(pick_waves(d.n_units, fixed, per_wave), fused_max_threads(NBP) / kWave);
   const size_t lds = fixed + per_wave * waves;
   const int grid = int(std::max<int64_t>(1, (d.n_units + waves - 1) / waves));
-  auto kern = d.seg_loads <= 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2> : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4>;
+  auto kern = d.flat ? (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, true>
+                                  : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4, true>)
+                     : (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, false>
+                                  : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4, false>);
   allow_full_lds(kern);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, static_cast<hipStream_t>(stream), d, X, ldx, nb, Y,
                      ldy);
@@ -952,8 +1169,12 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
   const int waves = pick_waves(d.n_units, fixed, per_wave);
   const size_t lds = fixed + per_wave * waves;
   const int grid = int(std::max<int64_t>(1, (int64_t(d.n_units) + waves - 1) / waves));
-  auto kern = is_pair(d) ? (d.seg_loads <= 2 ? decompress_kernel<true, 2> : decompress_kernel<true, 4>)
-                         : (d.seg_loads <= 2 ? decompress_kernel<false, 2> : decompress_kernel<false, 4>);
+  auto pick = [&](auto pair) {
+    constexpr bool P = decltype(pair)::value;
+    return d.flat ? (d.nq == 2 ? decompress_kernel<P, 2, true> : decompress_kernel<P, 4, true>)
+                  : (d.nq == 2 ? decompress_kernel<P, 2, false> : decompress_kernel<P, 4, false>);
+  };
+  auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
   allow_full_lds(kern);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, out, ld_out);
   return hip_check(hipGetLastError(), "decompress_kernel launch");
