@@ -478,11 +478,10 @@ __device__ __forceinline__ void issue_flat(__amdgpu_buffer_rsrc_t rsm, __amdgpu_
     asm volatile(
         "s_nop 4\n"
         "s_mov_b32 m0, %[slot]\n"
-        "s_nop 0\n"
+        "s_lshr_b32 %[t], %[sh], 8\n"  // also the wait state after the M0 write
         "buffer_load_dwordx4 %[l16], %[rsm], %[smo] offen lds\n"
         "s_lshr_b64 exec, -1, %[sh]\n"
         "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:1024 lds\n"
-        "s_lshr_b32 %[t], %[sh], 8\n"
         "s_lshr_b64 exec, -1, %[t]\n"
         "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:2048 lds\n"
         "s_mov_b64 exec, -1"
@@ -494,18 +493,17 @@ __device__ __forceinline__ void issue_flat(__amdgpu_buffer_rsrc_t rsm, __amdgpu_
     asm volatile(
         "s_nop 4\n"
         "s_mov_b32 m0, %[slot]\n"
-        "s_nop 0\n"
+        "s_lshr_b32 %[t], %[sh], 8\n"  // also the wait state after the M0 write
         "buffer_load_dwordx4 %[l16], %[rsm], %[smo] offen lds\n"
         "s_lshr_b64 exec, -1, %[sh]\n"
         "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:1024 lds\n"
-        "s_lshr_b32 %[t], %[sh], 8\n"
         "s_lshr_b64 exec, -1, %[t]\n"
         "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:2048 lds\n"
         // loads 2 and 3 from M0 = slot + 2 KB and the floor + 2 KB (the
         // immediate offset has 12 bits)
         "s_add_u32 m0, %[slot], 0x800\n"
-        "s_add_u32 %[f2], %[fl], 0x800\n"
         "s_lshr_b32 %[t], %[sh], 16\n"
+        "s_add_u32 %[f2], %[fl], 0x800\n"
         "s_lshr_b64 exec, -1, %[t]\n"
         "buffer_load_dwordx4 %[l16], %[rq], %[f2] offen offset:1024 lds\n"
         "s_lshr_b32 %[t], %[sh], 24\n"
@@ -518,14 +516,6 @@ __device__ __forceinline__ void issue_flat(__amdgpu_buffer_rsrc_t rsm, __amdgpu_
         : "memory", "m0", "exec");
   }
   (void)f2;
-}
-
-// Wait for tile step v: RS - 1 younger steps are in flight, except for the
-// last steps of the walk, which wait for everything issued.
-template <int RS, int NQ, int XTRA>
-__device__ __forceinline__ void wait_step(int v, int v_full) {
-  if (v < v_full) wait_oldest_step<RS, NQ, XTRA>();
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Resources of the flat walk's loads: the sign+mantissa section, and the
@@ -569,7 +559,6 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
   const uint32_t ring_last = ring + (RS - 1) * stride;
   const int T = d.T;
   const int u0 = b0 * T, u1 = std::min(b1 * T, d.n_tiles);
-  const int v_full = u1 - (RS - 1);  // steps before this one have RS - 1 younger steps
   const __amdgpu_buffer_rsrc_t rsm = flat_rsm(d), rq = flat_rq(d);
   // issue side: the descriptor of the next step to issue is read one step
   // ahead (the table has a spare entry at its end)
@@ -579,46 +568,52 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
   // consume side
   uint32_t qpos = scalar_word(d.block_off, b0);  // queue offset of the next segment
   int64_t row = row_base;
-  int c0 = 0;  // a unit starts a row
+  int c0 = 0, t = 0;  // a unit starts a row and a block
+  uint32_t tile_rm = 0;  // lane t: raw flags of tile t of the current block
   LaneDec s{};
   uint32_t slot = ring;
-  for (int v = u0; v < u1;) {
-    // a block: its head (in tile 0's segment) starts the lane decoders
-    wait_step<RS, NQ, XTRA>(v, v_full);
-    uint32_t rpos = lane_dec_start(s, slot + 1024u + (qpos & 15u), d.rb_words, lane);
-    // lane t: raw flags of tile t of the block
-    const uint32_t tile_rm =
-        (ld32(slot + 1024u + (qpos & 15u) + 128 + 4 * uint32_t(lane >> 1)) >> (16 * (lane & 1))) & 0xFFFFu;
-    const int v_end = std::min(v + T, u1);
-    for (int t = 0;;) {
-      const uint32_t q = slot + 1024u + (qpos & 15u);
-      const uint4 cur = ld128(slot + lane16);
-      const uint32_t rmask = __builtin_amdgcn_readlane(tile_rm, t);
-      qpos += __builtin_amdgcn_readfirstlane(decode_tile<PAIR>(d, s, q, rpos, cur, rmask, 16, true, row, c0, lane, sink));
-      rpos = 0;
-      sink.tile_end(t, 16);
-      c0 += 16;
-      if (c0 == d.gpr) {
-        c0 = 0;
-        ++row;
-        sink.row_end();
-      }
+  // One tile step: decode the slot's tile into the sink, then (FEED) refill
+  // the slot with the step RS ahead.
+  auto step = [&](auto feed) {
+    const uint32_t q = slot + 1024u + (qpos & 15u);
+    uint32_t rpos = 0;
+    if (t == 0) {
+      // block start: the head of tile 0's segment starts the lane decoders
+      rpos = lane_dec_start(s, q, d.rb_words, lane);
+      tile_rm = (ld32(q + 128 + 4 * uint32_t(lane >> 1)) >> (16 * (lane & 1))) & 0xFFFFu;
+    }
+    const uint4 cur = ld128(slot + lane16);
+    const uint32_t rmask = __builtin_amdgcn_readlane(tile_rm, t);
+    qpos += __builtin_amdgcn_readfirstlane(decode_tile<PAIR>(d, s, q, rpos, cur, rmask, 16, true, row, c0, lane, sink));
+    sink.tile_end(t, 16);
+    c0 += 16;
+    if (c0 == d.gpr) {
+      c0 = 0;
+      ++row;
+      sink.row_end();
+    }
+    if (++t == T) t = 0;
+    if constexpr (decltype(feed)::value) {
       // every LDS read of the slot is done before it is refilled (the
       // builtin form, so the compiler knows the reads have completed)
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      if (fv < u1) {
-        issue_flat<NQ>(rsm, rq, fv, f_floor, f_shifts, slot, lane16);
-        ++fv;
-        fstep += 2;
-        f_floor = fstep[0];
-        f_shifts = fstep[1];
-      }
-      slot = slot == ring_last ? ring : slot + stride;
-      ++t;
-      if (++v == v_end) break;
-      wait_step<RS, NQ, XTRA>(v, v_full);
+      issue_flat<NQ>(rsm, rq, fv, f_floor, f_shifts, slot, lane16);
+      ++fv;
+      fstep += 2;
+      f_floor = fstep[0];
+      f_shifts = fstep[1];
     }
+    slot = slot == ring_last ? ring : slot + stride;
+  };
+  int v = u0;
+  // steady state: RS - 1 younger steps in flight, and every step refills its slot
+  for (; v < u1 - RS; ++v) {
+    wait_oldest_step<RS, NQ, XTRA>();
+    step(std::true_type{});
   }
+  // the last RS steps: everything has been issued
+  if (v < u1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (; v < u1; ++v) step(std::false_type{});
 }
 
 constexpr int kRS = 4;  // tile steps in flight per wave
