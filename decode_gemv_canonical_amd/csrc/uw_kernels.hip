@@ -616,7 +616,8 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
   for (; v < u1; ++v) step(std::false_type{});
 }
 
-constexpr int kRS = 4;  // tile steps in flight per wave
+constexpr int kRS = 4;  // tile steps in flight per wave (the flat walk may use kRSLow)
+constexpr int kRSLow = 2;
 
 __host__ __device__ inline uint32_t ring_bytes(int rs, int slot_bytes) { return uint32_t(rs) * (1024u + uint32_t(slot_bytes)); }
 
@@ -674,20 +675,20 @@ struct DecompressSink {
   }
 };
 
-template <bool PAIR, int NQ, bool FLAT>
+template <bool PAIR, int NQ, bool FLAT, int RS>
 __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t* __restrict__ out, int64_t ld_out) {
   extern __shared__ uint32_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int waves = blockDim.x / kWave;
-  const uint32_t per_wave = ring_bytes(kRS, d.slot_bytes) + kTransposeWords * 4;
+  const uint32_t per_wave = ring_bytes(RS, d.slot_bytes) + kTransposeWords * 4;
   const uint32_t sm_ring = kAreaAddr + uint32_t(wave) * per_wave;
-  const uint32_t q_ring = sm_ring + kRS * 1024;
-  const uint32_t tile = sm_ring + ring_bytes(kRS, d.slot_bytes);
+  const uint32_t q_ring = sm_ring + RS * 1024;
+  const uint32_t tile = sm_ring + ring_bytes(RS, d.slot_bytes);
   const int u_first = blockIdx.x * waves + wave;
   int fv = 0;
   // the first unit's loads go out before the tables are built
   if (FLAT && u_first < d.n_units)
-    fv = flat_start<kRS, NQ>(d, u_first * d.unit_blocks, std::min(d.n_blocks, (u_first + 1) * d.unit_blocks), sm_ring,
+    fv = flat_start<RS, NQ>(d, u_first * d.unit_blocks, std::min(d.n_blocks, (u_first + 1) * d.unit_blocks), sm_ring,
                              lane);
   build_tables<PAIR>(d, lds, lds + kTableWords);
   lds_barrier();
@@ -696,10 +697,10 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
     const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
     // the two 16-byte stores per tile only make the ring waits stricter
     if (FLAT) {
-      if (u != u_first) fv = flat_start<kRS, NQ>(d, b0, b1, sm_ring, lane);
-      run_flat<kRS, NQ, 0, PAIR>(d, fv, b0, b1, int64_t(u) * d.rows_per_unit, sm_ring, lane, sink);
+      if (u != u_first) fv = flat_start<RS, NQ>(d, b0, b1, sm_ring, lane);
+      run_flat<RS, NQ, 0, PAIR>(d, fv, b0, b1, int64_t(u) * d.rows_per_unit, sm_ring, lane, sink);
     } else {
-      run_blocks<kRS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
+      run_blocks<RS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
     }
   }
 }
@@ -837,7 +838,7 @@ struct ProductSink {
 // Wide batch chunks need more registers per lane: at most 8 waves per workgroup.
 constexpr int fused_max_threads(int nbp) { return nbp >= 4 ? 512 : 1024; }
 
-template <int NBP, bool XF32, bool PAIR, bool YBF16, int NQ, bool FLAT>
+template <int NBP, bool XF32, bool PAIR, bool YBF16, int NQ, bool FLAT, int RS>
 __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(DevMatrix d, const void* __restrict__ X,
                                                                                int64_t ldx, int nb_valid,
                                                                                void* __restrict__ Y, int64_t ldy) {
@@ -845,13 +846,13 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
   const uint32_t x_words = XF32 ? uint32_t(d.cols) * NBP : ((uint32_t(d.gpr) + 1) / 2) * 64 * NBP;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int waves = blockDim.x / kWave;
-  const uint32_t sm_ring = kAreaAddr + x_words * 4 + uint32_t(wave) * ring_bytes(kRS, d.slot_bytes);
-  const uint32_t q_ring = sm_ring + kRS * 1024;
+  const uint32_t sm_ring = kAreaAddr + x_words * 4 + uint32_t(wave) * ring_bytes(RS, d.slot_bytes);
+  const uint32_t q_ring = sm_ring + RS * 1024;
   const int u_first = blockIdx.x * waves + wave;
   int fv = 0;
   // the first unit's loads go out before the tables and x are set up
   if (FLAT && u_first < d.n_units)
-    fv = flat_start<kRS, NQ>(d, u_first * d.unit_blocks, std::min(d.n_blocks, (u_first + 1) * d.unit_blocks), sm_ring,
+    fv = flat_start<RS, NQ>(d, u_first * d.unit_blocks, std::min(d.n_blocks, (u_first + 1) * d.unit_blocks), sm_ring,
                              lane);
   build_tables<PAIR>(d, lds, lds + kTableWords);
   load_x<NBP, XF32>(d, X, ldx, nb_valid, lds + kTableWords + kT1Words);
@@ -861,10 +862,10 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
     sink.unit_begin(u);
     const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
     if (FLAT) {
-      if (u != u_first) fv = flat_start<kRS, NQ>(d, b0, b1, sm_ring, lane);
-      run_flat<kRS, NQ, 0, PAIR>(d, fv, b0, b1, int64_t(u) * d.rows_per_unit, sm_ring, lane, sink);
+      if (u != u_first) fv = flat_start<RS, NQ>(d, b0, b1, sm_ring, lane);
+      run_flat<RS, NQ, 0, PAIR>(d, fv, b0, b1, int64_t(u) * d.rows_per_unit, sm_ring, lane, sink);
     } else {
-      run_blocks<kRS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
+      run_blocks<RS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
     }
     sink.unit_end();
   }
@@ -1098,26 +1099,57 @@ size_t x_bytes(const DevMatrix& d, int nbp, bool xf32) {
   return xf32 ? size_t(d.cols) * nbp * 4 : size_t((d.gpr + 1) / 2) * 64 * nbp * 4;
 }
 
-// Waves per workgroup: as many as the work and the LDS budget allow, up to 16.
-int pick_waves(int64_t units, size_t fixed, size_t per_wave) {
-  int w = int(std::min<int64_t>(16, std::max<int64_t>(1, (units + 255) / 256)));
+// Compute units of the current device.
+int cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Waves per workgroup (one workgroup per compute unit): enough for every
+// unit to start in the first round, as far as the LDS budget and max_waves
+// allow.
+int pick_waves(int64_t units, size_t fixed, size_t per_wave, int max_waves = 16) {
+  const int64_t cus = cu_count();
+  int w = int(std::min<int64_t>(max_waves, std::max<int64_t>(1, (units + cus - 1) / cus)));
   while (w > 1 && fixed + per_wave * w > size_t(kLdsLimit)) --w;
   return w;
+}
+
+// Ring depth of the flat walk: kRS steps in flight when the waves that put
+// every unit in the first round fit in LDS with it, else kRSLow (the decode,
+// not the load latency, sets the pace; the units per compute unit matter more).
+int flat_ring_depth(int64_t units, size_t fixed, int slot_bytes, size_t extra, int max_waves) {
+  const int64_t cus = cu_count();
+  const int need = int(std::min<int64_t>(max_waves, std::max<int64_t>(1, (units + cus - 1) / cus)));
+  return pick_waves(units, fixed, ring_bytes(kRS, slot_bytes) + extra, max_waves) >= need ? kRS : kRSLow;
 }
 
 template <int NBP, bool XF32, bool PAIR, bool YBF16>
 int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, void* stream) {
   const DevMatrix& d = m->dev;
   const size_t fixed = tables_bytes() + x_bytes(d, NBP, XF32);
-  const size_t per_wave = ring_bytes(kRS, d.slot_bytes);
+  const int max_waves = fused_max_threads(NBP) / kWave;
+  const int rs = d.flat ? flat_ring_depth(d.n_units, fixed, d.slot_bytes, 0, max_waves) : kRS;
+  const size_t per_wave = ring_bytes(rs, d.slot_bytes);
   if (fixed + per_wave > size_t(kLdsLimit)) return fail(UW_ERR_UNSUPPORTED, "fused product: x does not fit on chip");
-  const int waves = std::min(pick_waves(d.n_units, fixed, per_wave), fused_max_threads(NBP) / kWave);
+  const int waves = pick_waves(d.n_units, fixed, per_wave, max_waves);
   const size_t lds = fixed + per_wave * waves;
   const int grid = int(std::max<int64_t>(1, (d.n_units + waves - 1) / waves));
-  auto kern = d.flat ? (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, true>
-                                  : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4, true>)
-                     : (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, false>
-                                  : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4, false>);
+  auto kern = d.flat ? (rs == kRS ? (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, true, kRS>
+                                               : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4, true, kRS>)
+                                  : (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, true, kRSLow>
+                                               : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4, true, kRSLow>))
+                     : (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, false, kRS>
+                                  : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4, false, kRS>);
   allow_full_lds(kern);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, static_cast<hipStream_t>(stream), d, X, ldx, nb, Y,
                      ldy);
@@ -1146,7 +1178,7 @@ int run_fused_x(const uw_matrix* m, const void* X, int64_t ldx, int xt, int nb, 
 int fused_chunk(const DevMatrix& d, int64_t batch, bool xf32) {
   int nbp = 8;
   while (nbp > 1 && (nbp / 2 >= batch ||
-                     tables_bytes() + x_bytes(d, nbp, xf32) + ring_bytes(kRS, d.slot_bytes) * 4 >
+                     tables_bytes() + x_bytes(d, nbp, xf32) + ring_bytes(d.flat ? kRSLow : kRS, d.slot_bytes) * 4 >
                          size_t(kLdsLimit)))
     nbp /= 2;
   return nbp;
@@ -1160,14 +1192,17 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (m->h.plain()) return launch_copy_plain(d.plain, d.rows, d.cols, out, ld_out, stream);
   const size_t fixed = tables_bytes();
-  const size_t per_wave = ring_bytes(kRS, d.slot_bytes) + kTransposeWords * 4;
+  const int rs = d.flat ? flat_ring_depth(d.n_units, fixed, d.slot_bytes, kTransposeWords * 4, 16) : kRS;
+  const size_t per_wave = ring_bytes(rs, d.slot_bytes) + kTransposeWords * 4;
   const int waves = pick_waves(d.n_units, fixed, per_wave);
   const size_t lds = fixed + per_wave * waves;
   const int grid = int(std::max<int64_t>(1, (int64_t(d.n_units) + waves - 1) / waves));
   auto pick = [&](auto pair) {
     constexpr bool P = decltype(pair)::value;
-    return d.flat ? (d.nq == 2 ? decompress_kernel<P, 2, true> : decompress_kernel<P, 4, true>)
-                  : (d.nq == 2 ? decompress_kernel<P, 2, false> : decompress_kernel<P, 4, false>);
+    return d.flat ? (rs == kRS ? (d.nq == 2 ? decompress_kernel<P, 2, true, kRS> : decompress_kernel<P, 4, true, kRS>)
+                               : (d.nq == 2 ? decompress_kernel<P, 2, true, kRSLow>
+                                            : decompress_kernel<P, 4, true, kRSLow>))
+                  : (d.nq == 2 ? decompress_kernel<P, 2, false, kRS> : decompress_kernel<P, 4, false, kRS>);
   };
   auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
   allow_full_lds(kern);
@@ -1182,7 +1217,8 @@ bool fused_supported(const uw_matrix* m, int xt, std::string* why) {
     if (why) *why = "a work unit (lcm of G and the groups per row) spans more than 64 rows";
     return false;
   }
-  if (tables_bytes() + x_bytes(d, 1, xt == UW_F32) + ring_bytes(kRS, d.slot_bytes) > size_t(kLdsLimit)) {
+  if (tables_bytes() + x_bytes(d, 1, xt == UW_F32) + ring_bytes(d.flat ? kRSLow : kRS, d.slot_bytes) >
+      size_t(kLdsLimit)) {
     if (why) *why = "x of this width does not fit in LDS next to the decode tables";
     return false;
   }
