@@ -56,7 +56,8 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
-    _run([os.path.join(ROCM, "bin", "hipcc"), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs, "-lpthread"], verbose)
+    _run([os.path.join(ROCM, "bin", "hipcc"), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs,
+          f"-L{ROCM}/lib", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib", "-lpthread"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -292,9 +292,12 @@ int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ld
         have = true;
       }
     }
+    const bool ws_ok = d_ws && ws_bytes >= decompress_ws_bytes(m);
     if (have) variant = p.variant;
-    else if (batch > 8 && mfma_ok) variant = UW_VARIANT_FUSED_MFMA;
-    else variant = (batch <= 8 && fused_ok) || ws_bytes < decompress_ws_bytes(m) ? UW_VARIANT_FUSED : UW_VARIANT_DECOMPRESS_GEMM;
+    else if (batch <= 8 && fused_ok) variant = UW_VARIANT_FUSED;
+    else if (ws_ok && xt == UW_BF16) variant = UW_VARIANT_DECOMPRESS_GEMM;  // library GEMM above batch 8
+    else if (mfma_ok) variant = UW_VARIANT_FUSED_MFMA;
+    else variant = fused_ok || !ws_ok ? UW_VARIANT_FUSED : UW_VARIANT_DECOMPRESS_GEMM;
   }
   if (variant == UW_VARIANT_FUSED_MFMA) {
     if (!mfma_ok) return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused: " + why_mfma);

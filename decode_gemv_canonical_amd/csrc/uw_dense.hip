@@ -187,8 +187,12 @@ int launch_copy_plain(const uint16_t* src, int64_t rows, int64_t cols, uint16_t*
   return hip_check(hipGetLastError(), "copy_plain_kernel launch");
 }
 
+// Batches above this go to the library GEMM (bf16 x); up to it the
+// GEMV-style kernel, which reads W once per chunk of x columns, is used.
+constexpr int64_t kLibraryGemmMinBatch = 8;
+
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why) {
-  (void)batch;
+  if (batch > kLibraryGemmMinBatch && xt == UW_BF16) return true;  // library GEMM
   const size_t per = xt == UW_F32 ? size_t(cols) * 4 : size_t(cols) * 2;
   if (per > size_t(kLdsLimit)) {
     if (why) *why = "x of this width does not fit in LDS";
@@ -199,6 +203,8 @@ bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why) 
 
 int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X, int64_t batch,
                      int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream) {
+  if (batch > kLibraryGemmMinBatch && library_gemm_supported(rows, cols, batch, xt))
+    return launch_library_gemm(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
   const int nbp = bf16_chunk(cols, batch, xt == UW_F32);
   for (int64_t b0 = 0; b0 < batch; b0 += nbp) {
     const int nb = int(std::min<int64_t>(nbp, batch - b0));

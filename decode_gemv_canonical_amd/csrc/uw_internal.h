@@ -106,6 +106,10 @@ int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t 
                       void* stream);
 bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why);
 int launch_copy_plain(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* out, int64_t ld_out, void* stream);
+// rocBLAS bf16 GEMM (uw_blas.cpp): bf16 X only; Y fp32 or bf16.
+bool library_gemm_supported(int64_t rows, int64_t cols, int64_t batch, int xt);
+int launch_library_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X, int64_t batch,
+                        int64_t ldx, void* Y, int64_t ldy, int yt, void* stream);
 int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X,
                      int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream);
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why);

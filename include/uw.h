@@ -191,7 +191,9 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
  *   d_X  device, batch rows of cols elements of xt, row stride ldx >= cols.
  *   d_Y  device, batch rows of rows elements of yt, row stride ldy >= rows.
  *   variant  a uw_variant; UW_VARIANT_AUTO uses the plan uw_autotune stored
- *            for this batch, else a heuristic.
+ *            for this batch, else a heuristic (fused on VALU up to batch 8;
+ *            above it decompress + GEMM when d_ws is large enough, else the
+ *            matrix-core fused product).
  *   d_ws/ws_bytes  caller-owned device workspace (uw_workspace_size bytes for
  *            the chosen variant; may be NULL/0 for the fused variants).
  *   UW_VARIANT_FUSED_MFMA needs bf16 X that is 16-byte aligned with ldx a
@@ -231,6 +233,10 @@ int uw_get_plan(const uw_matrix* m, int64_t batch, uw_plan* out);
  * multiply of the "full decode" pipeline and the uncompressed comparator.
  *   d_W  device, rows x cols bf16, row stride ldw >= cols (multiple of 8),
  *        16-byte aligned.  Other arguments as for uw_gemm_fused.
+ * Up to batch 8 (or with fp32 X) a GEMV-style kernel of this library runs;
+ * above batch 8 with bf16 X, rocBLAS (gemm_ex, fp32 compute).  The first
+ * such call on a device creates that device's rocBLAS handle (it allocates;
+ * the handle lives until the process ends).
  * Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED, UW_ERR_HIP.
  */
 int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, const void* d_X,

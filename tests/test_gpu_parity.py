@@ -297,7 +297,8 @@ def test_gemm_batch_zero_is_noop():
 def test_bf16_gemm_uncompressed():
     wb, _ = matrix("gate", 96, 4096, 21)
     W = torch.from_numpy(wb.view(np.int16)).to(DEV).view(torch.bfloat16)
-    for batch in (1, 3, 8):
+    # up to batch 8 the GEMV-style kernel, above it the library GEMM
+    for batch in (1, 3, 8, 9, 40):
         X = workloads.activations(4096, batch, seed=500 + batch, dtype=torch.bfloat16)
         ref = products.gemm_f64(wb, X.float().numpy())
         Y = torch.empty(batch, 96, device=DEV)
@@ -305,6 +306,24 @@ def test_bf16_gemm_uncompressed():
         uw.uw_bf16_gemm(W, X.to(DEV), Y)
         torch.cuda.synchronize()
         check_f32(Y, ref, f"bf16 gemm b={batch}")
+        Yb = torch.empty(batch, 96, device=DEV, dtype=torch.bfloat16)
+        uw.uw_bf16_gemm(W, X.to(DEV), Yb)
+        torch.cuda.synchronize()
+        check_bf16(Yb, ref, f"bf16 gemm b={batch} bf16 out")
+
+
+def test_decompress_gemm_bf16_out_strided():
+    # decompress into the workspace, then the library GEMM, bf16 Y with a row stride
+    wb, m = matrix("gate", 256, 4096, 23)
+    batch = 24
+    X = workloads.activations(4096, batch, seed=523, dtype=torch.bfloat16)
+    ref = products.gemm_f64(wb, X.float().numpy())
+    Ybig = torch.zeros(batch, 256 + 64, device=DEV, dtype=torch.bfloat16)
+    _say(f"decompress+gemm bf16 out batch={batch}")
+    Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_DECOMPRESS_GEMM, ws=m.workspace(batch), Y=Ybig[:, :256])
+    torch.cuda.synchronize()
+    check_bf16(Y, ref, "decompress+gemm bf16 out")
+    assert torch.all(Ybig[:, 256:] == 0)
 
 
 def test_plain_mode_products():
