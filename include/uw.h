@@ -19,8 +19,10 @@
  *    calling thread;
  *  - all arguments are checked on the host before anything is launched;
  *  - device entry points are asynchronous on the given stream (a hipStream_t
- *    passed as void*, NULL = the null stream), allocate no memory and do not
- *    synchronise, except uw_autotune, which is blocking;
+ *    passed as void*, NULL = the null stream) and do not synchronise, except
+ *    uw_autotune, which is blocking; they allocate no memory, except that the
+ *    first product on a device that goes through rocBLAS creates that
+ *    device's rocBLAS handle;
  *  - "device pointer" means memory of the device that was current when the
  *    matrix handle was created; every device entry point runs on that device.
  *
@@ -158,8 +160,14 @@ int uw_blob_info(const void* blob, size_t n, uw_info* info);
  * same n bytes on the current device, 256-byte aligned.  The handle does not
  * own d_blob: the caller keeps it alive and unchanged until uw_matrix_destroy.
  * The handle keeps a copy of the header and the decode tables derived from
- * the code lengths, plus a per-batch plan cache (internally locked).
- * Errors: UW_ERR_INVALID, UW_ERR_FORMAT, UW_ERR_HIP (no current device).
+ * the code lengths, plus a per-batch plan cache (internally locked).  When G
+ * and cols/64 are multiples of 16 (no 1024-weight tile crosses a row) it
+ * also builds a step table, 8 bytes per tile (where each tile's segment
+ * starts and how many lanes load it), in device memory it allocates and
+ * frees in uw_matrix_destroy; the kernels then walk the tiles of a work unit
+ * as one sequence.
+ * Errors: UW_ERR_INVALID, UW_ERR_FORMAT, UW_ERR_HIP (no current device, or
+ *         the step table could not be allocated or copied).
  */
 int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_matrix** out);
 
