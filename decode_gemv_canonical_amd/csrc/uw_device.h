@@ -52,6 +52,15 @@ __device__ inline uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
+// s_waitcnt vmcnt(N) in the builtin form (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt and lgkmcnt left at their maxima), so the compiler's own
+// wait insertion knows which loads have completed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier for LDS data only: waits for this wave's LDS accesses,
 // not for its vector-memory loads still in flight.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

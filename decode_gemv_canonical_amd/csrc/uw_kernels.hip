@@ -518,6 +518,39 @@ __device__ __forceinline__ void issue_flat(__amdgpu_buffer_rsrc_t rsm, __amdgpu_
   (void)f2;
 }
 
+// N loads of 16 bytes on lane 0 only (from the start of the resource) into
+// the 16 bytes at dst: they keep a step's count of loads where there is
+// nothing to load.  Runs with all lanes active, like issue_flat.
+template <int N>
+__device__ __forceinline__ void issue_dummy(__amdgpu_buffer_rsrc_t r, uint32_t dst, uint32_t lane16) {
+  static_assert(N == 3 || N == 5, "loads per step");
+  if constexpr (N == 3) {
+    asm volatile(
+        "s_nop 4\n"
+        "s_mov_b32 m0, %[dst]\n"
+        "s_mov_b64 exec, 1\n"  // also the wait state after the M0 write
+        "buffer_load_dwordx4 %[l16], %[r], 0 offen lds\n"
+        "buffer_load_dwordx4 %[l16], %[r], 0 offen lds\n"
+        "buffer_load_dwordx4 %[l16], %[r], 0 offen lds\n"
+        "s_mov_b64 exec, -1" ::[dst] "s"(dst),
+        [l16] "v"(lane16), [r] "s"(r)
+        : "memory", "m0", "exec");
+  } else {
+    asm volatile(
+        "s_nop 4\n"
+        "s_mov_b32 m0, %[dst]\n"
+        "s_mov_b64 exec, 1\n"
+        "buffer_load_dwordx4 %[l16], %[r], 0 offen lds\n"
+        "buffer_load_dwordx4 %[l16], %[r], 0 offen lds\n"
+        "buffer_load_dwordx4 %[l16], %[r], 0 offen lds\n"
+        "buffer_load_dwordx4 %[l16], %[r], 0 offen lds\n"
+        "buffer_load_dwordx4 %[l16], %[r], 0 offen lds\n"
+        "s_mov_b64 exec, -1" ::[dst] "s"(dst),
+        [l16] "v"(lane16), [r] "s"(r)
+        : "memory", "m0", "exec");
+  }
+}
+
 // Resources of the flat walk's loads: the sign+mantissa section, and the
 // queue from 1 KB before it (so one immediate offset moves the global and
 // the LDS address of a queue load together).
@@ -875,7 +908,8 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
 // Fused product on the matrix cores (batch >= 16): Y[b, n] = sum_k X[b, k] W[n, k].
 //
 // A workgroup of nw waves decodes nw blocks (or nw rows of blocks) in
-// lockstep, one 16-group tile per step.  Every wave's tile lies in one row
+// lockstep, one 16-group tile per step, each wave with the flat walk's ring
+// of tile steps.  Every wave's tile lies in one row
 // and covers the same 1024 columns, so after a step the workgroup holds an
 // nw x 1024 bf16 slice of W in LDS (one row per wave, in natural column
 // order).  That slice is the A operand of v_mfma_f32_16x16x32_bf16 (rows of
@@ -884,7 +918,10 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
 // the k order of A and B agree).  The 32 k-steps of a slice are spread over
 // the waves; each wave accumulates its share for every batch tile, and the
 // partial sums are added across waves in a fixed order when the rows end.
-constexpr int kMfmaRS = 3;                 // tile steps per wave in flight
+// Two slices alternate, so one barrier per step separates the decode of a
+// step from the products of the previous one.
+constexpr int kMfmaRS = 2;                 // tile steps per wave in flight
+constexpr int kMfmaMaxRows = 64;           // batch rows per pass
 constexpr uint32_t kWRowBytes = 2048 + 16;  // one row of a slice; the pad keeps the A reads conflict-free
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -920,6 +957,17 @@ struct SliceSink {
   __device__ void single(int jj, int64_t, int, uint32_t w) { st16(row_addr + (jj * kWave + lane) * 2, w); }
 };
 
+// s_waitcnt vmcnt(N) that also names the activation registers as read and
+// written, so no use of them can be placed before it.
+template <int N, int IPW, int TB>
+__device__ __forceinline__ void wait_x(u32x4 (&xv)[IPW][TB]) {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+#pragma unroll
+  for (int i = 0; i < IPW; ++i)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) asm volatile("" : "+v"(xv[i][tb]));
+}
+
 // IPW k-steps per wave and slice go with the wave count (IPW = ceil(32 / nw)):
 // 16 waves (2), 11..15 (3), 8..10 (4); fewer waves leave more registers.
 constexpr int mfma_max_threads(int ipw) { return ipw == 2 ? 1024 : ipw == 3 ? 960 : 640; }
@@ -928,34 +976,44 @@ template <int TB, int IPW, bool PAIR, bool YBF16, int NQ>
 __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMatrix d, MfmaGeom g, const uint16_t* __restrict__ X,
                                                                           int64_t ldx, int nb_valid, void* __restrict__ Y,
                                                                           int64_t ldy) {
+  constexpr int RS = kMfmaRS;
+  constexpr int XTRA = IPW * TB;  // activation loads per step
   extern __shared__ uint32_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int nw = g.nw;
-  const uint32_t slice = kAreaAddr;  // nw rows of kWRowBytes; also the reduction area
-  const uint32_t sm_ring = slice + uint32_t(nw) * kWRowBytes + uint32_t(wave) * ring_bytes(kMfmaRS, d.slot_bytes);
-  const uint32_t q_ring = sm_ring + kMfmaRS * 1024;
-  const uint32_t my_row = slice + uint32_t(wave) * kWRowBytes;
+  const uint32_t lane16 = 16u * uint32_t(lane);
+  // two slices (steps alternate), then one ring per wave
+  const uint32_t slice0 = kAreaAddr, slice_bytes = uint32_t(nw) * kWRowBytes;
+  const uint32_t stride = 1024u + uint32_t(d.slot_bytes);
+  const uint32_t ring = slice0 + 2 * slice_bytes + uint32_t(wave) * RS * stride;
+  const uint32_t ring_last = ring + (RS - 1) * stride;
+  const __amdgpu_buffer_rsrc_t rsm = flat_rsm(d), rq = flat_rq(d);
+  const int tpt = g.tiles_per_block * g.seq_blocks;  // tiles per wave and task
   build_tables<PAIR>(d, lds, lds + kTableWords);
-  __syncthreads();
+  lds_barrier();
 
-  // A operand row of this lane (rows >= nw are zero padding)
+  // A operand row of this lane.  Rows >= nw and batch rows >= nb_valid read
+  // real but unrelated data: they only feed output rows and columns that are
+  // never stored (an MFMA output element depends on its own A row and B
+  // column only).
   const int a_row = lane % 16, a_quad = lane / 16;
-  const uint32_t a_addr = slice + uint32_t(a_row < nw ? a_row : 0) * kWRowBytes + a_quad * 16;
+  const uint32_t a_off = uint32_t(a_row < nw ? a_row : 0) * kWRowBytes + a_quad * 16;
   // B operand: activation row b = 16 tb + lane % 16 (clamped for the address), 8 columns at 8 * (lane / 16)
   const uint16_t* xrow[TB];
-  bool xvalid[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int b = 16 * tb + lane % 16;
-    xvalid[tb] = b < nb_valid;
     xrow[tb] = X + int64_t(b < nb_valid ? b : 0) * ldx + 8 * a_quad;
   }
+  // 16 bytes per wave that take the loads of a step with no refill to issue
+  const uint32_t dummy = slice0 + 2 * slice_bytes + uint32_t(nw) * RS * stride + uint32_t(wave) * 16;
 
   for (int task = blockIdx.x; task < g.n_tasks; task += gridDim.x) {
     floatx4 acc[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // this wave's blocks: one block, or the blocks of one row
+    // this wave's tiles: one block, or the blocks of one row (whole blocks
+    // either way, so the flat walk's tiles u0 .. u0 + tpt)
     int b0;
     bool valid;
     if (g.by_block) {
@@ -966,126 +1024,147 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
       valid = row < d.rows;
       b0 = int(row * g.seq_blocks);
     }
-    const int b1 = g.by_block ? b0 + 1 : b0 + g.seq_blocks;
-    Feeder<kMfmaRS, NQ> fd;
-    if (valid) fd.init(d, b0, b1, sm_ring, q_ring, lane);
-    BlockRef cr{};
-    int ct = 0, cblk = b0;  // the next step this wave decodes
-    LaneDec s{};
-    uint32_t rpos = 0, pos = 0;
-    int slot = 0;
-    uint4 xv[IPW][TB];
+    const int u0 = b0 * d.T;
+    int fv = u0;
+    uint32_t f_floor = 0, f_shifts = 0;
+    const const_word* fstep = (const const_word*)(d.steps) + 2u * uint32_t(u0);
+    if (valid) {
+      // the first RS steps, then the descriptor of the next one
+      uint32_t sl = ring;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int kk = (wave + i * nw) & 31;  // distinct per i
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) xv[i][tb] = *reinterpret_cast<const uint4*>(xrow[tb] + 32 * kk);
-    }
-    for (int sb = 0; sb < g.seq_blocks; ++sb) {
-      for (int t = 0; t < g.tiles_per_block; ++t) {
-        const int tau = sb * g.tiles_per_block + t;
-        // decode this wave's tile into its slice row (every tile here is full
-        // and lies in one row: cols is a multiple of 1024)
-        bool consumed = false;
-        const uint32_t sm_slot = sm_ring + 1024u * uint32_t(slot);
-        const uint32_t q_slot = q_ring + uint32_t(d.slot_bytes) * uint32_t(slot);
-        if (valid && cblk == b0 + sb && cblk < b1 && ct == t) {
-          if (t == 0) {
-            pos = 0;
-            cr = block_ref(d, cblk);
-          }
-          // each later step issues its refill and then the next activations;
-          // before the first step only the ring was filled
-          if (tau == 0) __builtin_amdgcn_s_waitcnt(0);
-          else wait_oldest_step<kMfmaRS, NQ, IPW * TB>();
-          const uint32_t q = q_slot + ((uint32_t(reinterpret_cast<uintptr_t>(cr.q)) + pos) & 15u);
-          rpos = t == 0 ? lane_dec_start(s, q, d.rb_words, lane) : 0u;
-          const uint4 cur = ld128(sm_slot + 16u * uint32_t(lane));
-          SliceSink sink{my_row, lane};
-          pos += decode_tile<PAIR>(d, s, q, rpos, cur, raw_mask16(s.raw_word, 16 * t), 16, true, 0, 0, lane, sink);
-          if (++ct == cr.nt) {
-            ct = 0;
-            ++cblk;
-          }
-          consumed = true;
-          slot = slot + 1 == kMfmaRS ? 0 : slot + 1;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) st32(my_row + (i * kWave + lane) * 4, 0u);
-        }
-        __syncthreads();
-        // matrix cores: k-steps wave, wave + nw, ... of the 32 in this slice
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-          const int kk = wave + i * nw;
-          if (kk < 32) {
-            uint4 a = ld128(a_addr + kk * 64);
-            if (a_row >= nw) a = uint4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-              const uint4 b = xvalid[tb] ? xv[i][tb] : uint4{0u, 0u, 0u, 0u};
-              acc[tb] = mfma_bf16(a, b, acc[tb]);
-            }
-          }
-        }
-        __syncthreads();
-        // refill the consumed slot, then the activations of the next step
-        if (consumed) {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          fd.feed(d, sm_slot, q_slot, lane);
-        }
-        if (t + 1 < g.tiles_per_block || sb + 1 < g.seq_blocks) {
-          const int64_t col0 = int64_t((tau + 1) % g.tiles_per_row) * 1024;
-#pragma unroll
-          for (int i = 0; i < IPW; ++i) {
-            const int kk = (wave + i * nw) & 31;
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) xv[i][tb] = *reinterpret_cast<const uint4*>(xrow[tb] + col0 + 32 * kk);
-          }
-        }
-        // the rows of this slice end here: add the partial sums of all waves
-        if ((tau + 1) % g.tiles_per_row == 0) {
-#pragma unroll
-          for (int r = 0; r < TB; r += 2) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              if (r + q < TB) {
-                const floatx4 v = acc[r + q];
-                st128(slice + ((wave * 2 + q) * kWave + lane) * 16,
-                      uint4{f32_bits(v.x), f32_bits(v.y), f32_bits(v.z), f32_bits(v.w)});
-              }
-            }
-            __syncthreads();
-            const int nvals = (TB - r >= 2 ? 2 : 1) * 256;
-            for (int v = threadIdx.x; v < nvals; v += blockDim.x) {
-              const int q = v / 256, rem = v % 256, l = rem / 4, e = rem % 4;
-              float sum = 0.f;
-              for (int w = 0; w < nw; ++w) sum += bits_f32(ld32(slice + ((w * 2 + q) * kWave + l) * 16 + e * 4));
-              const int m = 4 * (l / 16) + e;  // slice row
-              const int b = 16 * (r + q) + l % 16;
-              int64_t row;
-              bool ok;
-              if (g.by_block) {
-                const int64_t mb = int64_t(task) * nw + m;
-                row = mb * g.rows_per_block + tau / g.tiles_per_row;
-                ok = mb < d.n_blocks;
-              } else {
-                row = int64_t(task) * nw + m;
-                ok = true;
-              }
-              if (m < nw && ok && row < d.rows && b < nb_valid) {
-                if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + row] = f32_to_bf16(sum);
-                else static_cast<float*>(Y)[b * ldy + row] = sum;
-              }
-            }
-            __syncthreads();
-          }
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < RS; ++i) {
+        if (i < tpt) {
+          issue_flat<NQ>(rsm, rq, fv, fstep[0], fstep[1], sl, lane16);
+          ++fv;
+          fstep += 2;
+          sl += stride;
         }
       }
+      f_floor = fstep[0];
+      f_shifts = fstep[1];
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the repeated loads past the end land before the next task reuses the ring
+    const int v_end = u0 + tpt;
+    uint32_t qpos = valid ? scalar_word(d.block_off, b0) : 0u;
+    uint32_t tile_rm = 0;
+    LaneDec s{};
+    uint32_t slot = ring;
+    bool refill = false;  // the previous step consumed a slot that is not refilled yet
+    uint32_t rf_slot = 0;
+    for (int tau = 0; tau < tpt; ++tau) {
+      const int t = tau % g.tiles_per_block;
+      const uint32_t my_slice = slice0 + uint32_t(tau & 1) * slice_bytes;
+      // This step's activations first, then the refill of the slot the
+      // previous step consumed: so the wait for the activations never waits
+      // for that refill.  Both are issued in asm and every wait is explicit.
+      u32x4 xv[IPW][TB];
+      {
+        const int64_t col0 = int64_t(tau % g.tiles_per_row) * 1024;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+          const int kk = (wave + i * nw) & 31;
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(xv[i][tb]) : "v"(xrow[tb] + col0 + 32 * kk) : "memory");
+        }
+      }
+      // every step issues 1 + NQ loads after its activations: the refill, or
+      // one-lane loads into this wave's dummy bytes
+      if (refill && fv < v_end) {
+        issue_flat<NQ>(rsm, rq, fv, f_floor, f_shifts, rf_slot, lane16);
+        ++fv;
+        fstep += 2;
+        f_floor = fstep[0];
+        f_shifts = fstep[1];
+      } else {
+        issue_dummy<1 + NQ>(rsm, dummy, lane16);
+      }
+      refill = false;
+      const uint32_t my_row = my_slice + uint32_t(wave) * kWRowBytes;
+      if (valid) {
+        // loads younger than this step's: the RS - 1 steps issued after it
+        // (1 + NQ each) and this step's activations; near the end, where
+        // no refills follow, everything
+        if (u0 + tau + RS <= v_end) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((RS - 1) * (1 + NQ) + XTRA) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const uint32_t q = slot + 1024u + (qpos & 15u);
+        uint32_t rpos = 0;
+        if (t == 0) {
+          rpos = lane_dec_start(s, q, d.rb_words, lane);
+          tile_rm = (ld32(q + 128 + 4 * uint32_t(lane >> 1)) >> (16 * (lane & 1))) & 0xFFFFu;
+        }
+        const uint4 cur = ld128(slot + lane16);
+        SliceSink sink{my_row, lane};
+        qpos += __builtin_amdgcn_readfirstlane(
+            decode_tile<PAIR>(d, s, q, rpos, cur, __builtin_amdgcn_readlane(tile_rm, t), 16, true, 0, 0, lane, sink));
+        refill = true;
+        rf_slot = slot;
+        slot = slot == ring_last ? ring : slot + stride;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st32(my_row + (i * kWave + lane) * 4, 0u);
+      }
+      // the slice of this step is complete (and every wave is done with the
+      // one before it, which the next step overwrites)
+      lds_barrier();
+      // the activations have landed once only this step's 1 + NQ loads may
+      // be younger
+      wait_x<1 + NQ, IPW, TB>(xv);
+      // matrix cores: k-steps wave, wave + nw, ... of the 32 in this slice
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int kk = wave + i * nw;
+        if (kk < 32) {
+          const uint4 a = ld128(my_slice + a_off + kk * 64);
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+            acc[tb] = mfma_bf16(a, uint4{xv[i][tb].x, xv[i][tb].y, xv[i][tb].z, xv[i][tb].w}, acc[tb]);
+        }
+      }
+      // the rows of this slice end here: add the partial sums of all waves
+      // (through this step's slice, which the next step does not write)
+      if ((tau + 1) % g.tiles_per_row == 0) {
+#pragma unroll
+        for (int r = 0; r < TB; r += 2) {
+          lds_barrier();  // every wave is done reading the slice (or the previous partial sums)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (r + q < TB) {
+              const floatx4 v = acc[r + q];
+              st128(my_slice + ((wave * 2 + q) * kWave + lane) * 16,
+                    uint4{f32_bits(v.x), f32_bits(v.y), f32_bits(v.z), f32_bits(v.w)});
+            }
+          }
+          lds_barrier();
+          const int nvals = (TB - r >= 2 ? 2 : 1) * 256;
+          for (int v = threadIdx.x; v < nvals; v += blockDim.x) {
+            const int q = v / 256, rem = v % 256, l = rem / 4, e = rem % 4;
+            float sum = 0.f;
+            for (int w = 0; w < nw; ++w) sum += bits_f32(ld32(my_slice + ((w * 2 + q) * kWave + l) * 16 + e * 4));
+            const int m = 4 * (l / 16) + e;  // slice row
+            const int b = 16 * (r + q) + l % 16;
+            int64_t row;
+            bool ok;
+            if (g.by_block) {
+              const int64_t mb = int64_t(task) * nw + m;
+              row = mb * g.rows_per_block + tau / g.tiles_per_row;
+              ok = mb < d.n_blocks;
+            } else {
+              row = int64_t(task) * nw + m;
+              ok = true;
+            }
+            if (m < nw && ok && row < d.rows && b < nb_valid) {
+              if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + row] = f32_to_bf16(sum);
+              else static_cast<float*>(Y)[b * ldy + row] = sum;
+            }
+          }
+        }
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    // every load of this task has landed before the ring and slices are reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
   }
 }
 
@@ -1236,7 +1315,11 @@ bool mfma_geometry(const DevMatrix& d, MfmaGeom* g, std::string* why) {
     if (why) *why = "the matrix-core path needs G to divide, or be a multiple of, the groups per row";
     return false;
   }
-  const size_t per_wave = kWRowBytes + ring_bytes(kMfmaRS, d.slot_bytes);
+  if (!d.flat) {
+    if (why) *why = "the matrix-core path needs the flat walk (G and cols/64 multiples of 16)";
+    return false;
+  }
+  const size_t per_wave = 2 * kWRowBytes + ring_bytes(kMfmaRS, d.slot_bytes) + 16;
   const int nw_max = int(std::min<size_t>(16, (size_t(kLdsLimit) - tables_bytes()) / per_wave));
   if (nw_max < 8) {
     if (why) *why = "the blocks of this matrix are too large for the matrix-core path's LDS budget";
@@ -1266,9 +1349,9 @@ template <int TB, int IPW, bool PAIR>
 int run_mfma(const uw_matrix* m, const MfmaGeom& g, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy,
              int yt, hipStream_t s) {
   const DevMatrix& d = m->dev;
-  const size_t lds = tables_bytes() + size_t(g.nw) * (kWRowBytes + ring_bytes(kMfmaRS, d.slot_bytes));
-  auto kern = yt == UW_BF16 ? (d.seg_loads <= 2 ? fused_mfma_kernel<TB, IPW, PAIR, true, 2> : fused_mfma_kernel<TB, IPW, PAIR, true, 4>)
-                            : (d.seg_loads <= 2 ? fused_mfma_kernel<TB, IPW, PAIR, false, 2> : fused_mfma_kernel<TB, IPW, PAIR, false, 4>);
+  const size_t lds = tables_bytes() + size_t(g.nw) * (2 * kWRowBytes + ring_bytes(kMfmaRS, d.slot_bytes) + 16);
+  auto kern = yt == UW_BF16 ? (d.nq == 2 ? fused_mfma_kernel<TB, IPW, PAIR, true, 2> : fused_mfma_kernel<TB, IPW, PAIR, true, 4>)
+                            : (d.nq == 2 ? fused_mfma_kernel<TB, IPW, PAIR, false, 2> : fused_mfma_kernel<TB, IPW, PAIR, false, 4>);
   allow_full_lds(kern);
   hipLaunchKernelGGL(kern, dim3(g.n_tasks), dim3(g.nw * kWave), lds, s, d, g, X, ldx, nb, Y, ldy);
   return hip_check(hipGetLastError(), "fused_mfma_kernel launch");
@@ -1282,13 +1365,14 @@ int run_mfma_ipw(const uw_matrix* m, const MfmaGeom& g, const uint16_t* X, int64
   return run_mfma<TB, 4, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
 }
 
-// 32 batch rows per pass: two 16-row tiles keep the activations of three
-// k-steps and the accumulators in registers without spilling.
+// Up to 64 batch rows per pass (four 16-row tiles of activations and
+// accumulators in registers).
 template <bool PAIR>
 int run_mfma_tb(const uw_matrix* m, const MfmaGeom& g, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy,
                 int yt, hipStream_t s) {
   if (nb <= 16) return run_mfma_ipw<1, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
-  return run_mfma_ipw<2, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
+  if (nb <= 32) return run_mfma_ipw<2, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
+  return run_mfma_ipw<4, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
 }
 
 bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why) {
@@ -1313,8 +1397,8 @@ int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t 
   if (reinterpret_cast<uintptr_t>(X) % 16 || ldx % 8)
     return fail(UW_ERR_UNSUPPORTED, "fused matrix-core product: X must be 16-byte aligned with ldx a multiple of 8");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int64_t b0 = 0; b0 < batch; b0 += 32) {
-    const int nb = int(std::min<int64_t>(32, batch - b0));
+  for (int64_t b0 = 0; b0 < batch; b0 += kMfmaMaxRows) {
+    const int nb = int(std::min<int64_t>(kMfmaMaxRows, batch - b0));
     const uint16_t* Xb = static_cast<const uint16_t*>(X) + b0 * ldx;
     void* Yb = static_cast<char*>(Y) + b0 * ldy * elem_size(yt);
     const int rc = is_pair(d) ? run_mfma_tb<true>(m, g, Xb, ldx, nb, Yb, ldy, yt, s)
