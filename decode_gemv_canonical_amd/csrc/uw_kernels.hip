@@ -123,7 +123,7 @@ __device__ inline uint32_t peek(const LaneDec& s) { return __builtin_amdgcn_alig
 
 // Refill check of phase PH (checks alternate phases within a block): merge the
 // word read at the previous check, shift the lanes with qm >= 32 and read the
-// next word of those that still have words.  q = segment base, wp = byte
+// next word of those that still have words.  q = segment base, wp = word
 // offset of the next word to take (wave-uniform).  A lane that takes nothing
 // reads a word inside the segment or just past its end, which the slot holds.
 // left -= 1 on the lanes of mask m: one subtract with the mask as borrow
@@ -142,12 +142,18 @@ __device__ __forceinline__ void check(LaneDec& s, uint32_t q, uint32_t& wp) {
   s.w0 = adv ? s.w1 : s.w0;
   s.w1 = adv ? w2 : s.w1;
   s.w2 = w2;
-  s.nw[PH] = ld32(q + wp + 4 * lanes_below(m));
+  // the segment address of word wp, kept a scalar sum (an empty asm stops
+  // the compiler from folding it into the per-lane address arithmetic)
+  uint32_t base;
+  asm("s_lshl2_add_u32 %0, %1, %2"
+      : "=s"(base)
+      : "s"(__builtin_amdgcn_readfirstlane(wp)), "s"(__builtin_amdgcn_readfirstlane(q)));
+  s.nw[PH] = ld32(base + 4 * lanes_below(m));
   s.took[PH] = m;
   s.left = dec_masked(s.left, m);
   s.qm &= 31u;
-  wp += 4 * uint32_t(__builtin_popcountll(m));
-  wp = __builtin_amdgcn_readfirstlane(wp);  // wave-uniform: keeps q + wp a scalar sum
+  wp += uint32_t(__builtin_popcountll(m));
+  wp = __builtin_amdgcn_readfirstlane(wp);  // wave-uniform: keeps q + 4 wp a scalar sum
 }
 
 __device__ inline void check_rt(LaneDec& s, int ph, uint32_t q, uint32_t& wp) {
@@ -210,7 +216,7 @@ template <bool PAIR, class Sink>
 __device__ __forceinline__ uint32_t decode_tile(const DevMatrix& d, LaneDec& s, uint32_t q, uint32_t rpos,
                                             const uint4& cur, uint32_t rmask, int nt, bool aligned, int64_t row0,
                                             int c0, int lane, Sink& sink) {
-  uint32_t wp = rpos + 64 * uint32_t(__builtin_popcount(rmask));
+  uint32_t wp = (rpos >> 2) + 16 * uint32_t(__builtin_popcount(rmask));  // words
   const uint32_t pmask = PAIR ? 0x3FFCu : (((1u << d.L) - 1u) << 2);
   if (aligned) {
     sink.tile_begin(row0, c0);
@@ -291,7 +297,7 @@ __device__ __forceinline__ uint32_t decode_tile(const DevMatrix& d, LaneDec& s, 
       }
     }
   }
-  return wp;  // the segment's length: raw bytes and every word taken
+  return 4 * wp;  // the segment's length in bytes: raw bytes and every word taken
 }
 
 // ---------------------------------------------------------------------------
@@ -740,9 +746,12 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
 
 // ---------------------------------------------------------------------------
 // Fused product Y[b, n] = sum_k X[b, k] W[n, k] for NBP batch columns per pass.
-// X lives in LDS at kAreaAddr: bf16 as pairs, word (p*64 + l)*NBP + b =
-// X[b][128p + l] | X[b][128p + 64 + l] << 16 (column groups 2p and 2p+1 at
-// lane l); fp32 as word k*NBP + b = X[b][k].
+// X lives in LDS at kAreaAddr.  bf16 x as pairs: pair p at lane l holds
+// X[b][128p + l] | X[b][128p + 64 + l] << 16 (column groups 2p and 2p+1) in
+// word x_word(p, l)*NBP + b, where the 8 pairs of a 16-group tile are 8
+// consecutive words of the lane (two 16-byte reads per tile); fp32 x as word
+// k*NBP + b = X[b][k].
+__host__ __device__ inline uint32_t x_word(uint32_t p, uint32_t l) { return (((p >> 3) * 64 + l) << 3) + (p & 7); }
 template <int NBP, bool XF32>
 __device__ inline void load_x(const DevMatrix& d, const void* X, int64_t ldx, int nb_valid, uint32_t* xl) {
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -756,18 +765,18 @@ __device__ inline void load_x(const DevMatrix& d, const void* X, int64_t ldx, in
     }
   } else {
     const uint16_t* x = static_cast<const uint16_t*>(X);
-    const uint32_t npairs = (uint32_t(d.gpr) + 1) / 2;
+    const uint32_t npairs = (uint32_t(d.gpr) + 15) / 16 * 8;  // whole 8-pair chunks
     for (uint32_t i = tid; i < npairs * 64 * NBP; i += nt) {
       const uint32_t pl = i / NBP;
       const int b = int(i % NBP);
       const uint32_t p = pl / 64, l = pl % 64;
       const int64_t k0 = 128 * int64_t(p) + l, k1 = k0 + 64;
       uint32_t v = 0;
-      if (b < nb_valid) {
+      if (b < nb_valid && k0 < C) {
         v = x[b * ldx + k0];
         if (k1 < C) v |= uint32_t(x[b * ldx + k1]) << 16;
       }
-      xl[i] = v;
+      xl[x_word(p, l) * NBP + b] = v;
     }
   }
 }
@@ -783,6 +792,7 @@ struct ProductSink {
   int cur_row;  // row being accumulated, relative to first_row
   int c0;
   uint32_t xtile;  // x address of this lane for column group c0
+  uint32_t xw[8 * NBP];  // flat walk, bf16 x: the tile's x words of this lane
   float acc[NBP];
   // Finished rows are parked in registers (lane r holds the r-th finished row
   // of the unit) and written with one store after the unit, so the decode
@@ -821,15 +831,28 @@ struct ProductSink {
   __device__ void tile_begin(int64_t row0, int c) {
     if (!FLAT) to_row(row0);  // the flat walk ends rows with row_end()
     c0 = c;
-    xtile = XF32 ? xaddr + ((uint32_t(c) * 64 + lane) * NBP) * 4 : xaddr + (((uint32_t(c) >> 1) * 64 + lane) * NBP) * 4;
+    if (XF32) {
+      xtile = xaddr + ((uint32_t(c) * 64 + lane) * NBP) * 4;
+    } else if (FLAT) {
+      // c is a multiple of 16: the tile's 8 pairs are 8 * NBP consecutive words
+      const uint32_t a = xaddr + x_word(uint32_t(c) >> 1, uint32_t(lane)) * NBP * 4;
+#pragma unroll
+      for (int j = 0; j < 2 * NBP; ++j) {
+        const uint4 v = ld128(a + 16 * j);
+        xw[4 * j] = v.x;
+        xw[4 * j + 1] = v.y;
+        xw[4 * j + 2] = v.z;
+        xw[4 * j + 3] = v.w;
+      }
+    }
   }
   // x of column group cg at this lane
   __device__ float x_at(int cg, int b) const {
     if (XF32) return bits_f32(ld32(xaddr + ((uint32_t(cg) * 64 + lane) * NBP + b) * 4));
-    const uint32_t v = ld32(xaddr + (((uint32_t(cg) >> 1) * 64 + lane) * NBP + b) * 4);
+    const uint32_t v = ld32(xaddr + (x_word(uint32_t(cg) >> 1, uint32_t(lane)) * NBP + b) * 4);
     return bits_f32((cg & 1) ? (v & 0xFFFF0000u) : (v << 16));
   }
-  // tile_begin() guarantees an even c0, so pair k reads x word (c0/2 + k)*64 + lane
+  // tile_begin() guarantees an even c0: pair k is x pair c0/2 + k
   __device__ void pair(int k, uint32_t D) {
     if (XF32) {
       const float wa = bits_f32(D << 16), wb = bits_f32(D & 0xFFFF0000u);
@@ -839,8 +862,11 @@ struct ProductSink {
         acc[b] = __builtin_fmaf(wa, bits_f32(ld32(a + 4 * b)), acc[b]);
         acc[b] = __builtin_fmaf(wb, bits_f32(ld32(a + 64 * NBP * 4 + 4 * b)), acc[b]);
       }
+    } else if (FLAT) {
+#pragma unroll
+      for (int b = 0; b < NBP; ++b) acc[b] = dot2_bf16(D, xw[k * NBP + b], acc[b]);
     } else {
-      const uint32_t a = xtile + uint32_t(k * 64 * NBP * 4);
+      const uint32_t a = xaddr + x_word((uint32_t(c0) >> 1) + uint32_t(k), uint32_t(lane)) * NBP * 4;
 #pragma unroll
       for (int b = 0; b < NBP; ++b) acc[b] = dot2_bf16(D, ld32(a + 4 * b), acc[b]);
     }
@@ -876,7 +902,7 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
                                                                                int64_t ldx, int nb_valid,
                                                                                void* __restrict__ Y, int64_t ldy) {
   extern __shared__ uint32_t lds[];
-  const uint32_t x_words = XF32 ? uint32_t(d.cols) * NBP : ((uint32_t(d.gpr) + 1) / 2) * 64 * NBP;
+  const uint32_t x_words = XF32 ? uint32_t(d.cols) * NBP : ((uint32_t(d.gpr) + 15) / 16 * 8) * 64 * NBP;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int waves = blockDim.x / kWave;
   const uint32_t sm_ring = kAreaAddr + x_words * 4 + uint32_t(wave) * ring_bytes(RS, d.slot_bytes);
@@ -1175,7 +1201,7 @@ bool is_pair(const DevMatrix& d) { return d.L <= 6; }
 size_t tables_bytes() { return size_t(kTableWords + kT1Words) * 4; }
 
 size_t x_bytes(const DevMatrix& d, int nbp, bool xf32) {
-  return xf32 ? size_t(d.cols) * nbp * 4 : size_t((d.gpr + 1) / 2) * 64 * nbp * 4;
+  return xf32 ? size_t(d.cols) * nbp * 4 : size_t((d.gpr + 15) / 16 * 8) * 64 * nbp * 4;
 }
 
 // Compute units of the current device.
