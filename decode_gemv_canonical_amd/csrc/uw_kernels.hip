@@ -609,21 +609,25 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
   int64_t row = row_base;
   int c0 = 0, t = 0;  // a unit starts a row and a block
   uint32_t tile_rm = 0;  // lane t: raw flags of tile t of the current block
+  uint32_t rpos = 0;     // the segment's head bytes (tile 0 of a block)
   LaneDec s{};
   uint32_t slot = ring;
+  // A block start: the head of tile 0's segment starts the lane decoders.
+  // It runs before the tile loop and at the end of a block's last tile (after
+  // the next step's wait), so the loop itself has no block-start branch.
+  auto block_start = [&]() {
+    const uint32_t q = slot + 1024u + (qpos & 15u);
+    rpos = lane_dec_start(s, q, d.rb_words, lane);
+    tile_rm = (ld32(q + 128 + 4 * uint32_t(lane >> 1)) >> (16 * (lane & 1))) & 0xFFFFu;
+  };
   // One tile step: decode the slot's tile into the sink, then (FEED) refill
   // the slot with the step RS ahead.
   auto step = [&](auto feed) {
     const uint32_t q = slot + 1024u + (qpos & 15u);
-    uint32_t rpos = 0;
-    if (t == 0) {
-      // block start: the head of tile 0's segment starts the lane decoders
-      rpos = lane_dec_start(s, q, d.rb_words, lane);
-      tile_rm = (ld32(q + 128 + 4 * uint32_t(lane >> 1)) >> (16 * (lane & 1))) & 0xFFFFu;
-    }
     const uint4 cur = ld128(slot + lane16);
     const uint32_t rmask = __builtin_amdgcn_readlane(tile_rm, t);
     qpos += __builtin_amdgcn_readfirstlane(decode_tile<PAIR>(d, s, q, rpos, cur, rmask, 16, true, row, c0, lane, sink));
+    rpos = 0;
     sink.tile_end(t, 16);
     c0 += 16;
     if (c0 == d.gpr) {
@@ -631,7 +635,6 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
       ++row;
       sink.row_end();
     }
-    if (++t == T) t = 0;
     if constexpr (decltype(feed)::value) {
       // every LDS read of the slot is done before it is refilled (the
       // builtin form, so the compiler knows the reads have completed)
@@ -643,16 +646,31 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
       f_shifts = fstep[1];
     }
     slot = slot == ring_last ? ring : slot + stride;
+    return ++t == T;
   };
   int v = u0;
-  // steady state: RS - 1 younger steps in flight, and every step refills its slot
+  // steady state: RS - 1 younger steps in flight, and every step refills its
+  // slot (a second wait for the same step is satisfied at once)
+  if (v < u1 - RS) wait_oldest_step<RS, NQ, XTRA>();
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  block_start();
   for (; v < u1 - RS; ++v) {
     wait_oldest_step<RS, NQ, XTRA>();
-    step(std::true_type{});
+    if (step(std::true_type{})) {
+      t = 0;
+      if (v + 1 < u1 - RS) wait_oldest_step<RS, NQ, XTRA>();
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      block_start();
+    }
   }
   // the last RS steps: everything has been issued
   if (v < u1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  for (; v < u1; ++v) step(std::false_type{});
+  for (; v < u1; ++v) {
+    if (step(std::false_type{}) && v + 1 < u1) {
+      t = 0;
+      block_start();
+    }
+  }
 }
 
 constexpr int kRS = 4;  // tile steps in flight per wave (the flat walk may use kRSLow)
@@ -793,6 +811,7 @@ struct ProductSink {
   int c0;
   uint32_t xtile;  // x address of this lane for column group c0
   uint32_t xw[8 * NBP];  // flat walk, bf16 x: the tile's x words of this lane
+  uint32_t xlane;        // xaddr + lane * 32 * NBP
   float acc[NBP];
   // Finished rows are parked in registers (lane r holds the r-th finished row
   // of the unit) and written with one store after the unit, so the decode
@@ -834,8 +853,9 @@ struct ProductSink {
     if (XF32) {
       xtile = xaddr + ((uint32_t(c) * 64 + lane) * NBP) * 4;
     } else if (FLAT) {
-      // c is a multiple of 16: the tile's 8 pairs are 8 * NBP consecutive words
-      const uint32_t a = xaddr + x_word(uint32_t(c) >> 1, uint32_t(lane)) * NBP * 4;
+      // c is a multiple of 16: the tile's 8 pairs are the 8 * NBP words at
+      // x_word(c / 2, lane) * NBP = (c / 16 * 64 + lane) * 8 * NBP
+      const uint32_t a = xlane + (uint32_t(c) >> 4) * (2048u * NBP);
 #pragma unroll
       for (int j = 0; j < 2 * NBP; ++j) {
         const uint4 v = ld128(a + 16 * j);
@@ -881,6 +901,7 @@ struct ProductSink {
   __device__ void block_begin(int) {}
   // a unit covers whole rows; finished rows are stored when it ends
   __device__ void unit_begin(int unit) {
+    xlane = xaddr + uint32_t(lane) * 32u * NBP;
     first_row = int64_t(unit) * d.rows_per_unit;
     cur_row = 0;
     n_done = 0;
@@ -916,7 +937,7 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
   build_tables<PAIR>(d, lds, lds + kTableWords);
   load_x<NBP, XF32>(d, X, ldx, nb_valid, lds + kTableWords + kT1Words);
   lds_barrier();
-  ProductSink<NBP, XF32, YBF16, FLAT> sink{d, kAreaAddr, lane, nb_valid, Y, ldy, 0, 0, 0u, {}, {}, 0, 0};
+  ProductSink<NBP, XF32, YBF16, FLAT> sink{d, kAreaAddr, lane, nb_valid, Y, ldy};  // the rest set per unit
   for (int u = u_first; u < d.n_units; u += gridDim.x * waves) {
     sink.unit_begin(u);
     const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
