@@ -223,6 +223,11 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
       uw_matrix_destroy(m);
       return rc;
     }
+    // one wave per block when a unit has several blocks and each block holds
+    // a row end (G > groups per row): a row then spans at most two blocks,
+    // and the waves of one unit share a workgroup (at most 16 waves)
+    d.split = d.flat && d.unit_blocks > 1 && d.unit_blocks <= 8 && int64_t(h.G) > d.gpr;
+    d.n_items = d.split ? d.n_blocks : d.n_units;
   }
   *out = m;
   return UW_OK;

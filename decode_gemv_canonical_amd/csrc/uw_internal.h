@@ -80,6 +80,10 @@ struct DevMatrix {
                                        //  byte i: 64 - lanes of 1 KB queue load i (at least 1 lane)}
   int32_t unit_blocks;                 // blocks per work unit (a unit covers whole rows)
   int32_t n_units;
+  int32_t split;                       // flat walk, G > gpr and not a multiple of it: the VALU product and the
+                                       //  decompress give each wave one block, and a row that crosses a block
+                                       //  end is summed from the two waves' parts
+  int32_t n_items;                     // waves of work of those kernels: n_blocks when split, else n_units
   uint32_t sym[32];                    // rev code | len << 16 | exponent << 24
 };
 

@@ -565,6 +565,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t flat_rsm(const DevMatrix& d) {
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t flat_rq(const DevMatrix& d) { return byte_rsrc(d.queue - 1024, d.q_extent); }
 
+// Work item u of the flat-walk VALU product and decompress: blocks [b0, b1)
+// from row `row`, column group c0.  A work unit (whole rows), or with split
+// rows one block, whose first tile may start mid-row.
+struct WalkItem {
+  int b0, b1;
+  int64_t row;
+  int c0;
+};
+__device__ __forceinline__ WalkItem walk_item(const DevMatrix& d, int u) {
+  WalkItem w;
+  if (d.split) {
+    const int v = u * d.T, tpr = d.gpr >> 4;
+    const int r = v / tpr;
+    w.b0 = u;
+    w.b1 = u + 1;
+    w.row = r;
+    w.c0 = (v - r * tpr) * 16;
+  } else {
+    w.b0 = u * d.unit_blocks;
+    w.b1 = std::min(d.n_blocks, w.b0 + d.unit_blocks);
+    w.row = int64_t(u) * d.rows_per_unit;
+    w.c0 = 0;
+  }
+  return w;
+}
+// Split rows: whether the item's last row goes on in the next block.
+__device__ __forceinline__ bool item_ends_mid_row(const DevMatrix& d, const WalkItem& w) {
+  return std::min(w.b1 * d.T, d.n_tiles) % (d.gpr >> 4) != 0;
+}
+
 // Issue the first RS steps of the tiles of blocks [b0, b1) into the ring;
 // returns the next step to issue.
 template <int RS, int NQ>
@@ -588,11 +618,12 @@ __device__ __forceinline__ int flat_start(const DevMatrix& d, int b0, int b1, ui
   return fv;
 }
 
-// Tiles of blocks [b0, b1) of a unit whose first row is row_base; flat_start
-// has issued the steps before fv0.
+// Tiles of blocks [b0, b1), whose first tile is at row row_base, column
+// group c_start (0 unless blocks split rows); flat_start has issued the
+// steps before fv0.
 template <int RS, int NQ, int XTRA, bool PAIR, class Sink>
-__device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, int b1, int64_t row_base, uint32_t ring,
-                                         int lane, Sink& sink) {
+__device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, int b1, int64_t row_base, int c_start,
+                                         uint32_t ring, int lane, Sink& sink) {
   const uint32_t lane16 = 16u * uint32_t(lane);
   const uint32_t stride = 1024u + uint32_t(d.slot_bytes);
   const uint32_t ring_last = ring + (RS - 1) * stride;
@@ -607,7 +638,7 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
   // consume side
   uint32_t qpos = scalar_word(d.block_off, b0);  // queue offset of the next segment
   int64_t row = row_base;
-  int c0 = 0, t = 0;  // a unit starts a row and a block
+  int c0 = c_start, t = 0;  // a block start
   uint32_t tile_rm = 0;  // lane t: raw flags of tile t of the current block
   uint32_t rpos = 0;     // the segment's head bytes (tile 0 of a block)
   LaneDec s{};
@@ -742,21 +773,24 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   const uint32_t q_ring = sm_ring + RS * 1024;
   const uint32_t tile = sm_ring + ring_bytes(RS, d.slot_bytes);
   const int u_first = blockIdx.x * waves + wave;
+  const int n_items = FLAT ? d.n_items : d.n_units;
   int fv = 0;
   // the first unit's loads go out before the tables are built
-  if (FLAT && u_first < d.n_units)
-    fv = flat_start<RS, NQ>(d, u_first * d.unit_blocks, std::min(d.n_blocks, (u_first + 1) * d.unit_blocks), sm_ring,
-                             lane);
+  if (FLAT && u_first < n_items) {
+    const WalkItem it = walk_item(d, u_first);
+    fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
+  }
   build_tables<PAIR>(d, lds, lds + kTableWords);
   lds_barrier();
   DecompressSink<FLAT> sink{d.cols, d.G, out, ld_out, tile, lane, 0, 0};
-  for (int u = u_first; u < d.n_units; u += gridDim.x * waves) {
-    const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
+  for (int u = u_first; u < n_items; u += gridDim.x * waves) {
     // the two 16-byte stores per tile only make the ring waits stricter
     if (FLAT) {
-      if (u != u_first) fv = flat_start<RS, NQ>(d, b0, b1, sm_ring, lane);
-      run_flat<RS, NQ, 0, PAIR>(d, fv, b0, b1, int64_t(u) * d.rows_per_unit, sm_ring, lane, sink);
+      const WalkItem it = walk_item(d, u);
+      if (u != u_first) fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
+      run_flat<RS, NQ, 0, PAIR>(d, fv, it.b0, it.b1, it.row, it.c0, sm_ring, lane, sink);
     } else {
+      const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
       run_blocks<RS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
     }
   }
@@ -899,10 +933,10 @@ struct ProductSink {
   }
   __device__ void tile_end(int, int) {}
   __device__ void block_begin(int) {}
-  // a unit covers whole rows; finished rows are stored when it ends
-  __device__ void unit_begin(int unit) {
+  // finished rows are stored when the work item ends
+  __device__ void unit_begin(int64_t row0) {
     xlane = xaddr + uint32_t(lane) * 32u * NBP;
-    first_row = int64_t(unit) * d.rows_per_unit;
+    first_row = row0;
     cur_row = 0;
     n_done = 0;
 #pragma unroll
@@ -912,6 +946,22 @@ struct ProductSink {
   __device__ void unit_end() {
     if (!FLAT) flush();  // the flat walk has ended the unit's last row
     store_done();
+  }
+  // Split rows.  The item's last row goes on in the next block: its partial
+  // sums go to LDS at `at` (NBP floats) instead of Y.
+  __device__ void park_tail(uint32_t at) {
+    flush();
+    --n_done;
+#pragma unroll
+    for (int b = 0; b < NBP; ++b)
+      if (lane == n_done) st32(at + 4 * b, f32_bits(rows_done[b]));
+  }
+  // The item's first row began in the previous block, whose wave parked that
+  // part at `at`: the row is that part plus this one.
+  __device__ void add_head(uint32_t at) {
+#pragma unroll
+    for (int b = 0; b < NBP; ++b)
+      if (lane == 0) rows_done[b] = bits_f32(ld32(at + 4 * b)) + rows_done[b];
   }
 };
 
@@ -929,22 +979,48 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
   const uint32_t sm_ring = kAreaAddr + x_words * 4 + uint32_t(wave) * ring_bytes(RS, d.slot_bytes);
   const uint32_t q_ring = sm_ring + RS * 1024;
   const int u_first = blockIdx.x * waves + wave;
+  const int n_items = FLAT ? d.n_items : d.n_units;
   int fv = 0;
   // the first unit's loads go out before the tables and x are set up
-  if (FLAT && u_first < d.n_units)
-    fv = flat_start<RS, NQ>(d, u_first * d.unit_blocks, std::min(d.n_blocks, (u_first + 1) * d.unit_blocks), sm_ring,
-                             lane);
+  if (FLAT && u_first < n_items) {
+    const WalkItem it = walk_item(d, u_first);
+    fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
+  }
   build_tables<PAIR>(d, lds, lds + kTableWords);
   load_x<NBP, XF32>(d, X, ldx, nb_valid, lds + kTableWords + kT1Words);
   lds_barrier();
   ProductSink<NBP, XF32, YBF16, FLAT> sink{d, kAreaAddr, lane, nb_valid, Y, ldy};  // the rest set per unit
-  for (int u = u_first; u < d.n_units; u += gridDim.x * waves) {
-    sink.unit_begin(u);
-    const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
+  if (FLAT && d.split) {
+    // One block per wave (the grid covers every block, and a workgroup holds
+    // whole units, so the wave before this one has the previous block).  A
+    // row that crosses a block end is finished after one barrier: the first
+    // part is parked in LDS by the wave that ends its block mid-row.
+    const uint32_t parts = kAreaAddr + x_words * 4 + uint32_t(waves) * ring_bytes(RS, d.slot_bytes);
+    const bool live = u_first < n_items;
+    bool head = false;
+    if (live) {
+      const WalkItem it = walk_item(d, u_first);
+      sink.unit_begin(it.row);
+      run_flat<RS, NQ, 0, PAIR>(d, fv, it.b0, it.b1, it.row, it.c0, sm_ring, lane, sink);
+      head = it.c0 != 0;
+      if (item_ends_mid_row(d, it)) sink.park_tail(parts + uint32_t(wave) * 4u * NBP);
+    }
+    lds_barrier();
+    if (live) {
+      if (head) sink.add_head(parts + uint32_t(wave - 1) * 4u * NBP);
+      sink.store_done();
+    }
+    return;
+  }
+  for (int u = u_first; u < n_items; u += gridDim.x * waves) {
     if (FLAT) {
-      if (u != u_first) fv = flat_start<RS, NQ>(d, b0, b1, sm_ring, lane);
-      run_flat<RS, NQ, 0, PAIR>(d, fv, b0, b1, int64_t(u) * d.rows_per_unit, sm_ring, lane, sink);
+      const WalkItem it = walk_item(d, u);
+      sink.unit_begin(it.row);
+      if (u != u_first) fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
+      run_flat<RS, NQ, 0, PAIR>(d, fv, it.b0, it.b1, it.row, it.c0, sm_ring, lane, sink);
     } else {
+      sink.unit_begin(int64_t(u) * d.rows_per_unit);
+      const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
       run_blocks<RS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
     }
     sink.unit_end();
@@ -954,10 +1030,10 @@ __global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(D
 // ---------------------------------------------------------------------------
 // Fused product on the matrix cores (batch >= 16): Y[b, n] = sum_k X[b, k] W[n, k].
 //
-// A workgroup of nw waves decodes nw blocks (or nw rows of blocks) in
-// lockstep, one 16-group tile per step, each wave with the flat walk's ring
-// of tile steps.  Every wave's tile lies in one row
-// and covers the same 1024 columns, so after a step the workgroup holds an
+// A workgroup of nw waves decodes nw work units (whole rows and whole
+// blocks) in lockstep, one 16-group tile per step, each wave with the flat
+// walk's ring of tile steps.  Every unit starts a row, so every wave's tile
+// lies in one row and covers the same 1024 columns, so after a step the workgroup holds an
 // nw x 1024 bf16 slice of W in LDS (one row per wave, in natural column
 // order).  That slice is the A operand of v_mfma_f32_16x16x32_bf16 (rows of
 // the slice = M, padded to 16 with zeros); 16 activation rows are the B
@@ -977,13 +1053,9 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // How the workgroups walk the matrix (set on the host).
 struct MfmaGeom {
   int nw;               // waves per workgroup = W rows per slice
-  int by_block;         // 1: wave w decodes block task*nw + w (G a multiple of the groups per row)
-                        // 0: wave w decodes the blocks of row task*nw + w (G divides the groups per row)
-  int rows_per_block;   // by_block: G / groups per row
-  int seq_blocks;       // blocks per wave and task (1, or groups per row / G)
   int tiles_per_block;  // G / 16
   int tiles_per_row;    // groups per row / 16
-  int n_tasks;
+  int n_tasks;          // wave w of task k decodes work unit k * nw + w (whole rows, whole blocks)
 };
 
 __device__ inline floatx4 mfma_bf16(const uint4& a, const uint4& b, const floatx4& c) {
@@ -1035,7 +1107,7 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
   const uint32_t ring = slice0 + 2 * slice_bytes + uint32_t(wave) * RS * stride;
   const uint32_t ring_last = ring + (RS - 1) * stride;
   const __amdgpu_buffer_rsrc_t rsm = flat_rsm(d), rq = flat_rq(d);
-  const int tpt = g.tiles_per_block * g.seq_blocks;  // tiles per wave and task
+  const int tpt = g.tiles_per_block * d.unit_blocks;  // tiles per wave and task (a whole unit)
   build_tables<PAIR>(d, lds, lds + kTableWords);
   lds_barrier();
 
@@ -1059,28 +1131,23 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
     floatx4 acc[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // this wave's tiles: one block, or the blocks of one row (whole blocks
-    // either way, so the flat walk's tiles u0 .. u0 + tpt)
-    int b0;
-    bool valid;
-    if (g.by_block) {
-      b0 = task * nw + wave;
-      valid = b0 < d.n_blocks;
-    } else {
-      const int64_t row = int64_t(task) * nw + wave;
-      valid = row < d.rows;
-      b0 = int(row * g.seq_blocks);
-    }
+    // this wave's tiles: the flat walk's tiles u0 .. v_end of its unit (the
+    // last unit of the matrix may end early; the wave then idles in step)
+    const int unit = task * nw + wave;
+    const bool valid = unit < d.n_units;
+    const int b0 = unit * d.unit_blocks;
     const int u0 = b0 * d.T;
+    const int v_end = valid ? std::min(u0 + tpt, d.n_tiles) : u0;
     int fv = u0;
     uint32_t f_floor = 0, f_shifts = 0;
-    const const_word* fstep = (const const_word*)(d.steps) + 2u * uint32_t(u0);
+    const const_word* fstep = (const const_word*)(d.steps) + 2u * uint32_t(valid ? u0 : 0);
     if (valid) {
-      // the first RS steps, then the descriptor of the next one
+      // the first RS steps, then the descriptor of the next one (the table
+      // has a spare entry after the last tile)
       uint32_t sl = ring;
 #pragma unroll
       for (int i = 0; i < RS; ++i) {
-        if (i < tpt) {
+        if (fv < v_end) {
           issue_flat<NQ>(rsm, rq, fv, fstep[0], fstep[1], sl, lane16);
           ++fv;
           fstep += 2;
@@ -1090,7 +1157,6 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
       f_floor = fstep[0];
       f_shifts = fstep[1];
     }
-    const int v_end = u0 + tpt;
     uint32_t qpos = valid ? scalar_word(d.block_off, b0) : 0u;
     uint32_t tile_rm = 0;
     LaneDec s{};
@@ -1127,7 +1193,7 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
       }
       refill = false;
       const uint32_t my_row = my_slice + uint32_t(wave) * kWRowBytes;
-      if (valid) {
+      if (u0 + tau < v_end) {
         // loads younger than this step's: the RS - 1 steps issued after it
         // (1 + NQ each) and this step's activations; near the end, where
         // no refills follow, everything
@@ -1189,17 +1255,9 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
             for (int w = 0; w < nw; ++w) sum += bits_f32(ld32(my_slice + ((w * 2 + q) * kWave + l) * 16 + e * 4));
             const int m = 4 * (l / 16) + e;  // slice row
             const int b = 16 * (r + q) + l % 16;
-            int64_t row;
-            bool ok;
-            if (g.by_block) {
-              const int64_t mb = int64_t(task) * nw + m;
-              row = mb * g.rows_per_block + tau / g.tiles_per_row;
-              ok = mb < d.n_blocks;
-            } else {
-              row = int64_t(task) * nw + m;
-              ok = true;
-            }
-            if (m < nw && ok && row < d.rows && b < nb_valid) {
+            const int64_t mu = int64_t(task) * nw + m;  // the unit of slice row m
+            const int64_t row = mu * d.rows_per_unit + tau / g.tiles_per_row;
+            if (m < nw && mu < d.n_units && row < d.rows && b < nb_valid) {
               if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + row] = f32_to_bf16(sum);
               else static_cast<float*>(Y)[b * ldy + row] = sum;
             }
@@ -1261,15 +1319,27 @@ int flat_ring_depth(int64_t units, size_t fixed, int slot_bytes, size_t extra, i
 
 template <int NBP, bool XF32, bool PAIR, bool YBF16>
 int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, void* stream) {
-  const DevMatrix& d = m->dev;
+  DevMatrix d = m->dev;  // a copy: split rows may be turned off for this launch
   const size_t fixed = tables_bytes() + x_bytes(d, NBP, XF32);
   const int max_waves = fused_max_threads(NBP) / kWave;
-  const int rs = d.flat ? flat_ring_depth(d.n_units, fixed, d.slot_bytes, 0, max_waves) : kRS;
-  const size_t per_wave = ring_bytes(rs, d.slot_bytes);
-  if (fixed + per_wave > size_t(kLdsLimit)) return fail(UW_ERR_UNSUPPORTED, "fused product: x does not fit on chip");
-  const int waves = pick_waves(d.n_units, fixed, per_wave, max_waves);
+  // split rows: NBP partial sums per wave in LDS, and whole units per
+  // workgroup; where a unit's waves do not fit, one wave per unit
+  if (d.split && (d.unit_blocks > max_waves ||
+                  fixed + (ring_bytes(kRSLow, d.slot_bytes) + 4 * NBP) * d.unit_blocks > size_t(kLdsLimit))) {
+    d.split = 0;
+    d.n_items = d.n_units;
+  }
+  const int items = d.flat ? d.n_items : d.n_units;
+  const size_t extra = d.split ? 4 * NBP : 0;
+  int rs = d.flat ? flat_ring_depth(items, fixed, d.slot_bytes, extra, max_waves) : kRS;
+  if (d.split && fixed + (ring_bytes(rs, d.slot_bytes) + extra) * d.unit_blocks > size_t(kLdsLimit)) rs = kRSLow;
+  const size_t per_wave = ring_bytes(rs, d.slot_bytes) + extra;
+  if (fixed + per_wave * (d.split ? d.unit_blocks : 1) > size_t(kLdsLimit))
+    return fail(UW_ERR_UNSUPPORTED, "fused product: x does not fit on chip");
+  int waves = pick_waves(items, fixed, per_wave, max_waves);
+  if (d.split) waves = std::max(1, waves / d.unit_blocks) * d.unit_blocks;
   const size_t lds = fixed + per_wave * waves;
-  const int grid = int(std::max<int64_t>(1, (d.n_units + waves - 1) / waves));
+  const int grid = int(std::max<int64_t>(1, (items + waves - 1) / waves));
   auto kern = d.flat ? (rs == kRS ? (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, true, kRS>
                                                : fused_product_kernel<NBP, XF32, PAIR, YBF16, 4, true, kRS>)
                                   : (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, true, kRSLow>
@@ -1318,11 +1388,12 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (m->h.plain()) return launch_copy_plain(d.plain, d.rows, d.cols, out, ld_out, stream);
   const size_t fixed = tables_bytes();
-  const int rs = d.flat ? flat_ring_depth(d.n_units, fixed, d.slot_bytes, kTransposeWords * 4, 16) : kRS;
+  const int items = d.flat ? d.n_items : d.n_units;
+  const int rs = d.flat ? flat_ring_depth(items, fixed, d.slot_bytes, kTransposeWords * 4, 16) : kRS;
   const size_t per_wave = ring_bytes(rs, d.slot_bytes) + kTransposeWords * 4;
-  const int waves = pick_waves(d.n_units, fixed, per_wave);
+  const int waves = pick_waves(items, fixed, per_wave);
   const size_t lds = fixed + per_wave * waves;
-  const int grid = int(std::max<int64_t>(1, (int64_t(d.n_units) + waves - 1) / waves));
+  const int grid = int(std::max<int64_t>(1, (int64_t(items) + waves - 1) / waves));
   auto pick = [&](auto pair) {
     constexpr bool P = decltype(pair)::value;
     return d.flat ? (rs == kRS ? (d.nq == 2 ? decompress_kernel<P, 2, true, kRS> : decompress_kernel<P, 4, true, kRS>)
@@ -1358,10 +1429,6 @@ bool mfma_geometry(const DevMatrix& d, MfmaGeom* g, std::string* why) {
     if (why) *why = "the matrix-core path needs cols to be a multiple of 1024";
     return false;
   }
-  if (d.G % d.gpr && d.gpr % d.G) {
-    if (why) *why = "the matrix-core path needs G to divide, or be a multiple of, the groups per row";
-    return false;
-  }
   if (!d.flat) {
     if (why) *why = "the matrix-core path needs the flat walk (G and cols/64 multiples of 16)";
     return false;
@@ -1372,12 +1439,9 @@ bool mfma_geometry(const DevMatrix& d, MfmaGeom* g, std::string* why) {
     if (why) *why = "the blocks of this matrix are too large for the matrix-core path's LDS budget";
     return false;
   }
-  g->by_block = d.G % d.gpr == 0;
-  g->rows_per_block = g->by_block ? d.G / d.gpr : 0;
-  g->seq_blocks = g->by_block ? 1 : d.gpr / d.G;
   g->tiles_per_block = d.G / 16;
   g->tiles_per_row = d.gpr / 16;
-  const int64_t units = g->by_block ? int64_t(d.n_blocks) : d.rows;
+  const int64_t units = d.n_units;
   double best = -1.0;
   for (int nw = 8; nw <= nw_max; ++nw) {
     const int64_t tasks = (units + nw - 1) / nw;

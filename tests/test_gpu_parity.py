@@ -83,6 +83,9 @@ DECOMP_CASES = [
     ("randbits", 1024, 2048, None, {}),
     ("down", 13, 512, 7, {"G": 48}),
     ("down", 5, 1024, 8, {"G": 16}),
+    ("gate", 67, 4096, 16, {"G": 224}),
+    ("down", 24, 14336, 17, {"G": 256}),
+    ("small", 50, 3072, 18, {"G": 80}),
     ("small", 37, 1600, 9, {"K": 32, "L": 8}),
     ("small", 21, 960, 10, {"K": 16, "L": 12}),
     ("small", 9, 128, 12, {"K": 1, "L": 1}),
@@ -132,6 +135,12 @@ GEMV_CASES = [
     ("small", 9, 128, 12, {"K": 1, "L": 1}, torch.bfloat16),
     ("gate", 33, 4096, 13, {"G": 64}, torch.bfloat16),
     ("small", 7, 64 * 7, 14, {}, torch.bfloat16),
+    # blocks that end mid-row (G above the groups per row, not a multiple):
+    # one wave per block, the crossing rows summed from two waves' parts
+    ("gate", 70, 4096, 15, {"G": 224}, torch.bfloat16),
+    ("gate", 67, 4096, 16, {"G": 224}, torch.float32),
+    ("down", 24, 14336, 17, {"G": 256}, torch.bfloat16),
+    ("small", 50, 3072, 18, {"G": 80}, torch.float32),
 ]
 
 
@@ -174,8 +183,9 @@ def test_gemv_scale_by_two_is_exact():
 
 
 @pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 8, 11])
-def test_gemm_fused_valu(batch):
-    wb, m = matrix("gate", 96, 4096, 21)
+@pytest.mark.parametrize("G", [256, 224])
+def test_gemm_fused_valu(batch, G):
+    wb, m = matrix("gate", 96, 4096, 21, G=G)
     X = workloads.activations(4096, batch, seed=300 + batch, dtype=torch.bfloat16)
     ref = products.gemm_f64(wb, X.float().numpy())
     _say(f"gemm fused batch={batch}")
@@ -199,9 +209,9 @@ def test_gemm_down_both_variants(batch):
         check_f32(Y, ref, f"gemm down b={batch} v={v}")
 
 
-# Matrix-core path: every way a workgroup can walk the blocks (G a multiple of
-# the groups per row with 1, 2 or 4 rows per block; G dividing a row; a
-# partial last block), raw groups, the single-code table (L > 6), partial
+# Matrix-core path: every shape of work unit (G a multiple of the groups per
+# row with 1, 2 or 4 rows per block; G dividing a row; units of several
+# blocks and rows; a partial last block), raw groups, the single-code table (L > 6), partial
 # batch tiles and more than one 64-row pass.
 MFMA_CASES = [
     ("small", None, None, None, {}, (16, 17, 64)),
@@ -210,6 +220,11 @@ MFMA_CASES = [
     ("small", 13, 1024, 43, {"G": 64}, (16,)),
     ("small", 40, 2048, 44, {"K": 32, "L": 8}, (20,)),
     ("big", 96, 8192, 45, {}, (100,)),
+    # work units of several blocks and rows (G neither divides nor is a
+    # multiple of the groups per row), with a partial last unit
+    ("gate", 67, 4096, 46, {"G": 224}, (16, 40)),
+    ("down", 24, 14336, 47, {"G": 256}, (16,)),
+    ("small", 50, 3072, 48, {"G": 80}, (20,)),
 ]
 
 
