@@ -80,18 +80,35 @@ std::vector<int> limited_lengths(const std::vector<uint64_t>& counts, const std:
   return len;
 }
 
+// Default G.  Candidates: multiples of 16 up to 256 that divide the groups
+// per row or are a multiple of it, plus (groups per row a multiple of 16)
+// any larger G whose work unit, lcm(G, groups per row), has at most 8 blocks.
+// With at least 2048 blocks, pick the G that spreads one block per wave most
+// evenly over the 1024 SIMDs of a 256-CU part: least
+// ceil(blocks / 1024) * (tiles per block + 1 for the block start), ties to
+// the larger G.  Smaller matrices: the largest aligned G <= 64.
 int auto_groups_per_block(int64_t rows, int64_t cols) {
   const int64_t gpr = cols / 64, total = rows * gpr;
-  std::vector<int> aligned, all;
+  std::vector<int> aligned, wide, all;
   for (int g = 16; g <= 256; g += 16) {
     all.push_back(g);
-    if (gpr % g == 0 || g % gpr == 0) aligned.push_back(g);
+    const bool al = gpr % g == 0 || g % gpr == 0;
+    if (al) aligned.push_back(g);
+    if (al || (gpr % 16 == 0 && g > gpr && gpr / std::gcd<int64_t>(g, gpr) <= 8)) wide.push_back(g);
   }
-  const std::vector<int>& pool = aligned.empty() ? all : aligned;
   int best = -1;
-  for (int g : pool)
-    if ((total + g - 1) / g >= 2048) best = std::max(best, g);
+  int64_t best_load = 0;
+  for (int g : wide.empty() ? all : wide) {
+    const int64_t nb = (total + g - 1) / g;
+    if (nb < 2048) continue;
+    const int64_t load = (nb + 1023) / 1024 * (g / 16 + 1);
+    if (best < 0 || load < best_load || (load == best_load && g > best)) {
+      best = g;
+      best_load = load;
+    }
+  }
   if (best > 0) return best;
+  const std::vector<int>& pool = aligned.empty() ? all : aligned;
   int small = -1;
   for (int g : pool)
     if (g <= 64) small = std::max(small, g);

@@ -1056,6 +1056,9 @@ struct MfmaGeom {
   int tiles_per_block;  // G / 16
   int tiles_per_row;    // groups per row / 16
   int n_tasks;          // wave w of task k decodes work unit k * nw + w (whole rows, whole blocks)
+  int split;            // 1: wave w decodes block k * nw + w instead, started late by the column
+                        //    tile it begins at, so every wave's tile has the same columns
+  int steps;            // split: steps per task (a multiple of tiles_per_row)
 };
 
 __device__ inline floatx4 mfma_bf16(const uint4& a, const uint4& b, const floatx4& c) {
@@ -1107,7 +1110,9 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
   const uint32_t ring = slice0 + 2 * slice_bytes + uint32_t(wave) * RS * stride;
   const uint32_t ring_last = ring + (RS - 1) * stride;
   const __amdgpu_buffer_rsrc_t rsm = flat_rsm(d), rq = flat_rq(d);
-  const int tpt = g.tiles_per_block * d.unit_blocks;  // tiles per wave and task (a whole unit)
+  const int tpt = g.tiles_per_block * (g.split ? 1 : d.unit_blocks);  // tiles per wave and task
+  const int n_steps = g.split ? g.steps : tpt;
+  const int n_items = g.split ? d.n_blocks : d.n_units;
   build_tables<PAIR>(d, lds, lds + kTableWords);
   lds_barrier();
 
@@ -1126,6 +1131,9 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
   }
   // 16 bytes per wave that take the loads of a step with no refill to issue
   const uint32_t dummy = slice0 + 2 * slice_bytes + uint32_t(nw) * RS * stride + uint32_t(wave) * 16;
+  // split: the part of each slice row's first row that its block holds (a
+  // row that began in the previous block), per batch row of the pass
+  const uint32_t heads = dummy + uint32_t(nw - wave) * 16;
 
   for (int task = blockIdx.x; task < g.n_tasks; task += gridDim.x) {
     floatx4 acc[TB];
@@ -1134,10 +1142,12 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
     // this wave's tiles: the flat walk's tiles u0 .. v_end of its unit (the
     // last unit of the matrix may end early; the wave then idles in step)
     const int unit = task * nw + wave;
-    const bool valid = unit < d.n_units;
-    const int b0 = unit * d.unit_blocks;
+    const bool valid = unit < n_items;
+    const int b0 = g.split ? unit : unit * d.unit_blocks;
     const int u0 = b0 * d.T;
     const int v_end = valid ? std::min(u0 + tpt, d.n_tiles) : u0;
+    // split: a block that starts at column tile delta runs delta steps late
+    const int delta = g.split ? u0 % g.tiles_per_row : 0;
     int fv = u0;
     uint32_t f_floor = 0, f_shifts = 0;
     const const_word* fstep = (const const_word*)(d.steps) + 2u * uint32_t(valid ? u0 : 0);
@@ -1163,8 +1173,9 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
     uint32_t slot = ring;
     bool refill = false;  // the previous step consumed a slot that is not refilled yet
     uint32_t rf_slot = 0;
-    for (int tau = 0; tau < tpt; ++tau) {
-      const int t = tau % g.tiles_per_block;
+    for (int tau = 0; tau < n_steps; ++tau) {
+      const int tt = tau - delta;  // this wave's tile in its unit or block
+      const int t = tt % g.tiles_per_block;
       const uint32_t my_slice = slice0 + uint32_t(tau & 1) * slice_bytes;
       // This step's activations first, then the refill of the slot the
       // previous step consumed: so the wait for the activations never waits
@@ -1193,11 +1204,11 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
       }
       refill = false;
       const uint32_t my_row = my_slice + uint32_t(wave) * kWRowBytes;
-      if (u0 + tau < v_end) {
+      if (tt >= 0 && u0 + tt < v_end) {
         // loads younger than this step's: the RS - 1 steps issued after it
         // (1 + NQ each) and this step's activations; near the end, where
         // no refills follow, everything
-        if (u0 + tau + RS <= v_end) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((RS - 1) * (1 + NQ) + XTRA) : "memory");
+        if (u0 + tt + RS <= v_end) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((RS - 1) * (1 + NQ) + XTRA) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const uint32_t q = slot + 1024u + (qpos & 15u);
         uint32_t rpos = 0;
@@ -1255,9 +1266,32 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
             for (int w = 0; w < nw; ++w) sum += bits_f32(ld32(my_slice + ((w * 2 + q) * kWave + l) * 16 + e * 4));
             const int m = 4 * (l / 16) + e;  // slice row
             const int b = 16 * (r + q) + l % 16;
-            const int64_t mu = int64_t(task) * nw + m;  // the unit of slice row m
-            const int64_t row = mu * d.rows_per_unit + tau / g.tiles_per_row;
-            if (m < nw && mu < d.n_units && row < d.rows && b < nb_valid) {
+            const int64_t mu = int64_t(task) * nw + m;  // the unit (split: block) of slice row m
+            int64_t row;
+            bool store = m < nw && mu < n_items && b < nb_valid;
+            if (g.split && store) {
+              // slice row m covers, since the last row end, the second part of
+              // its first row (park it), a whole row, or the first part of its
+              // last row (add the next block's parked part), else nothing
+              const int tpr = g.tiles_per_row;
+              const int mu0 = int(mu) * d.T, dm = mu0 % tpr, nm = std::min(d.T, d.n_tiles - mu0);
+              const int last = dm + nm - 1;  // the step of its last tile
+              const uint32_t hb = heads + uint32_t(m * kMfmaMaxRows + b) * 4;
+              if (dm > 0 && tau == tpr - 1) {
+                st32(hb, f32_bits(sum));
+                store = false;
+              } else if (tau - tpr >= last) {
+                store = false;  // its last row was stored before
+              } else {
+                const int tm = std::min(tau - dm, nm - 1);
+                row = (int64_t(mu0) + tm) / tpr;
+                if (tau > last) sum += bits_f32(ld32(hb + kMfmaMaxRows * 4));
+              }
+            } else {
+              row = mu * d.rows_per_unit + tau / g.tiles_per_row;
+              store = store && row < d.rows;
+            }
+            if (store) {
               if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + row] = f32_to_bf16(sum);
               else static_cast<float*>(Y)[b * ldy + row] = sum;
             }
@@ -1441,9 +1475,21 @@ bool mfma_geometry(const DevMatrix& d, MfmaGeom* g, std::string* why) {
   }
   g->tiles_per_block = d.G / 16;
   g->tiles_per_row = d.gpr / 16;
-  const int64_t units = d.n_units;
+  // blocks that end mid-row: one block per wave when whole units fit in a
+  // workgroup of at least 8 waves with the parked row parts
+  const int nw_split = int(std::min<size_t>(16, (size_t(kLdsLimit) - tables_bytes()) / (per_wave + kMfmaMaxRows * 4)));
+  g->split = d.split && nw_split / d.unit_blocks * d.unit_blocks >= 8;
+  g->steps = 0;
+  if (g->split) {
+    int reach = 0;  // steps until the last block of a unit has its last tile
+    for (int b = 0; b < d.unit_blocks; ++b) reach = std::max(reach, b * d.T % g->tiles_per_row + d.T);
+    g->steps = (reach + g->tiles_per_row - 1) / g->tiles_per_row * g->tiles_per_row;
+  }
+  const int64_t units = g->split ? d.n_blocks : d.n_units;
+  const int step_nw = g->split ? d.unit_blocks : 1;
   double best = -1.0;
-  for (int nw = 8; nw <= nw_max; ++nw) {
+  for (int nw = 8; nw <= (g->split ? nw_split : nw_max); ++nw) {
+    if (nw % step_nw) continue;
     const int64_t tasks = (units + nw - 1) / nw;
     const int64_t rounds = (tasks + 255) / 256;
     const double eff = double(units) / double(rounds * 256 * nw);
@@ -1460,7 +1506,8 @@ template <int TB, int IPW, bool PAIR>
 int run_mfma(const uw_matrix* m, const MfmaGeom& g, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy,
              int yt, hipStream_t s) {
   const DevMatrix& d = m->dev;
-  const size_t lds = tables_bytes() + size_t(g.nw) * (2 * kWRowBytes + ring_bytes(kMfmaRS, d.slot_bytes) + 16);
+  const size_t lds = tables_bytes() + size_t(g.nw) * (2 * kWRowBytes + ring_bytes(kMfmaRS, d.slot_bytes) + 16 +
+                                                     (g.split ? kMfmaMaxRows * 4 : 0));
   auto kern = yt == UW_BF16 ? (d.nq == 2 ? fused_mfma_kernel<TB, IPW, PAIR, true, 2> : fused_mfma_kernel<TB, IPW, PAIR, true, 4>)
                             : (d.nq == 2 ? fused_mfma_kernel<TB, IPW, PAIR, false, 2> : fused_mfma_kernel<TB, IPW, PAIR, false, 4>);
   allow_full_lds(kern);

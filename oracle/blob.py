@@ -61,6 +61,7 @@ in group order; then the words taken at the tile's checks.
 """
 from __future__ import annotations
 
+import math
 import struct
 import zlib
 from dataclasses import dataclass
@@ -82,17 +83,27 @@ def _align(n: int) -> int:
 
 
 def choose_groups_per_block(rows: int, cols: int) -> int:
-    """Default G: the largest multiple of 16 (<= 256) that keeps at least 2048
-    blocks, preferring sizes that are a divisor or a multiple of the groups per
-    row; a matrix too small for 2048 blocks takes the largest such G <= 64."""
+    """Default G (a layout choice; the pages fix no block size).
+
+    Candidates are the multiples of 16 up to 256 that divide the groups per
+    row or are a multiple of it, and, when the groups per row are a multiple
+    of 16, every larger G whose work unit (lcm of G and the groups per row)
+    holds at most 8 blocks: a row then spans at most two blocks.  Among those
+    that keep at least 2048 blocks, the one whose blocks spread most evenly
+    over the 1024 SIMDs of a 256-CU part, one block per wave, counting a
+    block start as one more tile: the least ceil(blocks / 1024) * (G/16 + 1),
+    ties to the larger G.  A matrix too small for 2048 blocks takes the
+    largest divisor or multiple of the groups per row that is <= 64."""
     n = cols // 64
     total = rows * n
     cands = list(range(16, 257, 16))
     aligned = [g for g in cands if n % g == 0 or g % n == 0]
-    pool = aligned or cands
-    good = [g for g in pool if -(-total // g) >= 2048]
+    wide = aligned + [g for g in cands
+                      if n % 16 == 0 and g > n and g not in aligned and n // math.gcd(g, n) <= 8]
+    good = [g for g in (wide or cands) if -(-total // g) >= 2048]
     if good:
-        return max(good)
+        return min(good, key=lambda g: (-(-(-(-total // g)) // 1024) * (g // 16 + 1), -g))
+    pool = aligned or cands
     small = [g for g in pool if g <= 64]
     return max(small) if small else min(pool)
 

@@ -259,6 +259,13 @@ def test_rejects_bad_shapes():
 
 def test_choose_groups_per_block():
     assert blob.choose_groups_per_block(1024, 1024) == 64
-    assert blob.choose_groups_per_block(14336, 4096) == 256
+    # gate/up: 224 groups = 3.5 rows per block, 4096 blocks = 4 per SIMD of a
+    # 256-CU part (256 groups would leave 3.5 blocks per SIMD)
+    assert blob.choose_groups_per_block(14336, 4096) == 224
+    assert 14336 * 64 // 224 == 4 * 1024
+    # down: one row per block, 4096 blocks
     assert blob.choose_groups_per_block(4096, 14336) == 224
     assert blob.choose_groups_per_block(8192, 8192) == 256
+    # too small for 2048 blocks: the largest aligned G <= 64
+    assert blob.choose_groups_per_block(96, 4096) == 64
+    assert blob.choose_groups_per_block(13, 512) == 64
