@@ -9,9 +9,11 @@ product all run in that one kernel.  The weights are synthetic
 (workloads.py), shaped like Llama-3.1-8B MLP projections; the default
 workload is gate_proj 14336x4096 at batch 1.
 
-Timing: W untimed steps, then K steps replayed from a captured HIP graph
-(launch overhead out of the way), bracketed by synchronisation and by HIP
-events recorded on the stream the kernels run on.  The steps rotate over 8
+Timing: W untimed steps, then K steps, both replayed from a captured HIP
+graph (launch overhead out of the way); the timed steps are bracketed by
+synchronisation and by HIP events recorded on the stream the kernels run on.
+The default W (2000 steps, about 50 ms) lets the clocks settle at the level
+a continuous decode loop runs at.  The steps rotate over 8
 device copies of the compressed matrix so the working set (8 x 79 MB)
 exceeds the 256 MB Infinity Cache and every step reads HBM.
 
@@ -43,8 +45,8 @@ ROTATE = 8
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=400)
-    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--workload", default="gate", choices=["gate", "down", "big", "small"])
     p.add_argument("--no-extras", action="store_true", help="skip comparators, GEMM sweep and CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -80,22 +82,27 @@ def recorded_traffic(workload: str):
 
 
 def time_graph(fn_list, steps, warmup, torch):
-    """Warm up, capture one graph holding len(fn_list) launches, replay it to
-    cover `steps` launches; returns (avg launch us from events, wall seconds)."""
+    """Capture one graph holding len(fn_list) launches (after one eager pass
+    that loads the kernels), replay it untimed to cover `warmup` launches, so
+    the clocks reach the level a continuous decode loop runs at, then replay
+    it to cover `steps` launches between two events; returns (avg launch us
+    from the events, wall seconds, launches timed)."""
     stream = torch.cuda.Stream()
     n = len(fn_list)
     with torch.cuda.stream(stream):
-        for i in range(warmup):
-            fn_list[i % n]()
+        for fn in fn_list:
+            fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for fn in fn_list:
             fn()
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // n))
-    g.replay()  # one untimed replay of the captured graph
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, -(-warmup // n))):
+            g.replay()
     torch.cuda.synchronize()
+    reps = max(1, -(-steps // n))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
@@ -181,13 +188,13 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
                 ws = mats[0].workspace(B, v)
                 try:
                     us, _, _ = time_graph([(lambda m=m: uw.uw_gemm_fused(m.handle, X, Y, v, ws)) for m in mats],
-                                          steps, 4, torch)
+                                          steps, steps, torch)
                 except uw.UwError:
                     continue
                 rec[vn + "_us"] = round(us, 2)
                 del ws
             Yb = torch.empty(B, rows, dtype=torch.bfloat16, device=dev)
-            us, _, _ = time_graph([(lambda W=W: torch.matmul(X, W.t(), out=Yb)) for W in Wb], steps, 4, torch)
+            us, _, _ = time_graph([(lambda W=W: torch.matmul(X, W.t(), out=Yb)) for W in Wb], steps, steps, torch)
             rec["torch_bf16_matmul_us"] = round(us, 2)
             best = min(v for k, v in rec.items() if k.startswith(("fused", "decompress")))
             rec["blob_GBs_best"] = round(len(blob) / (best * 1e-6) / 1e9, 1)
@@ -307,7 +314,7 @@ def main():
         out_w = [torch.empty(rows, cols, dtype=torch.bfloat16, device=dev) for _ in range(2)]
         log("timing decompress")
         us_d, _, _ = time_graph([(lambda m=m, o=out_w[i % 2]: uw.uw_decompress(m.handle, o, cols))
-                                 for i, m in enumerate(mats)], 64, 8, torch)
+                                 for i, m in enumerate(mats)], 400, 400, torch)
         dbytes = info["total_bytes"] + 2 * weights
         extras["decompress"] = {"us": round(us_d, 3), "GBs_read_plus_write": round(dbytes / (us_d * 1e-6) / 1e9, 1),
                                 "frac_hbm_peak": round(dbytes / (us_d * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}

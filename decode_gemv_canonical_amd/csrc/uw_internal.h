@@ -106,6 +106,8 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
 int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, int xt, void* Y,
                  int64_t ldy, int yt, void* stream);
 bool fused_supported(const uw_matrix* m, int xt, std::string* why);
+// Batch rows the VALU fused product takes per pass (its x copy fits in LDS).
+int fused_rows_per_pass(const uw_matrix* m, int64_t batch, int xt);
 int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, void* Y, int64_t ldy, int yt,
                       void* stream);
 bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why);

@@ -1441,6 +1441,10 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
   return hip_check(hipGetLastError(), "decompress_kernel launch");
 }
 
+int fused_rows_per_pass(const uw_matrix* m, int64_t batch, int xt) {
+  return m->h.plain() ? int(std::min<int64_t>(batch, 8)) : fused_chunk(m->dev, batch, xt == UW_F32);
+}
+
 bool fused_supported(const uw_matrix* m, int xt, std::string* why) {
   if (m->h.plain()) return true;  // handled by the bf16 product
   const DevMatrix& d = m->dev;

@@ -199,15 +199,15 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
  *   d_X  device, batch rows of cols elements of xt, row stride ldx >= cols.
  *   d_Y  device, batch rows of rows elements of yt, row stride ldy >= rows.
  *   variant  a uw_variant; UW_VARIANT_AUTO uses the plan uw_autotune stored
- *            for this batch, else a heuristic (batch 1: fused on VALU;
- *            up to 64: fused on the matrix cores where supported; above:
- *            decompress + GEMM when d_ws is large enough).
+ *            for this batch, else a heuristic (batch 1, and batch 2 when
+ *            one VALU pass takes both rows: fused on VALU; up to 64: fused on
+ *            the matrix cores where supported; above: decompress + GEMM when
+ *            d_ws is large enough).
  *   d_ws/ws_bytes  caller-owned device workspace (uw_workspace_size bytes for
  *            the chosen variant; may be NULL/0 for the fused variants).
  *   UW_VARIANT_FUSED_MFMA needs bf16 X that is 16-byte aligned with ldx a
- *   multiple of 8, cols a multiple of 1024, G dividing or a multiple of
- *   cols/64 and a multiple of 16 (else UW_ERR_UNSUPPORTED); it runs 64 batch
- *   rows per pass.
+ *   multiple of 8, cols a multiple of 1024 and G a multiple of 16 (else
+ *   UW_ERR_UNSUPPORTED); it runs 64 batch rows per pass.
  * batch == 0 is a no-op.  fp32 accumulation.
  * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE (workspace), UW_ERR_UNSUPPORTED, UW_ERR_HIP.
  */
