@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATE = 8
+PARITY_TOL = 1e-3  # max |y - y64| / max(|y64|, rms(y64)) for fp32 outputs
 
 
 def parse():
@@ -52,6 +53,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--skip-gemm", action="store_true", help="skip the batched-product sweep")
     p.add_argument("--gemm-only", action="store_true", help="run only the batched-product sweep (prints its JSON)")
+    p.add_argument("--stack", action="store_true",
+                   help="run only the 32-layer MLP stack at batch 1 and 32 (prints its JSON; ~2 min of encoding)")
     return p.parse_args()
 
 
@@ -207,6 +210,97 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
     return out
 
 
+def stack_run(uw, workloads, torch, dev, steps, warmup):
+    """The 32-layer MLP stack (Llama-3.1-8B MLP shapes, per-layer sigma): per
+    token and layer h = silu(W_gate x) * (W_up x), x' = rmsnorm(W_down h), with
+    no learned scale and no residual.  At batch 1 and 32 it times the 96 matrix
+    calls of one token (the AUTO variant, replayed from a graph), the
+    elementwise ops alone, and the same 96 products on the uncompressed bf16
+    weights; every product of one token is checked on sampled rows against the
+    fp64 product of the original weights."""
+    import numpy as np
+
+    from oracle import products
+    H, F = workloads.SHAPES["gate"][1], workloads.SHAPES["gate"][0]
+    layers, bfw, blob_bytes = [], [], 0
+    t0 = time.perf_counter()
+    for li in range(workloads.STACK_LAYERS):
+        L = workloads.stack_layer(li)
+        mats = {}
+        for k, v in L.items():
+            b = uw.uw_encode(v)
+            blob_bytes += len(b)
+            mats[k] = uw.CompressedMatrix(b, device="cuda:0")
+        layers.append(mats)
+        bfw.append({k: v.to(dev).view(torch.bfloat16) for k, v in L.items()})
+        log(f"stack layer {li} encoded and uploaded ({time.perf_counter() - t0:.0f} s)")
+    out = {"layers": workloads.STACK_LAYERS, "matrices": 3 * workloads.STACK_LAYERS, "blob_bytes": blob_bytes,
+           "bf16_bytes": 3 * workloads.STACK_LAYERS * 2 * H * F, "prep_s": round(time.perf_counter() - t0, 1)}
+    rng = np.random.default_rng(7)
+    for B in (1, 32):
+        n = workloads.STACK_LAYERS
+        xs = [torch.empty(B, H, dtype=torch.bfloat16, device=dev) for _ in range(n + 1)]
+        xs[0].copy_(workloads.activations(H, B, seed=workloads.STACK_LAYER_SEED0 + 100 + B, dtype=torch.bfloat16))
+        g = [torch.empty(B, F, dtype=torch.float32, device=dev) for _ in range(n)]
+        u = [torch.empty(B, F, dtype=torch.float32, device=dev) for _ in range(n)]
+        h = [torch.empty(B, F, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+        d = [torch.empty(B, H, dtype=torch.float32, device=dev) for _ in range(n)]
+        ws = torch.empty(max(layers[0][k].workspace(B).numel() for k in ("gate", "up", "down")), dtype=torch.uint8,
+                         device=dev)
+
+        def matrix_calls(li):
+            m = layers[li]
+            uw.uw_gemm_fused(m["gate"].handle, xs[li], g[li], uw.UW_VARIANT_AUTO, ws)
+            uw.uw_gemm_fused(m["up"].handle, xs[li], u[li], uw.UW_VARIANT_AUTO, ws)
+            uw.uw_gemm_fused(m["down"].handle, h[li], d[li], uw.UW_VARIANT_AUTO, ws)
+
+        def elementwise(li):
+            h[li].copy_(torch.nn.functional.silu(g[li]) * u[li])
+            v = d[li]
+            xs[li + 1].copy_(v * torch.rsqrt(v.pow(2).mean(dim=1, keepdim=True) + 1e-6))
+
+        # one eager token fills every buffer; its products are the parity sample
+        for li in range(n):
+            uw.uw_gemm_fused(layers[li]["gate"].handle, xs[li], g[li], uw.UW_VARIANT_AUTO, ws)
+            uw.uw_gemm_fused(layers[li]["up"].handle, xs[li], u[li], uw.UW_VARIANT_AUTO, ws)
+            h[li].copy_(torch.nn.functional.silu(g[li]) * u[li])
+            uw.uw_gemm_fused(layers[li]["down"].handle, h[li], d[li], uw.UW_VARIANT_AUTO, ws)
+            v = d[li]
+            xs[li + 1].copy_(v * torch.rsqrt(v.pow(2).mean(dim=1, keepdim=True) + 1e-6))
+        torch.cuda.synchronize()
+        worst = 0.0
+        for li in range(n):
+            for k, inp, res, r in (("gate", xs[li], g[li], F), ("up", xs[li], u[li], F), ("down", h[li], d[li], H)):
+                rows = rng.choice(r, size=64, replace=False)
+                wb = bfw[li][k][torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+                ref = products.gemm_f64(wb, inp.float().cpu().numpy())
+                got = res[:, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+                worst = max(worst, products.rel_error_floored(got, ref))
+        reps = max(1, steps // 96)
+        us_m, _, _ = time_graph([lambda: [matrix_calls(li) for li in range(n)]], reps, reps, torch)
+        us_e, _, _ = time_graph([lambda: [elementwise(li) for li in range(n)]], reps, reps, torch)
+        gb = [torch.empty(B, F, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        db = torch.empty(B, H, dtype=torch.bfloat16, device=dev)
+
+        def bf16_calls():
+            for li in range(n):
+                torch.matmul(xs[li], bfw[li]["gate"].t(), out=gb[0])
+                torch.matmul(xs[li], bfw[li]["up"].t(), out=gb[1])
+                torch.matmul(h[li], bfw[li]["down"].t(), out=db)
+
+        us_b, _, _ = time_graph([bf16_calls], reps, reps, torch)
+        out[f"b{B}"] = {"matrix_ms_per_token": round(us_m / 1e3, 4), "elementwise_ms_per_token": round(us_e / 1e3, 4),
+                        "bf16_matmul_ms_per_token": round(us_b / 1e3, 4),
+                        "speedup_vs_bf16": round(us_b / us_m, 4),
+                        "effective_weight_GBs": round(out["bf16_bytes"] / (us_m * 1e-6) / 1e9, 1),
+                        "compressed_GBs": round(blob_bytes / (us_m * 1e-6) / 1e9, 1),
+                        "parity_max_rel_err_sampled": worst, "parity_ok": worst <= PARITY_TOL}
+        log(f"stack B={B}: {out[f'b{B}']}")
+        del xs, g, u, h, d, ws, gb, db
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -222,6 +316,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.gemm_only:
         print(json.dumps({"gemm": gemm_sweep(uw, workloads, torch, dev, 48)}), flush=True)
+        return
+    if args.stack:
+        print(json.dumps({"stack": stack_run(uw, workloads, torch, dev, 960, 960)}), flush=True)
         return
     name = args.workload
     rows, cols = workloads.SHAPES[name]
@@ -276,7 +373,7 @@ def main():
                         "raw_group_frac": round(info["n_raw_groups"] / (weights // 64), 6),
                         "blob_bytes": info["total_bytes"], "bf16_bytes": 2 * weights,
                         "K": info["K"], "L": info["L"], "G": info["G"], "encode_s": round(t_encode, 3)},
-        "parity": {"max_rel_err_vs_fp64": err, "tolerance": 1e-3, "ok": bool(err <= 1e-3)},
+        "parity": {"max_rel_err_vs_fp64": err, "tolerance": PARITY_TOL, "ok": bool(err <= PARITY_TOL)},
     }
 
     if not args.no_extras:
