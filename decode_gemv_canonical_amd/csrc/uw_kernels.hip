@@ -965,11 +965,14 @@ struct ProductSink {
   }
 };
 
-// Wide batch chunks need more registers per lane: at most 8 waves per workgroup.
-constexpr int fused_max_threads(int nbp) { return nbp >= 4 ? 512 : 1024; }
+// Up to 16 waves per workgroup (4 per SIMD, so every unit of a 4096-unit
+// matrix starts in the first round); 8 batch rows of fp32 x, or on the block
+// walk, need more registers per lane than 4 waves per SIMD leave: at most 8
+// waves there.
+constexpr int fused_max_threads(int nbp, bool xf32, bool flat) { return nbp >= 8 && (xf32 || !flat) ? 512 : 1024; }
 
 template <int NBP, bool XF32, bool PAIR, bool YBF16, int NQ, bool FLAT, int RS>
-__global__ __launch_bounds__(fused_max_threads(NBP)) void fused_product_kernel(DevMatrix d, const void* __restrict__ X,
+__global__ __launch_bounds__(fused_max_threads(NBP, XF32, FLAT)) void fused_product_kernel(DevMatrix d, const void* __restrict__ X,
                                                                                int64_t ldx, int nb_valid,
                                                                                void* __restrict__ Y, int64_t ldy) {
   extern __shared__ uint32_t lds[];
@@ -1355,7 +1358,7 @@ template <int NBP, bool XF32, bool PAIR, bool YBF16>
 int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, void* stream) {
   DevMatrix d = m->dev;  // a copy: split rows may be turned off for this launch
   const size_t fixed = tables_bytes() + x_bytes(d, NBP, XF32);
-  const int max_waves = fused_max_threads(NBP) / kWave;
+  const int max_waves = fused_max_threads(NBP, XF32, d.flat) / kWave;
   // split rows: NBP partial sums per wave in LDS, and whole units per
   // workgroup; where a unit's waves do not fit, one wave per unit
   if (d.split && (d.unit_blocks > max_waves ||
