@@ -710,8 +710,10 @@ constexpr int kRSLow = 2;
 __host__ __device__ inline uint32_t ring_bytes(int rs, int slot_bytes) { return uint32_t(rs) * (1024u + uint32_t(slot_bytes)); }
 
 // ---------------------------------------------------------------------------
-// Decompress: weights pass through a per-wave LDS tile [16][64] bf16 so that
-// each lane stores 2 x 16 bytes of consecutive columns.
+// Decompress.  On the flat walk each pair of weights goes straight to its
+// row; on the block walk (tiles may cross rows) weights pass through a
+// per-wave LDS tile [16][64] bf16 so that each lane stores 2 x 16 bytes of
+// consecutive columns.
 template <bool FLAT>
 struct DecompressSink {
   int64_t cols, G;
@@ -721,6 +723,7 @@ struct DecompressSink {
   int lane;
   int64_t trow;   // (row, col) of the current tile's first weight
   int64_t tcol;
+  uint16_t* dst;  // flat walk: this lane's column of the tile's first group
   __device__ void unit_begin(int) {}
   __device__ void unit_end() {}
   __device__ void block_begin(int blk) {
@@ -734,13 +737,22 @@ struct DecompressSink {
     if (!FLAT) return;
     trow = row0;
     tcol = int64_t(c0) * 64;
+    dst = out + row0 * ld_out + tcol + lane;
   }
+  // flat walk: weight (group 2k or 2k+1, lane) straight to its row; each
+  // store instruction writes 128 contiguous bytes across the wave
   __device__ void pair(int k, uint32_t D) {
+    if (FLAT) {
+      dst[(2 * k) * kWave] = uint16_t(D);
+      dst[(2 * k + 1) * kWave] = uint16_t(D >> 16);
+      return;
+    }
     st16(tile + ((2 * k) * kWave + lane) * 2, D);
     st16(tile + ((2 * k + 1) * kWave + lane) * 2, D >> 16);
   }
   __device__ void single(int jj, int64_t, int, uint32_t w) { st16(tile + (jj * kWave + lane) * 2, w); }
   __device__ void tile_end(int, int nt) {
+    if (FLAT) return;
     wave_lds_fence();
     if (lane * 16 < nt * 64) {
       const uint4 a = ld128(tile + lane * 32), b = ld128(tile + lane * 32 + 16);
@@ -768,7 +780,7 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   extern __shared__ uint32_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int waves = blockDim.x / kWave;
-  const uint32_t per_wave = ring_bytes(RS, d.slot_bytes) + kTransposeWords * 4;
+  const uint32_t per_wave = ring_bytes(RS, d.slot_bytes) + (FLAT ? 0u : kTransposeWords * 4);
   const uint32_t sm_ring = kAreaAddr + uint32_t(wave) * per_wave;
   const uint32_t q_ring = sm_ring + RS * 1024;
   const uint32_t tile = sm_ring + ring_bytes(RS, d.slot_bytes);
@@ -1426,8 +1438,8 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
   if (m->h.plain()) return launch_copy_plain(d.plain, d.rows, d.cols, out, ld_out, stream);
   const size_t fixed = tables_bytes();
   const int items = d.flat ? d.n_items : d.n_units;
-  const int rs = d.flat ? flat_ring_depth(items, fixed, d.slot_bytes, kTransposeWords * 4, 16) : kRS;
-  const size_t per_wave = ring_bytes(rs, d.slot_bytes) + kTransposeWords * 4;
+  const int rs = d.flat ? flat_ring_depth(items, fixed, d.slot_bytes, 0, 16) : kRS;
+  const size_t per_wave = ring_bytes(rs, d.slot_bytes) + (d.flat ? 0 : kTransposeWords * 4);
   const int waves = pick_waves(items, fixed, per_wave);
   const size_t lds = fixed + per_wave * waves;
   const int grid = int(std::max<int64_t>(1, (int64_t(items) + waves - 1) / waves));
