@@ -138,32 +138,39 @@ def cpu_baseline(workload: str, target_s: float):
 
     import decode_gemv_canonical_amd as uw
 
-    def run(rows):
+    def run(rows, reps=1):
         w = workloads.weights(workload, rows=rows).numpy().view(np.uint16)
         b = uw.uw_encode(w)  # byte-identical to the oracle's encoder (CPU tests); only the decode is timed
         t0 = time.perf_counter()
-        dec = oblob.decode(b)
-        y = products.gemm_f32(dec, x)
+        for _ in range(reps):
+            dec = oblob.decode(b)
+            y = products.gemm_f32(dec, x)
         dt = time.perf_counter() - t0
         assert np.array_equal(dec, w) and y.shape == (rows,)
-        return dt
+        return dt / reps, dt
 
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     if ctx:
         ctx.__enter__()
     try:
-        dt = run(rows)
+        dt, total = run(rows)
         while dt < target_s / 4 and rows < r_full:
             rows = min(r_full, int(rows * min(8.0, max(2.0, target_s / max(dt, 1e-3)))))
-            dt = run(rows)
+            dt, total = run(rows)
+        reps = 1
+        if rows == r_full and dt < target_s / 2:
+            # the whole matrix is less work than the target: repeat it
+            reps = max(1, int(target_s / dt))
+            dt, total = run(rows, reps)
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
     gbs = 2.0 * rows * c / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} of {r_full} rows of the {workload} matrix: numpy lane-lockstep decode of the "
-                      f"blob + fp32 matvec, {dt:.2f} s on 1 thread (os.cpu_count()={os.cpu_count()})",
-            "seconds": round(dt, 3)}
+            "sample": f"{rows} of {r_full} rows of the {workload} matrix, {reps} pass(es): numpy lane-lockstep "
+                      f"decode of the blob + fp32 matvec, {dt:.2f} s per pass, {total:.1f} s in all, on 1 thread "
+                      f"(os.cpu_count()={os.cpu_count()})",
+            "seconds": round(total, 3)}
 
 
 def gemm_sweep(uw, workloads, torch, dev, steps):
