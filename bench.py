@@ -405,6 +405,20 @@ def main():
         }
         del Wb
         torch.cuda.empty_cache()
+        # code-length limit: L = 6 decodes two codes per lookup (4096-entry
+        # pair table); L = 8 and 12 decode one code per lookup (2^L entries)
+        ablation = {}
+        for L in (8, 12):
+            bl = uw.uw_encode(w, L=L)
+            ml = [uw.CompressedMatrix(bl, device="cuda:0") for _ in range(ROTATE)]
+            us_l, _, _ = time_graph([(lambda m=m: uw.uw_gemv_fused(m.handle, x, y)) for m in ml], args.steps,
+                                    args.warmup, torch)
+            ablation[f"L{L}"] = {"us": round(us_l, 3), "bits_per_weight": round(uw.uw_blob_info(bl)["bits_per_weight"], 4)}
+            for m in ml:
+                m.close()
+        ablation["L6"] = {"us": round(us, 3), "bits_per_weight": round(info["bits_per_weight"], 4)}
+        extras["lut_ablation"] = ablation
+        log(f"L ablation: {ablation}")
         # streaming-read probe over 1 GiB
         log("read probe")
         buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)

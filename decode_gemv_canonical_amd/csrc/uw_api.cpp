@@ -298,14 +298,14 @@ int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ld
       }
     }
     // Without a plan: one or two rows on VALU (when one pass takes them);
-    // up to 64 rows (one pass) on the matrix cores; beyond that decompress +
-    // library GEMM when the workspace is given (the measured crossovers on
-    // the MLP shapes).
+    // up to 32 rows on the matrix cores; beyond that decompress + library
+    // GEMM when the workspace is given (the measured crossovers on the MLP
+    // shapes: at 64 rows decompress + GEMM is ahead on down_proj).
     const bool ws_ok = d_ws && ws_bytes >= decompress_ws_bytes(m);
     if (have) variant = p.variant;
     else if (fused_ok && (batch == 1 || (batch == 2 && fused_rows_per_pass(m, batch, xt) >= 2)))
       variant = UW_VARIANT_FUSED;
-    else if (batch <= 64 && mfma_ok) variant = UW_VARIANT_FUSED_MFMA;
+    else if (mfma_ok && (batch <= 32 || (batch <= 64 && !ws_ok))) variant = UW_VARIANT_FUSED_MFMA;
     else if (ws_ok && (xt == UW_BF16 || !fused_ok)) variant = UW_VARIANT_DECOMPRESS_GEMM;
     else if (mfma_ok) variant = UW_VARIANT_FUSED_MFMA;
     else variant = fused_ok || !ws_ok ? UW_VARIANT_FUSED : UW_VARIANT_DECOMPRESS_GEMM;

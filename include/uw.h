@@ -200,9 +200,9 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
  *   d_Y  device, batch rows of rows elements of yt, row stride ldy >= rows.
  *   variant  a uw_variant; UW_VARIANT_AUTO uses the plan uw_autotune stored
  *            for this batch, else a heuristic (batch 1, and batch 2 when
- *            one VALU pass takes both rows: fused on VALU; up to 64: fused on
+ *            one VALU pass takes both rows: fused on VALU; up to 32: fused on
  *            the matrix cores where supported; above: decompress + GEMM when
- *            d_ws is large enough).
+ *            d_ws is large enough, else the matrix cores).
  *   d_ws/ws_bytes  caller-owned device workspace (uw_workspace_size bytes for
  *            the chosen variant; may be NULL/0 for the fused variants).
  *   UW_VARIANT_FUSED_MFMA needs bf16 X that is 16-byte aligned with ldx a
