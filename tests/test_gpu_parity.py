@@ -302,6 +302,32 @@ def test_gemm_fp32_input_strided():
     assert (Y[:, 5:] == 0).all()
 
 
+@pytest.mark.parametrize("batch", [3, 8])
+def test_gemm_fused_valu_fp32_split_rows(batch):
+    # fp32 activations (8 rows: the 8-wave workgroup) on blocks that end mid-row
+    wb, m = matrix("gate", 67, 4096, 16, G=224)
+    X = workloads.activations(4096, batch, seed=320 + batch, dtype=torch.float32)
+    ref = products.gemm_f64(wb, X.numpy())
+    _say(f"gemm fused fp32 split batch={batch}")
+    Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_FUSED)
+    torch.cuda.synchronize()
+    check_f32(Y, ref, f"gemm fused fp32 split b={batch}")
+
+
+@pytest.mark.parametrize("batch", [2, 3, 40, 64])
+def test_gemm_auto_without_plan(batch):
+    # every heuristic branch of AUTO (VALU, matrix cores, decompress + GEMM with
+    # a workspace, matrix cores without one) against the fp64 product
+    wb, m = matrix("gate", 70, 4096, 15, G=224)
+    X = workloads.activations(4096, batch, seed=330 + batch, dtype=torch.bfloat16)
+    ref = products.gemm_f64(wb, X.float().numpy())
+    for ws in (m.workspace(batch), None):
+        _say(f"gemm auto batch={batch} ws={ws is not None}")
+        Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_AUTO, ws=ws)
+        torch.cuda.synchronize()
+        check_f32(Y, ref, f"gemm auto b={batch}")
+
+
 def test_gemm_batch_zero_is_noop():
     wb, m = matrix("small", None, None, None)
     X = torch.zeros(0, 1024, dtype=torch.bfloat16, device=DEV)
