@@ -103,6 +103,47 @@ int uw_blob_info(const void* blob, size_t n, uw_info* info) {
 }
 
 namespace {
+// Decode tables, as the kernels hold them in LDS.  single(i): for the next
+// L stream bits i (first bit in bit 0), len | exponent << 7 of the canonical
+// code that prefixes i.  L <= 6: words [0, 4096) are the pair table, entry
+// i = (len_a + len_b) | E_a << 7 | len_a << 16 | E_b << 23 for the two codes
+// that prefix the 12 bits i, and words [4096, 4160) hold single(i) for
+// i < 2^L.  L > 6: words [0, 2^L) hold single(i).
+int upload_decode_tables(uw_matrix* m) {
+  const BlobHeader& h = m->h;
+  DevMatrix& d = m->dev;
+  uint32_t code[32], rev[32];
+  canonical_codes(h, code, rev);
+  auto single = [&](uint32_t idx) -> uint32_t {
+    for (uint32_t s = 0; s < h.K; ++s) {
+      const uint32_t len = h.code_len[s];
+      if (len && (idx & ((1u << len) - 1u)) == rev[s]) return len | (uint32_t(h.palette[s]) << 7);
+    }
+    return 1u | (uint32_t(h.palette[0]) << 7);  // gaps exist only for a one-symbol code; never met in a valid stream
+  };
+  std::vector<uint32_t> t(kDecodeTableWords, 0u);
+  if (h.L <= 6) {
+    const uint32_t mask = (1u << h.L) - 1u;
+    for (uint32_t i = 0; i <= mask; ++i) t[4096 + i] = single(i);
+    for (uint32_t i = 0; i < 4096; ++i) {
+      const uint32_t a = t[4096 + (i & mask)], la = a & 0xF;
+      const uint32_t b = t[4096 + ((i >> la) & mask)], lb = b & 0xF;
+      t[i] = (la + lb) | (a & 0x7F80u) | (la << 16) | ((b & 0x7F80u) << 16);
+    }
+  } else {
+    for (uint32_t i = 0; i < (1u << h.L); ++i) t[i] = single(i);
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, kDecodeTableBytes) != hipSuccess) return fail(UW_ERR_HIP, "uw_matrix_create: cannot allocate the decode tables");
+  if (hipMemcpy(p, t.data(), kDecodeTableBytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(p);
+    return fail(UW_ERR_HIP, "uw_matrix_create: cannot copy the decode tables");
+  }
+  m->d_tables = p;
+  d.tables = static_cast<const uint32_t*>(p);
+  return UW_OK;
+}
+
 // Flat walk (G and the groups per row multiples of 16, so no tile crosses a
 // row): one descriptor per tile for the loads of its step, two words: the
 // 16-byte aligned floor of the tile's segment (byte offset in the queue) and,
@@ -198,12 +239,11 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
     d.T = int32_t((h.G + 15) / 16);
     d.R = int32_t(h.R);
     d.L = int32_t(h.L);
-    // the decode tables are built on chip from the canonical codes
-    uint32_t code[32], rev[32];
-    canonical_codes(h, code, rev);
-    d.n_sym = int32_t(h.K);
-    for (uint32_t i = 0; i < h.K; ++i)
-      d.sym[i] = rev[i] | (uint32_t(h.code_len[i]) << 16) | (uint32_t(h.palette[i]) << 24);
+    // the decode tables: built here, loaded into LDS by the kernels
+    if (int rc2 = upload_decode_tables(m)) {
+      uw_matrix_destroy(m);
+      return rc2;
+    }
     // an LDS slot holds any segment; it is filled by 1 KB direct loads
     // (a segment is loaded from its 16-byte aligned floor, up to 12 bytes
     // before it, and lanes that take no word read the word after its end)
@@ -235,11 +275,12 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
 
 void uw_matrix_destroy(uw_matrix* m) {
   if (!m) return;
-  if (m->d_steps) {
+  if (m->d_steps || m->d_tables) {
     int cur = -1;
     (void)hipGetDevice(&cur);
     if (cur != m->device) (void)hipSetDevice(m->device);
-    (void)hipFree(m->d_steps);
+    if (m->d_steps) (void)hipFree(m->d_steps);
+    if (m->d_tables) (void)hipFree(m->d_tables);
     if (cur != m->device && cur >= 0) (void)hipSetDevice(cur);
   }
   delete m;

@@ -68,7 +68,7 @@ struct DevMatrix {
   int32_t G, n_blocks, rb_words, gpr;  // gpr = groups per row = cols/64
   int32_t T;                           // tiles (segment entries) per block = ceil(G/16)
   int32_t R;                           // groups between refill checks
-  int32_t L, n_sym;
+  int32_t L;
   int32_t slot_bytes;                  // LDS bytes of one segment slot (>= the largest segment, multiple of 16)
   int32_t seg_loads;                   // 1 KB direct loads that fill a slot
   int32_t nq;                          // 1 KB queue loads issued per tile step (2 or 4)
@@ -84,8 +84,14 @@ struct DevMatrix {
                                        //  decompress give each wave one block, and a row that crosses a block
                                        //  end is summed from the two waves' parts
   int32_t n_items;                     // waves of work of those kernels: n_blocks when split, else n_units
-  uint32_t sym[32];                    // rev code | len << 16 | exponent << 24
+  const uint32_t* tables;              // decode tables, built on the host (kDecodeTableBytes, the LDS image:
+                                       //  pair table or 2^L single table, then the L <= 6 single table)
 };
+
+// Bytes of the decode-table image: 4096 words (pair table, or the 2^L
+// single table for L > 6), then 64 words (the single table for L <= 6).
+constexpr uint32_t kDecodeTableWords = 4096 + 64;
+constexpr uint32_t kDecodeTableBytes = kDecodeTableWords * 4;
 
 }  // namespace uw
 
@@ -94,6 +100,7 @@ struct uw_matrix {
   uw::DevMatrix dev;
   const uint8_t* d_blob = nullptr;
   void* d_steps = nullptr;  // device copy of the flat-walk step table (owned)
+  void* d_tables = nullptr;  // device copy of the decode tables (owned)
   int device = 0;
   mutable std::mutex mu;
   std::map<int64_t, uw_plan> plans;

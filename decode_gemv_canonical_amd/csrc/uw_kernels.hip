@@ -44,40 +44,39 @@ namespace uw {
 namespace {
 
 constexpr int kTableWords = 4096;     // pair table (or 2^L single table)
-constexpr int kT1Words = 64;          // single-code table for L <= 6, used to build the pair table
+constexpr int kT1Words = 64;          // single-code table for L <= 6 (the host builds the pair table from it)
 constexpr int kTransposeWords = 512;  // 16 groups x 64 lanes x bf16
 
 // ---------------------------------------------------------------------------
-// Decode tables in LDS.  T1[i] for an L-bit index i (next stream bits, first
-// bit in bit 0) = len | E << 7 of the code that prefixes i.  For L <= 6 the
-// pair table T2 is built from T1; for L > 6 T1 (2^L entries) is the table.
-__device__ inline uint32_t single_entry(const DevMatrix& d, uint32_t idx) {
-  uint32_t fallback = 1u | (uint32_t(d.sym[0] >> 24) << 7);
-  for (int s = 0; s < d.n_sym; ++s) {
-    const uint32_t sym = d.sym[s];
-    const uint32_t len = (sym >> 16) & 0xFF;
-    if (len && (idx & ((1u << len) - 1u)) == (sym & 0xFFFF)) return len | ((sym >> 24) << 7);
-  }
-  return fallback;  // only an incomplete (one-symbol) code leaves gaps; never met in a valid stream
+// Decode tables in LDS: the image the host built at matrix creation
+// (kDecodeTableBytes: the pair table, or the 2^L single table for L > 6, then
+// the single table for L <= 6), copied in with direct loads of 1 KB spread
+// over the waves; the last load moves 256 B (16 lanes).  Returns the loads
+// this wave issued.  Runs with all lanes active.
+constexpr int kTableLoads = int((kDecodeTableBytes + 1023) / 1024);
+// Buffer resource over [base, base + bytes) for raw byte-offset loads.
+__device__ inline __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), int16_t(0), int(bytes), 0x00020000);
 }
-
-template <bool PAIR>
-__device__ void build_tables(const DevMatrix& d, uint32_t* T, uint32_t* T1) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  if (PAIR) {
-    for (int i = tid; i < (1 << d.L); i += nt) T1[i] = single_entry(d, uint32_t(i));
-    __syncthreads();
-    const uint32_t m = (1u << d.L) - 1u;
-    for (int i = tid; i < kTableWords; i += nt) {
-      const uint32_t a = T1[uint32_t(i) & m];
-      const uint32_t la = a & 0xF;
-      const uint32_t b = T1[(uint32_t(i) >> la) & m];
-      const uint32_t lb = b & 0xF;
-      T[i] = (la + lb) | (a & 0x7F80u) | (la << 16) | ((b & 0x7F80u) << 16);
-    }
-  } else {
-    for (int i = tid; i < (1 << d.L); i += nt) T[i] = single_entry(d, uint32_t(i));
+__device__ __forceinline__ int issue_tables(const DevMatrix& d, int wave, int waves, int lane) {
+  const __amdgpu_buffer_rsrc_t r = byte_rsrc(d.tables, kDecodeTableBytes);
+  const uint32_t lane16 = 16u * uint32_t(lane);
+  int n = 0;
+  for (int i = wave; i < kTableLoads; i += waves, ++n) {
+    const uint32_t off = uint32_t(i) * 1024u;
+    const uint32_t lanes = std::min(64u, (kDecodeTableBytes - off) / 16u);
+    const uint64_t mask = lanes == 64 ? ~0ull : ((1ull << lanes) - 1ull);
+    asm volatile(
+        "s_nop 4\n"
+        "s_mov_b32 m0, %[m]\n"
+        "s_mov_b64 exec, %[ex]\n"  // also the wait state after the M0 write
+        "buffer_load_dwordx4 %[l16], %[r], %[so] offen lds\n"
+        "s_mov_b64 exec, -1"
+        :
+        : [m] "s"(off), [ex] "s"(mask), [l16] "v"(lane16), [r] "s"(r), [so] "s"(off)
+        : "memory", "m0", "exec");
   }
+  return n;
 }
 
 // LDS layout (bytes): [0, 16384) decode table, [16384, 16640) single table for
@@ -363,6 +362,15 @@ __device__ inline void wait_oldest_step() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"((RS - 1) * (1 + NQ + XTRA)) : "memory");
 }
 
+// The table loads were issued before `issued` ring steps (1 + NQ loads
+// each): wait until only those may be outstanding.
+template <int RS, int NQ>
+__device__ inline void wait_tables(int issued) {
+  static_assert(RS * (1 + NQ) < 64, "vmcnt field");
+  if (issued == RS) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RS * (1 + NQ)) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Issue side of the ring over the tiles of blocks [b, b_end): steps run RS
 // ahead of the consumer; past the end the last step is loaded again so the
 // count of loads stays fixed.  The end of the next tile's segment is read one
@@ -461,10 +469,6 @@ __device__ __forceinline__ void run_blocks(const DevMatrix& d, int b0, int b1, u
 // serves all loads of a step, the queue loads reaching their part through
 // the immediate offset 1024 (i + 1), which applies to both addresses.  The
 // step table gives each tile's segment floor and the lanes of each load.
-// Buffer resource over [base, base + bytes) for raw byte-offset loads.
-__device__ inline __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), int16_t(0), int(bytes), 0x00020000);
-}
 
 // The 1 + NQ loads of tile step v into a slot, from one M0 (the slot): the
 // sign+mantissa tile v at offset 0 (all lanes), then the queue segment from
@@ -787,12 +791,16 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   const int u_first = blockIdx.x * waves + wave;
   const int n_items = FLAT ? d.n_items : d.n_units;
   int fv = 0;
-  // the first unit's loads go out before the tables are built
+  // the decode tables, then the first unit's loads; the tables have landed
+  // once only the ring's loads may be younger
+  const int n_tab = issue_tables(d, wave, waves, lane);
+  int issued = 0;
   if (FLAT && u_first < n_items) {
     const WalkItem it = walk_item(d, u_first);
     fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
+    issued = fv - it.b0 * d.T;
   }
-  build_tables<PAIR>(d, lds, lds + kTableWords);
+  if (n_tab) wait_tables<RS, NQ>(issued);
   lds_barrier();
   DecompressSink<FLAT> sink{d.cols, d.G, out, ld_out, tile, lane, 0, 0};
   for (int u = u_first; u < n_items; u += gridDim.x * waves) {
@@ -996,12 +1004,16 @@ __global__ __launch_bounds__(fused_max_threads(NBP, XF32, FLAT)) void fused_prod
   const int u_first = blockIdx.x * waves + wave;
   const int n_items = FLAT ? d.n_items : d.n_units;
   int fv = 0;
-  // the first unit's loads go out before the tables and x are set up
+  // the decode tables, then the first unit's loads, then x; the tables have
+  // landed once only the ring's loads may be younger
+  const int n_tab = issue_tables(d, wave, waves, lane);
+  int issued = 0;
   if (FLAT && u_first < n_items) {
     const WalkItem it = walk_item(d, u_first);
     fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
+    issued = fv - it.b0 * d.T;
   }
-  build_tables<PAIR>(d, lds, lds + kTableWords);
+  if (n_tab) wait_tables<RS, NQ>(issued);
   load_x<NBP, XF32>(d, X, ldx, nb_valid, lds + kTableWords + kT1Words);
   lds_barrier();
   ProductSink<NBP, XF32, YBF16, FLAT> sink{d, kAreaAddr, lane, nb_valid, Y, ldy};  // the rest set per unit
@@ -1128,7 +1140,8 @@ __global__ __launch_bounds__(mfma_max_threads(IPW)) void fused_mfma_kernel(DevMa
   const int tpt = g.tiles_per_block * (g.split ? 1 : d.unit_blocks);  // tiles per wave and task
   const int n_steps = g.split ? g.steps : tpt;
   const int n_items = g.split ? d.n_blocks : d.n_units;
-  build_tables<PAIR>(d, lds, lds + kTableWords);
+  issue_tables(d, wave, nw, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
 
   // A operand row of this lane.  Rows >= nw and batch rows >= nb_valid read
