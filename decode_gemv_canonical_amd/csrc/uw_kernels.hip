@@ -853,6 +853,45 @@ __device__ inline void load_x(const DevMatrix& d, const void* X, int64_t ldx, in
   }
 }
 
+// One row of bf16 x, issued before the ring's first steps so that its loads
+// are not queued behind them: each thread loads the two halves of up to
+// kXIters words of the x_word layout into registers (asm loads, which the
+// compiler does not wait for), and x_store writes them once a wait has
+// covered them.  Covers cols up to 2 * 64 * kXIters * threads / 64.
+constexpr int kXIters = 8;
+struct XEarly {
+  uint32_t lo[kXIters], hi[kXIters];
+};
+__device__ inline bool x_early_fits(const DevMatrix& d, int threads) {
+  return ((uint32_t(d.gpr) + 15) / 16 * 8) * 64u <= uint32_t(kXIters) * uint32_t(threads);
+}
+__device__ __forceinline__ void x_issue(const DevMatrix& d, const uint16_t* x, XEarly& xe) {
+  const uint32_t C = uint32_t(d.cols), words = ((uint32_t(d.gpr) + 15) / 16 * 8) * 64u;
+#pragma unroll
+  for (int j = 0; j < kXIters; ++j) {
+    const uint32_t i = threadIdx.x + uint32_t(j) * blockDim.x;
+    xe.lo[j] = xe.hi[j] = 0u;
+    if (i < words) {
+      const uint32_t k0 = 128u * (i / 64u) + i % 64u, k1 = k0 + 64u;
+      asm volatile("global_load_ushort %0, %1, off" : "=v"(xe.lo[j]) : "v"(x + (k0 < C ? k0 : 0u)) : "memory");
+      asm volatile("global_load_ushort %0, %1, off" : "=v"(xe.hi[j]) : "v"(x + (k1 < C ? k1 : 0u)) : "memory");
+    }
+  }
+}
+// After a wait that covers x_issue's loads.
+__device__ __forceinline__ void x_store(const DevMatrix& d, XEarly& xe, uint32_t* xl) {
+  const uint32_t C = uint32_t(d.cols), words = ((uint32_t(d.gpr) + 15) / 16 * 8) * 64u;
+#pragma unroll
+  for (int j = 0; j < kXIters; ++j) {
+    asm volatile("" : "+v"(xe.lo[j]), "+v"(xe.hi[j]));
+    const uint32_t i = threadIdx.x + uint32_t(j) * blockDim.x;
+    if (i < words) {
+      const uint32_t p = i / 64u, l = i % 64u, k0 = 128u * p + l, k1 = k0 + 64u;
+      xl[x_word(p, l)] = (k0 < C ? (xe.lo[j] & 0xFFFFu) : 0u) | (k1 < C ? (xe.hi[j] << 16) : 0u);
+    }
+  }
+}
+
 template <int NBP, bool XF32, bool YBF16, bool FLAT>
 struct ProductSink {
   const DevMatrix& d;
@@ -1004,17 +1043,22 @@ __global__ __launch_bounds__(fused_max_threads(NBP, XF32, FLAT)) void fused_prod
   const int u_first = blockIdx.x * waves + wave;
   const int n_items = FLAT ? d.n_items : d.n_units;
   int fv = 0;
-  // the decode tables, then the first unit's loads, then x; the tables have
-  // landed once only the ring's loads may be younger
+  // the decode tables, x (one bf16 row), then the first unit's ring steps:
+  // tables and x have landed once only the ring's loads may be younger
   const int n_tab = issue_tables(d, wave, waves, lane);
+  constexpr bool kEarlyX = NBP == 1 && !XF32;
+  const bool early_x = kEarlyX && x_early_fits(d, blockDim.x);
+  XEarly xe;
+  if (kEarlyX && early_x) x_issue(d, static_cast<const uint16_t*>(X), xe);
   int issued = 0;
   if (FLAT && u_first < n_items) {
     const WalkItem it = walk_item(d, u_first);
     fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
     issued = fv - it.b0 * d.T;
   }
-  if (n_tab) wait_tables<RS, NQ>(issued);
-  load_x<NBP, XF32>(d, X, ldx, nb_valid, lds + kTableWords + kT1Words);
+  if (n_tab || early_x) wait_tables<RS, NQ>(issued);
+  if (kEarlyX && early_x) x_store(d, xe, lds + kTableWords + kT1Words);
+  else load_x<NBP, XF32>(d, X, ldx, nb_valid, lds + kTableWords + kT1Words);
   lds_barrier();
   ProductSink<NBP, XF32, YBF16, FLAT> sink{d, kAreaAddr, lane, nb_valid, Y, ldy};  // the rest set per unit
   if (FLAT && d.split) {
