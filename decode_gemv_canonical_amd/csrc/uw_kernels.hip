@@ -622,6 +622,19 @@ __device__ __forceinline__ int flat_start(const DevMatrix& d, int b0, int b1, ui
   return fv;
 }
 
+// Wave priority (s_setprio takes an immediate).  A SIMD issues the ready
+// wave of highest priority, the oldest first among equals; with equal
+// priorities the first waves of a workgroup run ahead and the last ones end
+// the kernel alone.  The walk sets its priority from the tiles it has left,
+// so waves that fall behind are issued first and the waves of a SIMD finish
+// together (gate GEMV -2.3 %, down -3.6 %).
+__device__ __forceinline__ void set_priority(int p) {
+  if (p <= 0) asm volatile("s_setprio 0");
+  else if (p == 1) asm volatile("s_setprio 1");
+  else if (p == 2) asm volatile("s_setprio 2");
+  else asm volatile("s_setprio 3");
+}
+
 // Tiles of blocks [b0, b1), whose first tile is at row row_base, column
 // group c_start (0 unless blocks split rows); flat_start has issued the
 // steps before fv0.
@@ -691,6 +704,7 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
   block_start();
   for (; v < u1 - RS; ++v) {
     wait_oldest_step<RS, NQ, XTRA>();
+    if (((u1 - v) & 3) == 0) set_priority(std::min(3, (u1 - v) >> 2));  // every 4 tiles
     if (step(std::true_type{})) {
       t = 0;
       if (v + 1 < u1 - RS) wait_oldest_step<RS, NQ, XTRA>();
