@@ -159,15 +159,16 @@ int uw_blob_info(const void* blob, size_t n, uw_info* info);
  * memory.  host_blob/n is validated as by uw_blob_info; d_blob must hold the
  * same n bytes on the current device, 256-byte aligned.  The handle does not
  * own d_blob: the caller keeps it alive and unchanged until uw_matrix_destroy.
- * The handle keeps a copy of the header and the decode tables derived from
- * the code lengths, plus a per-batch plan cache (internally locked).  When G
- * and cols/64 are multiples of 16 (no 1024-weight tile crosses a row) it
- * also builds a step table, 8 bytes per tile (where each tile's segment
- * starts and how many lanes load it), in device memory it allocates and
- * frees in uw_matrix_destroy; the kernels then walk the tiles of a work unit
- * as one sequence.
+ * The handle keeps a copy of the header and a per-batch plan cache
+ * (internally locked).  In device memory it allocates, and frees in
+ * uw_matrix_destroy, it builds the decode tables (16640 bytes, derived from
+ * the code lengths; every kernel copies them into LDS) and, when G and
+ * cols/64 are multiples of 16 (no 1024-weight tile crosses a row), a step
+ * table, 8 bytes per tile (where each tile's segment starts and how many
+ * lanes load it); the kernels then walk the tiles of a work unit as one
+ * sequence.
  * Errors: UW_ERR_INVALID, UW_ERR_FORMAT, UW_ERR_HIP (no current device, or
- *         the step table could not be allocated or copied).
+ *         the tables could not be allocated or copied).
  */
 int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_matrix** out);
 
