@@ -84,9 +84,10 @@ std::vector<int> limited_lengths(const std::vector<uint64_t>& counts, const std:
 // per row or are a multiple of it, plus (groups per row a multiple of 16)
 // any larger G whose work unit, lcm(G, groups per row), has at most 8 blocks.
 // With at least 2048 blocks, pick the G that spreads one block per wave most
-// evenly over the 1024 SIMDs of a 256-CU part: least
-// ceil(blocks / 1024) * (tiles per block + 1 for the block start), ties to
-// the larger G.  Smaller matrices: the largest aligned G <= 64.
+// evenly over the 1024 SIMDs of a 256-CU part, 4 waves per SIMD in a round:
+// with b = ceil(blocks / 1024), the least ceil(b / 4) * 4 * (tiles per block
+// + 1 for the block start) (a partial round costs a full one), ties to the
+// larger G.  Smaller matrices: the largest aligned G <= 64.
 int auto_groups_per_block(int64_t rows, int64_t cols) {
   const int64_t gpr = cols / 64, total = rows * gpr;
   std::vector<int> aligned, wide, all;
@@ -101,7 +102,8 @@ int auto_groups_per_block(int64_t rows, int64_t cols) {
   for (int g : wide.empty() ? all : wide) {
     const int64_t nb = (total + g - 1) / g;
     if (nb < 2048) continue;
-    const int64_t load = (nb + 1023) / 1024 * (g / 16 + 1);
+    const int64_t per_simd = (nb + 1023) / 1024;
+    const int64_t load = (per_simd + 3) / 4 * 4 * (g / 16 + 1);
     if (best < 0 || load < best_load || (load == best_load && g > best)) {
       best = g;
       best_load = load;

@@ -90,10 +90,12 @@ def choose_groups_per_block(rows: int, cols: int) -> int:
     of 16, every larger G whose work unit (lcm of G and the groups per row)
     holds at most 8 blocks: a row then spans at most two blocks.  Among those
     that keep at least 2048 blocks, the one whose blocks spread most evenly
-    over the 1024 SIMDs of a 256-CU part, one block per wave, counting a
-    block start as one more tile: the least ceil(blocks / 1024) * (G/16 + 1),
-    ties to the larger G.  A matrix too small for 2048 blocks takes the
-    largest divisor or multiple of the groups per row that is <= 64."""
+    over the 1024 SIMDs of a 256-CU part, one block per wave and 4 waves per
+    SIMD in a round, counting a block start as one more tile: with
+    b = ceil(blocks / 1024) blocks per SIMD, the least
+    ceil(b / 4) * 4 * (G/16 + 1) (a round costs as much as a full one), ties
+    to the larger G.  A matrix too small for 2048 blocks takes the largest
+    divisor or multiple of the groups per row that is <= 64."""
     n = cols // 64
     total = rows * n
     cands = list(range(16, 257, 16))
@@ -102,7 +104,10 @@ def choose_groups_per_block(rows: int, cols: int) -> int:
                       if n % 16 == 0 and g > n and g not in aligned and n // math.gcd(g, n) <= 8]
     good = [g for g in (wide or cands) if -(-total // g) >= 2048]
     if good:
-        return min(good, key=lambda g: (-(-(-(-total // g)) // 1024) * (g // 16 + 1), -g))
+        def cost(g):
+            per_simd = -(-(-(-total // g)) // 1024)
+            return -(-per_simd // 4) * 4 * (g // 16 + 1)
+        return min(good, key=lambda g: (cost(g), -g))
     pool = aligned or cands
     small = [g for g in pool if g <= 64]
     return max(small) if small else min(pool)

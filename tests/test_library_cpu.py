@@ -42,7 +42,7 @@ def test_encoder_matches_oracle_bytes(name, rows, cols, kw):
 
 
 @pytest.mark.parametrize("rows,cols", [(14336, 4096), (4096, 14336), (8192, 8192), (11008, 4096), (4096, 11008),
-                                       (3000, 3072), (96, 4096), (13, 512), (1024, 1024)])
+                                       (28672, 4096), (3000, 3072), (96, 4096), (13, 512), (1024, 1024)])
 def test_default_block_size_matches_oracle(rows, cols):
     # the two encoders implement the default G separately
     b = uw.uw_encode(np.zeros((rows, cols), np.uint16), flags=uw.UW_ENC_NO_PLAIN)

@@ -266,6 +266,9 @@ def test_choose_groups_per_block():
     # down: one row per block, 4096 blocks
     assert blob.choose_groups_per_block(4096, 14336) == 224
     assert blob.choose_groups_per_block(8192, 8192) == 256
+    # gate and up as one matrix: 8192 blocks, two full rounds of 4 per SIMD
+    # (256 groups would leave 7 per SIMD: a round of 4, then one of 3)
+    assert blob.choose_groups_per_block(28672, 4096) == 224
     # too small for 2048 blocks: the largest aligned G <= 64
     assert blob.choose_groups_per_block(96, 4096) == 64
     assert blob.choose_groups_per_block(13, 512) == 64
