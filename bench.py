@@ -224,7 +224,10 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
     calls of one token (the AUTO variant, replayed from a graph), the
     elementwise ops alone, and the same 96 products on the uncompressed bf16
     weights; every product of one token is checked on sampled rows against the
-    fp64 product of the original weights."""
+    fp64 product of the original weights.  A second layout encodes gate and up
+    as one 28672x4096 matrix per layer (one launch for both, as a fused
+    gate_up projection): its 64 calls per token are timed and checked the
+    same way."""
     import numpy as np
 
     from oracle import products
@@ -238,6 +241,7 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
             b = uw.uw_encode(v)
             blob_bytes += len(b)
             mats[k] = uw.CompressedMatrix(b, device="cuda:0")
+        mats["gate_up"] = uw.CompressedMatrix(uw.uw_encode(torch.cat([L["gate"], L["up"]])), device="cuda:0")
         layers.append(mats)
         bfw.append({k: v.to(dev).view(torch.bfloat16) for k, v in L.items()})
         log(f"stack layer {li} encoded and uploaded ({time.perf_counter() - t0:.0f} s)")
@@ -296,14 +300,36 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
                 torch.matmul(h[li], bfw[li]["down"].t(), out=db)
 
         us_b, _, _ = time_graph([bf16_calls], reps, reps, torch)
+        # gate and up as one matrix: 64 calls per token
+        gu = [torch.empty(B, 2 * F, dtype=torch.float32, device=dev) for _ in range(n)]
+
+        def fused_calls(li):
+            uw.uw_gemm_fused(layers[li]["gate_up"].handle, xs[li], gu[li], uw.UW_VARIANT_AUTO, ws)
+            uw.uw_gemm_fused(layers[li]["down"].handle, h[li], d[li], uw.UW_VARIANT_AUTO, ws)
+
+        for li in range(n):
+            fused_calls(li)
+        torch.cuda.synchronize()
+        worst_gu = 0.0
+        for li in range(n):
+            rows = rng.choice(2 * F, size=64, replace=False)
+            wcat = torch.cat([bfw[li]["gate"], bfw[li]["up"]])
+            wb = wcat[torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+            ref = products.gemm_f64(wb, xs[li].float().cpu().numpy())
+            got = gu[li][:, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+            worst_gu = max(worst_gu, products.rel_error_floored(got, ref))
+            del wcat
+        us_f, _, _ = time_graph([lambda: [fused_calls(li) for li in range(n)]], reps, reps, torch)
         out[f"b{B}"] = {"matrix_ms_per_token": round(us_m / 1e3, 4), "elementwise_ms_per_token": round(us_e / 1e3, 4),
+                        "gate_up_fused_matrix_ms_per_token": round(us_f / 1e3, 4),
+                        "gate_up_fused_parity_max_rel_err_sampled": worst_gu,
                         "bf16_matmul_ms_per_token": round(us_b / 1e3, 4),
                         "speedup_vs_bf16": round(us_b / us_m, 4),
                         "effective_weight_GBs": round(out["bf16_bytes"] / (us_m * 1e-6) / 1e9, 1),
                         "compressed_GBs": round(blob_bytes / (us_m * 1e-6) / 1e9, 1),
                         "parity_max_rel_err_sampled": worst, "parity_ok": worst <= PARITY_TOL}
         log(f"stack B={B}: {out[f'b{B}']}")
-        del xs, g, u, h, d, ws, gb, db
+        del xs, g, u, h, d, ws, gb, db, gu
         torch.cuda.empty_cache()
     return out
 
