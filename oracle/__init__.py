@@ -18,6 +18,9 @@ LLM 22% without sacrificing quality"):
   * Huffman coding of the exponent byte only (paragraph on Huffman coding),
     made length-limited by package-merge and canonical per RFC 1951 3.2.2;
   * lossless round trip (results paragraph: 100% bit-exact);
+  * the direct-palette form (4-bit palette index + sign+mantissa byte per
+    weight, raw groups verbatim) built at load time (section on the four
+    execution pipelines), in palette.py;
   * the products y = W x and Y = X W^T over the original weights with fp64
     ground truth and an fp32 reference (paragraph on the reconstructive
     matmul: the kernel multiplies the reconstructed bf16 weights).
@@ -27,4 +30,4 @@ from this package: hand-derived streams, the RFC's printed example, brute
 force over all length vectors, closed forms, exact rational sums and
 invariants.
 """
-from . import huffman, blob, products  # noqa: F401
+from . import huffman, blob, palette, products  # noqa: F401
