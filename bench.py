@@ -464,6 +464,36 @@ def main():
                                 "frac_hbm_peak": round(dbytes / (us_d * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del out_w
         torch.cuda.empty_cache()
+        # direct-palette pipeline on the same weights: 4-bit index + sm byte,
+        # no entropy decode (larger blob, lighter kernel)
+        log("timing direct-palette GEMV")
+        pblob = uw.uw_palette_encode(w)
+        pinfo = uw.uw_palette_info(pblob)
+        pmats = [uw.PaletteMatrix(pblob, device="cuda:0") for _ in range(ROTATE)]
+        yp = torch.empty(rows, dtype=torch.float32, device=dev)
+        us_pg, _, _ = time_graph([(lambda m=m: uw.uw_palette_gemv(m.handle, x, yp)) for m in pmats], args.steps,
+                                 args.warmup, torch)
+        perr = products.rel_error_floored(yp.cpu().numpy(), ref)
+        pbytes = pinfo["bytes"] + cols * x.element_size() + rows * 4
+        out_pw = [torch.empty(rows, cols, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        us_pd, _, _ = time_graph([(lambda m=m, o=out_pw[i % 2]: uw.uw_palette_decompress(m.handle, o, cols))
+                                  for i, m in enumerate(pmats)], 400, 400, torch)
+        extras["palette_pipeline"] = {
+            "ratio": round(pinfo["ratio"], 5), "blob_bytes": pinfo["bytes"],
+            "raw_group_frac": round(pinfo["n_raw"] / (weights // 64), 6),
+            "gemv_us": round(us_pg, 3), "gemv_GBs": round(pbytes / (us_pg * 1e-6) / 1e9, 1),
+            "gemv_frac_hbm_peak": round(pbytes / (us_pg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "effective_weight_GBs": round(2.0 * weights / (us_pg * 1e-6) / 1e9, 1),
+            "vs_huffman_fused": round(us / us_pg, 4), "vs_best_bf16": round(best_bf16 / us_pg, 4),
+            "max_rel_err_vs_fp64": perr, "parity_ok": bool(perr <= PARITY_TOL),
+            "decompress_us": round(us_pd, 3),
+            "decompress_GBs_read_plus_write": round((pinfo["bytes"] + 2 * weights) / (us_pd * 1e-6) / 1e9, 1),
+        }
+        log(f"palette: {extras['palette_pipeline']}")
+        for m in pmats:
+            m.close()
+        del out_pw, pmats
+        torch.cuda.empty_cache()
         # plain copy of known size (random bits store in plain mode: the
         # decompress is one read and one write of 128 MiB); its counter
         # readings calibrate FETCH_SIZE / WRITE_SIZE for the traffic figure

@@ -6,4 +6,4 @@ The work happens in libuw.so (include/uw.h); this package is its thin Python
 binding.  Importing it fails if the library has not been built.
 """
 from .uw import *  # noqa: F401,F403
-from .uw import CompressedMatrix, UwError, header_symbols, library  # noqa: F401
+from .uw import CompressedMatrix, PaletteMatrix, UwError, header_symbols, library  # noqa: F401

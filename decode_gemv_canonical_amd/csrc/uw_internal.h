@@ -56,6 +56,18 @@ void set_error(const std::string& msg);
 const char* last_error_text();
 int fail(int status, const std::string& msg);
 
+// Direct-palette form (format UWP1, uw_palette.cpp): section offsets in bytes.
+constexpr size_t kPaletteHeaderBytes = 64;
+struct PaletteLayout {
+  int64_t rows = 0, cols = 0, n_raw = 0;
+  int n_pal = 0;
+  uint8_t palette[16] = {0};
+  size_t off_sm = 0, off_idx = 0, off_flags = 0, off_prefix = 0, off_raw = 0, total = 0;
+};
+PaletteLayout palette_layout(int64_t rows, int64_t cols, int64_t n_raw);
+// Header fields, size and the raw flags/prefix counts; UW_ERR_FORMAT otherwise.
+int palette_parse(const void* blob, size_t n, PaletteLayout* out);
+
 // Kernel-side description of a compressed matrix, passed by value.
 struct DevMatrix {
   const uint32_t* block_off;  // byte offset of each block's data in the queue

@@ -1,0 +1,325 @@
+// Direct-palette pipeline on gfx950: the batch-1 product and the decode of
+// the UWP1 form (4-bit palette index + sign+mantissa byte per weight, raw
+// 64-weight groups verbatim; layout in uw_palette.cpp).
+//
+// "Unweight: how we compressed an LLM 22% without sacrificing quality",
+// section on the four execution pipelines: the direct palette skips
+// preprocessing and the matmul rebuilds bf16 from the indices on the fly.
+// Here there is no entropy decode at all, so the kernels are plain streams:
+// lane l of a wave owns 16 consecutive weights of each 1024-weight tile, reads
+// their 16 sign+mantissa bytes and 8 index bytes with one 16-byte and one
+// 8-byte load (coalesced across the wave), looks up two exponents per index
+// byte in a 256-entry LDS table, and multiplies with the 16 matching x values
+// read as two 16-byte loads (x is small and stays in cache).
+#include <algorithm>
+
+#include "uw_device.h"
+
+struct uw_palette {
+  uw::PaletteLayout l;
+  const uint8_t* d_blob = nullptr;
+  int device = 0;
+};
+
+namespace uw {
+namespace {
+
+constexpr int kPalThreads = 256;  // 4 waves
+constexpr int kPalChunk = 1;      // GEMV: tiles per register set (measured: 1 beats 2 and 4)
+constexpr int kPalDecChunk = 4;   // decompress: tiles whose loads a wave issues together
+
+struct DevPalette {
+  const uint8_t* sm;
+  const uint8_t* idx;
+  const uint32_t* flags;
+  const uint32_t* prefix;
+  const uint8_t* raw;
+  int64_t rows;
+  int64_t tpr;  // 1024-weight tiles per row
+  int64_t rows_per_wave;
+  uint32_t pal[4];  // palette bytes, index i in byte i % 4 of word i / 4
+};
+
+__device__ inline uint32_t pal_byte(const DevPalette& p, int i) {
+  const uint32_t w = i < 4 ? p.pal[0] : i < 8 ? p.pal[1] : i < 12 ? p.pal[2] : p.pal[3];
+  return (w >> (8 * (i & 3))) & 0xFFu;
+}
+
+// table[b] = the exponents of index byte b: low nibble (even weight) in bits
+// 7..14, high nibble (odd weight) in bits 23..30, where bf16 keeps them.
+__device__ inline void build_pair_table(const DevPalette& p, uint32_t* table) {
+  const int b = threadIdx.x;
+  table[b] = (pal_byte(p, b & 15) << 7) | (pal_byte(p, b >> 4) << 23);
+}
+
+struct TileIn {
+  uint4 sm;
+  uint2 idx;
+  uint32_t rmask;  // raw flags of the tile's 16 groups (wave-uniform)
+  uint4 rawe;      // this lane's 16 raw exponents when its group is raw
+};
+
+__device__ inline void load_tile(const DevPalette& p, int64_t T, int lane, TileIn& in) {
+  in.sm = *reinterpret_cast<const uint4*>(p.sm + T * 1024 + 16 * lane);
+  in.idx = *reinterpret_cast<const uint2*>(p.idx + T * 512 + 8 * lane);
+  in.rmask = (scalar_word(p.flags, T >> 1) >> (16 * (T & 1))) & 0xFFFFu;
+  in.rawe = uint4{0u, 0u, 0u, 0u};
+  if (in.rmask) {
+    const int g = lane >> 2;  // the lane's group within the tile
+    if ((in.rmask >> g) & 1u) {
+      const uint32_t slot = scalar_word(p.prefix, T) + uint32_t(__builtin_popcount(in.rmask & ((1u << g) - 1u)));
+      in.rawe = *reinterpret_cast<const uint4*>(p.raw + int64_t(slot) * 64 + 16 * (lane & 3));
+    }
+  }
+}
+
+__device__ inline uint32_t word_of(const uint4& v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; }
+
+// Weights 2k, 2k+1 of the lane's 16 as one register of two bf16.  RAW: the
+// tile has raw groups (the lane's own may or may not be one).
+template <bool RAW>
+__device__ inline uint32_t pair_weights(const TileIn& in, const uint32_t* table, int lane, int k) {
+  const uint32_t q = (k < 4 ? in.idx.x : in.idx.y) >> (8 * (k & 3));
+  uint32_t E = table[q & 0xFFu];
+  if (RAW && ((in.rmask >> (lane >> 2)) & 1u))
+    E = __builtin_amdgcn_perm(0u, word_of(in.rawe, k >> 1), (k & 1) ? 0x0c030c02u : 0x0c010c00u) << 7;
+  const uint32_t S = __builtin_amdgcn_perm(0u, word_of(in.sm, k >> 1), (k & 1) ? 0x03030202u : 0x01010000u);
+  return (S & 0x807F807Fu) | (E & 0x7F807F80u);
+}
+
+template <bool XF32>
+struct XTile {
+  uint4 v[XF32 ? 4 : 2];
+};
+
+template <bool XF32>
+__device__ inline void load_x(const void* X, int64_t t, int lane, XTile<XF32>& x) {
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(X) + (t * 1024 + 16 * lane) * (XF32 ? 4 : 2));
+#pragma unroll
+  for (int i = 0; i < (XF32 ? 4 : 2); ++i) x.v[i] = src[i];
+}
+
+template <bool XF32, bool RAW>
+__device__ inline float tile_dot_as(const TileIn& in, const XTile<XF32>& x, const uint32_t* table, int lane, float acc) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t W = pair_weights<RAW>(in, table, lane, k);
+    if (XF32) {
+      const uint32_t x0 = word_of(x.v[k >> 1], 2 * (k & 1)), x1 = word_of(x.v[k >> 1], 2 * (k & 1) + 1);
+      acc = __builtin_fmaf(bits_f32(W << 16), bits_f32(x0), acc);
+      acc = __builtin_fmaf(bits_f32(W & 0xFFFF0000u), bits_f32(x1), acc);
+    } else {
+      acc = dot2_bf16(W, word_of(x.v[k >> 2], k & 3), acc);
+    }
+  }
+  return acc;
+}
+
+template <bool XF32>
+__device__ inline float tile_dot(const TileIn& in, const XTile<XF32>& x, const uint32_t* table, int lane, float acc) {
+  return in.rmask ? tile_dot_as<XF32, true>(in, x, table, lane, acc) : tile_dot_as<XF32, false>(in, x, table, lane, acc);
+}
+
+// The loads of kPalChunk consecutive tiles of the wave's walk (row-major
+// tile order); tt = column tile of the first, advanced past the last.
+template <bool XF32>
+__device__ __forceinline__ void issue_chunk(const DevPalette& p, const void* X, int64_t T, int64_t T1, int64_t& tt,
+                                            int lane, TileIn (&in)[kPalChunk], XTile<XF32> (&xs)[kPalChunk]) {
+#pragma unroll
+  for (int i = 0; i < kPalChunk; ++i) {
+    if (T + i < T1) {
+      load_tile(p, T + i, lane, in[i]);
+      load_x<XF32>(X, tt, lane, xs[i]);
+    }
+    if (++tt == p.tpr) tt = 0;
+  }
+}
+
+// The products of a chunk; a row's sum is reduced and stored at its last tile.
+template <bool XF32, bool YBF16>
+__device__ __forceinline__ void consume_chunk(const DevPalette& p, int64_t T, int64_t T1, int64_t& t, int64_t& row,
+                                              float& acc, int lane, const uint32_t* table,
+                                              const TileIn (&in)[kPalChunk], const XTile<XF32> (&xs)[kPalChunk],
+                                              void* Y) {
+#pragma unroll
+  for (int i = 0; i < kPalChunk; ++i) {
+    if (T + i < T1) {
+      acc = tile_dot<XF32>(in[i], xs[i], table, lane, acc);
+      if (++t == p.tpr) {
+        const float s = wave_sum(acc);
+        if (lane == 0) {
+          if (YBF16) static_cast<uint16_t*>(Y)[row] = f32_to_bf16(s);
+          else static_cast<float*>(Y)[row] = s;
+        }
+        acc = 0.f;
+        t = 0;
+        ++row;
+      }
+    }
+  }
+}
+
+// One wave per rows_per_wave consecutive rows.  The wave walks their tiles in
+// chunks of kPalChunk with two register sets: the loads of the next chunk are
+// in flight while the current one is multiplied.
+template <bool XF32, bool YBF16>
+__global__ __launch_bounds__(kPalThreads) void palette_gemv_kernel(DevPalette p, const void* __restrict__ X,
+                                                                   void* __restrict__ Y) {
+  __shared__ uint32_t table[256];
+  build_pair_table(p, table);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = int64_t(blockIdx.x) * (kPalThreads / 64) + (threadIdx.x >> 6);
+  const int64_t r0 = wave * p.rows_per_wave;
+  if (r0 >= p.rows) return;
+  const int64_t r1 = min(p.rows, r0 + p.rows_per_wave);
+  const int64_t T1 = r1 * p.tpr;
+  int64_t row = r0, t = 0, tt = 0;  // t, tt: column tile of the next tile to multiply / to load
+  float acc = 0.f;
+  TileIn a[kPalChunk], b[kPalChunk];
+  XTile<XF32> xa[kPalChunk], xb[kPalChunk];
+  int64_t T = r0 * p.tpr;
+  issue_chunk<XF32>(p, X, T, T1, tt, lane, a, xa);
+  for (; T < T1; T += 2 * kPalChunk) {
+    issue_chunk<XF32>(p, X, T + kPalChunk, T1, tt, lane, b, xb);
+    consume_chunk<XF32, YBF16>(p, T, T1, t, row, acc, lane, table, a, xa, Y);
+    issue_chunk<XF32>(p, X, T + 2 * kPalChunk, T1, tt, lane, a, xa);
+    consume_chunk<XF32, YBF16>(p, T + kPalChunk, T1, t, row, acc, lane, table, b, xb, Y);
+  }
+}
+
+// bf16 weights to out[r * ld + c]: lane l writes its 16 weights as two
+// 16-byte stores.
+__global__ __launch_bounds__(kPalThreads) void palette_decompress_kernel(DevPalette p, uint16_t* __restrict__ out,
+                                                                         int64_t ld) {
+  __shared__ uint32_t table[256];
+  build_pair_table(p, table);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = int64_t(blockIdx.x) * (kPalThreads / 64) + (threadIdx.x >> 6);
+  const int64_t r0 = wave * p.rows_per_wave;
+  if (r0 >= p.rows) return;
+  const int64_t r1 = min(p.rows, r0 + p.rows_per_wave);
+  for (int64_t row = r0; row < r1; ++row) {
+    for (int64_t t = 0; t < p.tpr; t += kPalDecChunk) {
+      TileIn in[kPalDecChunk];
+#pragma unroll
+      for (int i = 0; i < kPalDecChunk; ++i)
+        if (t + i < p.tpr) load_tile(p, row * p.tpr + t + i, lane, in[i]);
+#pragma unroll
+      for (int i = 0; i < kPalDecChunk; ++i) {
+        if (t + i < p.tpr) {
+          uint32_t w[8];
+          if (in[i].rmask) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w[k] = pair_weights<true>(in[i], table, lane, k);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w[k] = pair_weights<false>(in[i], table, lane, k);
+          }
+          uint4* dst = reinterpret_cast<uint4*>(out + row * ld + (t + i) * 1024 + 16 * lane);
+          dst[0] = uint4{w[0], w[1], w[2], w[3]};
+          dst[1] = uint4{w[4], w[5], w[6], w[7]};
+        }
+      }
+    }
+  }
+}
+
+DevPalette dev_palette(const uw_palette* m) {
+  const PaletteLayout& l = m->l;
+  DevPalette p;
+  p.sm = m->d_blob + l.off_sm;
+  p.idx = m->d_blob + l.off_idx;
+  p.flags = reinterpret_cast<const uint32_t*>(m->d_blob + l.off_flags);
+  p.prefix = reinterpret_cast<const uint32_t*>(m->d_blob + l.off_prefix);
+  p.raw = m->d_blob + l.off_raw;
+  p.rows = l.rows;
+  p.tpr = l.cols / 1024;
+  // about 4 tiles per wave (one row of a 4096-column matrix): many short
+  // waves keep the loads of many tiles in flight and shorten the tail
+  p.rows_per_wave = std::max<int64_t>(1, 4 / p.tpr);
+  for (int i = 0; i < 4; ++i)
+    p.pal[i] = uint32_t(l.palette[4 * i]) | uint32_t(l.palette[4 * i + 1]) << 8 | uint32_t(l.palette[4 * i + 2]) << 16 |
+               uint32_t(l.palette[4 * i + 3]) << 24;
+  return p;
+}
+
+unsigned palette_blocks(const DevPalette& p) {
+  const int64_t waves = (p.rows + p.rows_per_wave - 1) / p.rows_per_wave;
+  return unsigned((waves + kPalThreads / 64 - 1) / (kPalThreads / 64));
+}
+
+int check_palette(const uw_palette* m, const char* where) {
+  if (!m) return fail(UW_ERR_INVALID, std::string(where) + ": null handle");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(UW_ERR_HIP, std::string(where) + ": no current HIP device");
+  if (dev != m->device) return fail(UW_ERR_INVALID, std::string(where) + ": handle belongs to another device");
+  return UW_OK;
+}
+
+bool aligned_to(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+}  // namespace
+}  // namespace uw
+
+using namespace uw;
+
+extern "C" int uw_palette_create(const void* host_blob, size_t n, const void* d_blob, uw_palette** out) {
+  if (!host_blob || !d_blob || !out) return fail(UW_ERR_INVALID, "uw_palette_create: null pointer");
+  if (!aligned_to(d_blob, 256)) return fail(UW_ERR_INVALID, "uw_palette_create: device blob must be 256-byte aligned");
+  PaletteLayout l;
+  if (int rc = palette_parse(host_blob, n, &l)) return rc;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(UW_ERR_HIP, "uw_palette_create: no current HIP device");
+  uw_palette* m = new uw_palette;
+  m->l = l;
+  m->d_blob = static_cast<const uint8_t*>(d_blob);
+  m->device = dev;
+  *out = m;
+  return UW_OK;
+}
+
+extern "C" void uw_palette_destroy(uw_palette* m) { delete m; }
+
+extern "C" int uw_palette_gemv(const uw_palette* m, const void* d_x, int xt, void* d_y, int yt, void* stream) {
+  if (int rc = check_palette(m, "uw_palette_gemv")) return rc;
+  if ((xt != UW_F32 && xt != UW_BF16) || (yt != UW_F32 && yt != UW_BF16))
+    return fail(UW_ERR_INVALID, "uw_palette_gemv: types must be UW_F32 or UW_BF16");
+  if (!d_x || !aligned_to(d_x, 16)) return fail(UW_ERR_INVALID, "uw_palette_gemv: x must be non-null and 16-byte aligned");
+  if (!d_y || !aligned_to(d_y, yt == UW_F32 ? 4 : 2))
+    return fail(UW_ERR_INVALID, "uw_palette_gemv: y must be non-null and aligned to its element");
+  const DevPalette p = dev_palette(m);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(palette_blocks(p)), block(kPalThreads);
+  if (xt == UW_BF16) {
+    if (yt == UW_BF16) hipLaunchKernelGGL((palette_gemv_kernel<false, true>), grid, block, 0, s, p, d_x, d_y);
+    else hipLaunchKernelGGL((palette_gemv_kernel<false, false>), grid, block, 0, s, p, d_x, d_y);
+  } else {
+    if (yt == UW_BF16) hipLaunchKernelGGL((palette_gemv_kernel<true, true>), grid, block, 0, s, p, d_x, d_y);
+    else hipLaunchKernelGGL((palette_gemv_kernel<true, false>), grid, block, 0, s, p, d_x, d_y);
+  }
+  return hip_check(hipGetLastError(), "palette_gemv_kernel launch");
+}
+
+extern "C" int uw_palette_decompress(const uw_palette* m, uint16_t* d_out, int64_t ld_out, void* stream) {
+  if (int rc = check_palette(m, "uw_palette_decompress")) return rc;
+  if (!d_out || !aligned_to(d_out, 16))
+    return fail(UW_ERR_INVALID, "uw_palette_decompress: output must be non-null and 16-byte aligned");
+  if (ld_out < m->l.cols || ld_out % 8)
+    return fail(UW_ERR_INVALID, "uw_palette_decompress: ld_out must be >= cols and a multiple of 8");
+  const DevPalette p = dev_palette(m);
+  hipLaunchKernelGGL(palette_decompress_kernel, dim3(palette_blocks(p)), dim3(kPalThreads), 0,
+                     static_cast<hipStream_t>(stream), p, d_out, ld_out);
+  return hip_check(hipGetLastError(), "palette_decompress_kernel launch");
+}
+
+extern "C" int uw_palette_info(const void* blob, size_t n, int64_t* rows, int64_t* cols, int64_t* n_raw) {
+  if (!blob || !rows || !cols || !n_raw) return fail(UW_ERR_INVALID, "uw_palette_info: null pointer");
+  PaletteLayout l;
+  if (int rc = palette_parse(blob, n, &l)) return rc;
+  *rows = l.rows;
+  *cols = l.cols;
+  *n_raw = l.n_raw;
+  return UW_OK;
+}

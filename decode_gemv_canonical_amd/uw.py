@@ -81,6 +81,12 @@ def _load() -> ctypes.CDLL:
         "uw_bf16_gemm": (I, [P, I64, I64, I64, P, I64, I64, I, P, I64, I, P]),
         "uw_read_probe": (I, [P, SZ, P, P]),
         "uw_read_probe_sink_size": (SZ, []),
+        "uw_palette_encode": (I, [P, I64, I64, P, ctypes.POINTER(SZ)]),
+        "uw_palette_info": (I, [P, SZ, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+        "uw_palette_create": (I, [P, SZ, P, ctypes.POINTER(P)]),
+        "uw_palette_destroy": (None, [P]),
+        "uw_palette_gemv": (I, [P, P, I, P, I, P]),
+        "uw_palette_decompress": (I, [P, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -248,6 +254,51 @@ def uw_read_probe(src, sink, stream=None) -> None:
            "uw_read_probe")
 
 
+def uw_palette_encode(w_bf16) -> bytes:
+    a = _as_u16(w_bf16)
+    if a.ndim != 2:
+        raise ValueError("weights must be a 2-D matrix")
+    size = ctypes.c_size_t(0)
+    _check(_lib.uw_palette_encode(a.ctypes.data, a.shape[0], a.shape[1], None, ctypes.byref(size)), "uw_palette_encode")
+    buf = np.zeros(size.value, dtype=np.uint8)
+    _check(_lib.uw_palette_encode(a.ctypes.data, a.shape[0], a.shape[1], buf.ctypes.data, ctypes.byref(size)),
+           "uw_palette_encode")
+    return buf.tobytes()
+
+
+def uw_palette_info(blob: bytes) -> dict:
+    arr = np.frombuffer(blob, dtype=np.uint8)
+    rows, cols, n_raw = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.uw_palette_info(arr.ctypes.data, arr.size, ctypes.byref(rows), ctypes.byref(cols), ctypes.byref(n_raw)),
+           "uw_palette_info")
+    return {"rows": rows.value, "cols": cols.value, "n_raw": n_raw.value, "bytes": arr.size,
+            "ratio": arr.size / (2 * rows.value * cols.value)}
+
+
+def uw_palette_create(host_blob: bytes, d_blob) -> int:
+    arr = np.frombuffer(host_blob, dtype=np.uint8)
+    if d_blob.numel() != arr.size:
+        raise ValueError("device blob size differs from the host blob")
+    h = ctypes.c_void_p()
+    _check(_lib.uw_palette_create(arr.ctypes.data, arr.size, d_blob.data_ptr(), ctypes.byref(h)), "uw_palette_create")
+    return h.value
+
+
+def uw_palette_destroy(handle: int) -> None:
+    _lib.uw_palette_destroy(handle)
+
+
+def uw_palette_gemv(handle: int, x, y, stream=None) -> None:
+    _check(_lib.uw_palette_gemv(handle, x.data_ptr(), _dtype_code(x), y.data_ptr(), _dtype_code(y), _stream(stream)),
+           "uw_palette_gemv")
+
+
+def uw_palette_decompress(handle: int, d_out, ld_out: int | None = None, stream=None) -> None:
+    if ld_out is None:
+        ld_out = d_out.stride(0)
+    _check(_lib.uw_palette_decompress(handle, d_out.data_ptr(), ld_out, _stream(stream)), "uw_palette_decompress")
+
+
 # -- convenience owner of a device blob + handle -----------------------------
 
 class CompressedMatrix:
@@ -304,6 +355,49 @@ class CompressedMatrix:
     def close(self) -> None:
         if getattr(self, "handle", None):
             uw_matrix_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class PaletteMatrix:
+    """A UWP1 blob copied to the current CUDA device plus its library handle."""
+
+    def __init__(self, blob: bytes, device: str = "cuda"):
+        import torch
+        self.blob = blob
+        self.info = uw_palette_info(blob)
+        self.d_blob = torch.frombuffer(bytearray(blob), dtype=torch.uint8).to(device)
+        if self.d_blob.data_ptr() % 256:
+            raise RuntimeError("device blob is not 256-byte aligned")
+        self.handle = uw_palette_create(blob, self.d_blob)
+        self.rows, self.cols = self.info["rows"], self.info["cols"]
+
+    @classmethod
+    def from_weights(cls, w_bf16, device: str = "cuda") -> "PaletteMatrix":
+        return cls(uw_palette_encode(w_bf16), device)
+
+    def decompress(self, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(self.rows, self.cols, dtype=torch.bfloat16, device=self.d_blob.device)
+        uw_palette_decompress(self.handle, out, out.stride(0), stream)
+        return out
+
+    def gemv(self, x, y=None, out_dtype=None, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty(self.rows, dtype=out_dtype or torch.float32, device=x.device)
+        uw_palette_gemv(self.handle, x, y, stream)
+        return y
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            uw_palette_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -264,6 +264,63 @@ int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, c
 int uw_read_probe(const void* d_src, size_t bytes, void* d_sink, void* stream);
 size_t uw_read_probe_sink_size(void);
 
+/*
+ * Direct-palette pipeline (section on the four execution pipelines: the
+ * weights become 4-bit palette indices at load time and the matmul rebuilds
+ * bf16 from them with no preprocessing pass).  Form UWP1: per weight one
+ * sign+mantissa byte and a 4-bit index into the 16 most frequent exponents;
+ * 64-weight groups holding any other exponent keep their 64 exponent bytes
+ * (paragraph on rare exponents).  About 12 bits per weight plus raw groups.
+ */
+typedef struct uw_palette uw_palette;
+
+/*
+ * uw_palette_encode (host) - the UWP1 form of a bf16 matrix.
+ *   w_bf16   host, rows*cols bf16 bit patterns, row-major, not modified.
+ *   rows>=1, cols a positive multiple of 1024 (no 1024-weight tile crosses a
+ *   row).  out/out_size as for uw_encode (NULL out queries the size).
+ * Deterministic; the palette and the raw groups follow uw_encode's rule
+ * (count descending, exponent ascending; K = 16).
+ * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE.
+ */
+int uw_palette_encode(const uint16_t* w_bf16, int64_t rows, int64_t cols, void* out, size_t* out_size);
+
+/*
+ * uw_palette_info (host) - validate a UWP1 blob (header, size, raw flags
+ * against the per-tile prefix counts) and report its shape and raw groups.
+ * Errors: UW_ERR_INVALID (null), UW_ERR_FORMAT.
+ */
+int uw_palette_info(const void* blob, size_t n, int64_t* rows, int64_t* cols, int64_t* n_raw);
+
+/*
+ * uw_palette_create (host) - bind a handle to a UWP1 blob already copied to
+ * device memory (n bytes on the current device, 256-byte aligned; the caller
+ * keeps it alive and unchanged until uw_palette_destroy).  host_blob/n is
+ * validated as by uw_palette_info.  Allocates no device memory.
+ * Errors: UW_ERR_INVALID, UW_ERR_FORMAT, UW_ERR_HIP (no current device).
+ */
+int uw_palette_create(const void* host_blob, size_t n, const void* d_blob, uw_palette** out);
+
+/* Release a palette handle (NULL is ignored). */
+void uw_palette_destroy(uw_palette* m);
+
+/*
+ * uw_palette_gemv (device) - y = W x over the UWP1 form, decode fused.
+ *   d_x  device, cols elements of xt (UW_F32 or UW_BF16), 16-byte aligned.
+ *   d_y  device, rows elements of yt (UW_F32, or UW_BF16 rounded to nearest
+ *        even).  fp32 accumulation.
+ * Errors: UW_ERR_INVALID (null, misaligned, wrong device), UW_ERR_HIP.
+ */
+int uw_palette_gemv(const uw_palette* m, const void* d_x, int xt, void* d_y, int yt, void* stream);
+
+/*
+ * uw_palette_decompress (device) - the original bf16 bits of a UWP1 matrix,
+ * W[r][c] at d_out[r*ld_out + c]; d_out 16-byte aligned, ld_out >= cols and a
+ * multiple of 8.  Bit-exact.
+ * Errors: UW_ERR_INVALID, UW_ERR_HIP.
+ */
+int uw_palette_decompress(const uw_palette* m, uint16_t* d_out, int64_t ld_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,123 @@
+"""GPU parity of the direct-palette pipeline (UWP1) through the C-ABI.
+
+The blobs come from the library's host encoder, which the CPU tests hold
+byte-identical to oracle/palette.py.  Decompression must give back the
+original weights bit for bit (the form is lossless); the fused GEMV is checked
+against the fp64 product of the original weights with the same bars as the
+Huffman pipeline: max |y - y64| / max(|y64|, rms(y64)) <= 1e-3 for fp32
+outputs, 2 bf16 ulp (or the fp32 band) for bf16 outputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import palette as opal
+from oracle import products
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import decode_gemv_canonical_amd as uw  # noqa: E402
+
+from tests.test_gpu_parity import check_bf16, check_f32  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+_cache = {}
+
+
+def pmatrix(name, rows=None, cols=None, seed=None):
+    key = (name, rows, cols, seed)
+    if key not in _cache:
+        wb = workloads.weights(name, rows=rows, cols=cols, seed=seed).numpy().view(np.uint16)
+        _cache[key] = (wb, uw.PaletteMatrix.from_weights(wb, device="cuda:0"))
+    return _cache[key]
+
+
+CASES = [
+    ("small", None, None, None),       # 1024 x 1024, one tile per row
+    ("gate", None, None, None),        # 14336 x 4096 (0.5 % raw groups)
+    ("down", None, None, None),        # 4096 x 14336, outliers (8 % raw groups)
+    ("randbits", 2048, 8192, None),    # every group raw
+    ("gate", 37, 3072, 21),            # ragged: rows not a multiple of the rows per wave
+    ("down", 1, 1024, 22),             # one row
+    ("down", 5, 7168, 23),             # a row of 7 tiles (chunks of 4 cross rows)
+]
+
+
+@pytest.mark.parametrize("name,rows,cols,seed", CASES)
+def test_palette_decompress_bit_exact(name, rows, cols, seed):
+    wb, m = pmatrix(name, rows, cols, seed)
+    _say(f"palette decompress {name} {wb.shape}")
+    out = m.decompress()
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), wb)
+
+
+def test_palette_decompress_strided_output():
+    wb, m = pmatrix("gate", 37, 3072, 21)
+    _say("palette decompress strided")
+    big = torch.full((37, 3072 + 64), -1, dtype=torch.int16, device=DEV)
+    uw.uw_palette_decompress(m.handle, big, 3072 + 64)
+    torch.cuda.synchronize()
+    got = big.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got[:, :3072], wb)
+    assert (got[:, 3072:] == 0xFFFF).all()
+
+
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("name,rows,cols,seed", CASES)
+def test_palette_gemv(name, rows, cols, seed, xdt):
+    wb, m = pmatrix(name, rows, cols, seed)
+    x = workloads.activations(wb.shape[1], 1, seed=(seed or 0) + 300, dtype=xdt)[0]
+    ref = products.gemm_f64(wb, x.float().numpy())
+    _say(f"palette gemv {name} {wb.shape} x={xdt}")
+    y = m.gemv(x.to(DEV))
+    yb = m.gemv(x.to(DEV), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check_f32(y, ref, f"palette gemv {name}")
+    check_bf16(yb, ref, f"palette gemv bf16 {name}")
+
+
+def test_palette_gemv_one_hot_is_exact():
+    wb, m = pmatrix("down", 5, 7168, 23)
+    for k in (0, 15, 16, 1023, 1024, 7167):
+        x = torch.zeros(7168, dtype=torch.bfloat16)
+        x[k] = 1.0
+        _say(f"palette gemv one-hot k={k}")
+        y = m.gemv(x.to(DEV))
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), products.bf16_to_f32(wb[:, k]))
+
+
+def test_palette_matches_oracle_form_on_special_values():
+    wb = workloads.weights("small", rows=8, cols=1024).numpy().view(np.uint16).copy()
+    wb[3, :8] = [0x7FC1, 0xFF80, 0x7F80, 0x0001, 0x8001, 0x0000, 0x8000, 0xFFFF]
+    blob = opal.encode(wb)  # the oracle's bytes, handed to the device path
+    m = uw.PaletteMatrix(blob, device="cuda:0")
+    _say("palette special values")
+    out = m.decompress()
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), wb)
+
+
+def test_palette_argument_errors():
+    wb, m = pmatrix("small", None, None, None)
+    x = torch.zeros(1025, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty(1024, device=DEV)
+    with pytest.raises(uw.UwError):
+        uw.uw_palette_gemv(m.handle, x[1:], y)  # misaligned x
+    out = torch.empty(1024, 1028, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(uw.UwError):
+        uw.uw_palette_decompress(m.handle, out, 1028)  # ld not a multiple of 8
