@@ -178,7 +178,7 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
     gate_proj at 32 (one layer of the 32-layer stack), 8192x8192 at 256.
     Every candidate variant, plus torch.matmul on the uncompressed bf16
     weights; 4 rotated copies each."""
-    cases = [("down", (1, 4, 16, 64)), ("gate", (32,)), ("big", (256,))]
+    cases = [("down", (1, 4, 16, 64)), ("gate", (32, 64)), ("big", (256,))]
     names = {uw.UW_VARIANT_FUSED: "fused_valu", uw.UW_VARIANT_FUSED_MFMA: "fused_mfma",
              uw.UW_VARIANT_DECOMPRESS_GEMM: "decompress_gemm"}
     out = {}
@@ -187,6 +187,8 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
         w = workloads.weights(name)
         blob = uw.uw_encode(w)
         mats = [uw.CompressedMatrix(blob, device="cuda:0") for _ in range(4)]
+        pblob = uw.uw_palette_encode(w)
+        pmats = [uw.PaletteMatrix(pblob, device="cuda:0") for _ in range(4)]
         Wb = [torch.from_numpy(w.numpy()).to(dev).view(torch.bfloat16) for _ in range(2)]
         for B in batches:
             X = workloads.activations(cols, B, seed=workloads.SEEDS[name] + 200 + B, dtype=torch.bfloat16).to(dev)
@@ -203,6 +205,10 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
                     continue
                 rec[vn + "_us"] = round(us, 2)
                 del ws
+            # the direct-palette form on the matrix cores (larger blob, no entropy decode)
+            us, _, _ = time_graph([(lambda m=m: uw.uw_palette_gemm(m.handle, X, Y)) for m in pmats], steps, steps, torch)
+            rec["palette_mfma_us"] = round(us, 2)
+            rec["palette_blob_GBs"] = round(len(pblob) / (us * 1e-6) / 1e9, 1)
             Yb = torch.empty(B, rows, dtype=torch.bfloat16, device=dev)
             us, _, _ = time_graph([(lambda W=W: torch.matmul(X, W.t(), out=Yb)) for W in Wb], steps, steps, torch)
             rec["torch_bf16_matmul_us"] = round(us, 2)
@@ -210,9 +216,9 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
             rec["blob_GBs_best"] = round(len(blob) / (best * 1e-6) / 1e9, 1)
             out[f"{name}_{rows}x{cols}_b{B}"] = rec
             log(f"gemm {name} B={B}: {rec}")
-        for m in mats:
+        for m in mats + pmats:
             m.close()
-        del Wb, mats
+        del Wb, mats, pmats
         torch.cuda.empty_cache()
     return out
 

@@ -226,6 +226,137 @@ __global__ __launch_bounds__(kPalThreads) void palette_decompress_kernel(DevPale
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-batch product on the matrix cores: Y[b][n] = sum_k X[b][k] W[n][k].
+// A workgroup of KS waves owns 16 weight rows; wave w takes every KS-th
+// 128-column block of them.  Per block, lane (r = lane % 16, j = lane / 16)
+// loads 32 consecutive weights of row r (32 sm bytes, 16 index bytes) and, per
+// batch tile, 32 consecutive activations of batch row 16 tb + r.  K-step s of
+// the block then gives the lane weights 8s..8s+7 of its 32 as the A operand of
+// v_mfma_f32_16x16x32_bf16 (row r, k = 8 j + e) and activations 8s..8s+7 as B
+// (column r, k = 8 j + e): the matrix cores see k in a permuted order that A
+// and B share, so every load is 32 or 64 contiguous bytes per lane.  The
+// waves' partial sums meet in LDS at the end.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+constexpr int kPalMfmaMaxTB = 4;  // 64 batch rows per pass
+
+struct BlockIn {
+  uint4 sm[2];
+  uint4 idx;
+  uint4 rawe[2];
+  bool raw;
+};
+
+__device__ inline void load_block(const DevPalette& p, int64_t row, int64_t k0, BlockIn& in) {
+  const int64_t i0 = row * p.tpr * 1024 + k0;  // weight index of the lane's first weight
+  const uint4* s = reinterpret_cast<const uint4*>(p.sm + i0);
+  in.sm[0] = s[0];
+  in.sm[1] = s[1];
+  in.idx = *reinterpret_cast<const uint4*>(p.idx + i0 / 2);
+  const int64_t g = i0 >> 6, tile = i0 >> 10;
+  const uint32_t w = p.flags[g >> 5];
+  in.raw = (w >> (g & 31)) & 1u;
+  in.rawe[0] = in.rawe[1] = uint4{0u, 0u, 0u, 0u};
+  if (in.raw) {
+    const uint32_t mask16 = (w >> (16 * (tile & 1))) & 0xFFFFu;
+    const uint32_t slot = p.prefix[tile] + uint32_t(__builtin_popcount(mask16 & ((1u << (g & 15)) - 1u)));
+    const uint4* r = reinterpret_cast<const uint4*>(p.raw + int64_t(slot) * 64 + (i0 & 63));
+    in.rawe[0] = r[0];
+    in.rawe[1] = r[1];
+  }
+}
+
+// Weights 8s..8s+7 of the lane's 32 as 8 bf16.
+__device__ inline uint4 block_step_weights(const BlockIn& in, const uint32_t* table, int s) {
+  uint32_t W[4];
+  const uint32_t q = word_of(in.idx, s);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t E = table[(q >> (8 * p)) & 0xFFu];
+    const uint32_t smw = word_of(in.sm[s >> 1], 2 * (s & 1) + (p >> 1));
+    if (in.raw)
+      E = __builtin_amdgcn_perm(0u, word_of(in.rawe[s >> 1], 2 * (s & 1) + (p >> 1)),
+                                (p & 1) ? 0x0c030c02u : 0x0c010c00u) << 7;
+    const uint32_t S = __builtin_amdgcn_perm(0u, smw, (p & 1) ? 0x03030202u : 0x01010000u);
+    W[p] = (S & 0x807F807Fu) | (E & 0x7F807F80u);
+  }
+  return uint4{W[0], W[1], W[2], W[3]};
+}
+
+template <int TB, int RB, bool YBF16>
+__global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const uint16_t* __restrict__ X, int64_t ldx,
+                                                           int nb, void* __restrict__ Y, int64_t ldy) {
+  __shared__ uint32_t table[256];
+  extern __shared__ float4 red[];  // [waves][TB][64] partial sums of one 16-row block
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) table[b] = (pal_byte(p, b & 15) << 7) | (pal_byte(p, b >> 4) << 23);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ks = blockDim.x >> 6;
+  const int r = lane & 15, j = lane >> 4;
+  const int64_t base = int64_t(blockIdx.x) * 16 * RB;  // the workgroup's RB blocks of 16 rows
+  int64_t row[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) row[i] = std::min<int64_t>(p.rows - 1, base + 16 * i + r);  // rows past the end feed unstored outputs
+  const uint16_t* xr[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) xr[tb] = X + int64_t(std::min(16 * tb + r, nb - 1)) * ldx + 32 * j;
+  floatx4 acc[RB][TB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[i][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t n_blocks = p.tpr * 8;  // 128-column blocks per row
+  for (int64_t kb = wave; kb < n_blocks; kb += ks) {
+    const int64_t k0 = kb * 128 + 32 * j;
+    // the activations once per block, shared by the RB row blocks
+    uint4 xv[TB][4];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const uint4* xs = reinterpret_cast<const uint4*>(xr[tb] + kb * 128);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xv[tb][s] = xs[s];
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      BlockIn in;
+      load_block(p, row[i], k0, in);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 a = block_step_weights(in, table, s);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+          acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                               __builtin_bit_cast(bf16x8_t, xv[tb][s]), acc[i][tb], 0, 0, 0);
+      }
+    }
+  }
+  // the waves' partial sums, one 16-row block at a time
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    if (i) __syncthreads();  // the previous block's sums are read
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+      red[(wave * TB + tb) * 64 + lane] = float4{acc[i][tb][0], acc[i][tb][1], acc[i][tb][2], acc[i][tb][3]};
+    __syncthreads();
+    // output (weight row m, batch column b) sits in lane 16 (m / 4) + b % 16, element m % 4
+    for (int v = threadIdx.x; v < TB * 256; v += blockDim.x) {
+      const int tb = v >> 8, m = (v >> 4) & 15, bc = v & 15;
+      const int l = 16 * (m >> 2) + bc, e = m & 3;
+      float sum = 0.f;
+      for (int w = 0; w < ks; ++w) {
+        const float4 q = red[(w * TB + tb) * 64 + l];
+        sum += e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
+      }
+      const int64_t n = base + 16 * i + m;
+      const int b = 16 * tb + bc;
+      if (n < p.rows && b < nb) {
+        if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + n] = f32_to_bf16(sum);
+        else static_cast<float*>(Y)[b * ldy + n] = sum;
+      }
+    }
+  }
+}
+
 DevPalette dev_palette(const uw_palette* m) {
   const PaletteLayout& l = m->l;
   DevPalette p;
@@ -312,6 +443,70 @@ extern "C" int uw_palette_decompress(const uw_palette* m, uint16_t* d_out, int64
   hipLaunchKernelGGL(palette_decompress_kernel, dim3(palette_blocks(p)), dim3(kPalThreads), 0,
                      static_cast<hipStream_t>(stream), p, d_out, ld_out);
   return hip_check(hipGetLastError(), "palette_decompress_kernel launch");
+}
+
+// Workgroup shape: RB blocks of 16 rows share each activation load (fewer
+// re-reads of X from cache as the batch grows), and KS waves split K (at most
+// 8: a 1024-column multiple splits into 8 blocks of 128).  The largest RB
+// that still leaves about 1792 waves, then the fewest KS that reach it.
+void palette_mfma_shape(int64_t rows, int* rb, int* ks) {
+  const int64_t blocks16 = (rows + 15) / 16;
+  *rb = 1;
+  for (int c : {4, 2})
+    if ((blocks16 + c - 1) / c * 8 >= 1792) {
+      *rb = c;
+      break;
+    }
+  const int64_t wgs = (blocks16 + *rb - 1) / *rb;
+  *ks = 1;
+  while (*ks < 8 && wgs * *ks < 1792) *ks *= 2;
+}
+
+template <int TB, int RB>
+int launch_palette_mfma_rb(const DevPalette& p, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt,
+                           int ks, hipStream_t s) {
+  const size_t lds = size_t(ks) * TB * 64 * sizeof(float4);
+  const dim3 grid(unsigned((p.rows + 16 * RB - 1) / (16 * RB))), block(64 * ks);
+  if (yt == UW_BF16) hipLaunchKernelGGL((palette_mfma_kernel<TB, RB, true>), grid, block, lds, s, p, X, ldx, nb, Y, ldy);
+  else hipLaunchKernelGGL((palette_mfma_kernel<TB, RB, false>), grid, block, lds, s, p, X, ldx, nb, Y, ldy);
+  return hip_check(hipGetLastError(), "palette_mfma_kernel launch");
+}
+
+template <int TB>
+int launch_palette_mfma(const DevPalette& p, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt,
+                        hipStream_t s) {
+  int rb, ks;
+  palette_mfma_shape(p.rows, &rb, &ks);
+  if (rb == 4) return launch_palette_mfma_rb<TB, 4>(p, X, ldx, nb, Y, ldy, yt, ks, s);
+  if (rb == 2) return launch_palette_mfma_rb<TB, 2>(p, X, ldx, nb, Y, ldy, yt, ks, s);
+  return launch_palette_mfma_rb<TB, 1>(p, X, ldx, nb, Y, ldy, yt, ks, s);
+}
+
+extern "C" int uw_palette_gemm(const uw_palette* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y,
+                               int64_t ldy, int yt, void* stream) {
+  if (int rc = check_palette(m, "uw_palette_gemm")) return rc;
+  if (xt != UW_BF16) return fail(UW_ERR_UNSUPPORTED, "uw_palette_gemm: X must be bf16 (the matrix cores take bf16)");
+  if (yt != UW_F32 && yt != UW_BF16) return fail(UW_ERR_INVALID, "uw_palette_gemm: Y must be UW_F32 or UW_BF16");
+  if (batch < 1 || !d_X || !d_Y) return fail(UW_ERR_INVALID, "uw_palette_gemm: batch >= 1 and non-null X, Y");
+  if (!aligned_to(d_X, 16) || ldx < m->l.cols || ldx % 8)
+    return fail(UW_ERR_INVALID, "uw_palette_gemm: X 16-byte aligned, ldx >= cols and a multiple of 8");
+  if (ldy < m->l.rows || !aligned_to(d_Y, yt == UW_F32 ? 4 : 2))
+    return fail(UW_ERR_INVALID, "uw_palette_gemm: ldy >= rows and Y aligned to its element");
+  const DevPalette p = dev_palette(m);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* X = static_cast<const uint16_t*>(d_X);
+  const size_t ysz = yt == UW_F32 ? 4 : 2;
+  for (int64_t b0 = 0; b0 < batch; b0 += 16 * kPalMfmaMaxTB) {
+    const int nb = int(std::min<int64_t>(batch - b0, 16 * kPalMfmaMaxTB));
+    const uint16_t* Xp = X + b0 * ldx;
+    void* Yp = static_cast<char*>(d_Y) + size_t(b0) * size_t(ldy) * ysz;
+    int rc;
+    if (nb <= 16) rc = launch_palette_mfma<1>(p, Xp, ldx, nb, Yp, ldy, yt, s);
+    else if (nb <= 32) rc = launch_palette_mfma<2>(p, Xp, ldx, nb, Yp, ldy, yt, s);
+    else rc = launch_palette_mfma<4>(p, Xp, ldx, nb, Yp, ldy, yt, s);
+    if (rc) return rc;
+  }
+  return UW_OK;
 }
 
 extern "C" int uw_palette_info(const void* blob, size_t n, int64_t* rows, int64_t* cols, int64_t* n_raw) {

@@ -87,6 +87,7 @@ def _load() -> ctypes.CDLL:
         "uw_palette_destroy": (None, [P]),
         "uw_palette_gemv": (I, [P, P, I, P, I, P]),
         "uw_palette_decompress": (I, [P, P, I64, P]),
+        "uw_palette_gemm": (I, [P, P, I64, I64, I, P, I64, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -293,6 +294,12 @@ def uw_palette_gemv(handle: int, x, y, stream=None) -> None:
            "uw_palette_gemv")
 
 
+def uw_palette_gemm(handle: int, X, Y, stream=None) -> None:
+    batch = X.shape[0]
+    _check(_lib.uw_palette_gemm(handle, X.data_ptr(), batch, X.stride(0), _dtype_code(X), Y.data_ptr(), Y.stride(0),
+                                _dtype_code(Y), _stream(stream)), "uw_palette_gemm")
+
+
 def uw_palette_decompress(handle: int, d_out, ld_out: int | None = None, stream=None) -> None:
     if ld_out is None:
         ld_out = d_out.stride(0)
@@ -394,6 +401,13 @@ class PaletteMatrix:
             y = torch.empty(self.rows, dtype=out_dtype or torch.float32, device=x.device)
         uw_palette_gemv(self.handle, x, y, stream)
         return y
+
+    def gemm(self, X, Y=None, out_dtype=None, stream=None):
+        import torch
+        if Y is None:
+            Y = torch.empty(X.shape[0], self.rows, dtype=out_dtype or torch.float32, device=X.device)
+        uw_palette_gemm(self.handle, X, Y, stream)
+        return Y
 
     def close(self) -> None:
         if getattr(self, "handle", None):

@@ -314,6 +314,19 @@ void uw_palette_destroy(uw_palette* m);
 int uw_palette_gemv(const uw_palette* m, const void* d_x, int xt, void* d_y, int yt, void* stream);
 
 /*
+ * uw_palette_gemm (device) - Y = X W^T over the UWP1 form on the matrix
+ * cores (v_mfma_f32_16x16x32_bf16), 64 batch rows per pass; the indices are
+ * rebuilt into bf16 in registers, no preprocessing pass (the pages expect this
+ * pipeline to pay off at larger batches).
+ *   d_X  device bf16 [batch, ldx], 16-byte aligned, ldx >= cols, multiple of 8.
+ *   d_Y  device [batch, ldy] of yt (UW_F32 or UW_BF16), ldy >= rows.
+ * fp32 accumulation.
+ * Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED (X not bf16), UW_ERR_HIP.
+ */
+int uw_palette_gemm(const uw_palette* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y,
+                    int64_t ldy, int yt, void* stream);
+
+/*
  * uw_palette_decompress (device) - the original bf16 bits of a UWP1 matrix,
  * W[r][c] at d_out[r*ld_out + c]; d_out 16-byte aligned, ld_out >= cols and a
  * multiple of 8.  Bit-exact.

@@ -121,3 +121,49 @@ def test_palette_argument_errors():
     out = torch.empty(1024, 1028, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(uw.UwError):
         uw.uw_palette_decompress(m.handle, out, 1028)  # ld not a multiple of 8
+
+
+# Matrix-core product over the palette form: 1, 2 and 4 blocks of 16 rows per
+# workgroup and 4 or 8 waves splitting K (both set by the row count), one to
+# four batch tiles per pass, several passes, ragged batches and row counts,
+# raw groups, every group raw.
+GEMM_CASES = [
+    ("gate", None, None, None, [16, 32, 64]),   # 4 row blocks per workgroup, 8 waves split K
+    ("down", None, None, None, [4, 64, 100]),  # 1 row block per workgroup, 8 waves; 100 = two passes
+    ("gate", 28672, 1024, 31, [3]),            # 4 row blocks per workgroup, 4 waves split K
+    ("gate", 14344, 1024, 42, [9, 40]),        # 4 row blocks per workgroup, the last one partial
+    ("big", 8192, 1024, 41, [20]),             # 2 row blocks per workgroup
+    ("gate", 37, 3072, 21, [1, 5, 17]),        # a partial row block
+    ("randbits", 48, 2048, None, [7]),         # every group raw
+    ("down", 1, 1024, 22, [2]),                # one row
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}")
+def test_palette_gemm(case):
+    name, rows, cols, seed, batches = case
+    wb, m = pmatrix(name, rows, cols, seed)
+    for batch in batches:
+        X = workloads.activations(wb.shape[1], batch, seed=900 + batch, dtype=torch.bfloat16)
+        ref = products.gemm_f64(wb, X.float().numpy())
+        _say(f"palette gemm {name} {wb.shape} batch={batch}")
+        Y = m.gemm(X.to(DEV))
+        Yb = m.gemm(X.to(DEV), out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        check_f32(Y, ref, f"palette gemm {name} b={batch}")
+        check_bf16(Yb, ref, f"palette gemm bf16 {name} b={batch}")
+
+
+def test_palette_gemm_strided_and_errors():
+    wb, m = pmatrix("gate", 37, 3072, 21)
+    X = workloads.activations(3072, 9, seed=77, dtype=torch.bfloat16)
+    Xs = torch.zeros(9, 3072 + 64, dtype=torch.bfloat16)
+    Xs[:, :3072] = X
+    Ys = torch.full((9, 37 + 11), 7.0, device=DEV)
+    _say("palette gemm strided")
+    uw.uw_palette_gemm(m.handle, Xs.to(DEV), Ys)
+    torch.cuda.synchronize()
+    check_f32(Ys[:, :37], products.gemm_f64(wb, X.float().numpy()), "palette gemm strided")
+    assert (Ys[:, 37:].cpu() == 7.0).all()
+    with pytest.raises(uw.UwError):
+        uw.uw_palette_gemm(m.handle, X.float().to(DEV), torch.empty(9, 37, device=DEV))  # fp32 X
