@@ -460,6 +460,16 @@ def main():
         extras["read_probe_GBs"] = round(probe, 1)
         extras["fused_frac_of_read_probe"] = round(achieved / probe, 4)
         del buf
+        # the same probe at the blob's size, on rotated copies and timed like
+        # the fused step: the streaming ceiling for a read of this length
+        nbytes = (info["total_bytes"] + 255) // 256 * 256
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(ROTATE)]
+        us_ps, _, _ = time_graph([(lambda b=b: uw.uw_read_probe(b, sink)) for b in bufs], args.steps, args.warmup, torch)
+        probe_same = nbytes / (us_ps * 1e-6) / 1e9
+        extras["read_probe_blob_size"] = {"bytes": nbytes, "us": round(us_ps, 3), "GBs": round(probe_same, 1),
+                                          "fused_frac": round(achieved / probe_same, 4)}
+        log(f"read probe at the blob size: {extras['read_probe_blob_size']}")
+        del bufs
         # decompress-to-HBM alternative (reads the blob, writes bf16)
         out_w = [torch.empty(rows, cols, dtype=torch.bfloat16, device=dev) for _ in range(2)]
         log("timing decompress")
