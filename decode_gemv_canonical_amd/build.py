@@ -1,6 +1,9 @@
 """Build libuw.so in-tree: hipcc for the gfx950 kernels, g++ for the host C++.
 
-    python -m decode_gemv_canonical_amd.build
+    python decode_gemv_canonical_amd/build.py
+
+(run as a file: importing the package would first load the library being
+rebuilt)
 """
 from __future__ import annotations
 

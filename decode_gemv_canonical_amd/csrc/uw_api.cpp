@@ -308,6 +308,15 @@ size_t uw_workspace_size(const uw_matrix* m, int64_t batch, int variant) {
   return decompress_ws_bytes(m);
 }
 
+int uw_set_plan(uw_matrix* m, const uw_plan* plan) {
+  if (!m || !plan) return fail(UW_ERR_INVALID, "uw_set_plan: null pointer");
+  if (plan->batch < 1 || plan->variant <= UW_VARIANT_AUTO || plan->variant >= UW_VARIANT_COUNT)
+    return fail(UW_ERR_INVALID, "uw_set_plan: batch >= 1 and a concrete variant");
+  std::lock_guard<std::mutex> lk(m->mu);
+  m->plans[plan->batch] = *plan;
+  return UW_OK;
+}
+
 int uw_get_plan(const uw_matrix* m, int64_t batch, uw_plan* out) {
   if (!m || !out) return fail(UW_ERR_INVALID, "uw_get_plan: null pointer");
   std::lock_guard<std::mutex> lk(m->mu);

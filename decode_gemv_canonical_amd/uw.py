@@ -60,7 +60,7 @@ class uw_plan(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m decode_gemv_canonical_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python decode_gemv_canonical_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     sig = {
@@ -78,6 +78,7 @@ def _load() -> ctypes.CDLL:
         "uw_autotune": (I, [P, I64, P, SZ, P, ctypes.POINTER(uw_plan)]),
         "uw_autotune_scratch_size": (SZ, [P, I64]),
         "uw_get_plan": (I, [P, I64, ctypes.POINTER(uw_plan)]),
+        "uw_set_plan": (I, [P, ctypes.POINTER(uw_plan)]),
         "uw_bf16_gemm": (I, [P, I64, I64, I64, P, I64, I64, I, P, I64, I, P]),
         "uw_read_probe": (I, [P, SZ, P, P]),
         "uw_read_probe_sink_size": (SZ, []),
@@ -237,6 +238,16 @@ def uw_get_plan(handle: int, batch: int) -> dict:
     p = uw_plan()
     _check(_lib.uw_get_plan(handle, batch, ctypes.byref(p)), "uw_get_plan")
     return _plan_dict(p)
+
+
+def uw_set_plan(handle: int, batch: int, variant: int, time_us: float = -1.0) -> None:
+    p = uw_plan()
+    p.batch = batch
+    p.variant = variant
+    p.time_us = time_us
+    for i in range(UW_VARIANT_COUNT):
+        p.candidate_us[i] = -1.0
+    _check(_lib.uw_set_plan(handle, ctypes.byref(p)), "uw_set_plan")
 
 
 def uw_bf16_gemm(W, X, Y, stream=None) -> None:

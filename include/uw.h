@@ -239,6 +239,17 @@ size_t uw_autotune_scratch_size(const uw_matrix* m, int64_t batch);
 int uw_get_plan(const uw_matrix* m, int64_t batch, uw_plan* out);
 
 /*
+ * uw_set_plan (host) - store a plan for plan->batch (replacing any), so AUTO
+ * follows a choice made elsewhere: a model-level tuning pass or a plan file
+ * from an earlier run (autotuner paragraph: the tuner's result is a per-model
+ * configuration file the runtime reads).  Only batch and variant are used by
+ * the dispatch; the times are kept for reporting.
+ * Errors: UW_ERR_INVALID (null, batch < 1, variant not FUSED, DECOMPRESS_GEMM
+ *         or FUSED_MFMA).
+ */
+int uw_set_plan(uw_matrix* m, const uw_plan* plan);
+
+/*
  * uw_bf16_gemm (device) - Y = X W^T over an uncompressed bf16 matrix: the
  * multiply of the "full decode" pipeline and the uncompressed comparator.
  *   d_W  device, rows x cols bf16, row stride ldw >= cols (multiple of 8),
