@@ -238,7 +238,7 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
 
     from oracle import products
     H, F = workloads.SHAPES["gate"][1], workloads.SHAPES["gate"][0]
-    layers, bfw, blob_bytes = [], [], 0
+    layers, bfw, blob_bytes, pal_bytes = [], [], 0, 0
     t0 = time.perf_counter()
     for li in range(workloads.STACK_LAYERS):
         L = workloads.stack_layer(li)
@@ -248,10 +248,15 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
             blob_bytes += len(b)
             mats[k] = uw.CompressedMatrix(b, device="cuda:0")
         mats["gate_up"] = uw.CompressedMatrix(uw.uw_encode(torch.cat([L["gate"], L["up"]])), device="cuda:0")
+        for k, v in L.items():
+            pb = uw.uw_palette_encode(v)
+            pal_bytes += len(pb)
+            mats["pal_" + k] = uw.PaletteMatrix(pb, device="cuda:0")
         layers.append(mats)
         bfw.append({k: v.to(dev).view(torch.bfloat16) for k, v in L.items()})
         log(f"stack layer {li} encoded and uploaded ({time.perf_counter() - t0:.0f} s)")
     out = {"layers": workloads.STACK_LAYERS, "matrices": 3 * workloads.STACK_LAYERS, "blob_bytes": blob_bytes,
+           "palette_bytes": pal_bytes,
            "bf16_bytes": 3 * workloads.STACK_LAYERS * 2 * H * F, "prep_s": round(time.perf_counter() - t0, 1)}
     rng = np.random.default_rng(7)
     for B in (1, 32):
@@ -326,16 +331,49 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
             worst_gu = max(worst_gu, products.rel_error_floored(got, ref))
             del wcat
         us_f, _, _ = time_graph([lambda: [fused_calls(li) for li in range(n)]], reps, reps, torch)
+
+        # the same 96 products over the direct-palette form (GEMV at batch 1,
+        # matrix-core GEMM above), on the inputs of the eager token
+        gp = [torch.empty(B, F, dtype=torch.float32, device=dev) for _ in range(n)]
+        up_ = [torch.empty(B, F, dtype=torch.float32, device=dev) for _ in range(n)]
+        dp = [torch.empty(B, H, dtype=torch.float32, device=dev) for _ in range(n)]
+
+        def pal(m, X, Y):
+            if B == 1:
+                uw.uw_palette_gemv(m.handle, X[0], Y[0])
+            else:
+                uw.uw_palette_gemm(m.handle, X, Y)
+
+        def palette_calls(li):
+            m = layers[li]
+            pal(m["pal_gate"], xs[li], gp[li])
+            pal(m["pal_up"], xs[li], up_[li])
+            pal(m["pal_down"], h[li], dp[li])
+
+        for li in range(n):
+            palette_calls(li)
+        torch.cuda.synchronize()
+        worst_p = 0.0
+        for li in range(n):
+            for k, inp, res, r in (("gate", xs[li], gp[li], F), ("up", xs[li], up_[li], F), ("down", h[li], dp[li], H)):
+                rows = rng.choice(r, size=64, replace=False)
+                wb = bfw[li][k][torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+                ref = products.gemm_f64(wb, inp.float().cpu().numpy())
+                got = res[:, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+                worst_p = max(worst_p, products.rel_error_floored(got, ref))
+        us_p, _, _ = time_graph([lambda: [palette_calls(li) for li in range(n)]], reps, reps, torch)
         out[f"b{B}"] = {"matrix_ms_per_token": round(us_m / 1e3, 4), "elementwise_ms_per_token": round(us_e / 1e3, 4),
                         "gate_up_fused_matrix_ms_per_token": round(us_f / 1e3, 4),
                         "gate_up_fused_parity_max_rel_err_sampled": worst_gu,
+                        "palette_matrix_ms_per_token": round(us_p / 1e3, 4),
+                        "palette_parity_max_rel_err_sampled": worst_p,
                         "bf16_matmul_ms_per_token": round(us_b / 1e3, 4),
                         "speedup_vs_bf16": round(us_b / us_m, 4),
                         "effective_weight_GBs": round(out["bf16_bytes"] / (us_m * 1e-6) / 1e9, 1),
                         "compressed_GBs": round(blob_bytes / (us_m * 1e-6) / 1e9, 1),
                         "parity_max_rel_err_sampled": worst, "parity_ok": worst <= PARITY_TOL}
         log(f"stack B={B}: {out[f'b{B}']}")
-        del xs, g, u, h, d, ws, gb, db, gu
+        del xs, g, u, h, d, ws, gb, db, gu, gp, up_, dp
         torch.cuda.empty_cache()
     return out
 
