@@ -1,12 +1,13 @@
-// Direct-palette pipeline on gfx950: the batch-1 product and the decode of
-// the UWP1 form (4-bit palette index + sign+mantissa byte per weight, raw
-// 64-weight groups verbatim; layout in uw_palette.cpp).
+// Direct-palette pipeline on gfx950: the batch-1 product, the small-batch
+// product on the matrix cores and the decode of the UWP1 form (4-bit palette
+// index + sign+mantissa byte per weight, raw 64-weight groups verbatim;
+// layout in uw_palette.cpp).
 //
 // "Unweight: how we compressed an LLM 22% without sacrificing quality",
 // section on the four execution pipelines: the direct palette skips
 // preprocessing and the matmul rebuilds bf16 from the indices on the fly.
-// Here there is no entropy decode at all, so the kernels are plain streams:
-// lane l of a wave owns 16 consecutive weights of each 1024-weight tile, reads
+// Here there is no entropy decode at all, so the kernels are plain streams.
+// GEMV and decode: lane l of a wave owns 16 consecutive weights of each 1024-weight tile, reads
 // their 16 sign+mantissa bytes and 8 index bytes with one 16-byte and one
 // 8-byte load (coalesced across the wave), looks up two exponents per index
 // byte in a 256-entry LDS table, and multiplies with the 16 matching x values
@@ -284,6 +285,34 @@ __device__ inline uint4 block_step_weights(const BlockIn& in, const uint32_t* ta
   return uint4{W[0], W[1], W[2], W[3]};
 }
 
+// The loads of one 128-column block: the activations of every batch tile and
+// the lane's 32 weights of row `row`.
+template <int TB>
+__device__ __forceinline__ void load_mfma_block(const DevPalette& p, const uint16_t* const (&xr)[TB], int64_t row,
+                                                int64_t kb, int j, uint4 (&xv)[TB][4], BlockIn& in) {
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const uint4* xs = reinterpret_cast<const uint4*>(xr[tb] + kb * 128);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xv[tb][s] = xs[s];
+  }
+  load_block(p, row, kb * 128 + 32 * j, in);
+}
+
+// The four k-steps of a block for every batch tile.
+template <int TB>
+__device__ __forceinline__ void mfma_block(const BlockIn& in, const uint4 (&xv)[TB][4], const uint32_t* table,
+                                           floatx4 (&acc)[TB]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint4 a = block_step_weights(in, table, s);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                        __builtin_bit_cast(bf16x8_t, xv[tb][s]), acc[tb], 0, 0, 0);
+  }
+}
+
 template <int TB, int RB, bool YBF16>
 __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const uint16_t* __restrict__ X, int64_t ldx,
                                                            int nb, void* __restrict__ Y, int64_t ldy) {
@@ -306,6 +335,22 @@ __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const u
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[i][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int64_t n_blocks = p.tpr * 8;  // 128-column blocks per row
+  if constexpr (RB == 1 && TB <= 2) {
+    // one row block, up to 32 batch rows: two register sets (four batch
+    // tiles would not fit), so the next block's loads are in flight while
+    // this block's products run
+    uint4 xa[TB][4], xb[TB][4];
+    BlockIn wa, wb;
+    int64_t kb = wave;
+    if (kb < n_blocks) load_mfma_block<TB>(p, xr, row[0], kb, j, xa, wa);
+    for (; kb < n_blocks; kb += 2 * ks) {
+      if (kb + ks < n_blocks) load_mfma_block<TB>(p, xr, row[0], kb + ks, j, xb, wb);
+      mfma_block<TB>(wa, xa, table, acc[0]);
+      if (kb + ks >= n_blocks) break;
+      if (kb + 2 * ks < n_blocks) load_mfma_block<TB>(p, xr, row[0], kb + 2 * ks, j, xa, wa);
+      mfma_block<TB>(wb, xb, table, acc[0]);
+    }
+  } else {
   for (int64_t kb = wave; kb < n_blocks; kb += ks) {
     const int64_t k0 = kb * 128 + 32 * j;
     // the activations once per block, shared by the RB row blocks
@@ -329,6 +374,7 @@ __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const u
                                                                __builtin_bit_cast(bf16x8_t, xv[tb][s]), acc[i][tb], 0, 0, 0);
       }
     }
+  }
   }
   // the waves' partial sums, one 16-row block at a time
 #pragma unroll
