@@ -205,6 +205,13 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
                     continue
                 rec[vn + "_us"] = round(us, 2)
                 del ws
+            # the exponent-only pipeline: exponent bytes to HBM, then the
+            # reconstructive product on the matrix cores
+            wse = torch.empty(uw.uw_exponent_ws_size(mats[0].handle, B), dtype=torch.uint8, device=dev)
+            us, _, _ = time_graph([(lambda m=m: uw.uw_exponent_gemm(m.handle, X, Y, wse)) for m in mats], steps, steps,
+                                  torch)
+            rec["exponent_gemm_us"] = round(us, 2)
+            del wse
             # the direct-palette form on the matrix cores (larger blob, no entropy decode)
             us, _, _ = time_graph([(lambda m=m: uw.uw_palette_gemm(m.handle, X, Y)) for m in pmats], steps, steps, torch)
             rec["palette_mfma_us"] = round(us, 2)
@@ -212,7 +219,7 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
             Yb = torch.empty(B, rows, dtype=torch.bfloat16, device=dev)
             us, _, _ = time_graph([(lambda W=W: torch.matmul(X, W.t(), out=Yb)) for W in Wb], steps, steps, torch)
             rec["torch_bf16_matmul_us"] = round(us, 2)
-            best = min(v for k, v in rec.items() if k.startswith(("fused", "decompress")))
+            best = min(v for k, v in rec.items() if k.startswith(("fused", "decompress", "exponent")))
             rec["blob_GBs_best"] = round(len(blob) / (best * 1e-6) / 1e9, 1)
             out[f"{name}_{rows}x{cols}_b{B}"] = rec
             log(f"gemm {name} B={B}: {rec}")

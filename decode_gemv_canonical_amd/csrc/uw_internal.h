@@ -122,6 +122,8 @@ namespace uw {
 
 // Launchers (uw_kernels.hip).  Shapes and pointers are checked by the caller.
 int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* stream);
+// Exponent bytes (R*C, the sm section's tile order); flat walk, not plain.
+int launch_decode_exponents(const uw_matrix* m, uint8_t* out, void* stream);
 int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, int xt, void* Y,
                  int64_t ldy, int yt, void* stream);
 bool fused_supported(const uw_matrix* m, int xt, std::string* why);

@@ -37,6 +37,7 @@
 #include <algorithm>
 #include <cstring>
 #include <string>
+#include <type_traits>
 
 #include "uw_device.h"
 
@@ -793,7 +794,38 @@ struct DecompressSink {
   }
 };
 
-template <bool PAIR, int NQ, bool FLAT, int RS>
+// Exponent bytes only (the exponent-only pipeline, flat walk): tile T's
+// exponents go to out + 1024 T in the order of the sign+mantissa section
+// (lane l's 16 bytes at 16 l, byte jj = weight l of group jj), one 16-byte
+// store per lane per tile.
+struct ExpSink {
+  int64_t cols;
+  uint8_t* out;
+  int lane;
+  uint8_t* dst = nullptr;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  __device__ void unit_begin(int) {}
+  __device__ void unit_end() {}
+  __device__ void block_begin(int) {}
+  __device__ void row_end() {}
+  __device__ void tile_begin(int64_t row0, int c0) {
+    dst = out + row0 * cols + int64_t(c0) * 64 + 16 * lane;
+    w[0] = w[1] = w[2] = w[3] = 0u;
+  }
+  __device__ void pair(int k, uint32_t D) {
+    w[k >> 1] |= (((D >> 7) & 0xFFu) | (((D >> 23) & 0xFFu) << 8)) << (16 * (k & 1));
+  }
+  __device__ void single(int, int64_t, int, uint32_t) {}  // flat-walk tiles are always whole
+  __device__ void tile_end(int, int) { *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]}; }
+};
+
+template <bool EXP, bool FLAT>
+__device__ inline auto make_decompress_sink(const DevMatrix& d, uint16_t* out, int64_t ld_out, uint32_t tile, int lane) {
+  if constexpr (EXP) return ExpSink{d.cols, reinterpret_cast<uint8_t*>(out), lane};
+  else return DecompressSink<FLAT>{d.cols, d.G, out, ld_out, tile, lane, 0, 0};
+}
+
+template <bool PAIR, int NQ, bool FLAT, int RS, bool EXP = false>
 __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t* __restrict__ out, int64_t ld_out) {
   extern __shared__ uint32_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -816,7 +848,8 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   }
   if (n_tab) wait_tables<RS, NQ>(issued);
   lds_barrier();
-  DecompressSink<FLAT> sink{d.cols, d.G, out, ld_out, tile, lane, 0, 0};
+  using Sink = std::conditional_t<EXP, ExpSink, DecompressSink<FLAT>>;
+  Sink sink = make_decompress_sink<EXP, FLAT>(d, out, ld_out, tile, lane);
   for (int u = u_first; u < n_items; u += gridDim.x * waves) {
     // the two 16-byte stores per tile only make the ring waits stricter
     if (FLAT) {
@@ -1525,6 +1558,30 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
   allow_full_lds(kern);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, out, ld_out);
   return hip_check(hipGetLastError(), "decompress_kernel launch");
+}
+
+// Exponent bytes of every weight, in the sign+mantissa section's tile order
+// (flat walk only; the caller checks).
+int launch_decode_exponents(const uw_matrix* m, uint8_t* out, void* stream) {
+  const DevMatrix& d = m->dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t fixed = tables_bytes();
+  const int items = d.n_items;
+  const int rs = flat_ring_depth(items, fixed, d.slot_bytes, 0, 16);
+  const size_t per_wave = ring_bytes(rs, d.slot_bytes);
+  const int waves = pick_waves(items, fixed, per_wave);
+  const size_t lds = fixed + per_wave * waves;
+  const int grid = int(std::max<int64_t>(1, (int64_t(items) + waves - 1) / waves));
+  auto pick = [&](auto pair) {
+    constexpr bool P = decltype(pair)::value;
+    return rs == kRS ? (d.nq == 2 ? decompress_kernel<P, 2, true, kRS, true> : decompress_kernel<P, 4, true, kRS, true>)
+                     : (d.nq == 2 ? decompress_kernel<P, 2, true, kRSLow, true>
+                                  : decompress_kernel<P, 4, true, kRSLow, true>);
+  };
+  auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
+  allow_full_lds(kern);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, reinterpret_cast<uint16_t*>(out), int64_t(0));
+  return hip_check(hipGetLastError(), "decompress_kernel (exponents) launch");
 }
 
 int fused_rows_per_pass(const uw_matrix* m, int64_t batch, int xt) {

@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
         "uw_autotune_scratch_size": (SZ, [P, I64]),
         "uw_get_plan": (I, [P, I64, ctypes.POINTER(uw_plan)]),
         "uw_set_plan": (I, [P, ctypes.POINTER(uw_plan)]),
+        "uw_exponent_gemm": (I, [P, P, I64, I64, I, P, I64, I, P, SZ, P]),
+        "uw_exponent_ws_size": (SZ, [P, I64]),
         "uw_bf16_gemm": (I, [P, I64, I64, I64, P, I64, I64, I, P, I64, I, P]),
         "uw_read_probe": (I, [P, SZ, P, P]),
         "uw_read_probe_sink_size": (SZ, []),
@@ -238,6 +240,16 @@ def uw_get_plan(handle: int, batch: int) -> dict:
     p = uw_plan()
     _check(_lib.uw_get_plan(handle, batch, ctypes.byref(p)), "uw_get_plan")
     return _plan_dict(p)
+
+
+def uw_exponent_ws_size(handle: int, batch: int) -> int:
+    return _lib.uw_exponent_ws_size(handle, batch)
+
+
+def uw_exponent_gemm(handle: int, X, Y, ws, stream=None) -> None:
+    _check(_lib.uw_exponent_gemm(handle, X.data_ptr(), X.shape[0], X.stride(0), _dtype_code(X), Y.data_ptr(),
+                                 Y.stride(0), _dtype_code(Y), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "uw_exponent_gemm")
 
 
 def uw_set_plan(handle: int, batch: int, variant: int, time_us: float = -1.0) -> None:

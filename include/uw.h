@@ -276,6 +276,25 @@ int uw_read_probe(const void* d_src, size_t bytes, void* d_sink, void* stream);
 size_t uw_read_probe_sink_size(void);
 
 /*
+ * uw_exponent_gemm (device) - the exponent-only pipeline (section on the four
+ * execution pipelines: decode only the exponent bytes, half the preprocessing
+ * traffic, then a reconstructive matmul): the exponents of every weight are
+ * decoded into the workspace (1 byte per weight, in the order of the blob's
+ * sign+mantissa section), X is permuted into that order, and
+ * v_mfma_f32_16x16x32_bf16 multiplies bf16 rebuilt from the two byte planes,
+ * 64 batch rows per pass.  Needs a coded blob whose tiles never cross a row
+ * (G and cols/64 multiples of 16).
+ *   d_X   device bf16 [batch, ldx], ldx >= cols.   d_Y as for uw_gemm_fused.
+ *   d_ws  device, 256-byte aligned, >= uw_exponent_ws_size(m, batch) bytes.
+ * Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED (plain blob, tiles crossing rows,
+ *         X not bf16), UW_ERR_HIP.
+ */
+int uw_exponent_gemm(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y,
+                     int64_t ldy, int yt, void* d_ws, size_t ws_bytes, void* stream);
+/* Workspace bytes of uw_exponent_gemm: R*C (256-rounded) + min(batch, 64)*C*2; 0 for a null handle. */
+size_t uw_exponent_ws_size(const uw_matrix* m, int64_t batch);
+
+/*
  * Direct-palette pipeline (section on the four execution pipelines: the
  * weights become 4-bit palette indices at load time and the matmul rebuilds
  * bf16 from them with no preprocessing pass).  Form UWP1: per weight one

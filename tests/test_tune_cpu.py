@@ -56,3 +56,9 @@ def test_set_plan_argument_checks_without_a_gpu():
     p.batch, p.variant = 4, M
     assert lib.uw_set_plan(None, None) == uw.UW_ERR_INVALID
     assert lib.uw_set_plan(None, p) == uw.UW_ERR_INVALID
+
+
+def test_exponent_entry_points_reject_null_without_a_gpu():
+    lib = uw.library()
+    assert lib.uw_exponent_ws_size(None, 4) == 0
+    assert lib.uw_exponent_gemm(None, None, 1, 0, 1, None, 0, 0, None, 0, None) == uw.UW_ERR_INVALID
