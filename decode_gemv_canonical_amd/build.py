@@ -1,4 +1,5 @@
-"""Build libuw.so in-tree: hipcc for the gfx950 kernels, g++ for the host C++.
+"""Build libuw.so in-tree: hipcc for the gfx950 kernels, g++ for the host C++ (no
+library beyond the HIP runtime is linked).
 
     python decode_gemv_canonical_amd/build.py
 
@@ -60,7 +61,7 @@ def build(verbose: bool = False) -> str:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
     _run([os.path.join(ROCM, "bin", "hipcc"), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs,
-          f"-L{ROCM}/lib", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib", "-lpthread"], verbose)
+          "-lpthread"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,14 +1,19 @@
-// The C-ABI: handles, argument checks, variant dispatch and the autotuner.
+// The C-ABI: handles, argument checks, variant dispatch, the autotuner and
+// its plan files.
 //
 // "Unweight: how we compressed an LLM 22% without sacrificing quality": the
 // runtime picks an execution strategy per weight matrix and batch size from
 // measurements on the target hardware, not from heuristics (paragraph on the
-// four pipelines; paragraph on the autotuner).  Here the candidates are the
-// fused decode+product kernel and decompress-to-HBM followed by the bf16
-// product; uw_autotune times both with HIP events and stores the winner.
+// four pipelines; paragraph on the autotuner, whose result is a per-model
+// configuration file).  Here the candidates are the fused decode+product on
+// the vector ALU and on the matrix cores, decompress-to-HBM followed by the
+// bf16 product, and an attached direct-palette copy, each with its knobs;
+// uw_autotune times them cold with HIP events and stores the winner.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
 #include <string>
@@ -58,6 +63,89 @@ size_t decompress_ws_bytes(const uw_matrix* m) {
   return (size_t(m->h.rows) * size_t(m->h.cols) * 2 + 255) / 256 * 256;
 }
 
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+constexpr size_t kFlushBytes = size_t(512) << 20;  // twice the 256 MiB last-level cache
+
+// Whether a (variant, knob) can run a call with these operands, and why not.
+struct CallShape {
+  const void* X;
+  int64_t batch, ldx;
+  int xt;
+  const void* ws;
+  size_t ws_bytes;
+};
+
+bool knob_valid(int variant, int knob) {
+  switch (variant) {
+    case UW_VARIANT_FUSED: return knob == 0 || knob == 2 || knob == 4;
+    case UW_VARIANT_FUSED_MFMA: return knob == 0 || (knob >= 8 && knob <= 16);
+    case UW_VARIANT_DECOMPRESS_GEMM: {
+      const int shape = knob & 15, ks = knob >> 4;
+      return knob >= 0 && shape < mfma_gemm_shape_count() && (ks == 0 || ks == 1 || ks == 2 || ks == 4 || ks == 8);
+    }
+    case UW_VARIANT_PALETTE: return knob == 0;
+    default: return false;
+  }
+}
+
+bool runnable(const uw_matrix* m, int variant, int knob, const CallShape& c, std::string* why) {
+  const int64_t batch = c.batch;
+  switch (variant) {
+    case UW_VARIANT_FUSED:
+      if (!fused_supported(m, c.xt, why)) return false;
+      if (m->h.plain() && !bf16_gemm_supported(m->h.cols, batch, c.xt, why)) return false;
+      if (knob && !m->h.plain() && !m->dev.flat) {
+        if (why) *why = "the ring-depth knob needs the flat walk (G and cols/64 multiples of 16)";
+        return false;
+      }
+      return true;
+    case UW_VARIANT_FUSED_MFMA:
+      if (!fused_mfma_supported(m, c.xt, why, knob)) return false;
+      if (!aligned(c.X, 16) || c.ldx % 8) {
+        if (why) *why = "X must be 16-byte aligned with ldx a multiple of 8";
+        return false;
+      }
+      return true;
+    case UW_VARIANT_DECOMPRESS_GEMM:
+      if (!c.ws || c.ws_bytes < decompress_ws_bytes(m) || !aligned(c.ws, 256)) {
+        if (why) *why = "workspace missing, too small or not 256-byte aligned";
+        return false;
+      }
+      if (!bf16_gemm_supported(m->h.cols, batch, c.xt, why)) return false;
+      if ((knob & 15) && (c.xt != UW_BF16 || batch <= 8 || !aligned(c.X, 16) || c.ldx % 8)) {
+        if (why) *why = "a matrix-core GEMM shape needs batch > 8 and bf16 X, 16-byte aligned, ldx a multiple of 8";
+        return false;
+      }
+      return true;
+    case UW_VARIANT_PALETTE:
+      if (!m->palette) {
+        if (why) *why = "no direct-palette copy is attached";
+        return false;
+      }
+      if (!aligned(c.X, 16) || (batch > 1 && (c.xt != UW_BF16 || c.ldx % 8))) {
+        if (why) *why = "the palette path needs X 16-byte aligned (and bf16 with ldx a multiple of 8 above batch 1)";
+        return false;
+      }
+      return true;
+    default:
+      if (why) *why = "unknown variant";
+      return false;
+  }
+}
+
+const char* variant_name(int v) {
+  switch (v) {
+    case UW_VARIANT_FUSED: return "fused";
+    case UW_VARIANT_DECOMPRESS_GEMM: return "decompress_gemm";
+    case UW_VARIANT_FUSED_MFMA: return "fused_mfma";
+    case UW_VARIANT_PALETTE: return "palette";
+    default: return "auto";
+  }
+}
+
+uint32_t blob_crc(const uw_matrix* m) { return m->h.crc32; }
+
 }  // namespace
 
 extern "C" {
@@ -104,22 +192,23 @@ int uw_blob_info(const void* blob, size_t n, uw_info* info) {
 
 namespace {
 // Decode tables, as the kernels hold them in LDS.  single(i): for the next
-// L stream bits i (first bit in bit 0), len | exponent << 7 of the canonical
-// code that prefixes i.  L <= 6: words [0, 4096) are the pair table, entry
-// i = (len_a + len_b) | E_a << 7 | len_a << 16 | E_b << 23 for the two codes
-// that prefix the 12 bits i, and words [4096, 4160) hold single(i) for
-// i < 2^L.  L > 6: words [0, 2^L) hold single(i).
-int upload_decode_tables(uw_matrix* m) {
-  const BlobHeader& h = m->h;
-  DevMatrix& d = m->dev;
+// L stream bits i (first bit in bit 0), len | v << 7 of the canonical code
+// that prefixes i, where v is its exponent (the decode tables) or its
+// palette index (the index tables, for the transcode to the direct form).
+// L <= 6: words [0, 4096) are the pair table, entry i = (len_a + len_b) |
+// v_a << 7 | len_a << 16 | v_b << 23 for the two codes that prefix the 12
+// bits i, and words [4096, 4160) hold single(i) for i < 2^L.  L > 6: words
+// [0, 2^L) hold single(i).
+std::vector<uint32_t> decode_table_image(const BlobHeader& h, bool index) {
   uint32_t code[32], rev[32];
   canonical_codes(h, code, rev);
+  auto value = [&](uint32_t s) { return index ? s : uint32_t(h.palette[s]); };
   auto single = [&](uint32_t idx) -> uint32_t {
     for (uint32_t s = 0; s < h.K; ++s) {
       const uint32_t len = h.code_len[s];
-      if (len && (idx & ((1u << len) - 1u)) == rev[s]) return len | (uint32_t(h.palette[s]) << 7);
+      if (len && (idx & ((1u << len) - 1u)) == rev[s]) return len | (value(s) << 7);
     }
-    return 1u | (uint32_t(h.palette[0]) << 7);  // gaps exist only for a one-symbol code; never met in a valid stream
+    return 1u | (value(0) << 7);  // gaps exist only for a one-symbol code; never met in a valid stream
   };
   std::vector<uint32_t> t(kDecodeTableWords, 0u);
   if (h.L <= 6) {
@@ -133,16 +222,10 @@ int upload_decode_tables(uw_matrix* m) {
   } else {
     for (uint32_t i = 0; i < (1u << h.L); ++i) t[i] = single(i);
   }
-  void* p = nullptr;
-  if (hipMalloc(&p, kDecodeTableBytes) != hipSuccess) return fail(UW_ERR_HIP, "uw_matrix_create: cannot allocate the decode tables");
-  if (hipMemcpy(p, t.data(), kDecodeTableBytes, hipMemcpyHostToDevice) != hipSuccess) {
-    (void)hipFree(p);
-    return fail(UW_ERR_HIP, "uw_matrix_create: cannot copy the decode tables");
-  }
-  m->d_tables = p;
-  d.tables = static_cast<const uint32_t*>(p);
-  return UW_OK;
+  return t;
 }
+
+bool flat_shape(const BlobHeader& h) { return !h.plain() && h.G % 16 == 0 && (h.cols / 64) % 16 == 0; }
 
 // Flat walk (G and the groups per row multiples of 16, so no tile crosses a
 // row): one descriptor per tile for the loads of its step, two words: the
@@ -151,14 +234,15 @@ int upload_decode_tables(uw_matrix* m) {
 // floor (at least one lane, so every step issues the same number of loads).  A load with nothing
 // to move has lane 0 read 16 bytes at floor + 1024 i, so the blob must
 // extend that far past the queue; where it does not, the walk by blocks is
-// used instead.
-int build_step_table(const uint8_t* hb, size_t n, uw_matrix* m) {
+// used instead.  Returns the table (empty: no flat walk).
+int build_step_table(const uint8_t* hb, size_t n, uw_matrix* m, std::vector<uint32_t>* out) {
   const BlobHeader& h = m->h;
   DevMatrix& d = m->dev;
   d.flat = 0;
   d.steps = nullptr;
   d.n_tiles = 0;
-  if (h.G % 16 || d.gpr % 16) return UW_OK;
+  out->clear();
+  if (!flat_shape(h)) return UW_OK;
   // the loads address the queue from 1 KB before it and the sign+mantissa
   // section with 32-bit offsets
   const uint64_t extent = 1024 + h.size_queue + 1024 * uint64_t(d.nq - 1) + 16;
@@ -166,7 +250,8 @@ int build_step_table(const uint8_t* hb, size_t n, uw_matrix* m) {
     return UW_OK;
   const uint64_t nb = h.n_blocks, T = d.T;
   const int64_t n_tiles = d.n_groups / 16;
-  std::vector<uint32_t> st(2 * size_t(n_tiles + 1), 0u);  // + a spare entry read past the last step
+  std::vector<uint32_t>& st = *out;
+  st.assign(2 * size_t(n_tiles + 1), 0u);  // + a spare entry read past the last step
   const uint8_t* bo = hb + h.off_block;
   const uint8_t* sg = hb + h.off_seg;
   int64_t u = 0;
@@ -192,33 +277,64 @@ int build_step_table(const uint8_t* hb, size_t n, uw_matrix* m) {
     }
   }
   if (u != n_tiles) return fail(UW_ERR_FORMAT, "tile count does not match the shape");
-  void* p = nullptr;
-  if (hipMalloc(&p, st.size() * 4) != hipSuccess) return fail(UW_ERR_HIP, "uw_matrix_create: cannot allocate the step table");
-  if (hipMemcpy(p, st.data(), st.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
-    (void)hipFree(p);
-    return fail(UW_ERR_HIP, "uw_matrix_create: cannot copy the step table");
-  }
-  m->d_steps = p;
-  d.steps = static_cast<const uint32_t*>(p);
   d.n_tiles = int32_t(n_tiles);
   d.q_extent = uint32_t(extent);
   d.flat = 1;
   return UW_OK;
 }
+// Where uw_matrix_create puts the derived tables in the caller's device
+// buffer: after the blob (256-byte aligned), the decode tables, the index
+// tables, then the flat walk's step table (8 bytes per tile + a spare entry).
+struct AuxLayout {
+  size_t off_tables = 0, off_index_tables = 0, off_steps = 0, steps_bytes = 0, total = 0;
+};
+
+AuxLayout aux_layout(const BlobHeader& h, size_t blob_bytes) {
+  AuxLayout a;
+  size_t o = align256(blob_bytes);
+  if (h.plain()) {
+    a.off_tables = a.off_index_tables = a.off_steps = o;
+    a.total = o;
+    return a;
+  }
+  a.off_tables = o;
+  o += align256(kDecodeTableBytes);
+  a.off_index_tables = o;
+  o += align256(kDecodeTableBytes);
+  a.off_steps = o;
+  a.steps_bytes = flat_shape(h) ? 8 * (size_t(h.rows) * size_t(h.cols) / 1024 + 1) : 0;
+  o += align256(a.steps_bytes);
+  a.total = o;
+  return a;
+}
 }  // namespace
 
-int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_matrix** out) {
-  if (!host_blob || !d_blob || !out) return fail(UW_ERR_INVALID, "uw_matrix_create: null pointer");
-  if (!aligned(d_blob, 256)) return fail(UW_ERR_INVALID, "uw_matrix_create: device blob must be 256-byte aligned");
+size_t uw_matrix_device_bytes(const void* host_blob, size_t n) {
+  if (!host_blob) {
+    fail(UW_ERR_INVALID, "uw_matrix_device_bytes: null blob");
+    return 0;
+  }
+  BlobHeader h;
+  if (validate_blob(static_cast<const uint8_t*>(host_blob), n, &h)) return 0;
+  return aux_layout(h, n).total;
+}
+
+int uw_matrix_create(const void* host_blob, size_t n, void* d_buf, size_t d_bytes, uw_matrix** out) {
+  if (!host_blob || !d_buf || !out) return fail(UW_ERR_INVALID, "uw_matrix_create: null pointer");
+  if (!aligned(d_buf, 256)) return fail(UW_ERR_INVALID, "uw_matrix_create: device buffer must be 256-byte aligned");
   BlobHeader h;
   int rc = validate_blob(static_cast<const uint8_t*>(host_blob), n, &h);
   if (rc) return rc;
+  const AuxLayout aux = aux_layout(h, n);
+  if (d_bytes < aux.total)
+    return fail(UW_ERR_INVALID, "uw_matrix_create: the device buffer is smaller than uw_matrix_device_bytes()");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(UW_ERR_HIP, "uw_matrix_create: no current HIP device");
   uw_matrix* m = new uw_matrix();
   m->h = h;
   m->device = dev;
-  m->d_blob = static_cast<const uint8_t*>(d_blob);
+  m->d_blob = static_cast<const uint8_t*>(d_buf);
+  uint8_t* dwrite = static_cast<uint8_t*>(d_buf);
   DevMatrix& d = m->dev;
   std::memset(&d, 0, sizeof(d));
   const uint8_t* b = m->d_blob;
@@ -240,10 +356,14 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
     d.R = int32_t(h.R);
     d.L = int32_t(h.L);
     // the decode tables: built here, loaded into LDS by the kernels
-    if (int rc2 = upload_decode_tables(m)) {
-      uw_matrix_destroy(m);
-      return rc2;
+    const std::vector<uint32_t> tab = decode_table_image(h, false), itab = decode_table_image(h, true);
+    if (hipMemcpy(dwrite + aux.off_tables, tab.data(), kDecodeTableBytes, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(dwrite + aux.off_index_tables, itab.data(), kDecodeTableBytes, hipMemcpyHostToDevice) != hipSuccess) {
+      delete m;
+      return fail(UW_ERR_HIP, "uw_matrix_create: cannot copy the decode tables");
     }
+    d.tables = reinterpret_cast<const uint32_t*>(b + aux.off_tables);
+    d.index_tables = reinterpret_cast<const uint32_t*>(b + aux.off_index_tables);
     // an LDS slot holds any segment; it is filled by 1 KB direct loads
     // (a segment is loaded from its 16-byte aligned floor, up to 12 bytes
     // before it, and lanes that take no word read the word after its end)
@@ -258,10 +378,19 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
     d.unit_blocks = int32_t(lcm / h.G);
     d.rows_per_unit = int32_t(lcm / d.gpr);
     d.n_units = int32_t((int64_t(h.n_blocks) + d.unit_blocks - 1) / d.unit_blocks);
-    rc = build_step_table(static_cast<const uint8_t*>(host_blob), n, m);
+    std::vector<uint32_t> steps;
+    rc = build_step_table(static_cast<const uint8_t*>(host_blob), n, m, &steps);
     if (rc) {
-      uw_matrix_destroy(m);
+      delete m;
       return rc;
+    }
+    if (d.flat) {
+      if (steps.size() * 4 > aux.steps_bytes ||
+          hipMemcpy(dwrite + aux.off_steps, steps.data(), steps.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+        delete m;
+        return fail(UW_ERR_HIP, "uw_matrix_create: cannot copy the step table");
+      }
+      d.steps = reinterpret_cast<const uint32_t*>(b + aux.off_steps);
     }
     // one wave per block when a unit has several blocks and each block holds
     // a row end (G > groups per row): a row then spans at most two blocks,
@@ -273,17 +402,15 @@ int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_mat
   return UW_OK;
 }
 
-void uw_matrix_destroy(uw_matrix* m) {
-  if (!m) return;
-  if (m->d_steps || m->d_tables) {
-    int cur = -1;
-    (void)hipGetDevice(&cur);
-    if (cur != m->device) (void)hipSetDevice(m->device);
-    if (m->d_steps) (void)hipFree(m->d_steps);
-    if (m->d_tables) (void)hipFree(m->d_tables);
-    if (cur != m->device && cur >= 0) (void)hipSetDevice(cur);
-  }
-  delete m;
+void uw_matrix_destroy(uw_matrix* m) { delete m; }
+
+int uw_matrix_attach_palette(uw_matrix* m, const uw_palette* p) {
+  if (!m) return fail(UW_ERR_INVALID, "uw_matrix_attach_palette: null matrix handle");
+  if (p && (p->l.rows != m->h.rows || p->l.cols != m->h.cols))
+    return fail(UW_ERR_INVALID, "uw_matrix_attach_palette: the palette copy has another shape");
+  std::lock_guard<std::mutex> lk(m->mu);
+  m->palette = p;
+  return UW_OK;
 }
 
 int uw_decompress(const uw_matrix* m, uint16_t* d_out, int64_t ld_out, void* stream) {
@@ -304,7 +431,7 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
 
 size_t uw_workspace_size(const uw_matrix* m, int64_t batch, int variant) {
   if (!m || batch < 0) return 0;
-  if (variant == UW_VARIANT_FUSED || variant == UW_VARIANT_FUSED_MFMA) return 0;
+  if (variant == UW_VARIANT_FUSED || variant == UW_VARIANT_FUSED_MFMA || variant == UW_VARIANT_PALETTE) return 0;
   return decompress_ws_bytes(m);
 }
 
@@ -312,6 +439,7 @@ int uw_set_plan(uw_matrix* m, const uw_plan* plan) {
   if (!m || !plan) return fail(UW_ERR_INVALID, "uw_set_plan: null pointer");
   if (plan->batch < 1 || plan->variant <= UW_VARIANT_AUTO || plan->variant >= UW_VARIANT_COUNT)
     return fail(UW_ERR_INVALID, "uw_set_plan: batch >= 1 and a concrete variant");
+  if (!knob_valid(plan->variant, plan->knob)) return fail(UW_ERR_INVALID, "uw_set_plan: knob out of range for the variant");
   std::lock_guard<std::mutex> lk(m->mu);
   m->plans[plan->batch] = *plan;
   return UW_OK;
@@ -326,19 +454,57 @@ int uw_get_plan(const uw_matrix* m, int64_t batch, uw_plan* out) {
   return UW_OK;
 }
 
-int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y, int64_t ldy,
-                  int yt, int variant, void* d_ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Run one (variant, knob) after the checks of runnable().
+int run_variant(const uw_matrix* m, int variant, int knob, const void* d_X, int64_t batch, int64_t ldx, int xt,
+                void* d_Y, int64_t ldy, int yt, void* d_ws, void* stream) {
+  switch (variant) {
+    case UW_VARIANT_FUSED_MFMA: return launch_fused_mfma(m, d_X, batch, ldx, d_Y, ldy, yt, stream, knob);
+    case UW_VARIANT_FUSED: return launch_fused(m, d_X, batch, ldx, xt, d_Y, ldy, yt, stream, knob);
+    case UW_VARIANT_PALETTE: {
+      const uw_palette* p = m->palette;
+      if (batch == 1) return uw_palette_gemv(p, d_X, xt, d_Y, yt, stream);
+      return uw_palette_gemm(p, d_X, batch, ldx, xt, d_Y, ldy, yt, stream);
+    }
+    default: {
+      // decompress into the workspace, then the bf16 product
+      uint16_t* W = static_cast<uint16_t*>(d_ws);
+      if (int rc = launch_decompress(m, W, m->h.cols, stream)) return rc;
+      return launch_bf16_gemm(W, m->h.rows, m->h.cols, m->h.cols, d_X, batch, ldx, xt, d_Y, ldy, yt, stream, knob & 15,
+                              knob >> 4);
+    }
+  }
+}
+
+// AUTO without a usable plan: one or two rows on VALU (when one pass takes
+// them); up to 32 rows on the matrix cores; beyond that decompress + GEMM
+// when the workspace is given (the measured crossovers on the MLP shapes: at
+// 64 rows decompress + GEMM is ahead on down_proj).
+int heuristic_variant(const uw_matrix* m, const CallShape& c) {
+  const bool fused_ok = runnable(m, UW_VARIANT_FUSED, 0, c, nullptr);
+  const bool mfma_ok = runnable(m, UW_VARIANT_FUSED_MFMA, 0, c, nullptr);
+  const bool ws_ok = runnable(m, UW_VARIANT_DECOMPRESS_GEMM, 0, c, nullptr);
+  const int64_t batch = c.batch;
+  if (fused_ok && (batch == 1 || (batch == 2 && fused_rows_per_pass(m, batch, c.xt) >= 2))) return UW_VARIANT_FUSED;
+  if (mfma_ok && (batch <= 32 || (batch <= 64 && !ws_ok))) return UW_VARIANT_FUSED_MFMA;
+  if (ws_ok && (c.xt == UW_BF16 || !fused_ok)) return UW_VARIANT_DECOMPRESS_GEMM;
+  if (mfma_ok) return UW_VARIANT_FUSED_MFMA;
+  return fused_ok || !ws_ok ? UW_VARIANT_FUSED : UW_VARIANT_DECOMPRESS_GEMM;
+}
+
+int gemm_dispatch(const uw_matrix* m, int variant, int knob, const void* d_X, int64_t batch, int64_t ldx, int xt,
+                  void* d_Y, int64_t ldy, int yt, void* d_ws, size_t ws_bytes, void* stream, const char* where) {
   if (int rc = check_matrix(m)) return rc;
   if (int rc = check_products(d_X, batch, ldx, xt, d_Y, ldy, yt, m->h.rows, m->h.cols)) return rc;
   if (batch == 0) return UW_OK;
-  if (variant < 0 || variant >= UW_VARIANT_COUNT) return fail(UW_ERR_INVALID, "uw_gemm_fused: unknown variant");
-  std::string why, why_mfma;
-  const bool fused_ok = fused_supported(m, xt, &why) && (!m->h.plain() || bf16_gemm_supported(m->h.cols, batch, xt, &why));
-  const bool mfma_ok = fused_mfma_supported(m, xt, &why_mfma) && aligned(d_X, 16) && ldx % 8 == 0;
-  if (!mfma_ok && why_mfma.empty()) why_mfma = "X must be 16-byte aligned with ldx a multiple of 8";
+  const CallShape c{d_X, batch, ldx, xt, d_ws, ws_bytes};
   if (variant == UW_VARIANT_AUTO) {
-    uw_plan p;
+    knob = 0;
     bool have = false;
+    uw_plan p;
     {
       std::lock_guard<std::mutex> lk(m->mu);
       auto it = m->plans.find(batch);
@@ -347,41 +513,50 @@ int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ld
         have = true;
       }
     }
-    // Without a plan: one or two rows on VALU (when one pass takes them);
-    // up to 32 rows on the matrix cores; beyond that decompress + library
-    // GEMM when the workspace is given (the measured crossovers on the MLP
-    // shapes: at 64 rows decompress + GEMM is ahead on down_proj).
-    const bool ws_ok = d_ws && ws_bytes >= decompress_ws_bytes(m);
-    if (have) variant = p.variant;
-    else if (fused_ok && (batch == 1 || (batch == 2 && fused_rows_per_pass(m, batch, xt) >= 2)))
-      variant = UW_VARIANT_FUSED;
-    else if (mfma_ok && (batch <= 32 || (batch <= 64 && !ws_ok))) variant = UW_VARIANT_FUSED_MFMA;
-    else if (ws_ok && (xt == UW_BF16 || !fused_ok)) variant = UW_VARIANT_DECOMPRESS_GEMM;
-    else if (mfma_ok) variant = UW_VARIANT_FUSED_MFMA;
-    else variant = fused_ok || !ws_ok ? UW_VARIANT_FUSED : UW_VARIANT_DECOMPRESS_GEMM;
+    // a stored plan is followed only when its variant can run this call (it
+    // was tuned for bf16 X with a workspace; other operands fall back)
+    if (have && runnable(m, p.variant, p.knob, c, nullptr)) {
+      variant = p.variant;
+      knob = p.knob;
+    } else {
+      variant = heuristic_variant(m, c);
+    }
   }
-  if (variant == UW_VARIANT_FUSED_MFMA) {
-    if (!mfma_ok) return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused: " + why_mfma);
-    return launch_fused_mfma(m, d_X, batch, ldx, d_Y, ldy, yt, stream);
+  if (variant <= UW_VARIANT_AUTO || variant >= UW_VARIANT_COUNT)
+    return fail(UW_ERR_INVALID, std::string(where) + ": unknown variant");
+  if (!knob_valid(variant, knob)) return fail(UW_ERR_INVALID, std::string(where) + ": knob out of range");
+  std::string why;
+  if (!runnable(m, variant, knob, c, &why)) {
+    const bool space = variant == UW_VARIANT_DECOMPRESS_GEMM && why.rfind("workspace", 0) == 0;
+    return fail(space ? UW_ERR_NOSPACE : UW_ERR_UNSUPPORTED, std::string(where) + ": " + why);
   }
-  if (variant == UW_VARIANT_FUSED) {
-    if (!fused_ok) return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused: " + why);
-    return launch_fused(m, d_X, batch, ldx, xt, d_Y, ldy, yt, stream);
-  }
-  // decompress into the workspace, then the bf16 product
-  if (!d_ws || ws_bytes < decompress_ws_bytes(m) || !aligned(d_ws, 256))
-    return fail(UW_ERR_NOSPACE, "uw_gemm_fused: workspace missing, too small or not 256-byte aligned");
-  if (!bf16_gemm_supported(m->h.cols, batch, xt, &why)) return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused: " + why);
-  uint16_t* W = static_cast<uint16_t*>(d_ws);
-  if (int rc = launch_decompress(m, W, m->h.cols, stream)) return rc;
-  return launch_bf16_gemm(W, m->h.rows, m->h.cols, m->h.cols, d_X, batch, ldx, xt, d_Y, ldy, yt, stream);
+  return run_variant(m, variant, knob, d_X, batch, ldx, xt, d_Y, ldy, yt, d_ws, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y, int64_t ldy,
+                  int yt, int variant, void* d_ws, size_t ws_bytes, void* stream) {
+  if (variant < 0 || variant >= UW_VARIANT_COUNT) return fail(UW_ERR_INVALID, "uw_gemm_fused: unknown variant");
+  return gemm_dispatch(m, variant, 0, d_X, batch, ldx, xt, d_Y, ldy, yt, d_ws, ws_bytes, stream, "uw_gemm_fused");
+}
+
+int uw_gemm_with_plan(const uw_matrix* m, const uw_plan* plan, const void* d_X, int64_t batch, int64_t ldx, int xt,
+                      void* d_Y, int64_t ldy, int yt, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(UW_ERR_INVALID, "uw_gemm_with_plan: null plan");
+  if (plan->variant <= UW_VARIANT_AUTO || plan->variant >= UW_VARIANT_COUNT)
+    return fail(UW_ERR_INVALID, "uw_gemm_with_plan: a concrete variant is needed");
+  return gemm_dispatch(m, plan->variant, plan->knob, d_X, batch, ldx, xt, d_Y, ldy, yt, d_ws, ws_bytes, stream,
+                       "uw_gemm_with_plan");
 }
 
 size_t uw_autotune_scratch_size(const uw_matrix* m, int64_t batch) {
   if (!m || batch < 0) return 0;
-  const size_t xb = (size_t(batch) * size_t(m->h.cols) * 2 + 255) / 256 * 256;
-  const size_t yb = (size_t(batch) * size_t(m->h.rows) * 2 + 255) / 256 * 256;
-  return xb + yb;
+  const size_t xb = align256(size_t(batch) * size_t(m->h.cols) * 2);
+  const size_t yb = align256(size_t(batch) * size_t(m->h.rows) * 2);
+  return xb + yb + kFlushBytes;
 }
 
 int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* stream, uw_plan* out) {
@@ -393,53 +568,88 @@ int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(d_ws);
   void* X = base + need_ws;
-  void* Y = base + need_ws + (size_t(batch) * size_t(m->h.cols) * 2 + 255) / 256 * 256;
-  // X = 1.0 everywhere (values do not change the work of either candidate)
+  void* Y = base + need_ws + align256(size_t(batch) * size_t(m->h.cols) * 2);
+  void* flush = static_cast<char*>(Y) + align256(size_t(batch) * size_t(m->h.rows) * 2);
+  // X = 1.0 everywhere (values do not change the work of any candidate); the
+  // probe's checksum words land in the first bytes of Y, which the timed
+  // calls overwrite
   if (hipMemsetD16Async(reinterpret_cast<hipDeviceptr_t>(X), 0x3F80, size_t(batch) * size_t(m->h.cols), s) != hipSuccess)
     return fail(UW_ERR_HIP, "uw_autotune: memset failed");
+  // the probe reads the region but its last sink bytes, where it writes its checksums
+  const size_t flush_read = kFlushBytes - align256(read_probe_sink_bytes());
+  void* sink = static_cast<char*>(flush) + flush_read;
   hipEvent_t e0, e1;
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return fail(UW_ERR_HIP, "uw_autotune: event");
+  if (hipEventCreate(&e0) != hipSuccess) return fail(UW_ERR_HIP, "uw_autotune: event");
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return fail(UW_ERR_HIP, "uw_autotune: event");
+  }
   uw_plan plan;
   std::memset(&plan, 0, sizeof(plan));
   plan.batch = batch;
-  for (int v = 0; v < UW_VARIANT_COUNT; ++v) plan.candidate_us[v] = -1.f;
+  for (int v = 0; v < UW_VARIANT_COUNT; ++v) {
+    plan.candidate_us[v] = -1.f;
+    plan.candidate_knob[v] = 0;
+  }
+  // candidates: every variant with the knobs that matter at this batch
+  std::vector<std::pair<int, int>> cands;
+  if (batch <= 16) {
+    cands.push_back({UW_VARIANT_FUSED, 0});
+    if (m->dev.flat) {
+      cands.push_back({UW_VARIANT_FUSED, 2});
+      cands.push_back({UW_VARIANT_FUSED, 4});
+    }
+  }
+  for (int nw : {0, 8, 12, 16}) cands.push_back({UW_VARIANT_FUSED_MFMA, nw});
+  if (batch <= 8) {
+    cands.push_back({UW_VARIANT_DECOMPRESS_GEMM, 0});
+  } else {
+    const std::vector<int> shapes = batch <= 16   ? std::vector<int>{1, 2}
+                                    : batch <= 32 ? std::vector<int>{3, 4, 8}
+                                    : batch <= 64 ? std::vector<int>{5, 4, 6}
+                                                  : std::vector<int>{6, 7, 9, 5};
+    for (int sh : shapes) cands.push_back({UW_VARIANT_DECOMPRESS_GEMM, sh});
+  }
+  cands.push_back({UW_VARIANT_PALETTE, 0});
+  const CallShape c{X, batch, int64_t(m->h.cols), UW_BF16, d_ws, need_ws};
   float best = 1e30f;
-  int best_v = -1;
+  int best_v = -1, best_k = 0;
   const int warm = 3, reps = 15;
-  for (int v = UW_VARIANT_FUSED; v < UW_VARIANT_COUNT; ++v) {
+  int rc = UW_OK;
+  for (const auto& [v, knob] : cands) {
+    if (!runnable(m, v, knob, c, nullptr)) continue;
     std::vector<float> t;
-    int rc = UW_OK;
     for (int i = 0; i < warm + reps && rc == UW_OK; ++i) {
-      hipEventRecord(e0, s);
-      rc = uw_gemm_fused(m, X, batch, m->h.cols, UW_BF16, Y, m->h.rows, UW_BF16, v, d_ws, need_ws, stream);
-      hipEventRecord(e1, s);
-      if (rc) break;
-      if (hipEventSynchronize(e1) != hipSuccess) {
-        rc = UW_ERR_HIP;
-        break;
-      }
+      // evict the blob: read 512 MiB that are not the matrix
+      if (i >= warm && (rc = launch_read_probe(flush, flush_read, sink, s))) break;
+      if (hipEventRecord(e0, s) != hipSuccess) rc = fail(UW_ERR_HIP, "uw_autotune: event record");
+      if (rc == UW_OK)
+        rc = run_variant(m, v, knob, X, batch, int64_t(m->h.cols), UW_BF16, Y, int64_t(m->h.rows), UW_BF16, d_ws, stream);
+      if (rc == UW_OK && hipEventRecord(e1, s) != hipSuccess) rc = fail(UW_ERR_HIP, "uw_autotune: event record");
+      if (rc == UW_OK && hipEventSynchronize(e1) != hipSuccess) rc = fail(UW_ERR_HIP, "uw_autotune: synchronize");
       float ms = 0;
-      hipEventElapsedTime(&ms, e0, e1);
-      if (i >= warm) t.push_back(ms * 1000.f);
+      if (rc == UW_OK) (void)hipEventElapsedTime(&ms, e0, e1);
+      if (rc == UW_OK && i >= warm) t.push_back(ms * 1000.f);
     }
-    if (rc == UW_ERR_HIP) {
-      hipEventDestroy(e0);
-      hipEventDestroy(e1);
-      return rc;
-    }
-    if (rc || t.empty()) continue;  // not applicable to this matrix/batch
+    if (rc != UW_OK) break;
     std::sort(t.begin(), t.end());
     const float med = t[t.size() / 2];
-    plan.candidate_us[v] = med;
+    if (plan.candidate_us[v] < 0 || med < plan.candidate_us[v]) {
+      plan.candidate_us[v] = med;
+      plan.candidate_knob[v] = knob;
+    }
     if (med < best) {
       best = med;
       best_v = v;
+      best_k = knob;
     }
   }
-  hipEventDestroy(e0);
-  hipEventDestroy(e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc != UW_OK) return rc;
   if (best_v < 0) return fail(UW_ERR_UNSUPPORTED, "uw_autotune: no candidate can run this matrix and batch");
   plan.variant = best_v;
+  plan.knob = best_k;
   plan.time_us = best;
   {
     std::lock_guard<std::mutex> lk(m->mu);
@@ -447,6 +657,152 @@ int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* 
   }
   if (out) *out = plan;
   set_error("");
+  return UW_OK;
+}
+
+// ---- plan files (JSON) ------------------------------------------------------
+
+int uw_plan_save(const uw_matrix* m, char* out, size_t* out_size) {
+  if (!m || !out_size) return fail(UW_ERR_INVALID, "uw_plan_save: null pointer");
+  std::string j = "{\"format\": \"uw-plan-1\", \"rows\": " + std::to_string(m->h.rows) +
+                  ", \"cols\": " + std::to_string(m->h.cols) + ", \"blob_crc32\": " + std::to_string(blob_crc(m)) +
+                  ", \"plans\": [";
+  {
+    std::lock_guard<std::mutex> lk(m->mu);
+    bool first = true;
+    for (const auto& [b, p] : m->plans) {
+      char buf[256];
+      std::snprintf(buf, sizeof buf, "%s{\"batch\": %lld, \"variant\": \"%s\", \"knob\": %d, \"time_us\": %.3f}",
+                    first ? "" : ", ", static_cast<long long>(b), variant_name(p.variant), int(p.knob),
+                    double(p.time_us));
+      j += buf;
+      first = false;
+    }
+  }
+  j += "]}";
+  const size_t need = j.size() + 1;
+  if (!out) {
+    *out_size = need;
+    return UW_OK;
+  }
+  if (*out_size < need) {
+    *out_size = need;
+    return fail(UW_ERR_NOSPACE, "uw_plan_save: output buffer too small");
+  }
+  std::memcpy(out, j.c_str(), need);
+  *out_size = need;
+  return UW_OK;
+}
+
+}  // extern "C"
+
+namespace {
+// A reader for the JSON uw_plan_save writes (objects, arrays, strings without
+// escapes, numbers); anything else is a format error.
+struct Json {
+  const char* p;
+  bool ok = true;
+  void ws() {
+    while (*p == ' ' || *p == '\n' || *p == '\t' || *p == '\r') ++p;
+  }
+  bool eat(char c) {
+    ws();
+    if (*p != c) return false;
+    ++p;
+    return true;
+  }
+  std::string str() {
+    ws();
+    std::string r;
+    if (*p != '"') {
+      ok = false;
+      return r;
+    }
+    ++p;
+    while (*p && *p != '"') {
+      if (*p == '\\') {
+        ok = false;
+        return r;
+      }
+      r += *p++;
+    }
+    if (*p != '"') ok = false;
+    else ++p;
+    return r;
+  }
+  double num() {
+    ws();
+    char* end = nullptr;
+    const double v = std::strtod(p, &end);
+    if (end == p) ok = false;
+    p = end ? end : p;
+    return v;
+  }
+};
+
+int variant_of(const std::string& n) {
+  for (int v = UW_VARIANT_FUSED; v < UW_VARIANT_COUNT; ++v)
+    if (n == variant_name(v)) return v;
+  return -1;
+}
+}  // namespace
+
+extern "C" {
+
+int uw_plan_load(uw_matrix* m, const char* json) {
+  if (!m || !json) return fail(UW_ERR_INVALID, "uw_plan_load: null pointer");
+  Json r{json};
+  double rows = -1, cols = -1, crc = -1;
+  std::string format;
+  std::vector<uw_plan> plans;
+  if (!r.eat('{')) return fail(UW_ERR_FORMAT, "uw_plan_load: not a JSON object");
+  bool more = !r.eat('}');
+  while (more && r.ok) {
+    const std::string key = r.str();
+    if (!r.ok || !r.eat(':')) return fail(UW_ERR_FORMAT, "uw_plan_load: expected a key");
+    if (key == "format") format = r.str();
+    else if (key == "rows") rows = r.num();
+    else if (key == "cols") cols = r.num();
+    else if (key == "blob_crc32") crc = r.num();
+    else if (key == "plans") {
+      if (!r.eat('[')) return fail(UW_ERR_FORMAT, "uw_plan_load: plans must be an array");
+      bool items = !r.eat(']');
+      while (items && r.ok) {
+        if (!r.eat('{')) return fail(UW_ERR_FORMAT, "uw_plan_load: a plan must be an object");
+        uw_plan p;
+        std::memset(&p, 0, sizeof(p));
+        p.batch = -1;
+        p.variant = -1;
+        for (int v = 0; v < UW_VARIANT_COUNT; ++v) p.candidate_us[v] = -1.f;
+        bool fields = !r.eat('}');
+        while (fields && r.ok) {
+          const std::string k = r.str();
+          if (!r.ok || !r.eat(':')) return fail(UW_ERR_FORMAT, "uw_plan_load: expected a plan field");
+          if (k == "batch") p.batch = int64_t(r.num());
+          else if (k == "variant") p.variant = variant_of(r.str());
+          else if (k == "knob") p.knob = int32_t(r.num());
+          else if (k == "time_us") p.time_us = float(r.num());
+          else return fail(UW_ERR_FORMAT, "uw_plan_load: unknown plan field " + k);
+          fields = r.eat(',');
+          if (!fields && !r.eat('}')) return fail(UW_ERR_FORMAT, "uw_plan_load: unterminated plan");
+        }
+        if (!r.ok || p.batch < 1 || p.variant <= UW_VARIANT_AUTO || !knob_valid(p.variant, p.knob))
+          return fail(UW_ERR_FORMAT, "uw_plan_load: invalid plan entry");
+        plans.push_back(p);
+        items = r.eat(',');
+        if (!items && !r.eat(']')) return fail(UW_ERR_FORMAT, "uw_plan_load: unterminated plans");
+      }
+    } else {
+      return fail(UW_ERR_FORMAT, "uw_plan_load: unknown key " + key);
+    }
+    more = r.eat(',');
+    if (!more && !r.eat('}')) return fail(UW_ERR_FORMAT, "uw_plan_load: unterminated object");
+  }
+  if (!r.ok || format != "uw-plan-1") return fail(UW_ERR_FORMAT, "uw_plan_load: not a uw-plan-1 document");
+  if (rows != double(m->h.rows) || cols != double(m->h.cols) || crc != double(blob_crc(m)))
+    return fail(UW_ERR_FORMAT, "uw_plan_load: the plans belong to another matrix (rows, cols or blob CRC differ)");
+  std::lock_guard<std::mutex> lk(m->mu);
+  for (const uw_plan& p : plans) m->plans[p.batch] = p;
   return UW_OK;
 }
 
@@ -459,6 +815,51 @@ int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, c
   std::string why;
   if (!bf16_gemm_supported(cols, batch, xt, &why)) return fail(UW_ERR_UNSUPPORTED, "uw_bf16_gemm: " + why);
   return launch_bf16_gemm(d_W, rows, cols, ldw, d_X, batch, ldx, xt, d_Y, ldy, yt, stream);
+}
+
+int uw_bf16_gemm_shaped(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, const void* d_X, int64_t batch,
+                        int64_t ldx, void* d_Y, int64_t ldy, int yt, int shape, int ks, void* stream) {
+  if (!d_W || !aligned(d_W, 16)) return fail(UW_ERR_INVALID, "uw_bf16_gemm_shaped: W must be non-null and 16-byte aligned");
+  if (rows < 1 || cols < 8 || cols % 8 || ldw < cols || ldw % 8)
+    return fail(UW_ERR_INVALID, "uw_bf16_gemm_shaped: bad shape");
+  if (int rc = check_products(d_X, batch, ldx, UW_BF16, d_Y, ldy, yt, rows, cols)) return rc;
+  if (batch < 1 || !aligned(d_X, 16) || ldx % 8)
+    return fail(UW_ERR_INVALID, "uw_bf16_gemm_shaped: batch >= 1, X 16-byte aligned and ldx a multiple of 8");
+  if (shape < 1 || shape >= mfma_gemm_shape_count() || !(ks == 0 || ks == 1 || ks == 2 || ks == 4 || ks == 8))
+    return fail(UW_ERR_INVALID, "uw_bf16_gemm_shaped: unknown shape or ks");
+  return launch_mfma_gemm(d_W, rows, cols, ldw, static_cast<const uint16_t*>(d_X), batch, ldx, d_Y, ldy, yt, shape, ks,
+                          stream);
+}
+
+int uw_bf16_gemm_shape_count(void) { return mfma_gemm_shape_count(); }
+
+size_t uw_palette_transcode_size(const uw_matrix* m) {
+  if (!m || !palette_transcodable(m, nullptr)) return 0;
+  return transcode_layout(m).total;
+}
+
+int uw_palette_transcode(const uw_matrix* m, void* d_out, size_t out_bytes, void* stream) {
+  if (int rc = check_matrix(m)) return rc;
+  std::string why;
+  if (!palette_transcodable(m, &why)) return fail(UW_ERR_UNSUPPORTED, "uw_palette_transcode: " + why);
+  if (!d_out || !aligned(d_out, 256)) return fail(UW_ERR_INVALID, "uw_palette_transcode: output must be 256-byte aligned");
+  if (out_bytes < transcode_layout(m).total) return fail(UW_ERR_NOSPACE, "uw_palette_transcode: output too small");
+  return launch_palette_transcode(m, static_cast<uint8_t*>(d_out), stream);
+}
+
+int uw_palette_create_transcoded(const uw_matrix* m, const void* d_blob, uw_palette** out) {
+  if (!m || !d_blob || !out) return fail(UW_ERR_INVALID, "uw_palette_create_transcoded: null pointer");
+  if (!aligned(d_blob, 256)) return fail(UW_ERR_INVALID, "uw_palette_create_transcoded: blob must be 256-byte aligned");
+  std::string why;
+  if (!palette_transcodable(m, &why)) return fail(UW_ERR_UNSUPPORTED, "uw_palette_create_transcoded: " + why);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(UW_ERR_HIP, "uw_palette_create_transcoded: no current HIP device");
+  uw_palette* p = new uw_palette;
+  p->l = transcode_layout(m);
+  p->d_blob = static_cast<const uint8_t*>(d_blob);
+  p->device = dev;
+  *out = p;
+  return UW_OK;
 }
 
 size_t uw_read_probe_sink_size(void) { return read_probe_sink_bytes(); }

@@ -1,6 +1,7 @@
-// Uncompressed kernels for gfx950: the bf16 product on the vector ALU (the
-// comparator, the product half of decompress-then-multiply and the plain-mode
-// path), the plain-mode copy and a streaming-read probe.
+// Uncompressed kernels for gfx950: the bf16 product on the vector ALU for
+// small batches (the comparator, the product half of decompress-then-multiply
+// and the plain-mode path; larger batches go to the matrix-core kernel of
+// uw_gemm.hip), the plain-mode copy and a streaming-read probe.
 #include <algorithm>
 
 #include "uw_device.h"
@@ -187,12 +188,18 @@ int launch_copy_plain(const uint16_t* src, int64_t rows, int64_t cols, uint16_t*
   return hip_check(hipGetLastError(), "copy_plain_kernel launch");
 }
 
-// Batches above this go to the library GEMM (bf16 x); up to it the
-// GEMV-style kernel, which reads W once per chunk of x columns, is used.
-constexpr int64_t kLibraryGemmMinBatch = 8;
+// Batches above this, with bf16 activations that are 16-byte aligned and a
+// row stride that is a multiple of 8, go to the matrix-core kernel
+// (uw_gemm.hip); up to it the GEMV-style kernel, which reads W once per chunk
+// of up to 8 activation rows, is used (measured crossover on the MLP shapes).
+constexpr int64_t kValuMaxBatch = 8;
+
+static bool mfma_gemm_ok(const void* X, int64_t batch, int64_t ldx, int xt) {
+  return xt == UW_BF16 && batch > kValuMaxBatch && reinterpret_cast<uintptr_t>(X) % 16 == 0 && ldx % 8 == 0;
+}
 
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why) {
-  if (batch > kLibraryGemmMinBatch && xt == UW_BF16) return true;  // library GEMM
+  if (xt == UW_BF16 && batch > kValuMaxBatch) return true;  // matrix cores, or VALU passes when X is unaligned
   const size_t per = xt == UW_F32 ? size_t(cols) * 4 : size_t(cols) * 2;
   if (per > size_t(kLdsLimit)) {
     if (why) *why = "x of this width does not fit in LDS";
@@ -202,9 +209,12 @@ bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why) 
 }
 
 int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X, int64_t batch,
-                     int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream) {
-  if (batch > kLibraryGemmMinBatch && library_gemm_supported(rows, cols, batch, xt))
-    return launch_library_gemm(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+                     int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream, int shape, int ks) {
+  if (mfma_gemm_ok(X, batch, ldx, xt))
+    return launch_mfma_gemm(W, rows, cols, ldw, static_cast<const uint16_t*>(X), batch, ldx, Y, ldy, yt, shape, ks,
+                            stream);
+  if (xt == UW_BF16 && size_t(cols) * 2 > size_t(kLdsLimit))
+    return fail(UW_ERR_UNSUPPORTED, "bf16 product: X must be 16-byte aligned with ldx a multiple of 8 for this width");
   const int nbp = bf16_chunk(cols, batch, xt == UW_F32);
   for (int64_t b0 = 0; b0 < batch; b0 += nbp) {
     const int nb = int(std::min<int64_t>(nbp, batch - b0));

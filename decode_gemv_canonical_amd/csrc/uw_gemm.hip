@@ -1,0 +1,235 @@
+// Uncompressed bf16 product on the gfx950 matrix cores: the multiply of the
+// "full decode" pipeline (decompress to HBM, then a standard matmul; the
+// paragraph after the figure of the four execution pipelines in "Unweight:
+// how we compressed an LLM 22% without sacrificing quality") and the product
+// of plain-mode matrices.
+//
+// Y[b, n] = sum_k X[b, k] W[n, k]; W [rows, cols] and X [batch, cols] are
+// both k-contiguous, so v_mfma_f32_16x16x32_bf16 takes its operands straight
+// from global memory with no LDS staging: A = 16 weight rows, B = 16
+// activation rows, D[i][j] = Y[b_j][n_i].
+//
+// k order.  Per k-block of 128 columns, lane (r = lane % 16, q = lane / 16)
+// loads 32 consecutive values (64 bytes, four 16-byte loads) of its row at
+// k = 128 kb + 32 q, for W and for X alike; k-step s (0..3) hands the lane's
+// values 8 s .. 8 s + 7 to the matrix core.  MFMA element (s, q, e) is then
+// column 128 kb + 32 q + 8 s + e of both operands: the hardware sees k
+// permuted inside each block, identically for A and B, so the sum is the
+// same.  Every lane reads 64 contiguous bytes per row and k-block.
+//
+// A workgroup owns RB blocks of 16 weight rows and TB tiles of 16 batch
+// rows; its KS waves split the k-blocks (wave w takes kb = w, w + KS, ...)
+// and their partial tiles are summed in LDS at the end.  Workgroups are
+// numbered so that the batch tiles of one row group run back to back on one
+// XCD (workgroups are dealt to the 8 XCDs round-robin by index): the second
+// and later reads of a weight row come from that XCD's L2, not from HBM.
+#include <algorithm>
+
+#include "uw_device.h"
+
+namespace uw {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ floatx4 mfma16(const uint4& a, const uint4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// The lane's 32 values of one row for k-block k0 (zeros past cols; cols is a
+// multiple of 8, so each 16-byte piece is wholly inside or outside).
+__device__ __forceinline__ void load_row32(const uint16_t* p, int64_t k0, int64_t cols, uint4 (&v)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    v[u] = k0 + 8 * u + 8 <= cols ? *reinterpret_cast<const uint4*>(p + k0 + 8 * u) : uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int RB, int TB>
+struct Frag {
+  uint4 w[RB][4];
+  uint4 x[TB][4];
+};
+
+template <int RB, int TB>
+__device__ __forceinline__ void load_frag(const uint16_t* const (&wr)[RB], const uint16_t* const (&xr)[TB], int64_t k0,
+                                          int64_t kq, int64_t cols, Frag<RB, TB>& f) {
+#pragma unroll
+  for (int i = 0; i < RB; ++i) load_row32(wr[i], k0, cols - kq, f.w[i]);
+#pragma unroll
+  for (int t = 0; t < TB; ++t) load_row32(xr[t], k0, cols - kq, f.x[t]);
+}
+
+template <int RB, int TB>
+__device__ __forceinline__ void mma_frag(const Frag<RB, TB>& f, floatx4 (&acc)[RB][TB]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int t = 0; t < TB; ++t) acc[i][t] = mfma16(f.w[i][s], f.x[t][s], acc[i][t]);
+}
+
+// Grid: ceil(row groups / 8) * 8 * ny workgroups of KS waves (row group =
+// 16 RB weight rows, ny = batch tiles of 16 TB rows).  PIPE: the next
+// k-block's loads are issued before the current one is multiplied.
+template <int RB, int TB, bool YBF16, bool PIPE>
+__global__ __launch_bounds__(512) void bf16_mfma_kernel(const uint16_t* __restrict__ W, int64_t rows, int64_t cols,
+                                                        int64_t ldw, const uint16_t* __restrict__ X, int64_t ldx,
+                                                        int64_t batch, void* __restrict__ Y, int64_t ldy, int n_groups,
+                                                        int ny) {
+  extern __shared__ uint32_t lds[];
+  const int L = blockIdx.x;
+  const int grp = (L / (kXcds * ny)) * kXcds + L % kXcds;
+  const int y = (L / kXcds) % ny;
+  if (grp >= n_groups) return;
+  const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int ks = blockDim.x / kWave;
+  const int r = lane % 16, q = lane / 16;
+  const int64_t row0 = int64_t(grp) * 16 * RB, b0 = int64_t(y) * 16 * TB;
+  const int64_t kq = 32 * q;
+  const uint16_t* wr[RB];
+  const uint16_t* xr[TB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) wr[i] = W + std::min<int64_t>(row0 + 16 * i + r, rows - 1) * ldw + kq;
+#pragma unroll
+  for (int t = 0; t < TB; ++t) xr[t] = X + std::min<int64_t>(b0 + 16 * t + r, batch - 1) * ldx + kq;
+  floatx4 acc[RB][TB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t nkb = (cols + 127) / 128;
+  if constexpr (PIPE) {
+    Frag<RB, TB> fa, fb;
+    int64_t kb = wave;
+    if (kb < nkb) load_frag<RB, TB>(wr, xr, 128 * kb, kq, cols, fa);
+    for (; kb < nkb; kb += 2 * ks) {
+      if (kb + ks < nkb) load_frag<RB, TB>(wr, xr, 128 * (kb + ks), kq, cols, fb);
+      mma_frag<RB, TB>(fa, acc);
+      if (kb + ks >= nkb) break;
+      if (kb + 2 * ks < nkb) load_frag<RB, TB>(wr, xr, 128 * (kb + 2 * ks), kq, cols, fa);
+      mma_frag<RB, TB>(fb, acc);
+    }
+  } else {
+    for (int64_t kb = wave; kb < nkb; kb += ks) {
+      Frag<RB, TB> f;
+      load_frag<RB, TB>(wr, xr, 128 * kb, kq, cols, f);
+      mma_frag<RB, TB>(f, acc);
+    }
+  }
+  // partial tiles of the KS waves meet in LDS: tile (i, t) of wave w at
+  // ((w * RB + i) * TB + t) * 1 KB, lane-major 16 bytes per lane
+  if (ks > 1) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const floatx4 v = acc[i][t];
+        st128(uint32_t(((wave * RB + i) * TB + t) * 1024 + lane * 16),
+              uint4{f32_bits(v.x), f32_bits(v.y), f32_bits(v.z), f32_bits(v.w)});
+      }
+    lds_barrier();
+  }
+  // wave w stores the tiles with (i * TB + t) % KS == w; lane (r, q) holds
+  // rows 4 q .. 4 q + 3 of the tile for batch row r
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      if ((i * TB + t) % ks != wave) continue;
+      floatx4 v = acc[i][t];
+      if (ks > 1) {
+        v = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < ks; ++w) {
+          const uint4 p = ld128(uint32_t(((w * RB + i) * TB + t) * 1024 + lane * 16));
+          v += floatx4{bits_f32(p.x), bits_f32(p.y), bits_f32(p.z), bits_f32(p.w)};
+        }
+      }
+      const int64_t b = b0 + 16 * t + r;
+      const int64_t n = row0 + 16 * i + 4 * q;
+      if (b >= batch) continue;
+      const float vals[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e < rows) {
+          if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + n + e] = f32_to_bf16(vals[e]);
+          else static_cast<float*>(Y)[b * ldy + n + e] = vals[e];
+        }
+      }
+    }
+}
+
+template <int RB, int TB, bool PIPE>
+int run_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
+                  int64_t ldx, void* Y, int64_t ldy, int yt, int ks, void* stream) {
+  const int n_groups = int((rows + 16 * RB - 1) / (16 * RB));
+  const int ny = int((batch + 16 * TB - 1) / (16 * TB));
+  const int64_t grid = int64_t((n_groups + kXcds - 1) / kXcds) * kXcds * ny;
+  const size_t lds = ks > 1 ? size_t(ks) * RB * TB * 1024 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto kern = yt == UW_BF16 ? bf16_mfma_kernel<RB, TB, true, PIPE> : bf16_mfma_kernel<RB, TB, false, PIPE>;
+  allow_full_lds(kern);
+  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(ks * kWave), lds, s, W, rows, cols, ldw, X, ldx, batch, Y, ldy,
+                     n_groups, ny);
+  return hip_check(hipGetLastError(), "bf16_mfma_kernel launch");
+}
+
+}  // namespace
+
+// Shapes of the matrix-core product (a tuning knob: uw_bf16_gemm_config).
+// id: 0 = chosen by the heuristic below; else one of the listed shapes.
+struct MfmaShape {
+  int rb, tb, pipe;
+};
+constexpr MfmaShape kMfmaShapes[] = {
+    {0, 0, 0},  // heuristic
+    {1, 1, 1}, {2, 1, 1}, {1, 2, 1}, {2, 2, 1}, {1, 4, 1}, {2, 4, 0}, {4, 4, 0}, {4, 2, 0}, {2, 4, 1},
+};
+constexpr int kMfmaShapeCount = int(sizeof(kMfmaShapes) / sizeof(kMfmaShapes[0]));
+
+int mfma_gemm_shape_count() { return kMfmaShapeCount; }
+
+// The waves of a launch and the k-blocks each wave takes: KS (waves per
+// workgroup, 1..8) is the smallest that gives about 4096 waves, while every
+// wave keeps at least 2 k-blocks.
+static int pick_ks(int64_t rows, int64_t cols, int64_t batch, int rb, int tb) {
+  const int64_t groups = (rows + 16 * rb - 1) / (16 * rb);
+  const int64_t ny = (batch + 16 * tb - 1) / (16 * tb);
+  const int64_t nkb = (cols + 127) / 128;
+  int ks = 1;
+  while (ks < 8 && groups * ny * ks < 4096 && nkb / (2 * ks) >= 2) ks *= 2;
+  return ks;
+}
+
+int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
+                     int64_t ldx, void* Y, int64_t ldy, int yt, int shape, int ks, void* stream) {
+  if (shape <= 0 || shape >= kMfmaShapeCount) {
+    // heuristic: batch tiles of the pass up to 64 rows; more weight rows per
+    // workgroup when the batch is large (the activations are re-read once per
+    // weight row group)
+    if (batch <= 16) shape = 1;
+    else if (batch <= 32) shape = 3;
+    else if (batch <= 64) shape = 5;
+    else shape = 6;
+  }
+  const MfmaShape sh = kMfmaShapes[shape];
+  if (ks <= 0) ks = pick_ks(rows, cols, batch, sh.rb, sh.tb);
+  switch (shape) {
+    case 1: return run_mfma_gemm<1, 1, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 2: return run_mfma_gemm<2, 1, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 3: return run_mfma_gemm<1, 2, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 4: return run_mfma_gemm<2, 2, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 5: return run_mfma_gemm<1, 4, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 6: return run_mfma_gemm<2, 4, false>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 7: return run_mfma_gemm<4, 4, false>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 8: return run_mfma_gemm<4, 2, false>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    default: return run_mfma_gemm<2, 4, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+  }
+}
+
+}  // namespace uw

@@ -98,7 +98,9 @@ struct DevMatrix {
   int32_t n_items;                     // waves of work of those kernels: n_blocks when split, else n_units
   const uint32_t* tables;              // decode tables, built on the host (kDecodeTableBytes, the LDS image:
                                        //  pair table or 2^L single table, then the L <= 6 single table)
+  const uint32_t* index_tables;        // the same image with palette indices in place of exponents
 };
+
 
 // Bytes of the decode-table image: 4096 words (pair table, or the 2^L
 // single table for L > 6), then 64 words (the single table for L <= 6).
@@ -107,13 +109,19 @@ constexpr uint32_t kDecodeTableBytes = kDecodeTableWords * 4;
 
 }  // namespace uw
 
+// A direct-palette (UWP1) matrix bound to its device copy.
+struct uw_palette {
+  uw::PaletteLayout l;
+  const uint8_t* d_blob = nullptr;
+  int device = 0;
+};
+
 struct uw_matrix {
   uw::BlobHeader h;
   uw::DevMatrix dev;
-  const uint8_t* d_blob = nullptr;
-  void* d_steps = nullptr;  // device copy of the flat-walk step table (owned)
-  void* d_tables = nullptr;  // device copy of the decode tables (owned)
+  const uint8_t* d_blob = nullptr;    // the caller's device buffer: blob, then the derived tables
   int device = 0;
+  const uw_palette* palette = nullptr;  // attached direct-palette copy (not owned)
   mutable std::mutex mu;
   std::map<int64_t, uw_plan> plans;
 };
@@ -124,22 +132,34 @@ namespace uw {
 int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* stream);
 // Exponent bytes (R*C, the sm section's tile order); flat walk, not plain.
 int launch_decode_exponents(const uw_matrix* m, uint8_t* out, void* stream);
+// rs: ring depth of the flat walk (0 = chosen from the LDS budget, else 2 or 4).
 int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, int xt, void* Y,
-                 int64_t ldy, int yt, void* stream);
+                 int64_t ldy, int yt, void* stream, int rs = 0);
 bool fused_supported(const uw_matrix* m, int xt, std::string* why);
 // Batch rows the VALU fused product takes per pass (its x copy fits in LDS).
 int fused_rows_per_pass(const uw_matrix* m, int64_t batch, int xt);
+// nw: waves per workgroup (0 = chosen for the fewest idle waves, else 8..16).
 int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, void* Y, int64_t ldy, int yt,
-                      void* stream);
-bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why);
+                      void* stream, int nw = 0);
+bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why, int nw = 0);
+// Direct-palette transcode (uw_palette_transcode): the UWP1 layout of a
+// transcodable matrix, and the two kernels that write it.
+bool palette_transcodable(const uw_matrix* m, std::string* why);
+PaletteLayout transcode_layout(const uw_matrix* m);
+int launch_palette_transcode(const uw_matrix* m, uint8_t* out, void* stream);
 int launch_copy_plain(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* out, int64_t ld_out, void* stream);
-// rocBLAS bf16 GEMM (uw_blas.cpp): bf16 X only; Y fp32 or bf16.
-bool library_gemm_supported(int64_t rows, int64_t cols, int64_t batch, int xt);
-int launch_library_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X, int64_t batch,
-                        int64_t ldx, void* Y, int64_t ldy, int yt, void* stream);
+// bf16 product on the matrix cores (uw_gemm.hip): bf16 X, 16-byte aligned,
+// ldx and ldw multiples of 8.  shape: 0 = heuristic, else an index below
+// mfma_gemm_shape_count(); ks: waves per workgroup splitting k (0 = auto).
+int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
+                     int64_t ldx, void* Y, int64_t ldy, int yt, int shape, int ks, void* stream);
+int mfma_gemm_shape_count();
+// Any bf16 product: VALU up to batch 8 (or fp32 / unaligned X), else the matrix cores.
 int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X,
-                     int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream);
+                     int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream, int shape = 0,
+                     int ks = 0);
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why);
+// Cache eviction of the autotuner: read `bytes` (multiple of 16) at src.
 int launch_read_probe(const void* src, size_t bytes, void* sink, void* stream);
 size_t read_probe_sink_bytes();
 

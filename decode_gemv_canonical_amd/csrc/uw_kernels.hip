@@ -219,6 +219,7 @@ __device__ __forceinline__ uint32_t decode_tile(const DevMatrix& d, LaneDec& s, 
   uint32_t wp = (rpos >> 2) + 16 * uint32_t(__builtin_popcount(rmask));  // words
   const uint32_t pmask = PAIR ? 0x3FFCu : (((1u << d.L) - 1u) << 2);
   if (aligned) {
+    sink.tile_raw(rmask);
     sink.tile_begin(row0, c0);
     if (PAIR && rmask == 0) {
 #pragma unroll
@@ -752,6 +753,7 @@ struct DecompressSink {
     tcol = flat - trow * cols;
   }
   __device__ void row_end() {}
+  __device__ void tile_raw(uint32_t) {}
   __device__ void tile_begin(int64_t row0, int c0) {
     if (!FLAT) return;
     trow = row0;
@@ -808,6 +810,7 @@ struct ExpSink {
   __device__ void unit_end() {}
   __device__ void block_begin(int) {}
   __device__ void row_end() {}
+  __device__ void tile_raw(uint32_t) {}
   __device__ void tile_begin(int64_t row0, int c0) {
     dst = out + row0 * cols + int64_t(c0) * 64 + 16 * lane;
     w[0] = w[1] = w[2] = w[3] = 0u;
@@ -819,14 +822,72 @@ struct ExpSink {
   __device__ void tile_end(int, int) { *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]}; }
 };
 
-template <bool EXP, bool FLAT>
-__device__ inline auto make_decompress_sink(const DevMatrix& d, uint16_t* out, int64_t ld_out, uint32_t tile, int lane) {
-  if constexpr (EXP) return ExpSink{d.cols, reinterpret_cast<uint8_t*>(out), lane};
+// The direct-palette form (UWP1) of the decoded tiles, for the transcode at
+// load time.  The walk runs with the index tables, so a coded weight arrives
+// with its palette index where the exponent would be; a raw group's weights
+// arrive with their exponent bytes.  Tile T (1024 weights, flat walk: inside
+// one row) holds UWP1 weights 1024 T ..: the lane's weight of group j is
+// column 64 j + lane of the tile, so its sign+mantissa byte goes to sm
+// + 1024 T + 64 j + lane and its index nibble to idx byte 512 T + 32 j +
+// lane / 2 (even lane: low nibble; the odd neighbour's nibble comes over DPP);
+// raw group j of the tile (the rank-th raw group of the matrix, rank from
+// the prefix section the pre-pass wrote) puts its exponent bytes at raw +
+// 64 rank.
+struct PaletteOut {
+  uint8_t* sm;
+  uint8_t* idx;
+  uint8_t* raw;
+  const uint32_t* prefix;
+};
+
+struct PaletteSink {
+  PaletteOut o;
+  int tpr;  // tiles per row
+  int lane;
+  uint8_t* dsm = nullptr;
+  uint8_t* didx = nullptr;
+  uint8_t* draw = nullptr;
+  uint32_t rmask = 0;
+  __device__ void unit_begin(int) {}
+  __device__ void unit_end() {}
+  __device__ void block_begin(int) {}
+  __device__ void row_end() {}
+  __device__ void tile_raw(uint32_t r) { rmask = r; }
+  __device__ void tile_begin(int64_t row0, int c0) {
+    const int64_t T = row0 * tpr + (c0 >> 4);
+    dsm = o.sm + T * 1024 + lane;
+    didx = o.idx + T * 512 + (lane >> 1);
+    draw = o.raw + int64_t(scalar_word(o.prefix, T)) * 64 + lane;
+  }
+  __device__ void one(int j, uint32_t h) {  // h: the weight's bf16 bits (exponent field = index or raw exponent)
+    dsm[64 * j] = uint8_t(((h >> 8) & 0x80u) | (h & 0x7Fu));
+    const uint32_t e = (h >> 7) & 0xFFu;
+    const bool raw = (rmask >> j) & 1u;  // wave-uniform
+    const uint32_t nib = raw ? 0u : e;
+    const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(nib), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    if (!(lane & 1)) didx[32 * j] = uint8_t(nib | (other << 4));
+    if (raw) draw[64 * __builtin_popcount(rmask & ((1u << j) - 1u))] = uint8_t(e);
+  }
+  __device__ void pair(int k, uint32_t D) {
+    one(2 * k, D & 0xFFFFu);
+    one(2 * k + 1, D >> 16);
+  }
+  __device__ void single(int, int64_t, int, uint32_t) {}  // flat-walk tiles are always whole
+  __device__ void tile_end(int, int) {}
+};
+
+// SINK: 0 = bf16 weights, 1 = exponent bytes, 2 = the direct-palette form.
+template <int SINK, bool FLAT>
+__device__ inline auto make_decompress_sink(const DevMatrix& d, uint16_t* out, int64_t ld_out, const PaletteOut& po,
+                                            uint32_t tile, int lane) {
+  if constexpr (SINK == 1) return ExpSink{d.cols, reinterpret_cast<uint8_t*>(out), lane};
+  else if constexpr (SINK == 2) return PaletteSink{po, d.gpr >> 4, lane};
   else return DecompressSink<FLAT>{d.cols, d.G, out, ld_out, tile, lane, 0, 0};
 }
 
-template <bool PAIR, int NQ, bool FLAT, int RS, bool EXP = false>
-__global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t* __restrict__ out, int64_t ld_out) {
+template <bool PAIR, int NQ, bool FLAT, int RS, int SINK = 0>
+__global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t* __restrict__ out, int64_t ld_out,
+                                                          PaletteOut po) {
   extern __shared__ uint32_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int waves = blockDim.x / kWave;
@@ -848,8 +909,8 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   }
   if (n_tab) wait_tables<RS, NQ>(issued);
   lds_barrier();
-  using Sink = std::conditional_t<EXP, ExpSink, DecompressSink<FLAT>>;
-  Sink sink = make_decompress_sink<EXP, FLAT>(d, out, ld_out, tile, lane);
+  using Sink = std::conditional_t<SINK == 1, ExpSink, std::conditional_t<SINK == 2, PaletteSink, DecompressSink<FLAT>>>;
+  Sink sink = make_decompress_sink<SINK, FLAT>(d, out, ld_out, po, tile, lane);
   for (int u = u_first; u < n_items; u += gridDim.x * waves) {
     // the two 16-byte stores per tile only make the ring waits stricter
     if (FLAT) {
@@ -861,6 +922,59 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
       run_blocks<RS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
     }
   }
+}
+
+// Transcode pre-pass (one workgroup): the UWP1 raw flags (16 bits per tile)
+// and per-tile raw-group prefix counts from the raw bits in every block's
+// head.  Thread i takes a contiguous run of blocks; the runs' counts are
+// scanned in LDS.
+__global__ __launch_bounds__(1024) void palette_prefix_kernel(DevMatrix d, uint16_t* __restrict__ flags,
+                                                               uint32_t* __restrict__ prefix) {
+  __shared__ uint32_t part[1024];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (d.n_blocks + nt - 1) / nt;
+  const int b0 = std::min(d.n_blocks, tid * per), b1 = std::min(d.n_blocks, b0 + per);
+  auto raw_word = [&](int b, int w) {
+    return *reinterpret_cast<const uint32_t*>(d.queue + d.block_off[b] + 128 + 4 * w);
+  };
+  uint32_t cnt = 0;
+  for (int b = b0; b < b1; ++b)
+    for (int w = 0; w < d.rb_words; ++w) cnt += __builtin_popcount(raw_word(b, w));
+  part[tid] = cnt;
+  __syncthreads();
+  // exclusive scan of part[] (Hillis-Steele over the 1024 entries)
+  for (int off = 1; off < nt; off <<= 1) {
+    const uint32_t v = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  uint32_t run = part[tid] - cnt;
+  for (int b = b0; b < b1; ++b) {
+    // the last block may be short: only its own tiles (flat walk: whole tiles)
+    const int nt_b = int(std::min<int64_t>(d.G, d.n_groups - int64_t(b) * d.G) / 16);
+    for (int t = 0; t < nt_b; ++t) {
+      const int64_t T = int64_t(b) * d.T + t;
+      const uint32_t f = (raw_word(b, (16 * t) >> 5) >> ((16 * t) & 31)) & 0xFFFFu;
+      flags[T] = uint16_t(f);
+      prefix[T] = run;
+      run += __builtin_popcount(f);
+    }
+  }
+}
+
+// Header and the zero bytes between sections of the transcoded UWP1 blob.
+struct PaletteFill {
+  uint32_t head[16];        // the 64-byte header
+  uint64_t gap_lo[6], gap_hi[6];  // byte ranges to clear
+};
+__global__ void palette_fill_kernel(uint8_t* __restrict__ out, PaletteFill f) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid < 16) reinterpret_cast<uint32_t*>(out)[tid] = f.head[tid];
+  for (int g = 0; g < 6; ++g)
+    for (uint64_t i = f.gap_lo[g] + uint64_t(blockIdx.x) * blockDim.x + tid; i < f.gap_hi[g];
+         i += uint64_t(gridDim.x) * blockDim.x)
+      out[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -987,6 +1101,7 @@ struct ProductSink {
       cur_row = r;
     }
   }
+  __device__ void tile_raw(uint32_t) {}
   __device__ void tile_begin(int64_t row0, int c) {
     if (!FLAT) to_row(row0);  // the flat walk ends rows with row_end()
     c0 = c;
@@ -1189,6 +1304,7 @@ __device__ inline floatx4 mfma_bf16(const uint4& a, const uint4& b, const floatx
 struct SliceSink {
   uint32_t row_addr;
   int lane;
+  __device__ void tile_raw(uint32_t) {}
   __device__ void tile_begin(int64_t, int) {}
   __device__ void pair(int k, uint32_t D) {
     st16(row_addr + ((2 * k) * kWave + lane) * 2, D);
@@ -1471,7 +1587,7 @@ int flat_ring_depth(int64_t units, size_t fixed, int slot_bytes, size_t extra, i
 }
 
 template <int NBP, bool XF32, bool PAIR, bool YBF16>
-int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, void* stream) {
+int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, void* stream, int rs_knob) {
   DevMatrix d = m->dev;  // a copy: split rows may be turned off for this launch
   const size_t fixed = tables_bytes() + x_bytes(d, NBP, XF32);
   const int max_waves = fused_max_threads(NBP, XF32, d.flat) / kWave;
@@ -1485,6 +1601,7 @@ int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, i
   const int items = d.flat ? d.n_items : d.n_units;
   const size_t extra = d.split ? 4 * NBP : 0;
   int rs = d.flat ? flat_ring_depth(items, fixed, d.slot_bytes, extra, max_waves) : kRS;
+  if (d.flat && rs_knob) rs = rs_knob == 4 ? kRS : kRSLow;
   if (d.split && fixed + (ring_bytes(rs, d.slot_bytes) + extra) * d.unit_blocks > size_t(kLdsLimit)) rs = kRSLow;
   const size_t per_wave = ring_bytes(rs, d.slot_bytes) + extra;
   if (fixed + per_wave * (d.split ? d.unit_blocks : 1) > size_t(kLdsLimit))
@@ -1506,21 +1623,22 @@ int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, i
 }
 
 template <int NBP, bool XF32, bool PAIR>
-int run_fused_y(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt, void* stream) {
-  return yt == UW_BF16 ? run_fused<NBP, XF32, PAIR, true>(m, X, ldx, nb, Y, ldy, stream)
-                       : run_fused<NBP, XF32, PAIR, false>(m, X, ldx, nb, Y, ldy, stream);
+int run_fused_y(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt, void* stream, int rs) {
+  return yt == UW_BF16 ? run_fused<NBP, XF32, PAIR, true>(m, X, ldx, nb, Y, ldy, stream, rs)
+                       : run_fused<NBP, XF32, PAIR, false>(m, X, ldx, nb, Y, ldy, stream, rs);
 }
 
 template <int NBP, bool XF32>
-int run_fused_p(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt, void* stream) {
-  return is_pair(m->dev) ? run_fused_y<NBP, XF32, true>(m, X, ldx, nb, Y, ldy, yt, stream)
-                         : run_fused_y<NBP, XF32, false>(m, X, ldx, nb, Y, ldy, yt, stream);
+int run_fused_p(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt, void* stream, int rs) {
+  return is_pair(m->dev) ? run_fused_y<NBP, XF32, true>(m, X, ldx, nb, Y, ldy, yt, stream, rs)
+                         : run_fused_y<NBP, XF32, false>(m, X, ldx, nb, Y, ldy, yt, stream, rs);
 }
 
 template <int NBP>
-int run_fused_x(const uw_matrix* m, const void* X, int64_t ldx, int xt, int nb, void* Y, int64_t ldy, int yt, void* stream) {
-  return xt == UW_F32 ? run_fused_p<NBP, true>(m, X, ldx, nb, Y, ldy, yt, stream)
-                      : run_fused_p<NBP, false>(m, X, ldx, nb, Y, ldy, yt, stream);
+int run_fused_x(const uw_matrix* m, const void* X, int64_t ldx, int xt, int nb, void* Y, int64_t ldy, int yt, void* stream,
+                int rs) {
+  return xt == UW_F32 ? run_fused_p<NBP, true>(m, X, ldx, nb, Y, ldy, yt, stream, rs)
+                      : run_fused_p<NBP, false>(m, X, ldx, nb, Y, ldy, yt, stream, rs);
 }
 
 // Largest batch chunk (1, 2, 4 or 8) whose X copy fits next to the tables and one stage buffer per wave.
@@ -1556,7 +1674,7 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
   };
   auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
   allow_full_lds(kern);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, out, ld_out);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, out, ld_out, PaletteOut{});
   return hip_check(hipGetLastError(), "decompress_kernel launch");
 }
 
@@ -1574,14 +1692,89 @@ int launch_decode_exponents(const uw_matrix* m, uint8_t* out, void* stream) {
   const int grid = int(std::max<int64_t>(1, (int64_t(items) + waves - 1) / waves));
   auto pick = [&](auto pair) {
     constexpr bool P = decltype(pair)::value;
-    return rs == kRS ? (d.nq == 2 ? decompress_kernel<P, 2, true, kRS, true> : decompress_kernel<P, 4, true, kRS, true>)
-                     : (d.nq == 2 ? decompress_kernel<P, 2, true, kRSLow, true>
-                                  : decompress_kernel<P, 4, true, kRSLow, true>);
+    return rs == kRS ? (d.nq == 2 ? decompress_kernel<P, 2, true, kRS, 1> : decompress_kernel<P, 4, true, kRS, 1>)
+                     : (d.nq == 2 ? decompress_kernel<P, 2, true, kRSLow, 1>
+                                  : decompress_kernel<P, 4, true, kRSLow, 1>);
   };
   auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
   allow_full_lds(kern);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, reinterpret_cast<uint16_t*>(out), int64_t(0));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, reinterpret_cast<uint16_t*>(out), int64_t(0),
+                     PaletteOut{});
   return hip_check(hipGetLastError(), "decompress_kernel (exponents) launch");
+}
+
+bool palette_transcodable(const uw_matrix* m, std::string* why) {
+  const BlobHeader& h = m->h;
+  const char* no = nullptr;
+  if (h.plain()) no = "a plain-mode matrix has no palette";
+  else if (!m->dev.flat) no = "the transcode needs the flat walk (G and cols/64 multiples of 16)";
+  else if (h.cols % 1024) no = "the direct form needs cols to be a multiple of 1024";
+  else if (h.K > 16 || (h.K < 16 && h.n_raw_groups > 0))
+    no = "the palette is not the direct form's (K must be 16, or smaller with no raw group)";
+  if (no && why) *why = no;
+  return !no;
+}
+
+PaletteLayout transcode_layout(const uw_matrix* m) {
+  PaletteLayout l = palette_layout(m->h.rows, m->h.cols, int64_t(m->h.n_raw_groups));
+  l.n_pal = int(m->h.K);
+  std::memset(l.palette, 0, sizeof(l.palette));
+  std::memcpy(l.palette, m->h.palette, size_t(l.n_pal));
+  return l;
+}
+
+int launch_palette_transcode(const uw_matrix* m, uint8_t* out, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PaletteLayout l = transcode_layout(m);
+  DevMatrix d = m->dev;
+  const int64_t n = d.rows * d.cols, n_tiles = n / 1024;
+  // header and the gaps between sections
+  PaletteFill f;
+  std::memset(&f, 0, sizeof(f));
+  uint8_t head[64] = {0};
+  std::memcpy(head, "UWP1", 4);
+  const uint32_t version = 1, n_pal = uint32_t(l.n_pal);
+  const uint64_t rows = uint64_t(l.rows), cols = uint64_t(l.cols), n_raw = uint64_t(l.n_raw);
+  std::memcpy(head + 4, &version, 4);
+  std::memcpy(head + 8, &rows, 8);
+  std::memcpy(head + 16, &cols, 8);
+  std::memcpy(head + 24, &n_raw, 8);
+  std::memcpy(head + 32, l.palette, 16);
+  std::memcpy(head + 48, &n_pal, 4);
+  std::memcpy(f.head, head, 64);
+  const uint64_t lo[6] = {64, l.off_sm + uint64_t(n), l.off_idx + uint64_t(n / 2), l.off_flags + 2 * uint64_t(n_tiles),
+                          l.off_prefix + 4 * uint64_t(n_tiles), l.off_raw + 64 * n_raw};
+  const uint64_t hi[6] = {l.off_sm, l.off_idx, l.off_flags, l.off_prefix, l.off_raw, l.total};
+  for (int i = 0; i < 6; ++i) {
+    f.gap_lo[i] = lo[i];
+    f.gap_hi[i] = hi[i];
+  }
+  hipLaunchKernelGGL(palette_fill_kernel, dim3(4), dim3(256), 0, s, out, f);
+  if (int rc = hip_check(hipGetLastError(), "palette_fill_kernel launch")) return rc;
+  hipLaunchKernelGGL(palette_prefix_kernel, dim3(1), dim3(1024), 0, s, d, reinterpret_cast<uint16_t*>(out + l.off_flags),
+                     reinterpret_cast<uint32_t*>(out + l.off_prefix));
+  if (int rc = hip_check(hipGetLastError(), "palette_prefix_kernel launch")) return rc;
+  // the walk, with palette indices where the exponents would be
+  d.tables = d.index_tables;
+  const PaletteOut po{out + l.off_sm, out + l.off_idx, out + l.off_raw,
+                      reinterpret_cast<const uint32_t*>(out + l.off_prefix)};
+  const size_t fixed = tables_bytes();
+  const int items = d.n_items;
+  const int rs = flat_ring_depth(items, fixed, d.slot_bytes, 0, 16);
+  const size_t per_wave = ring_bytes(rs, d.slot_bytes);
+  const int waves = pick_waves(items, fixed, per_wave);
+  const size_t lds = fixed + per_wave * waves;
+  const int grid = int(std::max<int64_t>(1, (int64_t(items) + waves - 1) / waves));
+  auto pick = [&](auto pair) {
+    constexpr bool P = decltype(pair)::value;
+    return rs == kRS ? (d.nq == 2 ? decompress_kernel<P, 2, true, kRS, 2> : decompress_kernel<P, 4, true, kRS, 2>)
+                     : (d.nq == 2 ? decompress_kernel<P, 2, true, kRSLow, 2>
+                                  : decompress_kernel<P, 4, true, kRSLow, 2>);
+  };
+  auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
+  allow_full_lds(kern);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, static_cast<uint16_t*>(nullptr), int64_t(0), po);
+  return hip_check(hipGetLastError(), "decompress_kernel (palette transcode) launch");
 }
 
 int fused_rows_per_pass(const uw_matrix* m, int64_t batch, int xt) {
@@ -1605,7 +1798,7 @@ bool fused_supported(const uw_matrix* m, int xt, std::string* why) {
 
 // Walk of the matrix-core kernel: waves per workgroup from the LDS budget,
 // chosen so that the tasks fill whole rounds of 256 workgroups.
-bool mfma_geometry(const DevMatrix& d, MfmaGeom* g, std::string* why) {
+bool mfma_geometry(const DevMatrix& d, MfmaGeom* g, std::string* why, int nw_knob = 0) {
   if (d.gpr % 16) {
     if (why) *why = "the matrix-core path needs cols to be a multiple of 1024";
     return false;
@@ -1634,9 +1827,14 @@ bool mfma_geometry(const DevMatrix& d, MfmaGeom* g, std::string* why) {
   }
   const int64_t units = g->split ? d.n_blocks : d.n_units;
   const int step_nw = g->split ? d.unit_blocks : 1;
+  const int nw_top = g->split ? nw_split : nw_max;
+  if (nw_knob && (nw_knob < 8 || nw_knob > nw_top || nw_knob % step_nw)) {
+    if (why) *why = "this waves-per-workgroup knob does not fit the matrix's blocks";
+    return false;
+  }
   double best = -1.0;
-  for (int nw = 8; nw <= (g->split ? nw_split : nw_max); ++nw) {
-    if (nw % step_nw) continue;
+  for (int nw = 8; nw <= nw_top; ++nw) {
+    if (nw % step_nw || (nw_knob && nw != nw_knob)) continue;
     const int64_t tasks = (units + nw - 1) / nw;
     const int64_t rounds = (tasks + 255) / 256;
     const double eff = double(units) / double(rounds * 256 * nw);
@@ -1680,7 +1878,7 @@ int run_mfma_tb(const uw_matrix* m, const MfmaGeom& g, const uint16_t* X, int64_
   return run_mfma_ipw<4, PAIR>(m, g, X, ldx, nb, Y, ldy, yt, s);
 }
 
-bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why) {
+bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why, int nw) {
   if (m->h.plain()) {
     if (why) *why = "a plain-mode matrix has nothing to decode";
     return false;
@@ -1690,15 +1888,15 @@ bool fused_mfma_supported(const uw_matrix* m, int xt, std::string* why) {
     return false;
   }
   MfmaGeom g;
-  return mfma_geometry(m->dev, &g, why);
+  return mfma_geometry(m->dev, &g, why, nw);
 }
 
 int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, void* Y, int64_t ldy, int yt,
-                      void* stream) {
+                      void* stream, int nw) {
   const DevMatrix& d = m->dev;
   MfmaGeom g;
   std::string why;
-  if (!mfma_geometry(d, &g, &why)) return fail(UW_ERR_UNSUPPORTED, "fused matrix-core product: " + why);
+  if (!mfma_geometry(d, &g, &why, nw)) return fail(UW_ERR_UNSUPPORTED, "fused matrix-core product: " + why);
   if (reinterpret_cast<uintptr_t>(X) % 16 || ldx % 8)
     return fail(UW_ERR_UNSUPPORTED, "fused matrix-core product: X must be 16-byte aligned with ldx a multiple of 8");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1714,7 +1912,7 @@ int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t 
 }
 
 int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt,
-                 void* stream) {
+                 void* stream, int rs) {
   const DevMatrix& d = m->dev;
   if (m->h.plain()) return launch_bf16_gemm(d.plain, d.rows, d.cols, d.cols, X, batch, ldx, xt, Y, ldy, yt, stream);
   const int nbp = fused_chunk(d, batch, xt == UW_F32);
@@ -1724,10 +1922,10 @@ int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, 
     void* Yb = static_cast<char*>(Y) + b0 * ldy * elem_size(yt);
     int rc;
     switch (nbp) {
-      case 1: rc = run_fused_x<1>(m, Xb, ldx, xt, nb, Yb, ldy, yt, stream); break;
-      case 2: rc = run_fused_x<2>(m, Xb, ldx, xt, nb, Yb, ldy, yt, stream); break;
-      case 4: rc = run_fused_x<4>(m, Xb, ldx, xt, nb, Yb, ldy, yt, stream); break;
-      default: rc = run_fused_x<8>(m, Xb, ldx, xt, nb, Yb, ldy, yt, stream); break;
+      case 1: rc = run_fused_x<1>(m, Xb, ldx, xt, nb, Yb, ldy, yt, stream, rs); break;
+      case 2: rc = run_fused_x<2>(m, Xb, ldx, xt, nb, Yb, ldy, yt, stream, rs); break;
+      case 4: rc = run_fused_x<4>(m, Xb, ldx, xt, nb, Yb, ldy, yt, stream, rs); break;
+      default: rc = run_fused_x<8>(m, Xb, ldx, xt, nb, Yb, ldy, yt, stream, rs); break;
     }
     if (rc) return rc;
   }

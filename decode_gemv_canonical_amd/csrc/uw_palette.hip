@@ -16,12 +16,6 @@
 
 #include "uw_device.h"
 
-struct uw_palette {
-  uw::PaletteLayout l;
-  const uint8_t* d_blob = nullptr;
-  int device = 0;
-};
-
 namespace uw {
 namespace {
 

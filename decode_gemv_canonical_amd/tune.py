@@ -12,9 +12,11 @@ Here a "layer" is whatever callable the caller gives: it runs one pass of the
 layer with one variant per projection (for the MLP: h = silu(W_gate x) *
 (W_up x), y = W_down h).  Every product inside it is a library call; this
 module only times the layer (a captured HIP graph, replayed) and records the
-choice.  The plan file is JSON: {"model": name, "plans": {projection:
-{batch: {"variant": v, "layer_us": t}}}}; load_plan_file installs the choices
-with uw_set_plan so that UW_VARIANT_AUTO follows them.
+choice.  install_choice stores the choice on each projection's handle
+(uw_set_plan); the plan file is JSON {"format": "uw-model-plan-1", "model":
+name, "projections": {projection: <that handle's uw_plan_save document>}},
+and load_plan_file hands each document back to uw_plan_load, which checks
+that it belongs to the same matrix, so that UW_VARIANT_AUTO follows it.
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ import json
 
 from . import uw
 
-CANDIDATES = (uw.UW_VARIANT_FUSED, uw.UW_VARIANT_FUSED_MFMA, uw.UW_VARIANT_DECOMPRESS_GEMM)
+CANDIDATES = (uw.UW_VARIANT_FUSED, uw.UW_VARIANT_FUSED_MFMA, uw.UW_VARIANT_DECOMPRESS_GEMM, uw.UW_VARIANT_PALETTE)
 
 
 def time_layer_us(run, steps: int = 200, warmup: int = 200) -> float:
@@ -86,35 +88,43 @@ def coordinate_descent(projections, layer, start=None, candidates=CANDIDATES, ma
     return choice, best, history
 
 
-def save_plan_file(path: str, model: str, plans: dict) -> None:
-    """plans: {projection: {batch: (variant, layer_us)}}."""
-    out = {"model": model, "plans": {p: {str(b): {"variant": int(v), "layer_us": float(t)}
-                                         for b, (v, t) in sorted(by_batch.items())}
-                                     for p, by_batch in plans.items()}}
+def install_choice(handles: dict, batch: int, choice: dict, layer_us: float) -> None:
+    """Store the chosen variant of every projection for this batch on its
+    handle (handles: {projection: uw_matrix handle})."""
+    for p, v in choice.items():
+        uw.uw_set_plan(handles[p], batch, v, layer_us)
+
+
+def save_plan_file(path: str, model: str, handles: dict) -> dict:
+    """Write the plans stored on every projection's handle (uw_plan_save) as
+    one per-model file; returns the document written."""
+    doc = {"format": "uw-model-plan-1", "model": model,
+           "projections": {p: json.loads(uw.uw_plan_save(h)) for p, h in sorted(handles.items())}}
     with open(path, "w") as f:
-        json.dump(out, f, indent=1, sort_keys=True)
+        json.dump(doc, f, indent=1, sort_keys=True)
+    return doc
 
 
 def read_plan_file(path: str) -> dict:
-    """{projection: {batch: (variant, layer_us)}}, checked."""
+    """The per-model document, with its structure checked (each projection's
+    entries are checked again by uw_plan_load)."""
     with open(path) as f:
-        raw = json.load(f)
-    plans = {}
-    for p, by_batch in raw["plans"].items():
-        plans[p] = {}
-        for b, rec in by_batch.items():
-            v = int(rec["variant"])
-            if v not in CANDIDATES or int(b) < 1:
-                raise ValueError(f"plan file {path}: bad entry {p} batch {b}")
-            plans[p][int(b)] = (v, float(rec["layer_us"]))
-    return plans
+        doc = json.load(f)
+    if doc.get("format") != "uw-model-plan-1" or not isinstance(doc.get("projections"), dict):
+        raise ValueError(f"plan file {path}: not a uw-model-plan-1 document")
+    for p, entry in doc["projections"].items():
+        if not isinstance(entry, dict) or entry.get("format") != "uw-plan-1":
+            raise ValueError(f"plan file {path}: projection {p} is not a uw-plan-1 document")
+    return doc
 
 
 def load_plan_file(path: str, handles: dict) -> dict:
-    """Install every plan of the file on the handle of its projection
-    (handles: {projection: uw_matrix handle}); returns the plans read."""
-    plans = read_plan_file(path)
-    for p, by_batch in plans.items():
-        for b, (v, t) in by_batch.items():
-            uw.uw_set_plan(handles[p], b, v, t)
-    return plans
+    """Install every projection's plans on its handle (handles: {projection:
+    uw_matrix handle}) with uw_plan_load; returns the document read."""
+    doc = read_plan_file(path)
+    missing = set(doc["projections"]) - set(handles)
+    if missing:
+        raise ValueError(f"plan file {path}: no handle for {sorted(missing)}")
+    for p, entry in doc["projections"].items():
+        uw.uw_plan_load(handles[p], json.dumps(entry))
+    return doc

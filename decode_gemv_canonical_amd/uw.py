@@ -29,10 +29,11 @@ UW_VARIANT_AUTO = 0
 UW_VARIANT_FUSED = 1
 UW_VARIANT_DECOMPRESS_GEMM = 2
 UW_VARIANT_FUSED_MFMA = 3
-UW_VARIANT_COUNT = 4
+UW_VARIANT_PALETTE = 4
+UW_VARIANT_COUNT = 5
 UW_ENC_NO_PLAIN = 1
-VARIANT_NAMES = {UW_VARIANT_AUTO: "auto", UW_VARIANT_FUSED: "fused", UW_VARIANT_DECOMPRESS_GEMM: "decompress+gemm",
-                 UW_VARIANT_FUSED_MFMA: "fused-mfma"}
+VARIANT_NAMES = {UW_VARIANT_AUTO: "auto", UW_VARIANT_FUSED: "fused", UW_VARIANT_DECOMPRESS_GEMM: "decompress_gemm",
+                 UW_VARIANT_FUSED_MFMA: "fused_mfma", UW_VARIANT_PALETTE: "palette"}
 
 
 class UwError(RuntimeError):
@@ -54,8 +55,9 @@ class uw_info(ctypes.Structure):
 
 
 class uw_plan(ctypes.Structure):
-    _fields_ = [("batch", ctypes.c_int64), ("variant", ctypes.c_int32), ("time_us", ctypes.c_float),
-                ("candidate_us", ctypes.c_float * UW_VARIANT_COUNT)]
+    _fields_ = [("batch", ctypes.c_int64), ("variant", ctypes.c_int32), ("knob", ctypes.c_int32),
+                ("time_us", ctypes.c_float), ("candidate_us", ctypes.c_float * UW_VARIANT_COUNT),
+                ("candidate_knob", ctypes.c_int32 * UW_VARIANT_COUNT)]
 
 
 def _load() -> ctypes.CDLL:
@@ -69,11 +71,16 @@ def _load() -> ctypes.CDLL:
         "uw_last_error": (ctypes.c_char_p, []),
         "uw_encode": (I, [P, I64, I64, ctypes.POINTER(uw_encode_opts), P, ctypes.POINTER(SZ)]),
         "uw_blob_info": (I, [P, SZ, ctypes.POINTER(uw_info)]),
-        "uw_matrix_create": (I, [P, SZ, P, ctypes.POINTER(P)]),
+        "uw_matrix_device_bytes": (SZ, [P, SZ]),
+        "uw_matrix_create": (I, [P, SZ, P, SZ, ctypes.POINTER(P)]),
+        "uw_matrix_attach_palette": (I, [P, P]),
         "uw_matrix_destroy": (None, [P]),
         "uw_decompress": (I, [P, P, I64, P]),
         "uw_gemv_fused": (I, [P, P, I, P, I, P]),
         "uw_gemm_fused": (I, [P, P, I64, I64, I, P, I64, I, I, P, SZ, P]),
+        "uw_gemm_with_plan": (I, [P, ctypes.POINTER(uw_plan), P, I64, I64, I, P, I64, I, P, SZ, P]),
+        "uw_plan_save": (I, [P, ctypes.c_char_p, ctypes.POINTER(SZ)]),
+        "uw_plan_load": (I, [P, ctypes.c_char_p]),
         "uw_workspace_size": (SZ, [P, I64, I]),
         "uw_autotune": (I, [P, I64, P, SZ, P, ctypes.POINTER(uw_plan)]),
         "uw_autotune_scratch_size": (SZ, [P, I64]),
@@ -82,6 +89,8 @@ def _load() -> ctypes.CDLL:
         "uw_exponent_gemm": (I, [P, P, I64, I64, I, P, I64, I, P, SZ, P]),
         "uw_exponent_ws_size": (SZ, [P, I64]),
         "uw_bf16_gemm": (I, [P, I64, I64, I64, P, I64, I64, I, P, I64, I, P]),
+        "uw_bf16_gemm_shaped": (I, [P, I64, I64, I64, P, I64, I64, P, I64, I, I, I, P]),
+        "uw_bf16_gemm_shape_count": (I, []),
         "uw_read_probe": (I, [P, SZ, P, P]),
         "uw_read_probe_sink_size": (SZ, []),
         "uw_palette_encode": (I, [P, I64, I64, P, ctypes.POINTER(SZ)]),
@@ -91,6 +100,9 @@ def _load() -> ctypes.CDLL:
         "uw_palette_gemv": (I, [P, P, I, P, I, P]),
         "uw_palette_decompress": (I, [P, P, I64, P]),
         "uw_palette_gemm": (I, [P, P, I64, I64, I, P, I64, I, P]),
+        "uw_palette_transcode_size": (SZ, [P]),
+        "uw_palette_transcode": (I, [P, P, SZ, P]),
+        "uw_palette_create_transcoded": (I, [P, P, ctypes.POINTER(P)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -133,6 +145,49 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.bfloat16:
         return UW_BF16
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+# Shapes of live handles (rows, cols, device index), so that the wrappers can
+# check tensors before the library sees their pointers: the C side cannot
+# know how large a buffer is, and an undersized or foreign one would be read
+# or written out of bounds on the device.
+_handles: dict[int, tuple[int, int, int]] = {}
+
+
+def _register(handle: int, rows: int, cols: int, device_index: int) -> None:
+    _handles[handle] = (rows, cols, device_index)
+
+
+def _shape(handle: int) -> tuple[int, int, int]:
+    if handle not in _handles:
+        raise ValueError("unknown or closed handle")
+    return _handles[handle]
+
+
+def _on_device(t, dev: int, name: str) -> None:
+    if not hasattr(t, "is_cuda") or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if t.device.index != dev:
+        raise ValueError(f"{name} is on cuda:{t.device.index}, the handle on cuda:{dev}")
+
+
+def _check_vector(t, n: int, dev: int, name: str) -> None:
+    if t.dim() != 1 or t.numel() != n or (n > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous vector of {n} elements, got shape {tuple(t.shape)}")
+    _on_device(t, dev, name)
+
+
+def _check_rows(t, batch: int | None, width: int, dev: int, name: str, exact: bool = True) -> None:
+    """A [batch, >= width] (or == width) row-major tensor with unit inner stride."""
+    if t.dim() != 2 or (batch is not None and t.shape[0] != batch):
+        raise ValueError(f"{name} must be 2-D with {batch} rows, got shape {tuple(t.shape)}")
+    if (t.shape[1] != width) if exact else (t.shape[1] < width):
+        raise ValueError(f"{name} must have {'' if exact else 'at least '}{width} columns, got {t.shape[1]}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have a unit inner stride")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} rows overlap")
+    _on_device(t, dev, name)
 
 
 def _as_u16(w) -> np.ndarray:
@@ -182,37 +237,103 @@ def uw_blob_info(blob: bytes) -> dict:
     return out
 
 
-def uw_matrix_create(host_blob: bytes, d_blob) -> int:
-    """Handle for a blob already copied into the CUDA uint8 tensor d_blob (256-byte aligned)."""
+def uw_matrix_device_bytes(host_blob: bytes) -> int:
     arr = np.frombuffer(host_blob, dtype=np.uint8)
-    if d_blob.numel() != arr.size:
-        raise ValueError("device blob size differs from the host blob")
+    n = _lib.uw_matrix_device_bytes(arr.ctypes.data, arr.size)
+    if n == 0:
+        raise UwError(UW_ERR_FORMAT, "uw_matrix_device_bytes", uw_last_error())
+    return n
+
+
+def uw_matrix_create(host_blob: bytes, d_buf) -> int:
+    """Handle for a blob already copied to the start of the CUDA uint8 tensor
+    d_buf (256-byte aligned, at least uw_matrix_device_bytes(host_blob) bytes;
+    the library writes its derived tables after the blob)."""
+    arr = np.frombuffer(host_blob, dtype=np.uint8)
+    if d_buf.dtype.itemsize != 1 or not d_buf.is_contiguous():
+        raise ValueError("the device buffer must be a contiguous byte tensor")
     h = ctypes.c_void_p()
-    _check(_lib.uw_matrix_create(arr.ctypes.data, arr.size, d_blob.data_ptr(), ctypes.byref(h)), "uw_matrix_create")
+    _check(_lib.uw_matrix_create(arr.ctypes.data, arr.size, d_buf.data_ptr(), d_buf.numel(), ctypes.byref(h)),
+           "uw_matrix_create")
+    info = uw_blob_info(host_blob)
+    _register(h.value, info["rows"], info["cols"], d_buf.device.index)
     return h.value
 
 
 def uw_matrix_destroy(handle: int) -> None:
+    _handles.pop(handle, None)
     _lib.uw_matrix_destroy(handle)
 
 
+def uw_matrix_attach_palette(handle: int, palette_handle: int | None) -> None:
+    _check(_lib.uw_matrix_attach_palette(handle, palette_handle), "uw_matrix_attach_palette")
+
+
 def uw_decompress(handle: int, d_out, ld_out: int | None = None, stream=None) -> None:
+    rows, cols, dev = _shape(handle)
+    if d_out.element_size() != 2:
+        raise ValueError("the output must hold 16-bit elements")
+    _check_rows(d_out, rows, cols, dev, "out", exact=False)
     if ld_out is None:
         ld_out = d_out.stride(0)
+    if ld_out != d_out.stride(0):
+        raise ValueError("ld_out must be the output's row stride")
     _check(_lib.uw_decompress(handle, d_out.data_ptr(), ld_out, _stream(stream)), "uw_decompress")
 
 
 def uw_gemv_fused(handle: int, x, y, stream=None) -> None:
+    rows, cols, dev = _shape(handle)
+    _check_vector(x, cols, dev, "x")
+    _check_vector(y, rows, dev, "y")
     _check(_lib.uw_gemv_fused(handle, x.data_ptr(), _dtype_code(x), y.data_ptr(), _dtype_code(y), _stream(stream)),
            "uw_gemv_fused")
 
 
+def _gemm_operands(handle: int, X, Y):
+    rows, cols, dev = _shape(handle)
+    _check_rows(X, None, cols, dev, "X")
+    _check_rows(Y, X.shape[0], rows, dev, "Y", exact=False)
+    return X.shape[0]
+
+
+def _ws(ws, dev: int):
+    if ws is None:
+        return None, 0
+    _on_device(ws, dev, "ws")
+    if not ws.is_contiguous():
+        raise ValueError("ws must be contiguous")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
 def uw_gemm_fused(handle: int, X, Y, variant: int = UW_VARIANT_AUTO, ws=None, stream=None) -> None:
-    batch = X.shape[0]
-    ws_ptr = ws.data_ptr() if ws is not None else None
-    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    batch = _gemm_operands(handle, X, Y)
+    ws_ptr, ws_bytes = _ws(ws, _shape(handle)[2])
     _check(_lib.uw_gemm_fused(handle, X.data_ptr(), batch, X.stride(0), _dtype_code(X), Y.data_ptr(), Y.stride(0),
                               _dtype_code(Y), variant, ws_ptr, ws_bytes, _stream(stream)), "uw_gemm_fused")
+
+
+def uw_gemm_with_plan(handle: int, variant: int, knob: int, X, Y, ws=None, stream=None) -> None:
+    batch = _gemm_operands(handle, X, Y)
+    ws_ptr, ws_bytes = _ws(ws, _shape(handle)[2])
+    p = uw_plan()
+    p.batch = batch
+    p.variant = variant
+    p.knob = knob
+    _check(_lib.uw_gemm_with_plan(handle, ctypes.byref(p), X.data_ptr(), batch, X.stride(0), _dtype_code(X),
+                                  Y.data_ptr(), Y.stride(0), _dtype_code(Y), ws_ptr, ws_bytes, _stream(stream)),
+           "uw_gemm_with_plan")
+
+
+def uw_plan_save(handle: int) -> str:
+    size = ctypes.c_size_t(0)
+    _check(_lib.uw_plan_save(handle, None, ctypes.byref(size)), "uw_plan_save")
+    buf = ctypes.create_string_buffer(size.value)
+    _check(_lib.uw_plan_save(handle, buf, ctypes.byref(size)), "uw_plan_save")
+    return buf.value.decode()
+
+
+def uw_plan_load(handle: int, text: str) -> None:
+    _check(_lib.uw_plan_load(handle, text.encode()), "uw_plan_load")
 
 
 def uw_workspace_size(handle: int, batch: int, variant: int = UW_VARIANT_AUTO) -> int:
@@ -225,11 +346,15 @@ def uw_autotune_scratch_size(handle: int, batch: int) -> int:
 
 def _plan_dict(p: uw_plan) -> dict:
     return {"batch": p.batch, "variant": p.variant, "variant_name": VARIANT_NAMES.get(p.variant, "?"),
-            "time_us": p.time_us, "candidate_us": {VARIANT_NAMES[v]: p.candidate_us[v]
-                                                   for v in range(1, UW_VARIANT_COUNT) if p.candidate_us[v] >= 0}}
+            "knob": p.knob, "time_us": p.time_us,
+            "candidate_us": {VARIANT_NAMES[v]: p.candidate_us[v]
+                             for v in range(1, UW_VARIANT_COUNT) if p.candidate_us[v] >= 0},
+            "candidate_knob": {VARIANT_NAMES[v]: p.candidate_knob[v]
+                               for v in range(1, UW_VARIANT_COUNT) if p.candidate_us[v] >= 0}}
 
 
 def uw_autotune(handle: int, batch: int, ws, stream=None) -> dict:
+    _ws(ws, _shape(handle)[2])
     p = uw_plan()
     _check(_lib.uw_autotune(handle, batch, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream),
                             ctypes.byref(p)), "uw_autotune")
@@ -247,26 +372,51 @@ def uw_exponent_ws_size(handle: int, batch: int) -> int:
 
 
 def uw_exponent_gemm(handle: int, X, Y, ws, stream=None) -> None:
+    _gemm_operands(handle, X, Y)
+    _ws(ws, _shape(handle)[2])
     _check(_lib.uw_exponent_gemm(handle, X.data_ptr(), X.shape[0], X.stride(0), _dtype_code(X), Y.data_ptr(),
                                  Y.stride(0), _dtype_code(Y), ws.data_ptr(), ws.numel() * ws.element_size(),
                                  _stream(stream)), "uw_exponent_gemm")
 
 
-def uw_set_plan(handle: int, batch: int, variant: int, time_us: float = -1.0) -> None:
+def uw_set_plan(handle: int, batch: int, variant: int, time_us: float = -1.0, knob: int = 0) -> None:
     p = uw_plan()
     p.batch = batch
     p.variant = variant
+    p.knob = knob
     p.time_us = time_us
     for i in range(UW_VARIANT_COUNT):
         p.candidate_us[i] = -1.0
     _check(_lib.uw_set_plan(handle, ctypes.byref(p)), "uw_set_plan")
 
 
-def uw_bf16_gemm(W, X, Y, stream=None) -> None:
+def _bf16_operands(W, X, Y):
+    if W.dim() != 2 or W.element_size() != 2:
+        raise ValueError("W must be a 2-D 16-bit tensor")
     rows, cols = W.shape
+    dev = W.device.index if W.is_cuda else -1
+    _check_rows(W, rows, cols, dev, "W")
+    _check_rows(X, None, cols, dev, "X")
+    _check_rows(Y, X.shape[0], rows, dev, "Y", exact=False)
+    return rows, cols
+
+
+def uw_bf16_gemm(W, X, Y, stream=None) -> None:
+    rows, cols = _bf16_operands(W, X, Y)
     _check(_lib.uw_bf16_gemm(W.data_ptr(), rows, cols, W.stride(0), X.data_ptr(), X.shape[0], X.stride(0),
                              _dtype_code(X), Y.data_ptr(), Y.stride(0), _dtype_code(Y), _stream(stream)),
            "uw_bf16_gemm")
+
+
+def uw_bf16_gemm_shaped(W, X, Y, shape: int, ks: int = 0, stream=None) -> None:
+    rows, cols = _bf16_operands(W, X, Y)
+    _check(_lib.uw_bf16_gemm_shaped(W.data_ptr(), rows, cols, W.stride(0), X.data_ptr(), X.shape[0], X.stride(0),
+                                    Y.data_ptr(), Y.stride(0), _dtype_code(Y), shape, ks, _stream(stream)),
+           "uw_bf16_gemm_shaped")
+
+
+def uw_bf16_gemm_shape_count() -> int:
+    return _lib.uw_bf16_gemm_shape_count()
 
 
 def uw_read_probe_sink_size() -> int:
@@ -305,27 +455,62 @@ def uw_palette_create(host_blob: bytes, d_blob) -> int:
         raise ValueError("device blob size differs from the host blob")
     h = ctypes.c_void_p()
     _check(_lib.uw_palette_create(arr.ctypes.data, arr.size, d_blob.data_ptr(), ctypes.byref(h)), "uw_palette_create")
+    info = uw_palette_info(host_blob)
+    _register(h.value, info["rows"], info["cols"], d_blob.device.index)
     return h.value
 
 
 def uw_palette_destroy(handle: int) -> None:
+    _handles.pop(handle, None)
     _lib.uw_palette_destroy(handle)
 
 
+def uw_palette_transcode_size(handle: int) -> int:
+    return _lib.uw_palette_transcode_size(handle)
+
+
+def uw_palette_transcode(handle: int, d_out, stream=None) -> None:
+    _on_device(d_out, _shape(handle)[2], "out")
+    if not d_out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    _check(_lib.uw_palette_transcode(handle, d_out.data_ptr(), d_out.numel() * d_out.element_size(), _stream(stream)),
+           "uw_palette_transcode")
+
+
+def uw_palette_create_transcoded(handle: int, d_blob) -> int:
+    rows, cols, dev = _shape(handle)
+    _on_device(d_blob, dev, "d_blob")
+    if d_blob.numel() * d_blob.element_size() < uw_palette_transcode_size(handle):
+        raise ValueError("d_blob is smaller than the transcoded form")
+    h = ctypes.c_void_p()
+    _check(_lib.uw_palette_create_transcoded(handle, d_blob.data_ptr(), ctypes.byref(h)), "uw_palette_create_transcoded")
+    _register(h.value, rows, cols, dev)
+    return h.value
+
+
 def uw_palette_gemv(handle: int, x, y, stream=None) -> None:
+    rows, cols, dev = _shape(handle)
+    _check_vector(x, cols, dev, "x")
+    _check_vector(y, rows, dev, "y")
     _check(_lib.uw_palette_gemv(handle, x.data_ptr(), _dtype_code(x), y.data_ptr(), _dtype_code(y), _stream(stream)),
            "uw_palette_gemv")
 
 
 def uw_palette_gemm(handle: int, X, Y, stream=None) -> None:
-    batch = X.shape[0]
+    batch = _gemm_operands(handle, X, Y)
     _check(_lib.uw_palette_gemm(handle, X.data_ptr(), batch, X.stride(0), _dtype_code(X), Y.data_ptr(), Y.stride(0),
                                 _dtype_code(Y), _stream(stream)), "uw_palette_gemm")
 
 
 def uw_palette_decompress(handle: int, d_out, ld_out: int | None = None, stream=None) -> None:
+    rows, cols, dev = _shape(handle)
+    if d_out.element_size() != 2:
+        raise ValueError("the output must hold 16-bit elements")
+    _check_rows(d_out, rows, cols, dev, "out", exact=False)
     if ld_out is None:
         ld_out = d_out.stride(0)
+    if ld_out != d_out.stride(0):
+        raise ValueError("ld_out must be the output's row stride")
     _check(_lib.uw_palette_decompress(handle, d_out.data_ptr(), ld_out, _stream(stream)), "uw_palette_decompress")
 
 
@@ -338,12 +523,15 @@ class CompressedMatrix:
         import torch
         self.blob = blob
         self.info = uw_blob_info(blob)
-        host = torch.frombuffer(bytearray(blob), dtype=torch.uint8)
-        self.d_blob = host.to(device)
-        if self.d_blob.data_ptr() % 256:
-            raise RuntimeError("device blob is not 256-byte aligned")
-        self.handle = uw_matrix_create(blob, self.d_blob)
+        # the blob, then room for the tables the library derives from it
+        self.d_buf = torch.empty(uw_matrix_device_bytes(blob), dtype=torch.uint8, device=device)
+        if self.d_buf.data_ptr() % 256:
+            raise RuntimeError("device buffer is not 256-byte aligned")
+        self.d_buf[: len(blob)].copy_(torch.frombuffer(bytearray(blob), dtype=torch.uint8))
+        self.d_blob = self.d_buf[: len(blob)]
+        self.handle = uw_matrix_create(blob, self.d_buf)
         self.rows, self.cols = self.info["rows"], self.info["cols"]
+        self.palette = None
 
     @classmethod
     def from_weights(cls, w_bf16, device: str = "cuda", **opts) -> "CompressedMatrix":
@@ -381,6 +569,37 @@ class CompressedMatrix:
         if ws is None:
             ws = self.workspace(batch, autotune=True)
         return uw_autotune(self.handle, batch, ws, stream)
+
+    def transcode_palette(self, attach: bool = True, stream=None) -> "PaletteMatrix":
+        """The direct-palette form of the same weights, built on the device
+        from this blob (uw_palette_transcode); attached as a candidate of
+        this matrix unless attach is False."""
+        import torch
+        n = uw_palette_transcode_size(self.handle)
+        if n == 0:
+            raise UwError(UW_ERR_UNSUPPORTED, "uw_palette_transcode_size", "this matrix cannot be transcoded")
+        d = torch.empty(n, dtype=torch.uint8, device=self.d_buf.device)
+        uw_palette_transcode(self.handle, d, stream)
+        p = PaletteMatrix.__new__(PaletteMatrix)
+        p.blob = None
+        p.d_blob = d
+        p.handle = uw_palette_create_transcoded(self.handle, d)
+        p.rows, p.cols = self.rows, self.cols
+        p.info = {"rows": self.rows, "cols": self.cols, "n_raw": self.info["n_raw_groups"], "bytes": n,
+                  "ratio": n / (2 * self.rows * self.cols)}
+        if attach:
+            self.attach_palette(p)
+        return p
+
+    def attach_palette(self, p: "PaletteMatrix | None") -> None:
+        uw_matrix_attach_palette(self.handle, p.handle if p is not None else None)
+        self.palette = p
+
+    def save_plans(self) -> str:
+        return uw_plan_save(self.handle)
+
+    def load_plans(self, text: str) -> None:
+        uw_plan_load(self.handle, text)
 
     def close(self) -> None:
         if getattr(self, "handle", None):

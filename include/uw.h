@@ -20,9 +20,9 @@
  *  - all arguments are checked on the host before anything is launched;
  *  - device entry points are asynchronous on the given stream (a hipStream_t
  *    passed as void*, NULL = the null stream) and do not synchronise, except
- *    uw_autotune, which is blocking; they allocate no memory, except that the
- *    first product on a device that goes through rocBLAS creates that
- *    device's rocBLAS handle;
+ *    uw_autotune, which is blocking; no entry point allocates device memory:
+ *    every device buffer (blob, derived tables, inputs, outputs, workspaces)
+ *    belongs to the caller;
  *  - "device pointer" means memory of the device that was current when the
  *    matrix handle was created; every device entry point runs on that device.
  *
@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define UW_VERSION 10000 /* 1.0.0 */
+#define UW_VERSION 20000 /* 2.0.0 */
 
 typedef enum {
   UW_OK = 0,
@@ -85,7 +85,8 @@ typedef enum {
   UW_VARIANT_FUSED = 1,            /* decode on chip, multiply on VALU, no bf16 in HBM  */
   UW_VARIANT_DECOMPRESS_GEMM = 2,  /* uw_decompress into the workspace, then bf16 GEMM  */
   UW_VARIANT_FUSED_MFMA = 3,       /* decode on chip, multiply on the matrix cores      */
-  UW_VARIANT_COUNT = 4
+  UW_VARIANT_PALETTE = 4,          /* the attached direct-palette copy (uw_matrix_attach_palette) */
+  UW_VARIANT_COUNT = 5
 } uw_variant;
 
 #define UW_ENC_NO_PLAIN 1u /* never fall back to plain mode unless nothing can be coded */
@@ -109,11 +110,20 @@ typedef struct {
   double bits_per_weight; /* 8*total_bytes / (rows*cols) */
 } uw_info;
 
+/* A plan: how uw_gemm_fused runs one batch size under UW_VARIANT_AUTO.
+ * knob is variant-specific (0 = the library's own choice):
+ *   UW_VARIANT_FUSED            ring depth, tile steps in flight per wave: 2 or 4;
+ *   UW_VARIANT_FUSED_MFMA       waves per workgroup (decoded rows per slice): 8..16;
+ *   UW_VARIANT_DECOMPRESS_GEMM  matrix-core GEMM shape (1..uw_bf16_gemm_shape_count()-1)
+ *                               + 16 * waves splitting k (1, 2, 4 or 8; 0 = auto);
+ *   UW_VARIANT_PALETTE          unused. */
 typedef struct {
   int64_t batch;
-  int32_t variant;                        /* the chosen uw_variant */
-  float time_us;                          /* its measured time per call */
-  float candidate_us[UW_VARIANT_COUNT];   /* per variant, < 0 = not measured */
+  int32_t variant;                          /* the chosen uw_variant */
+  int32_t knob;                             /* its knob */
+  float time_us;                            /* its measured time per call */
+  float candidate_us[UW_VARIANT_COUNT];     /* per variant, its best knob's time; < 0 = not measured */
+  int32_t candidate_knob[UW_VARIANT_COUNT]; /* per variant, that best knob */
 } uw_plan;
 
 typedef struct uw_matrix uw_matrix;
@@ -155,22 +165,31 @@ int uw_encode(const uint16_t* w_bf16, int64_t rows, int64_t cols, const uw_encod
 int uw_blob_info(const void* blob, size_t n, uw_info* info);
 
 /*
- * uw_matrix_create (host) - bind a handle to a blob already copied to device
- * memory.  host_blob/n is validated as by uw_blob_info; d_blob must hold the
- * same n bytes on the current device, 256-byte aligned.  The handle does not
- * own d_blob: the caller keeps it alive and unchanged until uw_matrix_destroy.
- * The handle keeps a copy of the header and a per-batch plan cache
- * (internally locked).  In device memory it allocates, and frees in
- * uw_matrix_destroy, it builds the decode tables (16640 bytes, derived from
- * the code lengths; every kernel copies them into LDS) and, when G and
- * cols/64 are multiples of 16 (no 1024-weight tile crosses a row), a step
- * table, 8 bytes per tile (where each tile's segment starts and how many
- * lanes load it); the kernels then walk the tiles of a work unit as one
- * sequence.
- * Errors: UW_ERR_INVALID, UW_ERR_FORMAT, UW_ERR_HIP (no current device, or
- *         the tables could not be allocated or copied).
+ * uw_matrix_device_bytes (host) - bytes of the device buffer uw_matrix_create
+ * takes for this blob: the blob itself (rounded up to 256 bytes), then tables
+ * the kernels read that are derived from the blob and not part of it: the
+ * decode tables (16640 bytes, from the code lengths; every kernel copies them
+ * into LDS), the same tables with palette indices in place of exponents
+ * (16640 bytes, for uw_palette_transcode) and, when G and cols/64 are
+ * multiples of 16 (no 1024-weight tile crosses a row), a step table of
+ * 8 bytes per tile (where each tile's segment starts and how many lanes load
+ * it).  0 if the blob is invalid (uw_blob_info says why).
  */
-int uw_matrix_create(const void* host_blob, size_t n, const void* d_blob, uw_matrix** out);
+size_t uw_matrix_device_bytes(const void* host_blob, size_t n);
+
+/*
+ * uw_matrix_create (host) - bind a handle to a blob on the current device.
+ * host_blob/n is validated as by uw_blob_info.  d_buf (256-byte aligned,
+ * d_bytes >= uw_matrix_device_bytes(host_blob, n)) must already hold the
+ * same n bytes at its start; the call writes the derived tables after them
+ * (a synchronous host-to-device copy) and allocates no device memory.  The
+ * handle does not own d_buf: the caller keeps it alive and unchanged until
+ * uw_matrix_destroy.  The handle keeps a copy of the header and a per-batch
+ * plan cache (internally locked).
+ * Errors: UW_ERR_INVALID (null, misaligned, d_bytes too small),
+ *         UW_ERR_FORMAT, UW_ERR_HIP (no current device, copy failed).
+ */
+int uw_matrix_create(const void* host_blob, size_t n, void* d_buf, size_t d_bytes, uw_matrix** out);
 
 /* Release a handle (NULL is ignored).  Work already queued keeps running. */
 void uw_matrix_destroy(uw_matrix* m);
@@ -199,16 +218,21 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
  * uw_gemm_fused (device) - Y = X W^T for a small batch.
  *   d_X  device, batch rows of cols elements of xt, row stride ldx >= cols.
  *   d_Y  device, batch rows of rows elements of yt, row stride ldy >= rows.
- *   variant  a uw_variant; UW_VARIANT_AUTO uses the plan uw_autotune stored
- *            for this batch, else a heuristic (batch 1, and batch 2 when
- *            one VALU pass takes both rows: fused on VALU; up to 32: fused on
- *            the matrix cores where supported; above: decompress + GEMM when
- *            d_ws is large enough, else the matrix cores).
+ *   variant  a uw_variant; UW_VARIANT_AUTO uses the plan stored for this
+ *            batch (uw_autotune, uw_set_plan, uw_plan_load) when that plan's
+ *            variant can run this call, else a heuristic (batch 1, and batch
+ *            2 when one VALU pass takes both rows: fused on VALU; up to 32:
+ *            fused on the matrix cores where supported; above: decompress +
+ *            GEMM when d_ws is large enough, else the matrix cores).  An
+ *            explicit variant runs with its default knob (uw_gemm_with_plan
+ *            runs a given knob).
  *   d_ws/ws_bytes  caller-owned device workspace (uw_workspace_size bytes for
  *            the chosen variant; may be NULL/0 for the fused variants).
  *   UW_VARIANT_FUSED_MFMA needs bf16 X that is 16-byte aligned with ldx a
  *   multiple of 8, cols a multiple of 1024 and G a multiple of 16 (else
- *   UW_ERR_UNSUPPORTED); it runs 64 batch rows per pass.
+ *   UW_ERR_UNSUPPORTED); it runs 64 batch rows per pass.  UW_VARIANT_PALETTE
+ *   needs an attached palette copy (uw_matrix_attach_palette) and bf16 X
+ *   above batch 1.
  * batch == 0 is a no-op.  fp32 accumulation.
  * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE (workspace), UW_ERR_UNSUPPORTED, UW_ERR_HIP.
  */
@@ -216,23 +240,39 @@ int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ld
                   void* d_Y, int64_t ldy, int yt, int variant, void* d_ws, size_t ws_bytes,
                   void* stream);
 
+/*
+ * uw_gemm_with_plan (device) - as uw_gemm_fused, running exactly
+ * plan->variant with plan->knob (plan->batch is not used): the form the
+ * autotuner times and the tests check every knob through.
+ * Errors: as uw_gemm_fused; UW_ERR_INVALID for an unknown variant or knob.
+ */
+int uw_gemm_with_plan(const uw_matrix* m, const uw_plan* plan, const void* d_X, int64_t batch, int64_t ldx, int xt,
+                      void* d_Y, int64_t ldy, int yt, void* d_ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes uw_gemm_fused needs for the given variant and batch
  * (UW_VARIANT_AUTO: the largest any candidate may need). */
 size_t uw_workspace_size(const uw_matrix* m, int64_t batch, int variant);
 
 /*
- * uw_autotune (device, BLOCKING) - autotuner paragraph: time every applicable
- * variant for this matrix and batch on the given stream with HIP events (bf16
- * X and Y; inputs and outputs inside the workspace) and store the fastest in
- * the handle's plan cache; *out (may be NULL) gets a copy.
- *   d_ws/ws_bytes  device workspace of at least
+ * uw_autotune (device, BLOCKING) - autotuner paragraph (the runtime measures
+ * real throughput on the target hardware instead of relying on heuristics):
+ * time every applicable variant, each over its knobs, for this matrix and
+ * batch on the given stream with HIP events (bf16 X and Y inside the
+ * workspace), and store the fastest (variant, knob) in the handle's plan
+ * cache; *out (may be NULL) gets a copy.  Every timed call runs cold: a read
+ * of a 512 MiB region of the workspace (twice the 256 MiB last-level cache)
+ * comes before it, so the blob is read from HBM as in a model's layer sweep.
+ * Each candidate is warmed up 3 times and timed 15 times; its median counts.
+ *   d_ws/ws_bytes  device workspace, 256-byte aligned, of at least
  *                  uw_workspace_size(m, batch, UW_VARIANT_AUTO) +
  *                  uw_autotune_scratch_size(m, batch) bytes.
- * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE, UW_ERR_HIP.
+ * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE, UW_ERR_UNSUPPORTED (no candidate
+ *         runs), UW_ERR_HIP.
  */
 int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* stream, uw_plan* out);
 
-/* Extra workspace uw_autotune uses for its own X and Y. */
+/* Extra workspace uw_autotune uses: its own X and Y and the 512 MiB region
+ * it reads to evict the blob from the caches. */
 size_t uw_autotune_scratch_size(const uw_matrix* m, int64_t batch);
 
 /* The stored plan for a batch; UW_ERR_INVALID if none. */
@@ -242,26 +282,59 @@ int uw_get_plan(const uw_matrix* m, int64_t batch, uw_plan* out);
  * uw_set_plan (host) - store a plan for plan->batch (replacing any), so AUTO
  * follows a choice made elsewhere: a model-level tuning pass or a plan file
  * from an earlier run (autotuner paragraph: the tuner's result is a per-model
- * configuration file the runtime reads).  Only batch and variant are used by
- * the dispatch; the times are kept for reporting.
- * Errors: UW_ERR_INVALID (null, batch < 1, variant not FUSED, DECOMPRESS_GEMM
- *         or FUSED_MFMA).
+ * configuration file the runtime reads).  Only batch, variant and knob are
+ * used by the dispatch; the times are kept for reporting.
+ * Errors: UW_ERR_INVALID (null, batch < 1, variant not a concrete one, knob
+ *         out of range).
  */
 int uw_set_plan(uw_matrix* m, const uw_plan* plan);
+
+/*
+ * uw_plan_save (host) - the handle's plans as JSON text (NUL-terminated):
+ *   {"format": "uw-plan-1", "rows": R, "cols": C, "blob_crc32": N,
+ *    "plans": [{"batch": B, "variant": "fused" | "decompress_gemm" |
+ *               "fused_mfma" | "palette", "knob": K, "time_us": T}, ...]}
+ * in increasing batch.  out == NULL queries: *out_size gets the bytes
+ * needed (with the NUL).  Errors: UW_ERR_INVALID, UW_ERR_NOSPACE.
+ */
+int uw_plan_save(const uw_matrix* m, char* out, size_t* out_size);
+
+/*
+ * uw_plan_load (host) - install the plans of JSON text written by
+ * uw_plan_save (replacing plans of the same batch).  rows, cols and
+ * blob_crc32 must match the handle's blob: a plan file belongs to one matrix.
+ * Nothing is installed unless every entry is valid.
+ * Errors: UW_ERR_INVALID (null), UW_ERR_FORMAT (not such JSON, or it belongs
+ *         to another matrix).
+ */
+int uw_plan_load(uw_matrix* m, const char* json);
 
 /*
  * uw_bf16_gemm (device) - Y = X W^T over an uncompressed bf16 matrix: the
  * multiply of the "full decode" pipeline and the uncompressed comparator.
  *   d_W  device, rows x cols bf16, row stride ldw >= cols (multiple of 8),
  *        16-byte aligned.  Other arguments as for uw_gemm_fused.
- * Up to batch 8 (or with fp32 X) a GEMV-style kernel of this library runs;
- * above batch 8 with bf16 X, rocBLAS (gemm_ex, fp32 compute).  The first
- * such call on a device creates that device's rocBLAS handle (it allocates;
- * the handle lives until the process ends).
+ * Up to batch 8 (or with fp32 X, or bf16 X that is not 16-byte aligned with
+ * ldx a multiple of 8) a GEMV-style kernel on the vector ALU runs, in passes
+ * of up to 8 rows; above batch 8 the matrix-core kernel
+ * (v_mfma_f32_16x16x32_bf16, operands straight from global memory).
  * Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED, UW_ERR_HIP.
  */
 int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, const void* d_X,
                  int64_t batch, int64_t ldx, int xt, void* d_Y, int64_t ldy, int yt, void* stream);
+
+/*
+ * uw_bf16_gemm_shaped (device) - uw_bf16_gemm on the matrix cores with a
+ * given shape: shape in [1, uw_bf16_gemm_shape_count()) picks the weight rows
+ * (16, 32 or 64) and batch rows (16, 32 or 64) a workgroup holds, ks (1, 2,
+ * 4, 8; 0 = auto) the waves that split k.  Needs bf16 X, 16-byte aligned,
+ * ldx a multiple of 8, and batch >= 1.
+ * Errors: UW_ERR_INVALID, UW_ERR_HIP.
+ */
+int uw_bf16_gemm_shaped(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, const void* d_X,
+                        int64_t batch, int64_t ldx, void* d_Y, int64_t ldy, int yt, int shape, int ks, void* stream);
+/* Number of shape ids of uw_bf16_gemm_shaped (shape 0 is the automatic one). */
+int uw_bf16_gemm_shape_count(void);
 
 /*
  * uw_read_probe (device) - streaming read of `bytes` bytes (multiple of 16,
@@ -363,6 +436,48 @@ int uw_palette_gemm(const uw_palette* m, const void* d_X, int64_t batch, int64_t
  * Errors: UW_ERR_INVALID, UW_ERR_HIP.
  */
 int uw_palette_decompress(const uw_palette* m, uint16_t* d_out, int64_t ld_out, void* stream);
+
+/*
+ * uw_palette_transcode_size (host) - bytes of the UWP1 form uw_palette_transcode
+ * writes for a Huffman-form matrix: the same as uw_palette_encode of the
+ * matrix's weights.  0 when the matrix cannot be transcoded: plain mode,
+ * cols not a multiple of 1024, G not a multiple of 16, or a palette that is
+ * not the direct form's (K must be 16, or smaller with no raw group).
+ */
+size_t uw_palette_transcode_size(const uw_matrix* m);
+
+/*
+ * uw_palette_transcode (device) - the page's "transcoded at model load"
+ * step: decode the Huffman form on the device and write its UWP1 form, byte
+ * for byte what uw_palette_encode produces from the original weights
+ * (section on the four execution pipelines: one Huffman bundle serves both
+ * distribution and inference).  Two kernels: one writes the raw flags and
+ * per-tile raw counts from the blob's raw bits, the other walks the tiles
+ * with a decode table that yields palette indices and writes sign+mantissa
+ * bytes, index nibbles and the raw groups' exponent bytes.
+ *   d_out  device, 256-byte aligned, out_bytes >= uw_palette_transcode_size(m).
+ * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE, UW_ERR_UNSUPPORTED, UW_ERR_HIP.
+ */
+int uw_palette_transcode(const uw_matrix* m, void* d_out, size_t out_bytes, void* stream);
+
+/*
+ * uw_palette_create_transcoded (host) - a palette handle over d_blob, which
+ * holds (or, once the stream has run, will hold) uw_palette_transcode's
+ * output for m; the layout is taken from m, so no host copy is needed.
+ * Allocates no device memory.  Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED, UW_ERR_HIP.
+ */
+int uw_palette_create_transcoded(const uw_matrix* m, const void* d_blob, uw_palette** out);
+
+/*
+ * uw_matrix_attach_palette (host) - make a direct-palette copy of the same
+ * weights (same rows and cols; uw_palette_transcode of m, or
+ * uw_palette_encode of the original weights) a candidate of m: then
+ * UW_VARIANT_PALETTE runs it, uw_autotune times it, and AUTO may pick it
+ * (the four-pipelines paragraph: format and pipeline are chosen per matrix
+ * and batch).  p == NULL detaches.  The handle does not own p.
+ * Errors: UW_ERR_INVALID (null m, shapes differ).
+ */
+int uw_matrix_attach_palette(uw_matrix* m, const uw_palette* p);
 
 #ifdef __cplusplus
 }

@@ -497,6 +497,106 @@ def decode(blob: bytes) -> np.ndarray:
     return huffman.join_bf16(e, smg).reshape(rows, cols)
 
 
+def decode_reference(blob: bytes) -> np.ndarray:
+    """blob -> bf16 bit patterns [rows, cols] (uint16), one weight at a time.
+
+    A second decoder of the same layout, written as plain loops over blocks,
+    groups and lanes so that each step can be checked by eye against the
+    layout description at the top of this module; only meant for small
+    matrices.  For every block: read the head (lane word counts, raw bits,
+    the first two words of every lane), then for each group j of the block,
+    and for each lane, either copy the raw exponent byte or decode one code
+    from the lane's window; after every R-th group run the refill check,
+    lanes in order 0..63.
+    """
+    h = parse_header(blob)
+    rows, cols = h.rows, h.cols
+    if h.flags & FLAG_PLAIN:
+        out = []
+        for i in range(rows * cols):
+            o = h.off_plain + 2 * i
+            out.append(blob[o] | (blob[o + 1] << 8))
+        return np.array(out, dtype=np.uint16).reshape(rows, cols)
+
+    def u16(o):
+        return blob[o] | (blob[o + 1] << 8)
+
+    def u32(o):
+        return blob[o] | (blob[o + 1] << 8) | (blob[o + 2] << 16) | (blob[o + 3] << 24)
+
+    # canonical code table: bit-reversed pattern and length of each palette entry
+    codes = huffman.canonical_codes(h.code_len, h.palette)
+    table = [(huffman.reverse_bits(c, l), l, h.palette[s]) for s, (c, l) in enumerate(zip(codes, h.code_len)) if l]
+    n_groups = rows * cols // 64
+    G, R = h.G, h.R
+    W = -(-G // 32)
+    T = -(-G // 16)
+    exps = [0] * (n_groups * 64)
+    for b in range(h.n_blocks):
+        g0 = b * G
+        gb = min(G, n_groups - g0)
+        start = h.off_queue + u32(h.off_block + 4 * b)  # this block's data
+        n = [u16(start + 2 * l) for l in range(64)]
+        raw = [(u32(start + 128 + 4 * (j // 32)) >> (j % 32)) & 1 for j in range(gb)]
+        p = start + 128 + 4 * W
+        # window of each lane: words (s-1, s, s+1) as one integer, qm, words taken
+        win = [0] * 64
+        for k in range(2):  # word 0 of the lanes that have one, then word 1
+            for l in range(64):
+                if n[l] > k:
+                    win[l] |= u32(p) << (32 * (k + 1))
+                    p += 4
+        qm = [30] * 64
+        taken = [min(nl, 2) for nl in n]
+        raw_p = p
+        for j in range(gb):
+            if j % 16 == 0:
+                if j > 0:  # the next tile's segment starts where the last one ended
+                    seg_end = start + 4 * u16(h.off_seg + 2 * (b * T + j // 16 - 1))
+                    if p != seg_end:
+                        raise ValueError("segment length mismatch")
+                raw_p = p
+                p += 64 * sum(raw[jj] for jj in range(j, min(j + 16, gb)))
+            for l in range(64):
+                idx = g0 * 64 + j * 64 + l
+                if raw[j]:
+                    exps[idx] = blob[raw_p + l]
+                    continue
+                bits = win[l] >> (qm[l] + 2)
+                for pat, ln, e in table:
+                    if bits & ((1 << ln) - 1) == pat:
+                        exps[idx] = e
+                        qm[l] += ln
+                        break
+                else:
+                    raise ValueError("invalid code in stream")
+            if raw[j]:
+                raw_p += 64
+            if (j + 1) % R == 0:
+                for l in range(64):
+                    if qm[l] >= 64:
+                        raise ValueError("window overrun")
+                    if qm[l] >= 32:
+                        qm[l] -= 32
+                        win[l] >>= 32
+                        if taken[l] < n[l]:
+                            win[l] |= u32(p) << 64
+                            p += 4
+                            taken[l] += 1
+        if p != start + 4 * u16(h.off_seg + 2 * (b * T + (gb - 1) // 16)):
+            raise ValueError("segment length mismatch")
+        if taken != n:
+            raise ValueError("lane word count mismatch")
+    out = np.zeros(n_groups * 64, dtype=np.uint16)
+    for g in range(n_groups):
+        b, j = divmod(g, G)
+        for l in range(64):
+            sm = blob[h.off_sm + b * G * 64 + (j >> 4) * 1024 + l * 16 + (j & 15)]
+            e = exps[g * 64 + l]
+            out[g * 64 + l] = ((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)
+    return out.reshape(rows, cols)
+
+
 def stats(blob: bytes) -> dict:
     """Sizes and ratios of a blob, for reporting."""
     h = parse_header(blob)

@@ -3,8 +3,9 @@
 Decompression is bit-exact against the original weights (the method is
 lossless, so the oracle's decode is the identity).  Products use fp32
 accumulation and are checked against the fp64 product of the original
-weights: max |y - y64| / max(|y64|, rms(y64)) <= 1e-3 for fp32 outputs and
-<= 2 bf16 ulp against round-to-nearest-even(y64) for bf16 outputs.  Inputs
+weights: max |y - y64| / max(|y64|, rms(y64)) <= 1e-3 for fp32 outputs; bf16
+outputs within 2 bf16 ulp of round-to-nearest-even(y64), or RNE of a value
+inside the fp32 accumulation band (the rule and its cap are in tests/parity.py).  Inputs
 are the seeded synthetic workloads of workloads.py, at full size for the
 benchmarked configurations and at small, ragged sizes for the edge cases.
 """
@@ -24,9 +25,9 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import decode_gemv_canonical_amd as uw  # noqa: E402
+from tests.parity import TOL, check_bf16, check_f32  # noqa: E402,F401
 
 DEV = torch.device("cuda:0")
-TOL = 1e-3
 
 
 def _say(msg):
@@ -45,34 +46,6 @@ def matrix(name, rows=None, cols=None, seed=None, **opts):
         m = uw.CompressedMatrix.from_weights(w, device="cuda:0", **opts)
         _cache[key] = (wb, m)
     return _cache[key]
-
-
-def check_f32(y, ref64, what):
-    y = y.detach().float().cpu().numpy().astype(np.float64)
-    assert products.nonfinite_match(y, ref64), what + ": non-finite pattern differs"
-    err = products.rel_error_floored(y, ref64)
-    assert err <= TOL, f"{what}: rel err {err:.3e}"
-    return err
-
-
-def check_bf16(y, ref64, what):
-    """Within 2 bf16 ulp of RNE(y64), or RNE of a value inside the fp32
-    tolerance band |v - y64| <= TOL * max(|y64|, rms): the fp32 sum's error
-    scales with the row's rms, so an output near zero may sit more than 2 bf16
-    ulp (of its own tiny magnitude) from RNE(y64)."""
-    got = y.detach().view(torch.int16).cpu().numpy().view(np.uint16)
-    ref = products.round_to_bf16(ref64)
-    fin = np.isfinite(ref64)
-    r = ref64[fin]
-    k = products.bf16_order_key(got[fin])
-    near = products.bf16_ulp_distance(got[fin], ref[fin]) <= 2
-    rms = float(np.sqrt(np.mean(r ** 2))) if r.size else 1.0
-    eps = TOL * np.maximum(np.abs(r), rms if rms > 0 else 1.0)
-    band = (k >= products.bf16_order_key(products.round_to_bf16(r - eps))) & \
-           (k <= products.bf16_order_key(products.round_to_bf16(r + eps)))
-    bad = ~(near | band)
-    assert not bad.any(), f"{what}: {int(bad.sum())} outputs outside 2 bf16 ulp and the fp32 band"
-    assert np.array_equal(np.isnan(products.bf16_to_f64(got)), np.isnan(ref64)), what
 
 
 DECOMP_CASES = [
@@ -154,7 +127,7 @@ def test_gemv_fused(name, rows, cols, seed, opts, xdt):
     yb = m.gemv(x.to(DEV), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     check_f32(y, ref, f"gemv {name}")
-    check_bf16(yb, ref, f"gemv bf16 {name}")
+    check_bf16(yb, ref, f"gemv bf16 {name}", wb.shape[1])
 
 
 def test_gemv_one_hot_is_exact():
@@ -193,7 +166,7 @@ def test_gemm_fused_valu(batch, G):
     Yb = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_FUSED, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     check_f32(Y, ref, f"gemm fused b={batch}")
-    check_bf16(Yb, ref, f"gemm fused bf16 b={batch}")
+    check_bf16(Yb, ref, f"gemm fused bf16 b={batch}", wb.shape[1])
 
 
 @pytest.mark.parametrize("batch", [1, 4, 16, 64])
@@ -241,7 +214,7 @@ def test_gemm_fused_mfma(case):
         Yb = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_FUSED_MFMA, out_dtype=torch.bfloat16)
         torch.cuda.synchronize()
         check_f32(Y, ref, f"gemm mfma b={batch}")
-        check_bf16(Yb, ref, f"gemm mfma bf16 b={batch}")
+        check_bf16(Yb, ref, f"gemm mfma bf16 b={batch}", wb.shape[1])
 
 
 def test_gemm_fused_mfma_full_sizes():
@@ -338,8 +311,8 @@ def test_gemm_batch_zero_is_noop():
 def test_bf16_gemm_uncompressed():
     wb, _ = matrix("gate", 96, 4096, 21)
     W = torch.from_numpy(wb.view(np.int16)).to(DEV).view(torch.bfloat16)
-    # up to batch 8 the GEMV-style kernel, above it the library GEMM
-    for batch in (1, 3, 8, 9, 40):
+    # up to batch 8 the GEMV-style kernel, above it the matrix-core kernel
+    for batch in (1, 3, 8, 9, 40, 256):
         X = workloads.activations(4096, batch, seed=500 + batch, dtype=torch.bfloat16)
         ref = products.gemm_f64(wb, X.float().numpy())
         Y = torch.empty(batch, 96, device=DEV)
@@ -350,7 +323,34 @@ def test_bf16_gemm_uncompressed():
         Yb = torch.empty(batch, 96, device=DEV, dtype=torch.bfloat16)
         uw.uw_bf16_gemm(W, X.to(DEV), Yb)
         torch.cuda.synchronize()
-        check_bf16(Yb, ref, f"bf16 gemm b={batch} bf16 out")
+        check_bf16(Yb, ref, f"bf16 gemm b={batch} bf16 out", wb.shape[1])
+
+
+def test_bf16_gemm_every_shape_ragged():
+    # rows not a multiple of 16 (or 64), cols not a multiple of 128, batch
+    # not a multiple of 16, a row stride wider than cols
+    rows, cols = 100, 1000
+    wfull, _ = matrix("small", rows, 1024, 24)
+    wb = np.ascontiguousarray(wfull[:, :cols])
+    Wp = torch.from_numpy(wfull.view(np.int16)).to(DEV).view(torch.bfloat16)
+    W = Wp[:, :cols]
+    for batch in (9, 37, 100):
+        X = workloads.activations(cols, batch, seed=520 + batch, dtype=torch.bfloat16)
+        ref = products.gemm_f64(wb, X.float().numpy())
+        Xd = X.to(DEV)
+        for shape in range(1, uw.uw_bf16_gemm_shape_count()):
+            for ks in (0, 1, 2, 8):
+                Y = torch.full((batch, rows + 3), float("nan"), device=DEV)
+                uw.uw_bf16_gemm_shaped(W, Xd, Y[:, :rows], shape, ks)
+                torch.cuda.synchronize()
+                check_f32(Y[:, :rows], ref, f"bf16 gemm shape={shape} ks={ks} b={batch}")
+                assert torch.isnan(Y[:, rows:]).all(), "wrote past the rows"
+    # unaligned X (odd element offset): the VALU passes take it
+    X = workloads.activations(cols + 1, 12, seed=530, dtype=torch.bfloat16).to(DEV)[:, 1:]
+    Y = torch.empty(12, rows, device=DEV)
+    uw.uw_bf16_gemm(W, X, Y)
+    torch.cuda.synchronize()
+    check_f32(Y, products.gemm_f64(wb, X.float().cpu().numpy()), "bf16 gemm unaligned X")
 
 
 def test_decompress_gemm_bf16_out_strided():
@@ -363,7 +363,7 @@ def test_decompress_gemm_bf16_out_strided():
     _say(f"decompress+gemm bf16 out batch={batch}")
     Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_DECOMPRESS_GEMM, ws=m.workspace(batch), Y=Ybig[:, :256])
     torch.cuda.synchronize()
-    check_bf16(Y, ref, "decompress+gemm bf16 out")
+    check_bf16(Y, ref, "decompress+gemm bf16 out", wb.shape[1])
     assert torch.all(Ybig[:, 256:] == 0)
 
 
@@ -386,30 +386,117 @@ def test_autotune_plan_and_auto_dispatch():
         plan = m.autotune(batch)
         assert plan["variant"] in (uw.UW_VARIANT_FUSED, uw.UW_VARIANT_DECOMPRESS_GEMM, uw.UW_VARIANT_FUSED_MFMA)
         assert plan["time_us"] == min(plan["candidate_us"].values())
-        assert uw.uw_get_plan(m.handle, batch)["variant"] == plan["variant"]
-        X = workloads.activations(14336, batch, seed=600 + batch, dtype=torch.bfloat16).to(DEV)
+        got = uw.uw_get_plan(m.handle, batch)
+        assert (got["variant"], got["knob"]) == (plan["variant"], plan["knob"])
+        X = workloads.activations(14336, batch, seed=600 + batch, dtype=torch.bfloat16)
+        ref = products.gemm_f64(wb, X.float().numpy())
+        X = X.to(DEV)
         ws = m.workspace(batch)
         Ya = m.gemm(X, variant=uw.UW_VARIANT_AUTO, ws=ws)
-        Yv = m.gemm(X, variant=plan["variant"], ws=ws)
+        torch.cuda.synchronize()
+        check_f32(Ya, ref, f"auto after autotune b={batch}")
+        # AUTO runs the plan's (variant, knob): the same bits
+        Yv = torch.empty_like(Ya)
+        uw.uw_gemm_with_plan(m.handle, plan["variant"], plan["knob"], X, Yv, ws)
         torch.cuda.synchronize()
         assert torch.equal(Ya, Yv)
 
 
+def test_auto_falls_back_when_the_plan_cannot_run():
+    # a plan tuned for bf16 X with a workspace must not break calls it cannot
+    # serve: fp32 X, or no workspace
+    wb, m = matrix("gate", 64, 4096, 32)
+    for v, knob in ((uw.UW_VARIANT_DECOMPRESS_GEMM, 0), (uw.UW_VARIANT_FUSED_MFMA, 0)):
+        uw.uw_set_plan(m.handle, 4, v, knob=knob)
+        for xdt, ws in ((torch.float32, m.workspace(4)), (torch.bfloat16, None), (torch.float32, None)):
+            X = workloads.activations(4096, 4, seed=640, dtype=xdt)
+            ref = products.gemm_f64(wb, X.float().numpy())
+            _say(f"auto fallback plan={v} x={xdt} ws={ws is not None}")
+            Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_AUTO, ws=ws)
+            torch.cuda.synchronize()
+            check_f32(Y, ref, f"auto fallback plan={v}")
+
+
+def test_every_knob_matches_the_oracle():
+    wb, m = matrix("gate", 96, 4096, 33)
+    for batch in (1, 4, 20, 40, 72):
+        X = workloads.activations(4096, batch, seed=650 + batch, dtype=torch.bfloat16)
+        ref = products.gemm_f64(wb, X.float().numpy())
+        X = X.to(DEV)
+        ws = m.workspace(batch)
+        knobs = [(uw.UW_VARIANT_FUSED, k) for k in (0, 2, 4) if batch <= 8]
+        knobs += [(uw.UW_VARIANT_FUSED_MFMA, k) for k in (0, 8, 12, 16)]
+        knobs += [(uw.UW_VARIANT_DECOMPRESS_GEMM, 0)]
+        if batch > 8:
+            knobs += [(uw.UW_VARIANT_DECOMPRESS_GEMM, sh + 16 * ks)
+                      for sh in range(1, uw.uw_bf16_gemm_shape_count()) for ks in (0, 1, 4)]
+        for v, k in knobs:
+            Y = torch.full((batch, 96), float("nan"), device=DEV)
+            try:
+                uw.uw_gemm_with_plan(m.handle, v, k, X, Y, ws)
+            except uw.UwError as e:
+                assert e.status == uw.UW_ERR_UNSUPPORTED, str(e)
+                continue
+            torch.cuda.synchronize()
+            check_f32(Y, ref, f"knob b={batch} v={v} k={k}")
+
+
+def test_plan_save_load_round_trip():
+    wb, m = matrix("gate", 64, 4096, 34)
+    uw.uw_set_plan(m.handle, 4, uw.UW_VARIANT_FUSED_MFMA, time_us=12.5, knob=12)
+    uw.uw_set_plan(m.handle, 64, uw.UW_VARIANT_DECOMPRESS_GEMM, time_us=40.0, knob=5 + 16 * 4)
+    text = m.save_plans()
+    import json
+    doc = json.loads(text)
+    assert doc["format"] == "uw-plan-1" and doc["rows"] == 64 and doc["cols"] == 4096
+    assert [(p["batch"], p["variant"], p["knob"]) for p in doc["plans"]] == \
+        [(4, "fused_mfma", 12), (64, "decompress_gemm", 69)]
+    fresh = uw.CompressedMatrix.from_weights(workloads.weights("gate", rows=64, cols=4096, seed=34), device="cuda:0")
+    fresh.load_plans(text)
+    for b in (4, 64):
+        a, c = uw.uw_get_plan(m.handle, b), uw.uw_get_plan(fresh.handle, b)
+        assert (a["variant"], a["knob"]) == (c["variant"], c["knob"])
+    # a plan file of another matrix, or a broken one, is rejected whole
+    other = uw.CompressedMatrix.from_weights(workloads.weights("gate", rows=64, cols=4096, seed=35), device="cuda:0")
+    for bad in (text, text.replace('"knob": 12', '"knob": 99'), text[:-3], '{"format": "uw-plan-1"}'):
+        with pytest.raises(uw.UwError) as e:
+            (other if bad == text else fresh).load_plans(bad)
+        assert e.value.status == uw.UW_ERR_FORMAT
+    with pytest.raises(uw.UwError):
+        uw.uw_get_plan(other.handle, 4)
+    fresh.close()
+    other.close()
+
+
 def test_device_argument_errors_are_caught_on_host():
     wb, m = matrix("small", None, None, None)
+    lib = uw.library()
     out = torch.empty(1024, 1024, dtype=torch.int16, device=DEV)
+    # the C-ABI's own checks
+    assert lib.uw_decompress(m.handle, out.data_ptr(), 1000, None) == uw.UW_ERR_INVALID
+    assert lib.uw_decompress(m.handle, out.data_ptr() + 2, 1024, None) == uw.UW_ERR_INVALID
+    X = torch.zeros(4, 1024, dtype=torch.bfloat16, device=DEV)
+    Y = torch.zeros(4, 1024, device=DEV)
     with pytest.raises(uw.UwError) as e:
-        uw.uw_decompress(m.handle, out, 1000)
-    assert e.value.status == uw.UW_ERR_INVALID
-    with pytest.raises(uw.UwError):
-        uw.uw_decompress(m.handle, out.view(-1)[1:].view(1, -1)[:, :1024 * 1023], 1024 * 1024)
-    x = torch.zeros(1024, dtype=torch.float16, device=DEV)
-    with pytest.raises(TypeError):
-        m.gemv(x)
-    with pytest.raises(uw.UwError) as e:
-        uw.uw_gemm_fused(m.handle, torch.zeros(4, 1024, dtype=torch.bfloat16, device=DEV),
-                         torch.zeros(4, 1024, device=DEV), uw.UW_VARIANT_DECOMPRESS_GEMM, None)
+        uw.uw_gemm_fused(m.handle, X, Y, uw.UW_VARIANT_DECOMPRESS_GEMM, None)
     assert e.value.status == uw.UW_ERR_NOSPACE
+    # the binding's checks of shapes, strides and devices
+    with pytest.raises(ValueError):
+        uw.uw_decompress(m.handle, out, 1000)
+    with pytest.raises(ValueError):
+        uw.uw_decompress(m.handle, out[:512])
+    with pytest.raises(TypeError):
+        m.gemv(torch.zeros(1024, dtype=torch.float16, device=DEV))
+    with pytest.raises(ValueError):
+        m.gemv(torch.zeros(1000, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        uw.uw_gemv_fused(m.handle, torch.zeros(1024, dtype=torch.bfloat16, device=DEV), torch.zeros(512, device=DEV))
+    with pytest.raises(ValueError):
+        uw.uw_gemm_fused(m.handle, X.t(), Y)
+    with pytest.raises(ValueError):
+        uw.uw_gemm_fused(m.handle, X, Y[:, :100])
+    with pytest.raises(ValueError):
+        uw.uw_gemm_fused(m.handle, X.cpu(), Y)
 
 
 def test_read_probe():

@@ -19,7 +19,7 @@ if not torch.cuda.is_available():
 import decode_gemv_canonical_amd as uw  # noqa: E402
 from decode_gemv_canonical_amd import tune  # noqa: E402
 
-from tests.test_gpu_parity import check_f32  # noqa: E402
+from tests.parity import check_f32  # noqa: E402
 
 DEV = torch.device("cuda:0")
 
@@ -63,7 +63,8 @@ def test_coordinate_descent_plan_file(batch, tmp_path):
     assert best > 0 and len(hist) >= 7
     assert best == min(t for _, t in hist)
     path = tmp_path / "plan.json"
-    tune.save_plan_file(str(path), "mlp-2048x1024", {p: {batch: (choice[p], best)} for p in choice})
+    tune.install_choice({p: m.handle for p, m in mats.items()}, batch, choice, best)
+    tune.save_plan_file(str(path), "mlp-2048x1024", {p: m.handle for p, m in mats.items()})
     _, fresh = _layer_mats()
     tune.load_plan_file(str(path), {p: m.handle for p, m in fresh.items()})
     for p, m in fresh.items():

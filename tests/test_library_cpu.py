@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol():
     assert len(syms) >= 15
     for s in syms:
         assert hasattr(lib, s), s
-    assert uw.uw_version() == 10000
+    assert uw.uw_version() == 20000
     assert uw.uw_status_string(uw.UW_ERR_FORMAT) == "invalid blob format"
 
 

@@ -28,7 +28,7 @@ def test_coordinate_descent_on_a_cost_table(monkeypatch):
         return t
 
     monkeypatch.setattr(tune, "time_layer_us", lambda run, steps=0, warmup=0: run)
-    choice, best, hist = tune.coordinate_descent(("gate", "up", "down"), layer)
+    choice, best, hist = tune.coordinate_descent(("gate", "up", "down"), layer, candidates=(F, M, D))
     assert choice == {"gate": M, "up": F, "down": F} and best == 6
     # start F,F,F = 8; gate sweep first (M then D), then up, then down
     assert hist[0] == ({"gate": F, "up": F, "down": F}, 8)
@@ -37,17 +37,38 @@ def test_coordinate_descent_on_a_cost_table(monkeypatch):
     assert all(not (c["down"] == D and c["gate"] == M) for c, _ in hist)
 
 
-def test_plan_file_round_trip(tmp_path):
+def test_plan_file_round_trip(tmp_path, monkeypatch):
+    # the per-matrix documents come from uw_plan_save and go back through
+    # uw_plan_load (both need a device handle; stand-ins record the calls)
+    docs = {1: {"format": "uw-plan-1", "rows": 8, "cols": 1024, "blob_crc32": 7,
+                "plans": [{"batch": 4, "variant": "fused_mfma", "knob": 0, "time_us": 80.5}]},
+            2: {"format": "uw-plan-1", "rows": 1024, "cols": 8, "blob_crc32": 9, "plans": []}}
+    loaded = {}
+    monkeypatch.setattr(tune.uw, "uw_plan_save", lambda h: json.dumps(docs[h]))
+    monkeypatch.setattr(tune.uw, "uw_plan_load", lambda h, text: loaded.__setitem__(h, json.loads(text)))
     path = tmp_path / "plan.json"
-    plans = {"gate": {4: (M, 80.5), 32: (D, 120.0)}, "down": {4: (F, 80.5)}}
-    tune.save_plan_file(str(path), "mlp-test", plans)
+    tune.save_plan_file(str(path), "mlp-test", {"gate": 1, "down": 2})
     raw = json.loads(path.read_text())
-    assert raw["model"] == "mlp-test" and raw["plans"]["gate"]["32"]["variant"] == D
-    assert tune.read_plan_file(str(path)) == plans
-    raw["plans"]["down"]["4"]["variant"] = uw.UW_VARIANT_AUTO
+    assert raw["model"] == "mlp-test" and raw["projections"]["gate"]["plans"][0]["variant"] == "fused_mfma"
+    tune.load_plan_file(str(path), {"gate": 11, "down": 12})
+    assert loaded == {11: docs[1], 12: docs[2]}
+    with pytest.raises(ValueError):
+        tune.load_plan_file(str(path), {"gate": 11})  # a projection without a handle
+    raw["projections"]["down"]["format"] = "something else"
     path.write_text(json.dumps(raw))
     with pytest.raises(ValueError):
         tune.read_plan_file(str(path))
+
+
+def test_plan_entry_points_reject_null_without_a_gpu():
+    lib = uw.library()
+    import ctypes
+    size = ctypes.c_size_t(0)
+    assert lib.uw_plan_save(None, None, ctypes.byref(size)) == uw.UW_ERR_INVALID
+    assert lib.uw_plan_load(None, b"{}") == uw.UW_ERR_INVALID
+    assert lib.uw_gemm_with_plan(None, None, None, 1, 0, 1, None, 0, 0, None, 0, None) == uw.UW_ERR_INVALID
+    assert lib.uw_matrix_attach_palette(None, None) == uw.UW_ERR_INVALID
+    assert lib.uw_palette_transcode_size(None) == 0
 
 
 def test_set_plan_argument_checks_without_a_gpu():
