@@ -9,13 +9,14 @@ product all run in that one kernel.  The weights are synthetic
 (workloads.py), shaped like Llama-3.1-8B MLP projections; the default
 workload is gate_proj 14336x4096 at batch 1.
 
-Timing: W untimed steps, then K steps, both replayed from a captured HIP
-graph (launch overhead out of the way); the timed steps are bracketed by
-synchronisation and by HIP events recorded on the stream the kernels run on.
-The default W (2000 steps, about 50 ms) lets the clocks settle at the level
-a continuous decode loop runs at.  The steps rotate over 8
-device copies of the compressed matrix so the working set (8 x 79 MB)
-exceeds the 256 MB Infinity Cache and every step reads HBM.
+Timing: at least W untimed steps and at least 0.5 s of them (the clocks
+settle at the level a continuous decode loop runs at only after ~10 ms of
+back-to-back launches, whatever W the caller asks for), then exactly K timed
+steps, all replayed from captured HIP graphs (launch overhead out of the
+way); the timed steps are bracketed by synchronisation and by HIP events
+recorded on the stream the kernels run on.  The steps rotate over 8 device
+copies of the compressed matrix so the working set (8 x 80 MB) exceeds the
+256 MB Infinity Cache and every step reads HBM.
 
 The JSON line carries the metric (effective uncompressed-weight GB/s), the
 roofline of the fused kernel (algorithmic bytes = every byte of the blob +
@@ -40,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATE = 8
+WARMUP_FLOOR_S = 0.5
 PARITY_TOL = 1e-3  # max |y - y64| / max(|y64|, rms(y64)) for fp32 outputs
 
 
@@ -62,9 +64,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# The sources the fused GEMV is built from: a recorded traffic figure is
+# valid only while these are unchanged.
+TRAFFIC_SOURCES = ("uw_kernels.hip", "uw_device.h", "uw_internal.h", "uw_api.cpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.join(ROOT, "decode_gemv_canonical_amd", "csrc"))):
+    for name in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "decode_gemv_canonical_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -84,12 +91,14 @@ def recorded_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def time_graph(fn_list, steps, warmup, torch):
-    """Capture one graph holding len(fn_list) launches (after one eager pass
-    that loads the kernels), replay it untimed to cover `warmup` launches, so
-    the clocks reach the level a continuous decode loop runs at, then replay
-    it to cover `steps` launches between two events; returns (avg launch us
-    from the events, wall seconds, launches timed)."""
+def time_graph(fn_list, steps, warmup, torch, floor_s=WARMUP_FLOOR_S):
+    """Time exactly `steps` launches of the rotation fn_list (launch i runs
+    fn_list[i % n]).  One eager pass loads the kernels; a graph of the n
+    launches and one of the steps % n remaining are captured; the rotation
+    graph is replayed untimed for at least `warmup` launches and `floor_s`
+    seconds, then the timed launches run between two events on the capture
+    stream.  Returns (avg launch us from the events, wall seconds of the timed
+    launches, launches timed, warm-up launches, warm-up seconds)."""
     stream = torch.cuda.Stream()
     n = len(fn_list)
     with torch.cuda.stream(stream):
@@ -100,43 +109,73 @@ def time_graph(fn_list, steps, warmup, torch):
     with torch.cuda.graph(g, stream=stream):
         for fn in fn_list:
             fn()
+    rem = steps % n
+    g_rem = None
+    if rem:
+        g_rem = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_rem, stream=stream):
+            for fn in fn_list[:rem]:
+                fn()
     torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    warm = 0
     with torch.cuda.stream(stream):
-        for _ in range(max(1, -(-warmup // n))):
-            g.replay()
-    torch.cuda.synchronize()
-    reps = max(1, -(-steps // n))
+        while warm < warmup or time.perf_counter() - w0 < floor_s:
+            for _ in range(16):
+                g.replay()
+            warm += 16 * n
+            torch.cuda.synchronize()
+    warm_s = time.perf_counter() - w0
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record(stream)
-        for _ in range(reps):
+        for _ in range(steps // n):
             g.replay()
+        if g_rem is not None:
+            g_rem.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-    return e0.elapsed_time(e1) * 1000.0 / (reps * n), (t1 - t0), reps * n
+    return e0.elapsed_time(e1) * 1000.0 / steps, (t1 - t0), steps, warm, warm_s
+
+
+def _oracle_chunk(args):
+    """One worker of the all-core baseline: the oracle's decode of one row
+    chunk's blob and its fp32 matvec, `reps` times (single-threaded BLAS)."""
+    blob_bytes, x, reps = args
+    from threadpoolctl import threadpool_limits
+
+    from oracle import blob as oblob
+    from oracle import products
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            dec = oblob.decode(blob_bytes)
+            y = products.gemm_f32(dec, x)
+        return time.perf_counter() - t0, int(y.shape[0])
 
 
 def cpu_baseline(workload: str, target_s: float):
-    """The oracle (numpy decode of the same blob format + fp32 matvec) on a
-    sample of rows of the same workload, single-threaded BLAS."""
-    import torch
+    """The oracle (numpy decode of the same blob format + fp32 matvec) on this
+    host, on a sample of rows of the same workload: on one thread, and on every
+    core of the process's affinity mask (the rows split into one chunk per
+    core, each chunk's blob decoded by its own process, BLAS on one thread per
+    process)."""
+    import multiprocessing as mp
 
     import workloads
     from oracle import blob as oblob
     from oracle import products
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    r_full, c = workloads.SHAPES[workload]
-    rows = 64
-    x = workloads.activations(c, 1, seed=workloads.SEEDS[workload] + 100).float().numpy()[0]
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import decode_gemv_canonical_amd as uw
+    r_full, c = workloads.SHAPES[workload]
+    x = workloads.activations(c, 1, seed=workloads.SEEDS[workload] + 100).float().numpy()[0]
+    affinity = len(os.sched_getaffinity(0))
+    blas = [f"{i.get('internal_api')}:{i.get('num_threads')}" for i in threadpool_info()]
 
     def run(rows, reps=1):
         w = workloads.weights(workload, rows=rows).numpy().view(np.uint16)
@@ -149,35 +188,50 @@ def cpu_baseline(workload: str, target_s: float):
         assert np.array_equal(dec, w) and y.shape == (rows,)
         return dt / reps, dt
 
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
+    rows = 64
+    with threadpool_limits(limits=1):
         dt, total = run(rows)
         while dt < target_s / 4 and rows < r_full:
             rows = min(r_full, int(rows * min(8.0, max(2.0, target_s / max(dt, 1e-3)))))
             dt, total = run(rows)
         reps = 1
         if rows == r_full and dt < target_s / 2:
-            # the whole matrix is less work than the target: repeat it
-            reps = max(1, int(target_s / dt))
+            reps = max(1, int(target_s / dt))  # the whole matrix is less work than the target: repeat it
             dt, total = run(rows, reps)
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    gbs = 2.0 * rows * c / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} of {r_full} rows of the {workload} matrix, {reps} pass(es): numpy lane-lockstep "
-                      f"decode of the blob + fp32 matvec, {dt:.2f} s per pass, {total:.1f} s in all, on 1 thread "
-                      f"(os.cpu_count()={os.cpu_count()})",
-            "seconds": round(total, 3)}
+    one = {"value": round(2.0 * rows * c / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{rows} of {r_full} rows of the {workload} matrix, {reps} pass(es): numpy lane-lockstep decode of "
+                     f"the blob + fp32 matvec, {dt:.2f} s per pass, {total:.1f} s in all, on 1 thread",
+           "seconds": round(total, 3)}
+    # all cores: the whole matrix in one row chunk per core, each its own blob
+    # (at most the CPU share the job is given: OMP_NUM_THREADS when set)
+    cores = max(1, min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity) or affinity)))
+    w = workloads.weights(workload).numpy().view(np.uint16)
+    bounds = np.linspace(0, r_full, cores + 1).astype(int)
+    chunks = [uw.uw_encode(np.ascontiguousarray(w[a:b])) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    per_chunk_s = dt / rows * (r_full / len(chunks))  # from the 1-thread rate
+    creps = max(1, int(target_s / 2 / max(per_chunk_s, 1e-3)))
+    with mp.get_context("spawn").Pool(len(chunks)) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_chunk, [(b, x, creps) for b in chunks])
+        wall = time.perf_counter() - t0
+    assert sum(r for _, r in res) == r_full
+    allc = {"value": round(2.0 * r_full * c * creps / wall / 1e9, 4), "unit": "GB/s", "cores": len(chunks),
+            "kind": "oracle",
+            "sample": f"all {r_full} rows of the {workload} matrix in {len(chunks)} row chunks (one blob and one "
+                      f"process each), {creps} pass(es), {wall:.1f} s wall",
+            "seconds": round(wall, 3)}
+    return {**allc, "one_thread": one, "host": {"os_cpu_count": os.cpu_count(), "affinity_cores": affinity,
+                                              "blas_threads_outside_the_timing": blas,
+                                              "blas_threads_timed": 1}}
 
 
 def gemm_sweep(uw, workloads, torch, dev, steps):
     """Batched products on the scope's batch sizes: down_proj at 1/4/16/64,
-    gate_proj at 32 (one layer of the 32-layer stack), 8192x8192 at 256.
-    Every candidate variant, plus torch.matmul on the uncompressed bf16
-    weights; 4 rotated copies each."""
+    gate_proj at 32 and 64 (one layer of the 32-layer stack), 8192x8192 at
+    256.  Every candidate variant, the palette form, plus torch.matmul on the
+    uncompressed bf16 weights; every operand rotates over 8 copies (the
+    compressed, palette and bf16 working sets each exceed twice the 256 MB
+    Infinity Cache), so every call reads HBM."""
     cases = [("down", (1, 4, 16, 64)), ("gate", (32, 64)), ("big", (256,))]
     names = {uw.UW_VARIANT_FUSED: "fused_valu", uw.UW_VARIANT_FUSED_MFMA: "fused_mfma",
              uw.UW_VARIANT_DECOMPRESS_GEMM: "decompress_gemm"}
@@ -186,10 +240,10 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
         rows, cols = workloads.SHAPES[name]
         w = workloads.weights(name)
         blob = uw.uw_encode(w)
-        mats = [uw.CompressedMatrix(blob, device="cuda:0") for _ in range(4)]
+        mats = [uw.CompressedMatrix(blob, device="cuda:0") for _ in range(ROTATE)]
         pblob = uw.uw_palette_encode(w)
-        pmats = [uw.PaletteMatrix(pblob, device="cuda:0") for _ in range(4)]
-        Wb = [torch.from_numpy(w.numpy()).to(dev).view(torch.bfloat16) for _ in range(2)]
+        pmats = [uw.PaletteMatrix(pblob, device="cuda:0") for _ in range(ROTATE)]
+        Wb = [torch.from_numpy(w.numpy()).to(dev).view(torch.bfloat16) for _ in range(ROTATE)]
         for B in batches:
             X = workloads.activations(cols, B, seed=workloads.SEEDS[name] + 200 + B, dtype=torch.bfloat16).to(dev)
             Y = torch.empty(B, rows, dtype=torch.float32, device=dev)
@@ -199,8 +253,8 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
                     continue  # one decode pass per 8 rows: not a candidate at this size
                 ws = mats[0].workspace(B, v)
                 try:
-                    us, _, _ = time_graph([(lambda m=m: uw.uw_gemm_fused(m.handle, X, Y, v, ws)) for m in mats],
-                                          steps, steps, torch)
+                    us = time_graph([(lambda m=m: uw.uw_gemm_fused(m.handle, X, Y, v, ws)) for m in mats],
+                                    steps, steps, torch, floor_s=0.05)[0]
                 except uw.UwError:
                     continue
                 rec[vn + "_us"] = round(us, 2)
@@ -208,17 +262,22 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
             # the exponent-only pipeline: exponent bytes to HBM, then the
             # reconstructive product on the matrix cores
             wse = torch.empty(uw.uw_exponent_ws_size(mats[0].handle, B), dtype=torch.uint8, device=dev)
-            us, _, _ = time_graph([(lambda m=m: uw.uw_exponent_gemm(m.handle, X, Y, wse)) for m in mats], steps, steps,
-                                  torch)
+            us = time_graph([(lambda m=m: uw.uw_exponent_gemm(m.handle, X, Y, wse)) for m in mats], steps, steps,
+                            torch, floor_s=0.05)[0]
             rec["exponent_gemm_us"] = round(us, 2)
             del wse
             # the direct-palette form on the matrix cores (larger blob, no entropy decode)
-            us, _, _ = time_graph([(lambda m=m: uw.uw_palette_gemm(m.handle, X, Y)) for m in pmats], steps, steps, torch)
+            us = time_graph([(lambda m=m: uw.uw_palette_gemm(m.handle, X, Y)) for m in pmats], steps, steps, torch,
+                            floor_s=0.05)[0]
             rec["palette_mfma_us"] = round(us, 2)
             rec["palette_blob_GBs"] = round(len(pblob) / (us * 1e-6) / 1e9, 1)
             Yb = torch.empty(B, rows, dtype=torch.bfloat16, device=dev)
-            us, _, _ = time_graph([(lambda W=W: torch.matmul(X, W.t(), out=Yb)) for W in Wb], steps, steps, torch)
+            us = time_graph([(lambda W=W: torch.matmul(X, W.t(), out=Yb)) for W in Wb], steps, steps, torch,
+                            floor_s=0.05)[0]
             rec["torch_bf16_matmul_us"] = round(us, 2)
+            # the library's own bf16 product on the uncompressed weights
+            us = time_graph([(lambda W=W: uw.uw_bf16_gemm(W, X, Y)) for W in Wb], steps, steps, torch, floor_s=0.05)[0]
+            rec["ours_bf16_gemm_us"] = round(us, 2)
             best = min(v for k, v in rec.items() if k.startswith(("fused", "decompress", "exponent")))
             rec["blob_GBs_best"] = round(len(blob) / (best * 1e-6) / 1e9, 1)
             out[f"{name}_{rows}x{cols}_b{B}"] = rec
@@ -306,8 +365,8 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
                 got = res[:, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
                 worst = max(worst, products.rel_error_floored(got, ref))
         reps = max(1, steps // 96)
-        us_m, _, _ = time_graph([lambda: [matrix_calls(li) for li in range(n)]], reps, reps, torch)
-        us_e, _, _ = time_graph([lambda: [elementwise(li) for li in range(n)]], reps, reps, torch)
+        us_m = time_graph([lambda: [matrix_calls(li) for li in range(n)]], reps, reps, torch)[0]
+        us_e = time_graph([lambda: [elementwise(li) for li in range(n)]], reps, reps, torch)[0]
         gb = [torch.empty(B, F, dtype=torch.bfloat16, device=dev) for _ in range(2)]
         db = torch.empty(B, H, dtype=torch.bfloat16, device=dev)
 
@@ -317,7 +376,7 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
                 torch.matmul(xs[li], bfw[li]["up"].t(), out=gb[1])
                 torch.matmul(h[li], bfw[li]["down"].t(), out=db)
 
-        us_b, _, _ = time_graph([bf16_calls], reps, reps, torch)
+        us_b = time_graph([bf16_calls], reps, reps, torch)[0]
         # gate and up as one matrix: 64 calls per token
         gu = [torch.empty(B, 2 * F, dtype=torch.float32, device=dev) for _ in range(n)]
 
@@ -337,7 +396,7 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
             got = gu[li][:, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
             worst_gu = max(worst_gu, products.rel_error_floored(got, ref))
             del wcat
-        us_f, _, _ = time_graph([lambda: [fused_calls(li) for li in range(n)]], reps, reps, torch)
+        us_f = time_graph([lambda: [fused_calls(li) for li in range(n)]], reps, reps, torch)[0]
 
         # the same 96 products over the direct-palette form (GEMV at batch 1,
         # matrix-core GEMM above), on the inputs of the eager token
@@ -368,7 +427,7 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
                 ref = products.gemm_f64(wb, inp.float().cpu().numpy())
                 got = res[:, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
                 worst_p = max(worst_p, products.rel_error_floored(got, ref))
-        us_p, _, _ = time_graph([lambda: [palette_calls(li) for li in range(n)]], reps, reps, torch)
+        us_p = time_graph([lambda: [palette_calls(li) for li in range(n)]], reps, reps, torch)[0]
         out[f"b{B}"] = {"matrix_ms_per_token": round(us_m / 1e3, 4), "elementwise_ms_per_token": round(us_e / 1e3, 4),
                         "gate_up_fused_matrix_ms_per_token": round(us_f / 1e3, 4),
                         "gate_up_fused_parity_max_rel_err_sampled": worst_gu,
@@ -421,7 +480,7 @@ def main():
     # the timed step
     fns = [(lambda m=m: uw.uw_gemv_fused(m.handle, x, y)) for m in mats]
     log(f"timing fused decode+GEMV: {args.steps} steps after {args.warmup} warm-up")
-    us, wall, done = time_graph(fns, args.steps, args.warmup, torch)
+    us, wall, done, warm_done, warm_s = time_graph(fns, args.steps, args.warmup, torch)
     algo_bytes = info["total_bytes"] + cols * x.element_size() + rows * 4
     achieved = algo_bytes / (us * 1e-6) / 1e9
     value = 2.0 * weights * done / wall / 1e9
@@ -439,6 +498,7 @@ def main():
         "n_gpus": 1,
         "steps": done,
         "warmup": args.warmup,
+        "warmup_done": {"launches": warm_done, "seconds": round(warm_s, 3), "floor_s": WARMUP_FLOOR_S},
         "ms_per_step": round(wall * 1000.0 / done, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -468,11 +528,11 @@ def main():
         xr = x.reshape(1, cols)
         yr = yb.reshape(1, rows)
         log("timing uncompressed bf16 GEMV (ours)")
-        us_b, _, _ = time_graph([(lambda W=W: uw.uw_bf16_gemm(W, xr, yr)) for W in Wb], args.steps, args.warmup, torch)
+        us_b = time_graph([(lambda W=W: uw.uw_bf16_gemm(W, xr, yr)) for W in Wb], args.steps, args.warmup, torch)[0]
         ybf = torch.empty(rows, dtype=torch.bfloat16, device=dev)
         log("timing torch.matmul (hipBLASLt) comparator")
-        us_t, _, _ = time_graph([(lambda W=W: torch.mv(W, x if x.dtype == torch.bfloat16 else x.bfloat16(), out=ybf))
-                                 for W in Wb], args.steps, args.warmup, torch)
+        us_t = time_graph([(lambda W=W: torch.mv(W, x if x.dtype == torch.bfloat16 else x.bfloat16(), out=ybf))
+                           for W in Wb], args.steps, args.warmup, torch)[0]
         best_bf16 = min(us_b, us_t)
         extras["uncompressed"] = {
             "ours_bf16_gemv_us": round(us_b, 3), "torch_mv_us": round(us_t, 3),
@@ -488,8 +548,8 @@ def main():
         for L in (8, 12):
             bl = uw.uw_encode(w, L=L)
             ml = [uw.CompressedMatrix(bl, device="cuda:0") for _ in range(ROTATE)]
-            us_l, _, _ = time_graph([(lambda m=m: uw.uw_gemv_fused(m.handle, x, y)) for m in ml], args.steps,
-                                    args.warmup, torch)
+            us_l = time_graph([(lambda m=m: uw.uw_gemv_fused(m.handle, x, y)) for m in ml], args.steps,
+                              args.warmup, torch)[0]
             ablation[f"L{L}"] = {"us": round(us_l, 3), "bits_per_weight": round(uw.uw_blob_info(bl)["bits_per_weight"], 4)}
             for m in ml:
                 m.close()
@@ -500,7 +560,7 @@ def main():
         log("read probe")
         buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         sink = torch.empty(uw.uw_read_probe_sink_size(), dtype=torch.uint8, device=dev)
-        us_p, _, _ = time_graph([lambda: uw.uw_read_probe(buf, sink)], 20, 3, torch)
+        us_p = time_graph([lambda: uw.uw_read_probe(buf, sink)], 20, 3, torch, floor_s=0.05)[0]
         probe = buf.numel() / (us_p * 1e-6) / 1e9
         extras["read_probe_GBs"] = round(probe, 1)
         extras["fused_frac_of_read_probe"] = round(achieved / probe, 4)
@@ -509,7 +569,7 @@ def main():
         # the fused step: the streaming ceiling for a read of this length
         nbytes = (info["total_bytes"] + 255) // 256 * 256
         bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(ROTATE)]
-        us_ps, _, _ = time_graph([(lambda b=b: uw.uw_read_probe(b, sink)) for b in bufs], args.steps, args.warmup, torch)
+        us_ps = time_graph([(lambda b=b: uw.uw_read_probe(b, sink)) for b in bufs], args.steps, args.warmup, torch)[0]
         probe_same = nbytes / (us_ps * 1e-6) / 1e9
         extras["read_probe_blob_size"] = {"bytes": nbytes, "us": round(us_ps, 3), "GBs": round(probe_same, 1),
                                           "fused_frac": round(achieved / probe_same, 4)}
@@ -518,8 +578,8 @@ def main():
         # decompress-to-HBM alternative (reads the blob, writes bf16)
         out_w = [torch.empty(rows, cols, dtype=torch.bfloat16, device=dev) for _ in range(2)]
         log("timing decompress")
-        us_d, _, _ = time_graph([(lambda m=m, o=out_w[i % 2]: uw.uw_decompress(m.handle, o, cols))
-                                 for i, m in enumerate(mats)], 400, 400, torch)
+        us_d = time_graph([(lambda m=m, o=out_w[i % 2]: uw.uw_decompress(m.handle, o, cols))
+                           for i, m in enumerate(mats)], 400, 400, torch, floor_s=0.05)[0]
         dbytes = info["total_bytes"] + 2 * weights
         extras["decompress"] = {"us": round(us_d, 3), "GBs_read_plus_write": round(dbytes / (us_d * 1e-6) / 1e9, 1),
                                 "frac_hbm_peak": round(dbytes / (us_d * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -532,13 +592,13 @@ def main():
         pinfo = uw.uw_palette_info(pblob)
         pmats = [uw.PaletteMatrix(pblob, device="cuda:0") for _ in range(ROTATE)]
         yp = torch.empty(rows, dtype=torch.float32, device=dev)
-        us_pg, _, _ = time_graph([(lambda m=m: uw.uw_palette_gemv(m.handle, x, yp)) for m in pmats], args.steps,
-                                 args.warmup, torch)
+        us_pg = time_graph([(lambda m=m: uw.uw_palette_gemv(m.handle, x, yp)) for m in pmats], args.steps,
+                           args.warmup, torch)[0]
         perr = products.rel_error_floored(yp.cpu().numpy(), ref)
         pbytes = pinfo["bytes"] + cols * x.element_size() + rows * 4
         out_pw = [torch.empty(rows, cols, dtype=torch.bfloat16, device=dev) for _ in range(2)]
-        us_pd, _, _ = time_graph([(lambda m=m, o=out_pw[i % 2]: uw.uw_palette_decompress(m.handle, o, cols))
-                                  for i, m in enumerate(pmats)], 400, 400, torch)
+        us_pd = time_graph([(lambda m=m, o=out_pw[i % 2]: uw.uw_palette_decompress(m.handle, o, cols))
+                            for i, m in enumerate(pmats)], 400, 400, torch, floor_s=0.05)[0]
         extras["palette_pipeline"] = {
             "ratio": round(pinfo["ratio"], 5), "blob_bytes": pinfo["bytes"],
             "raw_group_frac": round(pinfo["n_raw"] / (weights // 64), 6),
@@ -564,7 +624,7 @@ def main():
         del wr
         assert mplain.info["plain"], "random bits are expected to take plain mode"
         out_p = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
-        us_c, _, _ = time_graph([lambda: uw.uw_decompress(mplain.handle, out_p, 8192)], 16, 4, torch)
+        us_c = time_graph([lambda: uw.uw_decompress(mplain.handle, out_p, 8192)], 16, 4, torch, floor_s=0.05)[0]
         extras["plain_copy"] = {"bytes_each_way": 2 * 8192 * 8192, "us": round(us_c, 3),
                                 "GBs_read_plus_write": round(4 * 8192 * 8192 / (us_c * 1e-6) / 1e9, 1)}
         mplain.close()

@@ -111,31 +111,36 @@ __global__ __launch_bounds__(256) void bf16_gemv_kernel(const uint16_t* __restri
 
 // ---------------------------------------------------------------------------
 // Streaming read: every byte read once with 16-byte loads, xor-folded into
-// one word per workgroup so the loads cannot be removed.
-__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, int64_t n16,
-                                                         uint32_t* __restrict__ sink) {
+// one word per workgroup so the loads cannot be removed.  The launch shape is
+// the fastest of a sweep over workgroup sizes (256..1024 threads), grids (1 to
+// 16 workgroups per compute unit) and loads in flight per thread (1..8), for
+// 80 MiB and 1 GiB reads rotated over cold buffers: 1024 threads, 16
+// workgroups per compute unit, one load per thread per pass (14.2 us for
+// 80 MiB, 166 us for 1 GiB; a grid-stride loop over the whole buffer keeps
+// every wave's next address in the same DRAM pages as its neighbours').
+__global__ __launch_bounds__(1024) void read_probe_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                          uint32_t* __restrict__ sink) {
   uint32_t x = 0;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], e = src[i + 3 * stride];
-    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ e.x ^ e.y ^ e.z ^ e.w;
-  }
-  for (; i < n16; i += stride) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) {
     const uint4 a = src[i];
     x ^= a.x ^ a.y ^ a.z ^ a.w;
   }
-  __shared__ uint32_t red[256];
-  red[threadIdx.x] = x;
+  // wave xor, then one word per workgroup
+  for (int off = 32; off > 0; off >>= 1) x ^= uint32_t(__shfl_xor(int(x), off));
+  __shared__ uint32_t red[16];
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t s = 0;
-    for (int t = 0; t < int(blockDim.x); ++t) s ^= red[t];
+    for (int t = 0; t < int(blockDim.x / kWave); ++t) s ^= red[t];
     sink[blockIdx.x] = s;
   }
 }
 
-constexpr int kProbeBlocks = 2048;
+constexpr int kProbeThreads = 1024;
+constexpr int kProbeBlocksPerCu = 16;
+constexpr int kProbeMaxBlocks = 16 * 256;  // the sink holds one word per workgroup
 
 // Plain-mode matrices: a strided copy of the stored bf16 bits.
 __global__ void copy_plain_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
@@ -232,10 +237,14 @@ int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
   return UW_OK;
 }
 
-size_t read_probe_sink_bytes() { return size_t(kProbeBlocks) * 4; }
+size_t read_probe_sink_bytes() { return size_t(kProbeMaxBlocks) * 4; }
 
 int launch_read_probe(const void* src, size_t bytes, void* sink, void* stream) {
-  hipLaunchKernelGGL(read_probe_kernel, dim3(kProbeBlocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int blocks = std::min(kProbeMaxBlocks, std::max(1, cus) * kProbeBlocksPerCu);
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(kProbeThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(src), int64_t(bytes / 16), static_cast<uint32_t*>(sink));
   return hip_check(hipGetLastError(), "read_probe_kernel launch");
 }

@@ -164,6 +164,123 @@ __global__ __launch_bounds__(512) void bf16_mfma_kernel(const uint16_t* __restri
     }
 }
 
+// The large-batch form: the activations of a k-block (16 TB rows x 128
+// columns) are staged once in LDS and shared by the workgroup's 4 waves,
+// each of which streams its own 16 RB weight rows straight into registers.
+// Two LDS buffers alternate: while the matrix cores work on block kb, the
+// loads of block kb + 1 (activations and weights) are in flight; one barrier
+// per block.  A staged row is 256 bytes plus 16 of padding, so the 16 rows a
+// B-operand read touches start on different banks.
+constexpr int kXRowBytes = 256 + 16;
+
+template <int RB, int TB, bool YBF16>
+__global__ __launch_bounds__(256) void bf16_mfma_xlds_kernel(const uint16_t* __restrict__ W, int64_t rows, int64_t cols,
+                                                             int64_t ldw, const uint16_t* __restrict__ X, int64_t ldx,
+                                                             int64_t batch, void* __restrict__ Y, int64_t ldy,
+                                                             int n_groups, int ny) {
+  constexpr int kTileBytes = 16 * TB * kXRowBytes;
+  extern __shared__ uint32_t lds[];
+  const int L = blockIdx.x;
+  const int grp = (L / (kXcds * ny)) * kXcds + L % kXcds;
+  const int y = (L / kXcds) % ny;
+  if (grp >= n_groups) return;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int r = lane % 16, q = lane / 16;
+  const int64_t row0 = int64_t(grp) * 64 * RB + int64_t(wave) * 16 * RB, b0 = int64_t(y) * 16 * TB;
+  const int64_t kq = 32 * q;
+  const uint16_t* wr[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) wr[i] = W + std::min<int64_t>(row0 + 16 * i + r, rows - 1) * ldw + kq;
+  // staging: thread t moves 16 bytes (8 columns) of TB activation rows per block
+  const int srow = tid / 16, schunk = tid % 16;
+  const uint16_t* xs[TB];
+#pragma unroll
+  for (int u = 0; u < TB; ++u) xs[u] = X + std::min<int64_t>(b0 + 16 * u + srow, batch - 1) * ldx + 8 * schunk;
+  auto stage_load = [&](int64_t kb, uint4 (&v)[TB]) {
+    const int64_t k = 128 * kb + 8 * schunk;
+#pragma unroll
+    for (int u = 0; u < TB; ++u) v[u] = k + 8 <= cols ? *reinterpret_cast<const uint4*>(xs[u] + 128 * kb) : uint4{0u, 0u, 0u, 0u};
+  };
+  auto stage_store = [&](int buf, const uint4 (&v)[TB]) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u) st128(uint32_t(buf * kTileBytes + (16 * u + srow) * kXRowBytes + 16 * schunk), v[u]);
+  };
+  floatx4 acc[RB][TB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t nkb = (cols + 127) / 128;
+  uint4 xv[TB];
+  uint4 wc[RB][4], wn[RB][4];
+  stage_load(0, xv);
+#pragma unroll
+  for (int i = 0; i < RB; ++i) load_row32(wr[i], 0, cols - kq, wc[i]);
+  stage_store(0, xv);
+  lds_barrier();
+  // B operand of tile t, k-step s: row 16 t + r of the staged block, bytes 64 q + 16 s
+  const uint32_t bq = uint32_t(r * kXRowBytes + 64 * q);
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    const int buf = int(kb & 1);
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      stage_load(kb + 1, xv);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) load_row32(wr[i], 128 * (kb + 1), cols - kq, wn[i]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 xb[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) xb[t] = ld128(uint32_t(buf * kTileBytes + t * 16 * kXRowBytes) + bq + 16 * s);
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) acc[i][t] = mfma16(wc[i][s], xb[t], acc[i][t]);
+    }
+    if (more) {
+      stage_store(buf ^ 1, xv);
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wc[i][u] = wn[i][u];
+    }
+    lds_barrier();
+  }
+  // lane (r, q) holds rows 4 q .. 4 q + 3 of tile (i, t) for batch row r
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const int64_t b = b0 + 16 * t + r;
+      const int64_t n = row0 + 16 * i + 4 * q;
+      if (b >= batch) continue;
+      const float vals[4] = {acc[i][t].x, acc[i][t].y, acc[i][t].z, acc[i][t].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e < rows) {
+          if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + n + e] = f32_to_bf16(vals[e]);
+          else static_cast<float*>(Y)[b * ldy + n + e] = vals[e];
+        }
+      }
+    }
+}
+
+template <int RB, int TB>
+int run_xlds_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
+                  int64_t ldx, void* Y, int64_t ldy, int yt, void* stream) {
+  const int n_groups = int((rows + 64 * RB - 1) / (64 * RB));
+  const int ny = int((batch + 16 * TB - 1) / (16 * TB));
+  const int64_t grid = int64_t((n_groups + kXcds - 1) / kXcds) * kXcds * ny;
+  const size_t lds = size_t(2) * 16 * TB * kXRowBytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto kern = yt == UW_BF16 ? bf16_mfma_xlds_kernel<RB, TB, true> : bf16_mfma_xlds_kernel<RB, TB, false>;
+  allow_full_lds(kern);
+  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(256), lds, s, W, rows, cols, ldw, X, ldx, batch, Y, ldy, n_groups,
+                     ny);
+  return hip_check(hipGetLastError(), "bf16_mfma_xlds_kernel launch");
+}
+
 template <int RB, int TB, bool PIPE>
 int run_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
                   int64_t ldx, void* Y, int64_t ldy, int yt, int ks, void* stream) {
@@ -183,12 +300,17 @@ int run_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, co
 
 // Shapes of the matrix-core product (a tuning knob: uw_bf16_gemm_config).
 // id: 0 = chosen by the heuristic below; else one of the listed shapes.
+// Shapes 1..9: operands straight from global memory, RB x 16 weight rows and
+// TB x 16 batch rows per workgroup of KS waves splitting k.  Shapes 10..13:
+// the activations staged in LDS, 4 waves of RB x 16 weight rows each (ks
+// does not apply).
 struct MfmaShape {
-  int rb, tb, pipe;
+  int rb, tb, pipe, xlds;
 };
 constexpr MfmaShape kMfmaShapes[] = {
-    {0, 0, 0},  // heuristic
-    {1, 1, 1}, {2, 1, 1}, {1, 2, 1}, {2, 2, 1}, {1, 4, 1}, {2, 4, 0}, {4, 4, 0}, {4, 2, 0}, {2, 4, 1},
+    {0, 0, 0, 0},  // heuristic
+    {1, 1, 1, 0}, {2, 1, 1, 0}, {1, 2, 1, 0}, {2, 2, 1, 0}, {1, 4, 1, 0}, {2, 4, 0, 0}, {4, 4, 0, 0}, {4, 2, 0, 0},
+    {2, 4, 1, 0}, {1, 4, 1, 1}, {2, 4, 1, 1}, {2, 2, 1, 1}, {1, 8, 1, 1},
 };
 constexpr int kMfmaShapeCount = int(sizeof(kMfmaShapes) / sizeof(kMfmaShapes[0]));
 
@@ -209,16 +331,28 @@ static int pick_ks(int64_t rows, int64_t cols, int64_t batch, int rb, int tb) {
 int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
                      int64_t ldx, void* Y, int64_t ldy, int yt, int shape, int ks, void* stream) {
   if (shape <= 0 || shape >= kMfmaShapeCount) {
-    // heuristic: batch tiles of the pass up to 64 rows; more weight rows per
-    // workgroup when the batch is large (the activations are re-read once per
-    // weight row group)
-    if (batch <= 16) shape = 1;
-    else if (batch <= 32) shape = 3;
-    else if (batch <= 64) shape = 5;
-    else shape = 6;
+    // heuristic, from a sweep of every shape and ks on the MLP shapes and
+    // 8192^2 (8 rotated copies of W): up to 16 batch rows 32 weight rows per
+    // workgroup in 2 k-halves; up to 32, 64 x 32 in 4 k-quarters; up to 64,
+    // 64 x 64 in 4; above, the activations staged in LDS, 64 x 128
+    if (batch <= 16) {
+      shape = 2;
+      if (ks <= 0) ks = 2;
+    } else if (batch <= 32) {
+      shape = 8;
+      if (ks <= 0) ks = 4;
+    } else if (batch <= 64) {
+      shape = 7;
+      if (ks <= 0) ks = 4;
+    } else {
+      shape = 13;
+    }
+    // keep at least 2 k-blocks per wave
+    const int64_t nkb = (cols + 127) / 128;
+    while (ks > 1 && nkb / ks < 2) ks /= 2;
   }
   const MfmaShape sh = kMfmaShapes[shape];
-  if (ks <= 0) ks = pick_ks(rows, cols, batch, sh.rb, sh.tb);
+  if (ks <= 0 && !sh.xlds) ks = pick_ks(rows, cols, batch, sh.rb, sh.tb);
   switch (shape) {
     case 1: return run_mfma_gemm<1, 1, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
     case 2: return run_mfma_gemm<2, 1, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
@@ -228,7 +362,11 @@ int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
     case 6: return run_mfma_gemm<2, 4, false>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
     case 7: return run_mfma_gemm<4, 4, false>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
     case 8: return run_mfma_gemm<4, 2, false>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
-    default: return run_mfma_gemm<2, 4, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 9: return run_mfma_gemm<2, 4, true>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, ks, stream);
+    case 10: return run_xlds_gemm<1, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+    case 11: return run_xlds_gemm<2, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+    case 12: return run_xlds_gemm<2, 2>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+    default: return run_xlds_gemm<1, 8>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
   }
 }
 

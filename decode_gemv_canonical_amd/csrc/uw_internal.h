@@ -130,6 +130,11 @@ namespace uw {
 
 // Launchers (uw_kernels.hip).  Shapes and pointers are checked by the caller.
 int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* stream);
+// Work items [item0, item1) of a coded matrix (units, or blocks when rows
+// split across blocks; see DevMatrix::n_items), matrix row r written to
+// out + (r - row_base) * ld_out.
+int launch_decompress_items(const uw_matrix* m, uint16_t* out, int64_t ld_out, int item0, int item1, int64_t row_base,
+                            void* stream);
 // Exponent bytes (R*C, the sm section's tile order); flat walk, not plain.
 int launch_decode_exponents(const uw_matrix* m, uint8_t* out, void* stream);
 // rs: ring depth of the flat walk (0 = chosen from the LDS budget, else 2 or 4).

@@ -744,6 +744,7 @@ struct DecompressSink {
   int64_t trow;   // (row, col) of the current tile's first weight
   int64_t tcol;
   uint16_t* dst;  // flat walk: this lane's column of the tile's first group
+  int64_t row_base;  // output row 0 is matrix row row_base (a band of rows)
   __device__ void unit_begin(int) {}
   __device__ void unit_end() {}
   __device__ void block_begin(int blk) {
@@ -758,7 +759,7 @@ struct DecompressSink {
     if (!FLAT) return;
     trow = row0;
     tcol = int64_t(c0) * 64;
-    dst = out + row0 * ld_out + tcol + lane;
+    dst = out + (row0 - row_base) * ld_out + tcol + lane;
   }
   // flat walk: weight (group 2k or 2k+1, lane) straight to its row; each
   // store instruction writes 128 contiguous bytes across the wave
@@ -782,7 +783,7 @@ struct DecompressSink {
         col -= cols;
         ++row;
       }
-      uint4* dst = reinterpret_cast<uint4*>(out + row * ld_out + col);
+      uint4* dst = reinterpret_cast<uint4*>(out + (row - row_base) * ld_out + col);
       dst[0] = a;
       dst[1] = b;
     }
@@ -882,12 +883,14 @@ __device__ inline auto make_decompress_sink(const DevMatrix& d, uint16_t* out, i
                                             uint32_t tile, int lane) {
   if constexpr (SINK == 1) return ExpSink{d.cols, reinterpret_cast<uint8_t*>(out), lane};
   else if constexpr (SINK == 2) return PaletteSink{po, d.gpr >> 4, lane};
-  else return DecompressSink<FLAT>{d.cols, d.G, out, ld_out, tile, lane, 0, 0};
+  else return DecompressSink<FLAT>{d.cols, d.G, out, ld_out, tile, lane, 0, 0, nullptr, 0};
 }
 
+// Work items [item0, item1) (units, or with split rows blocks, whose rows
+// are whole); the bf16 sink writes matrix row r to output row r - row_base.
 template <bool PAIR, int NQ, bool FLAT, int RS, int SINK = 0>
 __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t* __restrict__ out, int64_t ld_out,
-                                                          PaletteOut po) {
+                                                          PaletteOut po, int item0, int item1, int64_t row_base) {
   extern __shared__ uint32_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int waves = blockDim.x / kWave;
@@ -895,8 +898,8 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   const uint32_t sm_ring = kAreaAddr + uint32_t(wave) * per_wave;
   const uint32_t q_ring = sm_ring + RS * 1024;
   const uint32_t tile = sm_ring + ring_bytes(RS, d.slot_bytes);
-  const int u_first = blockIdx.x * waves + wave;
-  const int n_items = FLAT ? d.n_items : d.n_units;
+  const int u_first = item0 + blockIdx.x * waves + wave;
+  const int n_items = item1;
   int fv = 0;
   // the decode tables, then the first unit's loads; the tables have landed
   // once only the ring's loads may be younger
@@ -911,6 +914,7 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   lds_barrier();
   using Sink = std::conditional_t<SINK == 1, ExpSink, std::conditional_t<SINK == 2, PaletteSink, DecompressSink<FLAT>>>;
   Sink sink = make_decompress_sink<SINK, FLAT>(d, out, ld_out, po, tile, lane);
+  if constexpr (SINK == 0) sink.row_base = row_base;
   for (int u = u_first; u < n_items; u += gridDim.x * waves) {
     // the two 16-byte stores per tile only make the ring waits stricter
     if (FLAT) {
@@ -1654,12 +1658,13 @@ int fused_chunk(const DevMatrix& d, int64_t batch, bool xf32) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* stream) {
+int launch_decompress_items(const uw_matrix* m, uint16_t* out, int64_t ld_out, int item0, int item1, int64_t row_base,
+                            void* stream) {
   const DevMatrix& d = m->dev;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (m->h.plain()) return launch_copy_plain(d.plain, d.rows, d.cols, out, ld_out, stream);
   const size_t fixed = tables_bytes();
-  const int items = d.flat ? d.n_items : d.n_units;
+  const int items = item1 - item0;
+  if (items <= 0) return UW_OK;
   const int rs = d.flat ? flat_ring_depth(items, fixed, d.slot_bytes, 0, 16) : kRS;
   const size_t per_wave = ring_bytes(rs, d.slot_bytes) + (d.flat ? 0 : kTransposeWords * 4);
   const int waves = pick_waves(items, fixed, per_wave);
@@ -1674,8 +1679,14 @@ int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* s
   };
   auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
   allow_full_lds(kern);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, out, ld_out, PaletteOut{});
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, out, ld_out, PaletteOut{}, item0, item1, row_base);
   return hip_check(hipGetLastError(), "decompress_kernel launch");
+}
+
+int launch_decompress(const uw_matrix* m, uint16_t* out, int64_t ld_out, void* stream) {
+  const DevMatrix& d = m->dev;
+  if (m->h.plain()) return launch_copy_plain(d.plain, d.rows, d.cols, out, ld_out, stream);
+  return launch_decompress_items(m, out, ld_out, 0, d.flat ? d.n_items : d.n_units, 0, stream);
 }
 
 // Exponent bytes of every weight, in the sign+mantissa section's tile order
@@ -1699,7 +1710,7 @@ int launch_decode_exponents(const uw_matrix* m, uint8_t* out, void* stream) {
   auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
   allow_full_lds(kern);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, reinterpret_cast<uint16_t*>(out), int64_t(0),
-                     PaletteOut{});
+                     PaletteOut{}, 0, items, int64_t(0));
   return hip_check(hipGetLastError(), "decompress_kernel (exponents) launch");
 }
 
@@ -1773,7 +1784,8 @@ int launch_palette_transcode(const uw_matrix* m, uint8_t* out, void* stream) {
   };
   auto kern = is_pair(d) ? pick(std::true_type{}) : pick(std::false_type{});
   allow_full_lds(kern);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, static_cast<uint16_t*>(nullptr), int64_t(0), po);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, s, d, static_cast<uint16_t*>(nullptr), int64_t(0), po, 0,
+                     items, int64_t(0));
   return hip_check(hipGetLastError(), "decompress_kernel (palette transcode) launch");
 }
 
