@@ -458,9 +458,13 @@ int uw_get_plan(const uw_matrix* m, int64_t batch, uw_plan* out) {
 
 namespace {
 
-// Run one (variant, knob) after the checks of runnable().
+// Run one (variant, knob) after the checks of runnable().  use_static:
+// decompress + GEMM goes through the library's static scratch, band by band,
+// instead of the workspace d_ws.
 int run_variant(const uw_matrix* m, int variant, int knob, const void* d_X, int64_t batch, int64_t ldx, int xt,
-                void* d_Y, int64_t ldy, int yt, void* d_ws, void* stream) {
+                void* d_Y, int64_t ldy, int yt, void* d_ws, void* stream, bool use_static = false) {
+  if (use_static && variant == UW_VARIANT_DECOMPRESS_GEMM)
+    return static_decompress_gemm(m, d_X, batch, ldx, xt, d_Y, ldy, yt, knob, stream);
   switch (variant) {
     case UW_VARIANT_FUSED_MFMA: return launch_fused_mfma(m, d_X, batch, ldx, d_Y, ldy, yt, stream, knob);
     case UW_VARIANT_FUSED: return launch_fused(m, d_X, batch, ldx, xt, d_Y, ldy, yt, stream, knob);
@@ -496,10 +500,20 @@ int heuristic_variant(const uw_matrix* m, const CallShape& c) {
 }
 
 int gemm_dispatch(const uw_matrix* m, int variant, int knob, const void* d_X, int64_t batch, int64_t ldx, int xt,
-                  void* d_Y, int64_t ldy, int yt, void* d_ws, size_t ws_bytes, void* stream, const char* where) {
+                  void* d_Y, int64_t ldy, int yt, void* d_ws, size_t ws_bytes, void* stream, const char* where,
+                  bool use_static = false) {
   if (int rc = check_matrix(m)) return rc;
   if (int rc = check_products(d_X, batch, ldx, xt, d_Y, ldy, yt, m->h.rows, m->h.cols)) return rc;
   if (batch == 0) return UW_OK;
+  // the static path: decompress + GEMM is runnable when a band of whole work
+  // units fits in the scratch (a stand-in workspace descriptor stands for it;
+  // it is never dereferenced: run_variant takes the static branch)
+  alignas(256) static const uint8_t stand_in[256] = {0};
+  if (use_static) {
+    const bool fits = m->h.plain() || static_band_units(m) >= 1;
+    d_ws = fits ? const_cast<uint8_t*>(stand_in) : nullptr;
+    ws_bytes = fits ? decompress_ws_bytes(m) : 0;
+  }
   const CallShape c{d_X, batch, ldx, xt, d_ws, ws_bytes};
   if (variant == UW_VARIANT_AUTO) {
     knob = 0;
@@ -527,10 +541,13 @@ int gemm_dispatch(const uw_matrix* m, int variant, int knob, const void* d_X, in
   if (!knob_valid(variant, knob)) return fail(UW_ERR_INVALID, std::string(where) + ": knob out of range");
   std::string why;
   if (!runnable(m, variant, knob, c, &why)) {
+    if (use_static && variant == UW_VARIANT_DECOMPRESS_GEMM && why.rfind("workspace", 0) == 0)
+      return fail(UW_ERR_UNSUPPORTED, std::string(where) + ": one work unit of this matrix does not fit in the " +
+                                          std::to_string(static_scratch_bytes() >> 20) + " MiB scratch");
     const bool space = variant == UW_VARIANT_DECOMPRESS_GEMM && why.rfind("workspace", 0) == 0;
     return fail(space ? UW_ERR_NOSPACE : UW_ERR_UNSUPPORTED, std::string(where) + ": " + why);
   }
-  return run_variant(m, variant, knob, d_X, batch, ldx, xt, d_Y, ldy, yt, d_ws, stream);
+  return run_variant(m, variant, knob, d_X, batch, ldx, xt, d_Y, ldy, yt, d_ws, stream, use_static);
 }
 
 }  // namespace
@@ -541,6 +558,13 @@ int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ld
                   int yt, int variant, void* d_ws, size_t ws_bytes, void* stream) {
   if (variant < 0 || variant >= UW_VARIANT_COUNT) return fail(UW_ERR_INVALID, "uw_gemm_fused: unknown variant");
   return gemm_dispatch(m, variant, 0, d_X, batch, ldx, xt, d_Y, ldy, yt, d_ws, ws_bytes, stream, "uw_gemm_fused");
+}
+
+int uw_gemm_fused_static(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y,
+                         int64_t ldy, int yt, int variant, void* stream) {
+  if (variant < 0 || variant >= UW_VARIANT_COUNT) return fail(UW_ERR_INVALID, "uw_gemm_fused_static: unknown variant");
+  return gemm_dispatch(m, variant, 0, d_X, batch, ldx, xt, d_Y, ldy, yt, nullptr, 0, stream, "uw_gemm_fused_static",
+                       true);
 }
 
 int uw_gemm_with_plan(const uw_matrix* m, const uw_plan* plan, const void* d_X, int64_t batch, int64_t ldx, int xt,

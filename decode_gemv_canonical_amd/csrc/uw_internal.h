@@ -166,6 +166,13 @@ int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why);
 // Cache eviction of the autotuner: read `bytes` (multiple of 16) at src.
 int launch_read_probe(const void* src, size_t bytes, void* sink, void* stream);
+// The allocation-free entry point's scratch (uw_static.hip): its size, the
+// work units one band of rows holds (0 when one unit does not fit), and
+// decompress + GEMM through it band by band.
+size_t static_scratch_bytes();
+int64_t static_band_units(const uw_matrix* m);
+int static_decompress_gemm(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy,
+                           int yt, int knob, void* stream);
 size_t read_probe_sink_bytes();
 
 }  // namespace uw

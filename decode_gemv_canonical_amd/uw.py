@@ -79,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "uw_gemv_fused": (I, [P, P, I, P, I, P]),
         "uw_gemm_fused": (I, [P, P, I64, I64, I, P, I64, I, I, P, SZ, P]),
         "uw_gemm_with_plan": (I, [P, ctypes.POINTER(uw_plan), P, I64, I64, I, P, I64, I, P, SZ, P]),
+        "uw_gemm_fused_static": (I, [P, P, I64, I64, I, P, I64, I, I, P]),
         "uw_plan_save": (I, [P, ctypes.c_char_p, ctypes.POINTER(SZ)]),
         "uw_plan_load": (I, [P, ctypes.c_char_p]),
         "uw_workspace_size": (SZ, [P, I64, I]),
@@ -310,6 +311,14 @@ def uw_gemm_fused(handle: int, X, Y, variant: int = UW_VARIANT_AUTO, ws=None, st
     ws_ptr, ws_bytes = _ws(ws, _shape(handle)[2])
     _check(_lib.uw_gemm_fused(handle, X.data_ptr(), batch, X.stride(0), _dtype_code(X), Y.data_ptr(), Y.stride(0),
                               _dtype_code(Y), variant, ws_ptr, ws_bytes, _stream(stream)), "uw_gemm_fused")
+
+
+def uw_gemm_fused_static(handle: int, X, Y, variant: int = UW_VARIANT_AUTO, stream=None) -> None:
+    """uw_gemm_fused with no workspace: decompress + GEMM runs through the
+    library's static scratch (nothing is allocated)."""
+    batch = _gemm_operands(handle, X, Y)
+    _check(_lib.uw_gemm_fused_static(handle, X.data_ptr(), batch, X.stride(0), _dtype_code(X), Y.data_ptr(),
+                                     Y.stride(0), _dtype_code(Y), variant, _stream(stream)), "uw_gemm_fused_static")
 
 
 def uw_gemm_with_plan(handle: int, variant: int, knob: int, X, Y, ws=None, stream=None) -> None:

@@ -241,6 +241,25 @@ int uw_gemm_fused(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ld
                   void* stream);
 
 /*
+ * uw_gemm_fused_static (device) - uw_gemm_fused for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It takes no workspace and allocates nothing: the
+ * decompress + GEMM variant (chosen explicitly, by a stored plan, or by the
+ * AUTO heuristic as if a workspace were given) runs band by band through a
+ * 64 MiB scratch array in the library's device image, one band of whole rows
+ * decompressed and multiplied at a time; the other variants need no scratch.
+ * Each GPU the library runs on holds its own scratch until the process ends;
+ * calls that overlap on one GPU (different streams) race on it, calls in one
+ * stream are ordered.  Results equal uw_gemm_fused's with a workspace (the
+ * same kernels; the bf16 product sees one band of rows at a time).
+ * Errors: as uw_gemm_fused; UW_ERR_UNSUPPORTED when the decompress + GEMM
+ *         variant is asked for and one work unit of the matrix (the rows of
+ *         lcm(G, cols/64) groups) holds more than 64 MiB of bf16 weights.
+ */
+int uw_gemm_fused_static(const uw_matrix* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y,
+                         int64_t ldy, int yt, int variant, void* stream);
+
+/*
  * uw_gemm_with_plan (device) - as uw_gemm_fused, running exactly
  * plan->variant with plan->knob (plan->batch is not used): the form the
  * autotuner times and the tests check every knob through.
