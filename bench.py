@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--gemm-only", action="store_true", help="run only the batched-product sweep (prints its JSON)")
     p.add_argument("--stack", action="store_true",
                    help="run only the 32-layer MLP stack at batch 1 and 32 (prints its JSON; ~2 min of encoding)")
+    p.add_argument("--stack-layers", type=int, default=None,
+                   help="layers of the stack to run (default all 32; fewer for a profiled run)")
+    p.add_argument("--stack-reps", type=int, default=10, help="timed tokens per stack schedule")
     return p.parse_args()
 
 
@@ -289,7 +292,7 @@ def gemm_sweep(uw, workloads, torch, dev, steps):
     return out
 
 
-def stack_run(uw, workloads, torch, dev, steps, warmup):
+def stack_run(uw, workloads, torch, dev, steps, warmup, n_layers=None):
     """The 32-layer MLP stack (Llama-3.1-8B MLP shapes, per-layer sigma): per
     token and layer h = silu(W_gate x) * (W_up x), x' = rmsnorm(W_down h), with
     no learned scale and no residual.  At batch 1 and 32 it times the 96 matrix
@@ -299,14 +302,18 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
     fp64 product of the original weights.  A second layout encodes gate and up
     as one 28672x4096 matrix per layer (one launch for both, as a fused
     gate_up projection): its 64 calls per token are timed and checked the
-    same way."""
+    same way.  The decode-ahead schedule decompresses each layer's down
+    projection on a side stream (all compute units, or 64 of them) while the
+    previous down product and the gate and up products run, and multiplies it
+    from its slot."""
     import numpy as np
 
     from oracle import products
     H, F = workloads.SHAPES["gate"][1], workloads.SHAPES["gate"][0]
     layers, bfw, blob_bytes, pal_bytes = [], [], 0, 0
     t0 = time.perf_counter()
-    for li in range(workloads.STACK_LAYERS):
+    n_layers = n_layers or workloads.STACK_LAYERS
+    for li in range(n_layers):
         L = workloads.stack_layer(li)
         mats = {}
         for k, v in L.items():
@@ -321,12 +328,12 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
         layers.append(mats)
         bfw.append({k: v.to(dev).view(torch.bfloat16) for k, v in L.items()})
         log(f"stack layer {li} encoded and uploaded ({time.perf_counter() - t0:.0f} s)")
-    out = {"layers": workloads.STACK_LAYERS, "matrices": 3 * workloads.STACK_LAYERS, "blob_bytes": blob_bytes,
+    out = {"layers": n_layers, "matrices": 3 * n_layers, "blob_bytes": blob_bytes,
            "palette_bytes": pal_bytes,
-           "bf16_bytes": 3 * workloads.STACK_LAYERS * 2 * H * F, "prep_s": round(time.perf_counter() - t0, 1)}
+           "bf16_bytes": 3 * n_layers * 2 * H * F, "prep_s": round(time.perf_counter() - t0, 1)}
     rng = np.random.default_rng(7)
     for B in (1, 32):
-        n = workloads.STACK_LAYERS
+        n = n_layers
         xs = [torch.empty(B, H, dtype=torch.bfloat16, device=dev) for _ in range(n + 1)]
         xs[0].copy_(workloads.activations(H, B, seed=workloads.STACK_LAYER_SEED0 + 100 + B, dtype=torch.bfloat16))
         g = [torch.empty(B, F, dtype=torch.float32, device=dev) for _ in range(n)]
@@ -366,6 +373,7 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
                 worst = max(worst, products.rel_error_floored(got, ref))
         reps = max(1, steps // 96)
         us_m = time_graph([lambda: [matrix_calls(li) for li in range(n)]], reps, reps, torch)[0]
+        log(f"stack B={B} fused (AUTO): {us_m / 1e3:.3f} ms/token")
         us_e = time_graph([lambda: [elementwise(li) for li in range(n)]], reps, reps, torch)[0]
         gb = [torch.empty(B, F, dtype=torch.bfloat16, device=dev) for _ in range(2)]
         db = torch.empty(B, H, dtype=torch.bfloat16, device=dev)
@@ -377,6 +385,7 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
                 torch.matmul(h[li], bfw[li]["down"].t(), out=db)
 
         us_b = time_graph([bf16_calls], reps, reps, torch)[0]
+        log(f"stack B={B} bf16 torch.matmul: {us_b / 1e3:.3f} ms/token")
         # gate and up as one matrix: 64 calls per token
         gu = [torch.empty(B, 2 * F, dtype=torch.float32, device=dev) for _ in range(n)]
 
@@ -397,6 +406,7 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
             worst_gu = max(worst_gu, products.rel_error_floored(got, ref))
             del wcat
         us_f = time_graph([lambda: [fused_calls(li) for li in range(n)]], reps, reps, torch)[0]
+        log(f"stack B={B} gate+up as one matrix: {us_f / 1e3:.3f} ms/token")
 
         # the same 96 products over the direct-palette form (GEMV at batch 1,
         # matrix-core GEMM above), on the inputs of the eager token
@@ -428,11 +438,74 @@ def stack_run(uw, workloads, torch, dev, steps, warmup):
                 got = res[:, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
                 worst_p = max(worst_p, products.rel_error_floored(got, ref))
         us_p = time_graph([lambda: [palette_calls(li) for li in range(n)]], reps, reps, torch)[0]
+        log(f"stack B={B} palette form: {us_p / 1e3:.3f} ms/token")
+
+        # decode-ahead: down_l+1 is decompressed on the side stream while
+        # down_l's product (from its slot) and gate_l+1 / up_l+1 run.  Graph
+        # replay with the side stream on every compute unit; the split of the
+        # compute units (side stream limited to 64 of them) is timed from eager
+        # launches at batch 32, where the kernels, not the host, set the pace
+        ahead = {}
+        for cus in ((0, 64) if B > 1 else (0,)):
+            sched = uw.DecodeAhead(slot_bytes=2 * H * F, n_slots=2, decode_cus=cus)
+            do = [torch.empty(B, H, dtype=torch.float32, device=dev) for _ in range(n)]
+
+            def ahead_calls(sched=sched, do=do):
+                slot = sched.prefetch(layers[0]["down"])
+                for li in range(n):
+                    m = layers[li]
+                    uw.uw_gemm_fused(m["gate"].handle, xs[li], g[li], uw.UW_VARIANT_AUTO, ws)
+                    uw.uw_gemm_fused(m["up"].handle, xs[li], u[li], uw.UW_VARIANT_AUTO, ws)
+                    nxt = sched.prefetch(layers[li + 1]["down"]) if li + 1 < n else None
+                    sched.gemm(slot, m["down"], h[li], do[li])
+                    slot = nxt
+
+            ahead_calls()
+            torch.cuda.synchronize()
+            worst_a = 0.0
+            for li in range(n):
+                rows = rng.choice(H, size=64, replace=False)
+                wb = bfw[li]["down"][torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+                ref = products.gemm_f64(wb, h[li].float().cpu().numpy())
+                got = do[li][:, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+                worst_a = max(worst_a, products.rel_error_floored(got, ref))
+            rec = {"parity_max_rel_err_sampled_down": worst_a}
+            if cus == 0:
+                rec["matrix_ms_per_token"] = round(time_graph([ahead_calls], reps, reps, torch)[0] / 1e3, 4)
+            if B > 1:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                for _ in range(3):
+                    ahead_calls()
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    ahead_calls()
+                e1.record()
+                torch.cuda.synchronize()
+                rec["eager_matrix_ms_per_token"] = round(e0.elapsed_time(e1) / reps, 4)
+            ahead[f"decode_cus_{sched.decode_cus}"] = rec
+            log(f"stack B={B} decode-ahead cus={sched.decode_cus}: {rec}")
+            sched.close()
+            del do
+        if B > 1:
+            # the fused schedule timed the same eager way, for the comparison
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for _ in range(3):
+                [matrix_calls(li) for li in range(n)]
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                [matrix_calls(li) for li in range(n)]
+            e1.record()
+            torch.cuda.synchronize()
+            ahead["fused_eager_matrix_ms_per_token"] = round(e0.elapsed_time(e1) / reps, 4)
+            log(f"stack B={B} fused eager: {ahead['fused_eager_matrix_ms_per_token']} ms/token")
         out[f"b{B}"] = {"matrix_ms_per_token": round(us_m / 1e3, 4), "elementwise_ms_per_token": round(us_e / 1e3, 4),
                         "gate_up_fused_matrix_ms_per_token": round(us_f / 1e3, 4),
                         "gate_up_fused_parity_max_rel_err_sampled": worst_gu,
                         "palette_matrix_ms_per_token": round(us_p / 1e3, 4),
                         "palette_parity_max_rel_err_sampled": worst_p,
+                        "decode_ahead": ahead,
                         "bf16_matmul_ms_per_token": round(us_b / 1e3, 4),
                         "speedup_vs_bf16": round(us_b / us_m, 4),
                         "effective_weight_GBs": round(out["bf16_bytes"] / (us_m * 1e-6) / 1e9, 1),
@@ -461,7 +534,8 @@ def main():
         print(json.dumps({"gemm": gemm_sweep(uw, workloads, torch, dev, 48)}), flush=True)
         return
     if args.stack:
-        print(json.dumps({"stack": stack_run(uw, workloads, torch, dev, 960, 960)}), flush=True)
+        print(json.dumps({"stack": stack_run(uw, workloads, torch, dev, 96 * args.stack_reps, 96 * args.stack_reps,
+                                             args.stack_layers)}), flush=True)
         return
     name = args.workload
     rows, cols = workloads.SHAPES[name]

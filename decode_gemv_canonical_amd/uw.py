@@ -104,6 +104,11 @@ def _load() -> ctypes.CDLL:
         "uw_palette_transcode_size": (SZ, [P]),
         "uw_palette_transcode": (I, [P, P, SZ, P]),
         "uw_palette_create_transcoded": (I, [P, P, ctypes.POINTER(P)]),
+        "uw_sched_create": (I, [P, SZ, I, I, ctypes.POINTER(P)]),
+        "uw_sched_destroy": (None, [P]),
+        "uw_sched_decode_cus": (I, [P]),
+        "uw_sched_prefetch": (I, [P, P, P, ctypes.POINTER(I)]),
+        "uw_sched_gemm": (I, [P, I, P, I64, I64, I, P, I64, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -521,6 +526,65 @@ def uw_palette_decompress(handle: int, d_out, ld_out: int | None = None, stream=
     if ld_out != d_out.stride(0):
         raise ValueError("ld_out must be the output's row stride")
     _check(_lib.uw_palette_decompress(handle, d_out.data_ptr(), ld_out, _stream(stream)), "uw_palette_decompress")
+
+
+def uw_sched_create(d_slots, slot_bytes: int, n_slots: int, decode_cus: int = 0) -> int:
+    if not d_slots.is_cuda or not d_slots.is_contiguous() or d_slots.numel() * d_slots.element_size() < slot_bytes * n_slots:
+        raise ValueError("d_slots must be a contiguous CUDA buffer of n_slots * slot_bytes bytes")
+    h = ctypes.c_void_p()
+    _check(_lib.uw_sched_create(d_slots.data_ptr(), slot_bytes, n_slots, decode_cus, ctypes.byref(h)), "uw_sched_create")
+    _register(h.value, 0, 0, d_slots.device.index)
+    return h.value
+
+
+def uw_sched_destroy(handle: int) -> None:
+    _handles.pop(handle, None)
+    _lib.uw_sched_destroy(handle)
+
+
+def uw_sched_prefetch(sched: int, handle: int, stream=None) -> int:
+    _shape(handle)
+    slot = ctypes.c_int(-1)
+    _check(_lib.uw_sched_prefetch(sched, handle, _stream(stream), ctypes.byref(slot)), "uw_sched_prefetch")
+    return slot.value
+
+
+def uw_sched_gemm(sched: int, slot: int, handle: int, X, Y, stream=None) -> None:
+    """Y = X W^T from the slot uw_sched_prefetch filled with `handle`'s matrix
+    (the handle is only used to check the operands' shapes)."""
+    batch = _gemm_operands(handle, X, Y)
+    _check(_lib.uw_sched_gemm(sched, slot, X.data_ptr(), batch, X.stride(0), _dtype_code(X), Y.data_ptr(), Y.stride(0),
+                              _dtype_code(Y), _stream(stream)), "uw_sched_gemm")
+
+
+class DecodeAhead:
+    """A decode-ahead scheduler with its slots (uw_sched_*): prefetch(m)
+    starts decompressing m on the side stream, gemm(slot, m, X, Y) multiplies
+    from the slot on the caller's stream."""
+
+    def __init__(self, slot_bytes: int, n_slots: int = 2, decode_cus: int = 0, device: str = "cuda"):
+        import torch
+        self.slot_bytes = (slot_bytes + 255) // 256 * 256
+        self.d_slots = torch.empty(self.slot_bytes * n_slots, dtype=torch.uint8, device=device)
+        self.handle = uw_sched_create(self.d_slots, self.slot_bytes, n_slots, decode_cus)
+        self.decode_cus = _lib.uw_sched_decode_cus(self.handle)
+
+    def prefetch(self, m: "CompressedMatrix", stream=None) -> int:
+        return uw_sched_prefetch(self.handle, m.handle, stream)
+
+    def gemm(self, slot: int, m: "CompressedMatrix", X, Y, stream=None) -> None:
+        uw_sched_gemm(self.handle, slot, m.handle, X, Y, stream)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            uw_sched_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # -- convenience owner of a device blob + handle -----------------------------

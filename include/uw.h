@@ -357,7 +357,7 @@ int uw_bf16_gemm_shape_count(void);
 
 /*
  * uw_read_probe (device) - streaming read of `bytes` bytes (multiple of 16,
- * 16-byte aligned) that writes one checksum word per workgroup into d_sink
+ * 16-byte aligned) that writes one checksum word per wave into d_sink
  * (uw_read_probe_sink_size bytes): the fastest sustainable read rate the
  * fused kernels are measured against (the Apple-silicon page's section on
  * the limits of further optimisation measures kernels against the fastest
@@ -497,6 +497,60 @@ int uw_palette_create_transcoded(const uw_matrix* m, const void* d_blob, uw_pale
  * Errors: UW_ERR_INVALID (null m, shapes differ).
  */
 int uw_matrix_attach_palette(uw_matrix* m, const uw_palette* p);
+
+/*
+ * Decode-ahead scheduling (the paragraph on "hard" and "easy" layers, the
+ * figure caption on decoding in separate streams during initial load,
+ * attention and easy MLPs, and the paragraph on splitting the compute units
+ * between decode and matmul): a "hard" matrix is decompressed on a side
+ * stream into one of a ring of slots while the caller's stream runs other
+ * work, and its product is then a plain bf16 product from the slot.
+ */
+typedef struct uw_sched uw_sched;
+
+/*
+ * uw_sched_create (host) - a scheduler with n_slots (1..64) decode slots of
+ * slot_bytes each at d_slots (caller-owned device memory, 256-byte aligned,
+ * slot_bytes a multiple of 256 and at least rows*cols*2 of any matrix it will
+ * hold) and a side stream on the current device.  decode_cus = 0 lets the
+ * side stream use every compute unit; k > 0 limits it to k of them, the same
+ * share on every XCD (hipExtStreamCreateWithCUMask).  Creates the stream and
+ * events; allocates no device memory.
+ * Errors: UW_ERR_INVALID, UW_ERR_HIP.
+ */
+int uw_sched_create(void* d_slots, size_t slot_bytes, int n_slots, int decode_cus, uw_sched** out);
+
+/* Waits for the side stream and releases the scheduler (NULL is ignored). */
+void uw_sched_destroy(uw_sched* s);
+
+/* Compute units the side stream may use (0 = all); -1 for NULL. */
+int uw_sched_decode_cus(const uw_sched* s);
+
+/*
+ * uw_sched_prefetch (host, enqueues device work) - decompress m into a free
+ * slot on the side stream, starting once `stream` (the caller's) has reached
+ * this point; *slot receives the slot.  Work the caller enqueues on `stream`
+ * after this call overlaps the decode.
+ * A scheduler with a compute-unit mask (decode_cus > 0) works on streams
+ * that are not being captured into a graph; under capture use decode_cus = 0.
+ * A scheduler is used from one host thread at a time.
+ * Errors: UW_ERR_INVALID, UW_ERR_NOSPACE (no free slot: every slot holds a
+ *         matrix whose uw_sched_gemm has not been called; or the matrix does
+ *         not fit a slot), UW_ERR_UNSUPPORTED (a masked scheduler under graph
+ *         capture), UW_ERR_HIP.
+ */
+int uw_sched_prefetch(uw_sched* s, const uw_matrix* m, void* stream, int* slot);
+
+/*
+ * uw_sched_gemm (host, enqueues device work) - Y = X W^T on `stream` from
+ * the slot filled by uw_sched_prefetch, after its decode (uw_bf16_gemm's
+ * kernels; operands as for uw_gemm_fused).  Frees the slot for the next
+ * prefetch, which will wait for this product through the caller's stream.
+ * Errors: UW_ERR_INVALID (no prefetched matrix in the slot, bad operands),
+ *         UW_ERR_UNSUPPORTED, UW_ERR_HIP.
+ */
+int uw_sched_gemm(uw_sched* s, int slot, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y, int64_t ldy,
+                  int yt, void* stream);
 
 #ifdef __cplusplus
 }
