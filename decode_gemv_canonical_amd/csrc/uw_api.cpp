@@ -81,7 +81,7 @@ bool knob_valid(int variant, int knob) {
     case UW_VARIANT_FUSED: return knob == 0 || knob == 2 || knob == 4;
     case UW_VARIANT_FUSED_MFMA: return knob == 0 || (knob >= 8 && knob <= 16);
     case UW_VARIANT_DECOMPRESS_GEMM: {
-      const int shape = knob & 15, ks = knob >> 4;
+      const int shape = knob & 31, ks = knob >> 5;
       return knob >= 0 && shape < mfma_gemm_shape_count() && (ks == 0 || ks == 1 || ks == 2 || ks == 4 || ks == 8);
     }
     case UW_VARIANT_PALETTE: return knob == 0;
@@ -113,7 +113,7 @@ bool runnable(const uw_matrix* m, int variant, int knob, const CallShape& c, std
         return false;
       }
       if (!bf16_gemm_supported(m->h.cols, batch, c.xt, why)) return false;
-      if ((knob & 15) && (c.xt != UW_BF16 || batch <= 8 || !aligned(c.X, 16) || c.ldx % 8)) {
+      if ((knob & 31) && (c.xt != UW_BF16 || batch <= 8 || !aligned(c.X, 16) || c.ldx % 8)) {
         if (why) *why = "a matrix-core GEMM shape needs batch > 8 and bf16 X, 16-byte aligned, ldx a multiple of 8";
         return false;
       }
@@ -477,8 +477,8 @@ int run_variant(const uw_matrix* m, int variant, int knob, const void* d_X, int6
       // decompress into the workspace, then the bf16 product
       uint16_t* W = static_cast<uint16_t*>(d_ws);
       if (int rc = launch_decompress(m, W, m->h.cols, stream)) return rc;
-      return launch_bf16_gemm(W, m->h.rows, m->h.cols, m->h.cols, d_X, batch, ldx, xt, d_Y, ldy, yt, stream, knob & 15,
-                              knob >> 4);
+      return launch_bf16_gemm(W, m->h.rows, m->h.cols, m->h.cols, d_X, batch, ldx, xt, d_Y, ldy, yt, stream, knob & 31,
+                              knob >> 5);
     }
   }
 }
@@ -628,11 +628,12 @@ int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* 
   if (batch <= 8) {
     cands.push_back({UW_VARIANT_DECOMPRESS_GEMM, 0});
   } else {
-    const std::vector<int> shapes = batch <= 16   ? std::vector<int>{1, 2}
-                                    : batch <= 32 ? std::vector<int>{3, 4, 8}
-                                    : batch <= 64 ? std::vector<int>{5, 4, 6}
-                                                  : std::vector<int>{6, 7, 9, 5};
-    for (int sh : shapes) cands.push_back({UW_VARIANT_DECOMPRESS_GEMM, sh});
+    // GEMM shape + 32 * waves splitting k (0 = the kernel's own pick)
+    const std::vector<int> knobs = batch <= 16   ? std::vector<int>{1 + 32 * 4, 2, 15}
+                                   : batch <= 32 ? std::vector<int>{4 + 32 * 4, 8, 15}
+                                   : batch <= 64 ? std::vector<int>{4 + 32 * 4, 6, 15}
+                                                 : std::vector<int>{16, 15, 14};
+    for (int k : knobs) cands.push_back({UW_VARIANT_DECOMPRESS_GEMM, k});
   }
   cands.push_back({UW_VARIANT_PALETTE, 0});
   const CallShape c{X, batch, int64_t(m->h.cols), UW_BF16, d_ws, need_ws};

@@ -110,14 +110,26 @@ __global__ __launch_bounds__(256) void bf16_gemv_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Streaming read: every byte read once with 16-byte loads, xor-folded into
-// one word per workgroup so the loads cannot be removed.  The launch shape is
-// the fastest of a sweep over workgroup sizes (256..1024 threads), grids (1 to
-// 16 workgroups per compute unit) and loads in flight per thread (1..8), for
-// 80 MiB and 1 GiB reads rotated over cold buffers: 1024 threads, 16
-// workgroups per compute unit, one load per thread per pass (14.2 us for
-// 80 MiB, 166 us for 1 GiB; a grid-stride loop over the whole buffer keeps
-// every wave's next address in the same DRAM pages as its neighbours').
+// Streaming read: every byte read once with 16-byte loads, xor-folded so the
+// loads cannot be removed.  The launch shape comes from a sweep over
+// workgroup sizes (256..1024 threads), grids (1 to 16 workgroups per compute
+// unit) and loads in flight per thread (1..8), for 80 MiB and 1 GiB reads
+// rotated over cold buffers: 1024 threads, 16 workgroups per compute unit,
+// a grid-stride loop, 13.6-14.3 us for 80 MiB.  The closing fold is four DPP
+// steps inside each row of 16 lanes and one store per row: the grid runs in 8
+// rounds of resident workgroups and each round waits for its slowest wave's
+// closing instructions, which with a 6-step LDS shuffle cost 4 us in all.
+__device__ __forceinline__ uint32_t xor_dpp(uint32_t v, int ctrl_id) {
+  int r;
+  switch (ctrl_id) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+    case 1: r = __builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+    case 2: r = __builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: r = __builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return v ^ uint32_t(r);
+}
+
 __global__ __launch_bounds__(1024) void read_probe_kernel(const uint4* __restrict__ src, int64_t n16,
                                                           uint32_t* __restrict__ sink) {
   uint32_t x = 0;
@@ -126,21 +138,18 @@ __global__ __launch_bounds__(1024) void read_probe_kernel(const uint4* __restric
     const uint4 a = src[i];
     x ^= a.x ^ a.y ^ a.z ^ a.w;
   }
-  // wave xor, then one word per workgroup
-  for (int off = 32; off > 0; off >>= 1) x ^= uint32_t(__shfl_xor(int(x), off));
-  __shared__ uint32_t red[16];
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t s = 0;
-    for (int t = 0; t < int(blockDim.x / kWave); ++t) s ^= red[t];
-    sink[blockIdx.x] = s;
-  }
+  // every lane of a row of 16 ends with the row's xor
+  x = xor_dpp(x, 0);
+  x = xor_dpp(x, 1);
+  x = xor_dpp(x, 2);
+  x = xor_dpp(x, 3);
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (threadIdx.x % 16 == 0) sink[t / 16] = x;
 }
 
 constexpr int kProbeThreads = 1024;
 constexpr int kProbeBlocksPerCu = 16;
-constexpr int kProbeMaxBlocks = 16 * 256;  // the sink holds one word per workgroup
+constexpr int kProbeMaxBlocks = 16 * 256;
 
 // Plain-mode matrices: a strided copy of the stored bf16 bits.
 __global__ void copy_plain_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
@@ -237,7 +246,7 @@ int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
   return UW_OK;
 }
 
-size_t read_probe_sink_bytes() { return size_t(kProbeMaxBlocks) * 4; }
+size_t read_probe_sink_bytes() { return size_t(kProbeMaxBlocks) * (kProbeThreads / 16) * 4; }  // a word per row of 16 lanes
 
 int launch_read_probe(const void* src, size_t bytes, void* sink, void* stream) {
   int dev = 0, cus = 256;

@@ -281,6 +281,148 @@ int run_xlds_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, co
   return hip_check(hipGetLastError(), "bf16_mfma_xlds_kernel launch");
 }
 
+// The large-batch form with a deeper pipeline: both operands of a k-block go
+// straight from global memory into LDS (buffer_load ... lds, no registers),
+// into a ring of NS stages, so NS - 1 k-blocks are in flight while the
+// matrix cores work on the oldest.  A workgroup of 4 waves holds 64 weight
+// rows (16 per wave) and 16 TB batch rows; per k-block each wave moves its 16
+// weight rows (4 KB, 4 loads) and a quarter of the activation tile (TB
+// loads).  A 16-byte chunk c of staged row r sits at chunk c ^ (r % 16) of
+// its 256-byte row, so the 16 rows an operand read touches hit 16 different
+// bank groups.  Needs cols to be a multiple of 128 (no partial k-block to
+// zero).
+constexpr int kStages = 3;
+
+// 16 bytes per lane from the buffer resource at byte voff into LDS at m0 +
+// 16 * lane (all lanes active).
+__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t m0) {
+  asm volatile(
+      "s_nop 4\n"
+      "s_mov_b32 m0, %[m]\n"
+      "s_nop 0\n"
+      "buffer_load_dwordx4 %[v], %[r], 0 offen lds"
+      :
+      : [m] "s"(m0), [v] "v"(voff), [r] "s"(r)
+      : "memory", "m0");
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), int16_t(0),
+                                           int(bytes > 0x7FFFFFFFull ? 0x7FFFFFFFull : bytes), 0x00020000);
+}
+
+template <int RB, int TB, bool YBF16>
+__global__ __launch_bounds__(256) void bf16_mfma_stage_kernel(const uint16_t* __restrict__ W, int64_t rows, int64_t cols,
+                                                              int64_t ldw, const uint16_t* __restrict__ X, int64_t ldx,
+                                                              int64_t batch, void* __restrict__ Y, int64_t ldy,
+                                                              int n_groups, int ny) {
+  constexpr uint32_t kW = uint32_t(RB) * 64 * 256;  // weight part of a stage: 64 RB rows x 256 B
+  constexpr uint32_t kX = uint32_t(TB) * 16 * 256;  // activation part: 16 TB rows x 256 B
+  constexpr uint32_t kStage = kW + kX;
+  const int L = blockIdx.x;
+  const int grp = (L / (kXcds * ny)) * kXcds + L % kXcds;
+  const int y = (L / kXcds) % ny;
+  if (grp >= n_groups) return;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int r = lane % 16, q = lane / 16;
+  const int64_t row0 = int64_t(grp) * 64 * RB + int64_t(wave) * 16 * RB, b0 = int64_t(y) * 16 * TB;
+  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(W, uint64_t(rows - 1) * uint64_t(ldw) * 2 + uint64_t(cols) * 2);
+  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(X, uint64_t(batch - 1) * uint64_t(ldx) * 2 + uint64_t(cols) * 2);
+  // the lane's part of a load: 4 staged rows of 256 B per load, lane l puts
+  // 16 bytes at 16 l, i.e. row 4 g + l / 16, stored chunk l % 16, which holds
+  // source chunk (l % 16) ^ (row % 16)
+  const int lrow = lane / 16, lchunk = lane % 16;
+  uint32_t wvo[4 * RB], xvo[TB];  // byte offsets at k = 0
+#pragma unroll
+  for (int g = 0; g < 4 * RB; ++g) {
+    const int srow = 4 * g + lrow;  // this wave's rows 16 RB w .. 16 RB (w + 1) - 1
+    const int64_t n = std::min<int64_t>(row0 + srow, rows - 1);
+    wvo[g] = uint32_t((n * ldw + 8 * (lchunk ^ (srow % 16))) * 2);
+  }
+#pragma unroll
+  for (int u = 0; u < TB; ++u) {
+    const int srow = 4 * (u * 4 + wave) + lrow;  // staged activation row
+    const int64_t b = std::min<int64_t>(b0 + srow, batch - 1);
+    xvo[u] = uint32_t((b * ldx + 8 * (lchunk ^ (srow % 16))) * 2);
+  }
+  const uint32_t wdst = uint32_t(wave) * 16 * RB * 256;  // this wave's weight rows in a stage
+  auto issue = [&](int64_t kb, int st) {
+    const uint32_t kbytes = uint32_t(kb) * 256;
+    const uint32_t base = uint32_t(st) * kStage;
+#pragma unroll
+    for (int g = 0; g < 4 * RB; ++g) stage_load(rw, wvo[g] + kbytes, base + wdst + uint32_t(g) * 1024);
+#pragma unroll
+    for (int u = 0; u < TB; ++u) stage_load(rx, xvo[u] + kbytes, base + kW + uint32_t(u * 4 + wave) * 1024);
+  };
+  floatx4 acc[RB][TB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t nkb = cols / 128;
+  // operand reads: row r of weight block i / of activation tile t, source
+  // chunk 4 q + s at stored chunk (4 q + s) ^ r
+  const uint32_t arow = wdst + uint32_t(r) * 256, xrow = kW + uint32_t(r) * 256;
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < nkb) issue(i, i);
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    const int st = int(kb % kStages);
+    // this wave's loads of block kb have landed once only the younger
+    // blocks' (up to kStages - 2 of them, 4 RB + TB loads each) may be pending
+    if (kb + kStages - 2 < nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * (4 * RB + TB)) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // every wave's loads of block kb have landed; block kb - 1 is no longer read
+    if (kb + kStages - 1 < nkb) issue(kb + kStages - 1, int((kb + kStages - 1) % kStages));
+    const uint32_t base = uint32_t(st) * kStage;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t ch = uint32_t(((4 * q + s) ^ r) * 16);
+      uint4 a[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) a[i] = ld128(base + arow + uint32_t(i) * 16 * 256 + ch);
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const uint4 b = ld128(base + xrow + uint32_t(t) * 16 * 256 + ch);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) acc[i][t] = mfma16(a[i], b, acc[i][t]);
+      }
+    }
+  }
+  // lane (r, q) holds rows 4 q .. 4 q + 3 of weight block i for batch row r of tile t
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const int64_t b = b0 + 16 * t + r;
+      const int64_t n = row0 + 16 * i + 4 * q;
+      if (b >= batch) continue;
+      const float vals[4] = {acc[i][t].x, acc[i][t].y, acc[i][t].z, acc[i][t].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e < rows) {
+          if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + n + e] = f32_to_bf16(vals[e]);
+          else static_cast<float*>(Y)[b * ldy + n + e] = vals[e];
+        }
+      }
+    }
+}
+
+template <int RB, int TB>
+int run_stage_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
+                   int64_t ldx, void* Y, int64_t ldy, int yt, void* stream) {
+  const int n_groups = int((rows + 64 * RB - 1) / (64 * RB));
+  const int ny = int((batch + 16 * TB - 1) / (16 * TB));
+  const int64_t grid = int64_t((n_groups + kXcds - 1) / kXcds) * kXcds * ny;
+  const size_t lds = size_t(kStages) * (size_t(RB) * 64 * 256 + size_t(TB) * 16 * 256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto kern = yt == UW_BF16 ? bf16_mfma_stage_kernel<RB, TB, true> : bf16_mfma_stage_kernel<RB, TB, false>;
+  allow_full_lds(kern);
+  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(256), lds, s, W, rows, cols, ldw, X, ldx, batch, Y, ldy, n_groups,
+                     ny);
+  return hip_check(hipGetLastError(), "bf16_mfma_stage_kernel launch");
+}
+
 template <int RB, int TB, bool PIPE>
 int run_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
                   int64_t ldx, void* Y, int64_t ldy, int yt, int ks, void* stream) {
@@ -303,7 +445,9 @@ int run_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, co
 // Shapes 1..9: operands straight from global memory, RB x 16 weight rows and
 // TB x 16 batch rows per workgroup of KS waves splitting k.  Shapes 10..13:
 // the activations staged in LDS, 4 waves of RB x 16 weight rows each (ks
-// does not apply).
+// does not apply).  Shapes 14..16: both operands staged through a ring of
+// LDS stages by direct loads (cols a multiple of 128 and each operand under
+// 2 GiB; else the LDS-activation kernel of the same tile runs).
 struct MfmaShape {
   int rb, tb, pipe, xlds;
 };
@@ -311,10 +455,18 @@ constexpr MfmaShape kMfmaShapes[] = {
     {0, 0, 0, 0},  // heuristic
     {1, 1, 1, 0}, {2, 1, 1, 0}, {1, 2, 1, 0}, {2, 2, 1, 0}, {1, 4, 1, 0}, {2, 4, 0, 0}, {4, 4, 0, 0}, {4, 2, 0, 0},
     {2, 4, 1, 0}, {1, 4, 1, 1}, {2, 4, 1, 1}, {2, 2, 1, 1}, {1, 8, 1, 1},
+    {1, 8, 1, 2}, {1, 4, 1, 2}, {2, 4, 1, 2},  // 14..16: both operands staged in LDS, kStages deep (cols % 128 == 0)
 };
 constexpr int kMfmaShapeCount = int(sizeof(kMfmaShapes) / sizeof(kMfmaShapes[0]));
 
 int mfma_gemm_shape_count() { return kMfmaShapeCount; }
+
+// The LDS-stage kernel addresses W and X with 32-bit buffer offsets and
+// loads whole 128-column blocks.
+static bool stage_ok(int64_t rows, int64_t cols, int64_t ldw, int64_t batch, int64_t ldx) {
+  const uint64_t lim = uint64_t(1) << 31;
+  return cols % 128 == 0 && uint64_t(rows) * uint64_t(ldw) * 2 < lim && uint64_t(batch) * uint64_t(ldx) * 2 < lim;
+}
 
 // The waves of a launch and the k-blocks each wave takes: KS (waves per
 // workgroup, 1..8) is the smallest that gives about 4096 waves, while every
@@ -332,17 +484,22 @@ int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
                      int64_t ldx, void* Y, int64_t ldy, int yt, int shape, int ks, void* stream) {
   if (shape <= 0 || shape >= kMfmaShapeCount) {
     // heuristic, from a sweep of every shape and ks on the MLP shapes and
-    // 8192^2 (8 rotated copies of W): up to 16 batch rows 32 weight rows per
-    // workgroup in 2 k-halves; up to 32, 64 x 32 in 4 k-quarters; up to 64,
-    // 64 x 64 in 4; above, the activations staged in LDS, 64 x 128
-    if (batch <= 16) {
-      shape = 2;
-      if (ks <= 0) ks = 2;
-    } else if (batch <= 32) {
-      shape = 8;
+    // 8192^2 (8 rotated copies of W).  With at least 128 workgroups, both
+    // operands staged in LDS: 64 weight rows per workgroup and 64 batch rows
+    // (128 weight rows above 64 batch rows when that still gives 192); with
+    // fewer weight rows (down_proj's 4096 at 16 to 64 batch rows), operands
+    // straight from global memory with 4 waves splitting k
+    const int64_t tiles64 = (batch + 63) / 64;
+    const bool stage = stage_ok(rows, cols, ldw, batch, ldx);
+    if (batch <= 64 && stage && (rows + 63) / 64 * tiles64 >= 128) {
+      shape = 15;
+    } else if (batch > 64 && stage) {
+      shape = (rows + 127) / 128 * tiles64 >= 192 ? 16 : 15;
+    } else if (batch <= 16) {
+      shape = 1;
       if (ks <= 0) ks = 4;
     } else if (batch <= 64) {
-      shape = 7;
+      shape = 4;
       if (ks <= 0) ks = 4;
     } else {
       shape = 13;
@@ -366,6 +523,15 @@ int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
     case 10: return run_xlds_gemm<1, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
     case 11: return run_xlds_gemm<2, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
     case 12: return run_xlds_gemm<2, 2>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+    case 14:
+      if (stage_ok(rows, cols, ldw, batch, ldx)) return run_stage_gemm<1, 8>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+      return run_xlds_gemm<1, 8>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+    case 15:
+      if (stage_ok(rows, cols, ldw, batch, ldx)) return run_stage_gemm<1, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+      return run_xlds_gemm<1, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+    case 16:
+      if (stage_ok(rows, cols, ldw, batch, ldx)) return run_stage_gemm<2, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+      return run_xlds_gemm<2, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
     default: return run_xlds_gemm<1, 8>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
   }
 }

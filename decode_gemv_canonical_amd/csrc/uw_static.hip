@@ -62,7 +62,7 @@ int static_decompress_gemm(const uw_matrix* m, const void* X, int64_t batch, int
                            int yt, int knob, void* stream) {
   const DevMatrix& d = m->dev;
   if (m->h.plain())  // the blob holds the bf16 weights: no scratch needed
-    return launch_bf16_gemm(d.plain, d.rows, d.cols, d.cols, X, batch, ldx, xt, Y, ldy, yt, stream, knob & 15, knob >> 4);
+    return launch_bf16_gemm(d.plain, d.rows, d.cols, d.cols, X, batch, ldx, xt, Y, ldy, yt, stream, knob & 31, knob >> 5);
   const int64_t band = static_band_units(m);
   if (band < 1)
     return fail(UW_ERR_UNSUPPORTED, "uw_gemm_fused_static: one work unit of this matrix (" +
@@ -80,8 +80,8 @@ int static_decompress_gemm(const uw_matrix* m, const void* X, int64_t batch, int
     const int i0 = int(u0 * ipu), i1 = int(std::min<int64_t>(n_items, u1 * ipu));
     if (int rc = launch_decompress_items(m, W, d.cols, i0, i1, r0, stream)) return rc;
     void* Yb = static_cast<char*>(Y) + size_t(r0) * ysz;
-    if (int rc = launch_bf16_gemm(W, r1 - r0, d.cols, d.cols, X, batch, ldx, xt, Yb, ldy, yt, stream, knob & 15,
-                                  knob >> 4))
+    if (int rc = launch_bf16_gemm(W, r1 - r0, d.cols, d.cols, X, batch, ldx, xt, Yb, ldy, yt, stream, knob & 31,
+                                  knob >> 5))
       return rc;
   }
   return UW_OK;

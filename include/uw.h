@@ -115,7 +115,7 @@ typedef struct {
  *   UW_VARIANT_FUSED            ring depth, tile steps in flight per wave: 2 or 4;
  *   UW_VARIANT_FUSED_MFMA       waves per workgroup (decoded rows per slice): 8..16;
  *   UW_VARIANT_DECOMPRESS_GEMM  matrix-core GEMM shape (1..uw_bf16_gemm_shape_count()-1)
- *                               + 16 * waves splitting k (1, 2, 4 or 8; 0 = auto);
+ *                               + 32 * waves splitting k (1, 2, 4 or 8; 0 = auto);
  *   UW_VARIANT_PALETTE          unused. */
 typedef struct {
   int64_t batch;
@@ -357,7 +357,7 @@ int uw_bf16_gemm_shape_count(void);
 
 /*
  * uw_read_probe (device) - streaming read of `bytes` bytes (multiple of 16,
- * 16-byte aligned) that writes one checksum word per wave into d_sink
+ * 16-byte aligned) that writes one checksum word per 16 threads into d_sink
  * (uw_read_probe_sink_size bytes): the fastest sustainable read rate the
  * fused kernels are measured against (the Apple-silicon page's section on
  * the limits of further optimisation measures kernels against the fastest

@@ -345,6 +345,17 @@ def test_bf16_gemm_every_shape_ragged():
                 torch.cuda.synchronize()
                 check_f32(Y[:, :rows], ref, f"bf16 gemm shape={shape} ks={ks} b={batch}")
                 assert torch.isnan(Y[:, rows:]).all(), "wrote past the rows"
+    # cols a multiple of 128: the LDS-stage kernels (shapes 14, 15) run too
+    w2, _ = matrix("small", 100, 1024, 25)
+    W2 = torch.from_numpy(w2.view(np.int16)).to(DEV).view(torch.bfloat16)
+    for batch in (9, 100, 200):
+        X = workloads.activations(1024, batch, seed=540 + batch, dtype=torch.bfloat16)
+        ref = products.gemm_f64(w2, X.float().numpy())
+        for shape in range(1, uw.uw_bf16_gemm_shape_count()):
+            Y = torch.full((batch, 100), float("nan"), device=DEV)
+            uw.uw_bf16_gemm_shaped(W2, X.to(DEV), Y, shape, 0)
+            torch.cuda.synchronize()
+            check_f32(Y, ref, f"bf16 gemm 100x1024 shape={shape} b={batch}")
     # unaligned X (odd element offset): the VALU passes take it
     X = workloads.activations(cols + 1, 12, seed=530, dtype=torch.bfloat16).to(DEV)[:, 1:]
     Y = torch.empty(12, rows, device=DEV)
@@ -428,7 +439,7 @@ def test_every_knob_matches_the_oracle():
         knobs += [(uw.UW_VARIANT_FUSED_MFMA, k) for k in (0, 8, 12, 16)]
         knobs += [(uw.UW_VARIANT_DECOMPRESS_GEMM, 0)]
         if batch > 8:
-            knobs += [(uw.UW_VARIANT_DECOMPRESS_GEMM, sh + 16 * ks)
+            knobs += [(uw.UW_VARIANT_DECOMPRESS_GEMM, sh + 32 * ks)
                       for sh in range(1, uw.uw_bf16_gemm_shape_count()) for ks in (0, 1, 4)]
         for v, k in knobs:
             Y = torch.full((batch, 96), float("nan"), device=DEV)
@@ -444,13 +455,13 @@ def test_every_knob_matches_the_oracle():
 def test_plan_save_load_round_trip():
     wb, m = matrix("gate", 64, 4096, 34)
     uw.uw_set_plan(m.handle, 4, uw.UW_VARIANT_FUSED_MFMA, time_us=12.5, knob=12)
-    uw.uw_set_plan(m.handle, 64, uw.UW_VARIANT_DECOMPRESS_GEMM, time_us=40.0, knob=5 + 16 * 4)
+    uw.uw_set_plan(m.handle, 64, uw.UW_VARIANT_DECOMPRESS_GEMM, time_us=40.0, knob=5 + 32 * 4)
     text = m.save_plans()
     import json
     doc = json.loads(text)
     assert doc["format"] == "uw-plan-1" and doc["rows"] == 64 and doc["cols"] == 4096
     assert [(p["batch"], p["variant"], p["knob"]) for p in doc["plans"]] == \
-        [(4, "fused_mfma", 12), (64, "decompress_gemm", 69)]
+        [(4, "fused_mfma", 12), (64, "decompress_gemm", 133)]
     fresh = uw.CompressedMatrix.from_weights(workloads.weights("gate", rows=64, cols=4096, seed=34), device="cuda:0")
     fresh.load_plans(text)
     for b in (4, 64):
