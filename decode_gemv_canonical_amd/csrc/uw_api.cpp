@@ -78,7 +78,10 @@ struct CallShape {
 
 bool knob_valid(int variant, int knob) {
   switch (variant) {
-    case UW_VARIANT_FUSED: return knob == 0 || knob == 2 || knob == 4;
+    case UW_VARIANT_FUSED: {
+      const int rs = knob & 7, wpw = knob >> 3;
+      return knob >= 0 && (rs == 0 || rs == 2 || rs == 4) && wpw <= 16;
+    }
     case UW_VARIANT_FUSED_MFMA: return knob == 0 || (knob >= 8 && knob <= 16);
     case UW_VARIANT_DECOMPRESS_GEMM: {
       const int shape = knob & 31, ks = knob >> 5;
@@ -95,7 +98,7 @@ bool runnable(const uw_matrix* m, int variant, int knob, const CallShape& c, std
     case UW_VARIANT_FUSED:
       if (!fused_supported(m, c.xt, why)) return false;
       if (m->h.plain() && !bf16_gemm_supported(m->h.cols, batch, c.xt, why)) return false;
-      if (knob && !m->h.plain() && !m->dev.flat) {
+      if ((knob & 7) && !m->h.plain() && !m->dev.flat) {
         if (why) *why = "the ring-depth knob needs the flat walk (G and cols/64 multiples of 16)";
         return false;
       }

@@ -1590,8 +1590,12 @@ int flat_ring_depth(int64_t units, size_t fixed, int slot_bytes, size_t extra, i
   return pick_waves(units, fixed, ring_bytes(kRS, slot_bytes) + extra, max_waves) >= need ? kRS : kRSLow;
 }
 
+// knob: ring depth (0 = auto, 2 or 4) + 8 * waves per workgroup (0 = one
+// workgroup per compute unit with enough waves for one round; else that many
+// waves, so that smaller workgroups can share a compute unit).
 template <int NBP, bool XF32, bool PAIR, bool YBF16>
-int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, void* stream, int rs_knob) {
+int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, int64_t ldy, void* stream, int knob) {
+  const int rs_knob = knob & 7, wpw_knob = knob >> 3;
   DevMatrix d = m->dev;  // a copy: split rows may be turned off for this launch
   const size_t fixed = tables_bytes() + x_bytes(d, NBP, XF32);
   const int max_waves = fused_max_threads(NBP, XF32, d.flat) / kWave;
@@ -1605,13 +1609,16 @@ int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, i
   const int items = d.flat ? d.n_items : d.n_units;
   const size_t extra = d.split ? 4 * NBP : 0;
   int rs = d.flat ? flat_ring_depth(items, fixed, d.slot_bytes, extra, max_waves) : kRS;
+  if (d.flat && wpw_knob) rs = kRSLow;  // several workgroups per compute unit: the short ring
   if (d.flat && rs_knob) rs = rs_knob == 4 ? kRS : kRSLow;
   if (d.split && fixed + (ring_bytes(rs, d.slot_bytes) + extra) * d.unit_blocks > size_t(kLdsLimit)) rs = kRSLow;
   const size_t per_wave = ring_bytes(rs, d.slot_bytes) + extra;
   if (fixed + per_wave * (d.split ? d.unit_blocks : 1) > size_t(kLdsLimit))
     return fail(UW_ERR_UNSUPPORTED, "fused product: x does not fit on chip");
-  int waves = pick_waves(items, fixed, per_wave, max_waves);
+  int waves = wpw_knob ? std::min(wpw_knob, max_waves) : pick_waves(items, fixed, per_wave, max_waves);
   if (d.split) waves = std::max(1, waves / d.unit_blocks) * d.unit_blocks;
+  if (fixed + per_wave * waves > size_t(kLdsLimit))
+    return fail(UW_ERR_UNSUPPORTED, "fused product: this many waves per workgroup do not fit in LDS");
   const size_t lds = fixed + per_wave * waves;
   const int grid = int(std::max<int64_t>(1, (items + waves - 1) / waves));
   auto kern = d.flat ? (rs == kRS ? (d.nq == 2 ? fused_product_kernel<NBP, XF32, PAIR, YBF16, 2, true, kRS>

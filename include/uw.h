@@ -112,7 +112,9 @@ typedef struct {
 
 /* A plan: how uw_gemm_fused runs one batch size under UW_VARIANT_AUTO.
  * knob is variant-specific (0 = the library's own choice):
- *   UW_VARIANT_FUSED            ring depth, tile steps in flight per wave: 2 or 4;
+ *   UW_VARIANT_FUSED            ring depth, tile steps in flight per wave (2 or 4; 0 = auto)
+ *                               + 8 * waves per workgroup (1..16; 0 = one workgroup per
+ *                               compute unit, sized to start every work unit at once);
  *   UW_VARIANT_FUSED_MFMA       waves per workgroup (decoded rows per slice): 8..16;
  *   UW_VARIANT_DECOMPRESS_GEMM  matrix-core GEMM shape (1..uw_bf16_gemm_shape_count()-1)
  *                               + 32 * waves splitting k (1, 2, 4 or 8; 0 = auto);

@@ -435,7 +435,7 @@ def test_every_knob_matches_the_oracle():
         ref = products.gemm_f64(wb, X.float().numpy())
         X = X.to(DEV)
         ws = m.workspace(batch)
-        knobs = [(uw.UW_VARIANT_FUSED, k) for k in (0, 2, 4) if batch <= 8]
+        knobs = [(uw.UW_VARIANT_FUSED, k) for k in (0, 2, 4, 2 + 8 * 8, 4 + 8 * 4) if batch <= 8]
         knobs += [(uw.UW_VARIANT_FUSED_MFMA, k) for k in (0, 8, 12, 16)]
         knobs += [(uw.UW_VARIANT_DECOMPRESS_GEMM, 0)]
         if batch > 8:
