@@ -116,8 +116,9 @@ bool runnable(const uw_matrix* m, int variant, int knob, const CallShape& c, std
         return false;
       }
       if (!bf16_gemm_supported(m->h.cols, batch, c.xt, why)) return false;
-      if ((knob & 31) && (c.xt != UW_BF16 || batch <= 8 || !aligned(c.X, 16) || c.ldx % 8)) {
-        if (why) *why = "a matrix-core GEMM shape needs batch > 8 and bf16 X, 16-byte aligned, ldx a multiple of 8";
+      if ((knob & 31) && !bf16_gemm_on_mfma(c.X, batch, m->h.cols, c.ldx, c.xt)) {
+        if (why)
+          *why = "a matrix-core GEMM shape needs bf16 X, 16-byte aligned, ldx a multiple of 8, and batch > 1 or cols > 8192";
         return false;
       }
       return true;
@@ -628,8 +629,10 @@ int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* 
     }
   }
   for (int nw : {0, 8, 12, 16}) cands.push_back({UW_VARIANT_FUSED_MFMA, nw});
-  if (batch <= 8) {
+  if (batch == 1) {
     cands.push_back({UW_VARIANT_DECOMPRESS_GEMM, 0});
+  } else if (batch <= 8) {
+    for (int k : {0, 2 + 32 * 2, 1 + 32 * 4}) cands.push_back({UW_VARIANT_DECOMPRESS_GEMM, k});
   } else {
     // GEMM shape + 32 * waves splitting k (0 = the kernel's own pick)
     const std::vector<int> knobs = batch <= 16   ? std::vector<int>{1 + 32 * 4, 2, 15}

@@ -202,18 +202,23 @@ int launch_copy_plain(const uint16_t* src, int64_t rows, int64_t cols, uint16_t*
   return hip_check(hipGetLastError(), "copy_plain_kernel launch");
 }
 
-// Batches above this, with bf16 activations that are 16-byte aligned and a
-// row stride that is a multiple of 8, go to the matrix-core kernel
-// (uw_gemm.hip); up to it the GEMV-style kernel, which reads W once per chunk
-// of up to 8 activation rows, is used (measured crossover on the MLP shapes).
-constexpr int64_t kValuMaxBatch = 8;
+// bf16 activations that are 16-byte aligned with a row stride that is a
+// multiple of 8 go to the matrix-core kernel (uw_gemm.hip), except a single
+// activation row of at most kValuMaxCols columns, which the GEMV-style kernel
+// (x in LDS, one wave per row) reads faster.  Measured on the MLP shapes with
+// 8 rotated copies of W: gate 14336x4096 batch 1 24.5 us on the vector ALU
+// against 27.8 on the matrix cores; batch 2..8 27-28 us on the matrix cores
+// against 31-144 us for the vector kernel's passes over W; down 4096x14336
+// batch 1 29.4 against 32.6 us.
+constexpr int64_t kValuMaxCols = 8192;
 
-static bool mfma_gemm_ok(const void* X, int64_t batch, int64_t ldx, int xt) {
-  return xt == UW_BF16 && batch > kValuMaxBatch && reinterpret_cast<uintptr_t>(X) % 16 == 0 && ldx % 8 == 0;
+bool bf16_gemm_on_mfma(const void* X, int64_t batch, int64_t cols, int64_t ldx, int xt) {
+  return xt == UW_BF16 && (batch > 1 || cols > kValuMaxCols) && reinterpret_cast<uintptr_t>(X) % 16 == 0 &&
+         ldx % 8 == 0;
 }
 
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why) {
-  if (xt == UW_BF16 && batch > kValuMaxBatch) return true;  // matrix cores, or VALU passes when X is unaligned
+  if (xt == UW_BF16 && (batch > 1 || cols > kValuMaxCols)) return true;  // matrix cores, or VALU passes when X is unaligned
   const size_t per = xt == UW_F32 ? size_t(cols) * 4 : size_t(cols) * 2;
   if (per > size_t(kLdsLimit)) {
     if (why) *why = "x of this width does not fit in LDS";
@@ -224,7 +229,7 @@ bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why) 
 
 int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X, int64_t batch,
                      int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream, int shape, int ks) {
-  if (mfma_gemm_ok(X, batch, ldx, xt))
+  if (bf16_gemm_on_mfma(X, batch, cols, ldx, xt))
     return launch_mfma_gemm(W, rows, cols, ldw, static_cast<const uint16_t*>(X), batch, ldx, Y, ldy, yt, shape, ks,
                             stream);
   if (xt == UW_BF16 && size_t(cols) * 2 > size_t(kLdsLimit))

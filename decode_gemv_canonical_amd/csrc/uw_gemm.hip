@@ -488,16 +488,22 @@ int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
     // operands staged in LDS: 64 weight rows per workgroup and 64 batch rows
     // (128 weight rows above 64 batch rows when that still gives 192); with
     // fewer weight rows (down_proj's 4096 at 16 to 64 batch rows), operands
-    // straight from global memory with 4 waves splitting k
+    // straight from global memory with 4 waves splitting k.  Up to 8 batch
+    // rows (one tile of 16, partly padding): 32 weight rows per workgroup and
+    // 2 waves splitting k where that gives 384 workgroups (gate), else 16
+    // rows and 4 or 8 waves (down)
     const int64_t tiles64 = (batch + 63) / 64;
     const bool stage = stage_ok(rows, cols, ldw, batch, ldx);
-    if (batch <= 64 && stage && (rows + 63) / 64 * tiles64 >= 128) {
+    if (batch > 8 && batch <= 64 && stage && (rows + 63) / 64 * tiles64 >= 128) {
       shape = 15;
     } else if (batch > 64 && stage) {
       shape = (rows + 127) / 128 * tiles64 >= 192 ? 16 : 15;
+    } else if (batch <= 8 && (rows + 31) / 32 >= 384) {
+      shape = 2;  // 32 weight rows per workgroup, one batch tile (gate at batch 1..8)
+      if (ks <= 0) ks = 2;
     } else if (batch <= 16) {
       shape = 1;
-      if (ks <= 0) ks = 4;
+      if (ks <= 0) ks = batch <= 2 ? 8 : 4;
     } else if (batch <= 64) {
       shape = 4;
       if (ks <= 0) ks = 4;

@@ -159,11 +159,14 @@ int launch_copy_plain(const uint16_t* src, int64_t rows, int64_t cols, uint16_t*
 int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
                      int64_t ldx, void* Y, int64_t ldy, int yt, int shape, int ks, void* stream);
 int mfma_gemm_shape_count();
-// Any bf16 product: VALU up to batch 8 (or fp32 / unaligned X), else the matrix cores.
+// Any bf16 product: the matrix cores for aligned bf16 X (bf16_gemm_on_mfma),
+// else the vector ALU in passes of up to 8 rows.  A shape or ks applies only
+// on the matrix cores.
 int launch_bf16_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const void* X,
                      int64_t batch, int64_t ldx, int xt, void* Y, int64_t ldy, int yt, void* stream, int shape = 0,
                      int ks = 0);
 bool bf16_gemm_supported(int64_t cols, int64_t batch, int xt, std::string* why);
+bool bf16_gemm_on_mfma(const void* X, int64_t batch, int64_t cols, int64_t ldx, int xt);
 // Cache eviction of the autotuner: read `bytes` (multiple of 16) at src.
 int launch_read_probe(const void* src, size_t bytes, void* sink, void* stream);
 // The allocation-free entry point's scratch (uw_static.hip): its size, the

@@ -335,10 +335,13 @@ int uw_plan_load(uw_matrix* m, const char* json);
  * multiply of the "full decode" pipeline and the uncompressed comparator.
  *   d_W  device, rows x cols bf16, row stride ldw >= cols (multiple of 8),
  *        16-byte aligned.  Other arguments as for uw_gemm_fused.
- * Up to batch 8 (or with fp32 X, or bf16 X that is not 16-byte aligned with
- * ldx a multiple of 8) a GEMV-style kernel on the vector ALU runs, in passes
- * of up to 8 rows; above batch 8 the matrix-core kernel
- * (v_mfma_f32_16x16x32_bf16, operands straight from global memory).
+ * bf16 X that is 16-byte aligned with ldx a multiple of 8 runs on the
+ * matrix cores (v_mfma_f32_16x16x32_bf16; operands straight from global
+ * memory, or staged through LDS), except a single row of X with cols <= 8192,
+ * and fp32 or unaligned X, which a GEMV-style kernel on the vector ALU takes
+ * in passes of up to 8 rows.
+ * 16, 32, 64 or 128 weight rows and 16 to 128 batch rows per workgroup; the
+ * shapes 14..16 also need cols a multiple of 128 and each operand under 2 GiB.
  * Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED, UW_ERR_HIP.
  */
 int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, const void* d_X,
@@ -347,8 +350,9 @@ int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, c
 /*
  * uw_bf16_gemm_shaped (device) - uw_bf16_gemm on the matrix cores with a
  * given shape: shape in [1, uw_bf16_gemm_shape_count()) picks the weight rows
- * (16, 32 or 64) and batch rows (16, 32 or 64) a workgroup holds, ks (1, 2,
- * 4, 8; 0 = auto) the waves that split k.  Needs bf16 X, 16-byte aligned,
+ * (16 to 128) and batch rows (16 to 128) a workgroup holds and whether the
+ * operands are staged in LDS, ks (1, 2, 4, 8; 0 = auto) the waves that split
+ * k (for the shapes that read straight from global memory).  Needs bf16 X, 16-byte aligned,
  * ldx a multiple of 8, and batch >= 1.
  * Errors: UW_ERR_INVALID, UW_ERR_HIP.
  */

@@ -311,8 +311,9 @@ def test_gemm_batch_zero_is_noop():
 def test_bf16_gemm_uncompressed():
     wb, _ = matrix("gate", 96, 4096, 21)
     W = torch.from_numpy(wb.view(np.int16)).to(DEV).view(torch.bfloat16)
-    # up to batch 8 the GEMV-style kernel, above it the matrix-core kernel
-    for batch in (1, 3, 8, 9, 40, 256):
+    # batch 1 (x fits the GEMV-style kernel's LDS) and fp32 X on the vector
+    # ALU, every other aligned bf16 batch on the matrix cores
+    for batch in (1, 2, 3, 8, 9, 40, 256):
         X = workloads.activations(4096, batch, seed=500 + batch, dtype=torch.bfloat16)
         ref = products.gemm_f64(wb, X.float().numpy())
         Y = torch.empty(batch, 96, device=DEV)
@@ -324,6 +325,19 @@ def test_bf16_gemm_uncompressed():
         uw.uw_bf16_gemm(W, X.to(DEV), Yb)
         torch.cuda.synchronize()
         check_bf16(Yb, ref, f"bf16 gemm b={batch} bf16 out", wb.shape[1])
+        if batch <= 8:
+            Yf = torch.empty(batch, 96, device=DEV)
+            uw.uw_bf16_gemm(W, X.float().to(DEV), Yf)  # fp32 X: the vector kernel's passes
+            torch.cuda.synchronize()
+            check_f32(Yf, products.gemm_f64(wb, X.float().numpy()), f"bf16 gemm b={batch} fp32 x")
+    # one row of X wider than 8192 columns: the matrix cores
+    wd, _ = matrix("down", 48, 14336, 22)
+    Wd = torch.from_numpy(wd.view(np.int16)).to(DEV).view(torch.bfloat16)
+    X = workloads.activations(14336, 1, seed=509, dtype=torch.bfloat16)
+    Y = torch.empty(1, 48, device=DEV)
+    uw.uw_bf16_gemm(Wd, X.to(DEV), Y)
+    torch.cuda.synchronize()
+    check_f32(Y, products.gemm_f64(wd, X.float().numpy()), "bf16 gemm b=1 cols=14336")
 
 
 def test_bf16_gemm_every_shape_ragged():
@@ -334,7 +348,7 @@ def test_bf16_gemm_every_shape_ragged():
     wb = np.ascontiguousarray(wfull[:, :cols])
     Wp = torch.from_numpy(wfull.view(np.int16)).to(DEV).view(torch.bfloat16)
     W = Wp[:, :cols]
-    for batch in (9, 37, 100):
+    for batch in (1, 5, 9, 37, 100):
         X = workloads.activations(cols, batch, seed=520 + batch, dtype=torch.bfloat16)
         ref = products.gemm_f64(wb, X.float().numpy())
         Xd = X.to(DEV)
