@@ -130,3 +130,28 @@ def test_gate_b32_autotune_with_palette_and_plan_file(tmp_path):
     assert torch.equal(Y, Y2)
     for h in (fp, fresh, p, m):
         h.close()
+
+
+def test_auto_without_a_plan_takes_the_attached_palette_copy():
+    # with no plan stored, AUTO's heuristic runs the palette product for 3..64
+    # batch rows once a palette copy is attached (bit-identical to the explicit
+    # variant), and the fused matrix-core product when none is
+    w = workloads.weights("gate", rows=256, cols=4096, seed=91)
+    wb = w.numpy().view(np.uint16)
+    m = uw.CompressedMatrix.from_weights(w, device="cuda:0")
+    for batch in (3, 16, 64):
+        X = workloads.activations(4096, batch, seed=700 + batch, dtype=torch.bfloat16).to(DEV)
+        ref = products.gemm_f64(wb, X.float().cpu().numpy())
+        y_mfma = m.gemm(X, variant=uw.UW_VARIANT_FUSED_MFMA)
+        y_auto0 = m.gemm(X, variant=uw.UW_VARIANT_AUTO)
+        p = m.transcode_palette()
+        y_pal = m.gemm(X, variant=uw.UW_VARIANT_PALETTE)
+        y_auto = m.gemm(X, variant=uw.UW_VARIANT_AUTO)
+        torch.cuda.synchronize()
+        _say(f"auto heuristic b={batch}")
+        assert torch.equal(y_auto0, y_mfma)
+        assert torch.equal(y_auto, y_pal)
+        check_f32(y_auto, ref, f"auto with palette b={batch}")
+        m.attach_palette(None)
+        p.close()
+    m.close()
