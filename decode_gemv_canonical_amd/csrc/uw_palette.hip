@@ -243,22 +243,38 @@ struct BlockIn {
   bool raw;
 };
 
-__device__ inline void load_block(const DevPalette& p, int64_t row, int64_t k0, BlockIn& in) {
+// The lane's 32 weights of row `row` from column k0: sign+mantissa and index
+// bytes, and the group's raw exponent bytes when it is raw.  The raw flag and
+// the raw slot come from the workgroup's copy of its rows' tile flags and
+// prefix counts in LDS (entry (row_local, tile) = (16-bit flags, prefix)), so
+// no load waits on another; a lane whose group is not raw loads 32 bytes from
+// the start of the sm section instead (FIXED), so every call issues the same
+// loads and the wait for one register set can leave the other's in flight;
+// else only raw lanes load them.
+template <bool FIXED>
+__device__ inline void load_block(const DevPalette& p, const uint2* rflags, int row_local, int64_t row, int64_t k0,
+                                  BlockIn& in) {
   const int64_t i0 = row * p.tpr * 1024 + k0;  // weight index of the lane's first weight
   const uint4* s = reinterpret_cast<const uint4*>(p.sm + i0);
   in.sm[0] = s[0];
   in.sm[1] = s[1];
   in.idx = *reinterpret_cast<const uint4*>(p.idx + i0 / 2);
-  const int64_t g = i0 >> 6, tile = i0 >> 10;
-  const uint32_t w = p.flags[g >> 5];
-  in.raw = (w >> (g & 31)) & 1u;
-  in.rawe[0] = in.rawe[1] = uint4{0u, 0u, 0u, 0u};
-  if (in.raw) {
-    const uint32_t mask16 = (w >> (16 * (tile & 1))) & 0xFFFFu;
-    const uint32_t slot = p.prefix[tile] + uint32_t(__builtin_popcount(mask16 & ((1u << (g & 15)) - 1u)));
-    const uint4* r = reinterpret_cast<const uint4*>(p.raw + int64_t(slot) * 64 + (i0 & 63));
+  const uint2 f = rflags[row_local * int(p.tpr) + int(k0 >> 10)];
+  const int gi = int((k0 >> 6) & 15);
+  in.raw = (f.x >> gi) & 1u;
+  const uint32_t slot = f.y + uint32_t(__builtin_popcount(f.x & ((1u << gi) - 1u)));
+  if (FIXED) {
+    const uint4* r = in.raw ? reinterpret_cast<const uint4*>(p.raw + int64_t(slot) * 64 + (i0 & 63))
+                            : reinterpret_cast<const uint4*>(p.sm);
     in.rawe[0] = r[0];
     in.rawe[1] = r[1];
+  } else {
+    in.rawe[0] = in.rawe[1] = uint4{0u, 0u, 0u, 0u};
+    if (in.raw) {
+      const uint4* r = reinterpret_cast<const uint4*>(p.raw + int64_t(slot) * 64 + (i0 & 63));
+      in.rawe[0] = r[0];
+      in.rawe[1] = r[1];
+    }
   }
 }
 
@@ -279,44 +295,68 @@ __device__ inline uint4 block_step_weights(const BlockIn& in, const uint32_t* ta
   return uint4{W[0], W[1], W[2], W[3]};
 }
 
-// The loads of one 128-column block: the activations of every batch tile and
-// the lane's 32 weights of row `row`.
-template <int TB>
-__device__ __forceinline__ void load_mfma_block(const DevPalette& p, const uint16_t* const (&xr)[TB], int64_t row,
-                                                int64_t kb, int j, uint4 (&xv)[TB][4], BlockIn& in) {
+// The loads of one 128-column block: the activations of every batch tile
+// (once, shared by the RB row blocks) and the lane's 32 weights of each of
+// the RB rows.
+template <int TB, int RB>
+struct BlockSet {
+  uint4 xv[TB][4];
+  BlockIn in[RB];
+};
+
+template <int TB, int RB, bool FIXED>
+__device__ __forceinline__ void load_set(const DevPalette& p, const uint2* rflags, const uint16_t* const (&xr)[TB],
+                                         const int64_t (&row)[RB], int r, int64_t kb, int j, BlockSet<TB, RB>& b) {
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const uint4* xs = reinterpret_cast<const uint4*>(xr[tb] + kb * 128);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xv[tb][s] = xs[s];
+    for (int s = 0; s < 4; ++s) b.xv[tb][s] = xs[s];
   }
-  load_block(p, row, kb * 128 + 32 * j, in);
+#pragma unroll
+  for (int i = 0; i < RB; ++i) load_block<FIXED>(p, rflags, 16 * i + r, row[i], kb * 128 + 32 * j, b.in[i]);
 }
 
-// The four k-steps of a block for every batch tile.
-template <int TB>
-__device__ __forceinline__ void mfma_block(const BlockIn& in, const uint4 (&xv)[TB][4], const uint32_t* table,
-                                           floatx4 (&acc)[TB]) {
+// The four k-steps of a block for every row block and batch tile.
+template <int TB, int RB>
+__device__ __forceinline__ void mfma_set(const BlockSet<TB, RB>& b, const uint32_t* table, floatx4 (&acc)[RB][TB]) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint4 a = block_step_weights(in, table, s);
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, xv[tb][s]), acc[tb], 0, 0, 0);
-  }
+    for (int s = 0; s < 4; ++s) {
+      const uint4 a = block_step_weights(b.in[i], table, s);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                             __builtin_bit_cast(bf16x8_t, b.xv[tb][s]), acc[i][tb], 0, 0, 0);
+    }
+}
+
+// Two block sets in registers (the next block's loads in flight while this
+// one's products run) when they fit; else one, whose loads are all issued
+// before its products.
+template <int TB, int RB>
+constexpr bool palette_two_sets() {
+  return 2 * (16 * TB + 21 * RB) + 4 * RB * TB <= 200;
 }
 
 template <int TB, int RB, bool YBF16>
 __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const uint16_t* __restrict__ X, int64_t ldx,
                                                            int nb, void* __restrict__ Y, int64_t ldy) {
   __shared__ uint32_t table[256];
-  extern __shared__ float4 red[];  // [waves][TB][64] partial sums of one 16-row block
-  for (int b = threadIdx.x; b < 256; b += blockDim.x) table[b] = (pal_byte(p, b & 15) << 7) | (pal_byte(p, b >> 4) << 23);
-  __syncthreads();
+  extern __shared__ float4 red[];  // [waves][TB][64] partial sums of one 16-row block, then the rows' tile flags
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ks = blockDim.x >> 6;
   const int r = lane & 15, j = lane >> 4;
+  const int tpr = int(p.tpr);
+  uint2* rflags = reinterpret_cast<uint2*>(red + ks * TB * 64);  // [16 RB rows][tpr]: (flags, prefix)
   const int64_t base = int64_t(blockIdx.x) * 16 * RB;  // the workgroup's RB blocks of 16 rows
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) table[b] = (pal_byte(p, b & 15) << 7) | (pal_byte(p, b >> 4) << 23);
+  for (int i = threadIdx.x; i < 16 * RB * tpr; i += blockDim.x) {
+    const int64_t row = std::min<int64_t>(p.rows - 1, base + i / tpr);
+    const int64_t T = row * tpr + i % tpr;
+    rflags[i] = uint2{(p.flags[T >> 1] >> (16 * (T & 1))) & 0xFFFFu, p.prefix[T]};
+  }
+  __syncthreads();
   int64_t row[RB];
 #pragma unroll
   for (int i = 0; i < RB; ++i) row[i] = std::min<int64_t>(p.rows - 1, base + 16 * i + r);  // rows past the end feed unstored outputs
@@ -329,46 +369,23 @@ __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const u
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[i][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int64_t n_blocks = p.tpr * 8;  // 128-column blocks per row
-  if constexpr (RB == 1 && TB <= 2) {
-    // one row block, up to 32 batch rows: two register sets (four batch
-    // tiles would not fit), so the next block's loads are in flight while
-    // this block's products run
-    uint4 xa[TB][4], xb[TB][4];
-    BlockIn wa, wb;
+  if constexpr (palette_two_sets<TB, RB>()) {
+    BlockSet<TB, RB> sa, sb;
     int64_t kb = wave;
-    if (kb < n_blocks) load_mfma_block<TB>(p, xr, row[0], kb, j, xa, wa);
+    if (kb < n_blocks) load_set<TB, RB, true>(p, rflags, xr, row, r, kb, j, sa);
     for (; kb < n_blocks; kb += 2 * ks) {
-      if (kb + ks < n_blocks) load_mfma_block<TB>(p, xr, row[0], kb + ks, j, xb, wb);
-      mfma_block<TB>(wa, xa, table, acc[0]);
+      if (kb + ks < n_blocks) load_set<TB, RB, true>(p, rflags, xr, row, r, kb + ks, j, sb);
+      mfma_set<TB, RB>(sa, table, acc);
       if (kb + ks >= n_blocks) break;
-      if (kb + 2 * ks < n_blocks) load_mfma_block<TB>(p, xr, row[0], kb + 2 * ks, j, xa, wa);
-      mfma_block<TB>(wb, xb, table, acc[0]);
+      if (kb + 2 * ks < n_blocks) load_set<TB, RB, true>(p, rflags, xr, row, r, kb + 2 * ks, j, sa);
+      mfma_set<TB, RB>(sb, table, acc);
     }
   } else {
-  for (int64_t kb = wave; kb < n_blocks; kb += ks) {
-    const int64_t k0 = kb * 128 + 32 * j;
-    // the activations once per block, shared by the RB row blocks
-    uint4 xv[TB][4];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const uint4* xs = reinterpret_cast<const uint4*>(xr[tb] + kb * 128);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xv[tb][s] = xs[s];
+    for (int64_t kb = wave; kb < n_blocks; kb += ks) {
+      BlockSet<TB, RB> sa;
+      load_set<TB, RB, false>(p, rflags, xr, row, r, kb, j, sa);
+      mfma_set<TB, RB>(sa, table, acc);
     }
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      BlockIn in;
-      load_block(p, row[i], k0, in);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 a = block_step_weights(in, table, s);
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-          acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                               __builtin_bit_cast(bf16x8_t, xv[tb][s]), acc[i][tb], 0, 0, 0);
-      }
-    }
-  }
   }
   // the waves' partial sums, one 16-row block at a time
 #pragma unroll
@@ -505,10 +522,18 @@ void palette_mfma_shape(int64_t rows, int* rb, int* ks) {
 template <int TB, int RB>
 int launch_palette_mfma_rb(const DevPalette& p, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt,
                            int ks, hipStream_t s) {
-  const size_t lds = size_t(ks) * TB * 64 * sizeof(float4);
+  const size_t lds = size_t(ks) * TB * 64 * sizeof(float4) + size_t(16) * RB * size_t(p.tpr) * 8;
   const dim3 grid(unsigned((p.rows + 16 * RB - 1) / (16 * RB))), block(64 * ks);
-  if (yt == UW_BF16) hipLaunchKernelGGL((palette_mfma_kernel<TB, RB, true>), grid, block, lds, s, p, X, ldx, nb, Y, ldy);
-  else hipLaunchKernelGGL((palette_mfma_kernel<TB, RB, false>), grid, block, lds, s, p, X, ldx, nb, Y, ldy);
+  // the kernel also holds a 1 KiB static table
+  if (lds + 1024 > size_t(kLdsLimit)) return fail(UW_ERR_UNSUPPORTED, "uw_palette_gemm: too many tiles per row");
+  auto kern = yt == UW_BF16 ? palette_mfma_kernel<TB, RB, true> : palette_mfma_kernel<TB, RB, false>;
+  if (lds > 48 * 1024) {
+    static std::mutex mu;
+    std::lock_guard<std::mutex> lk(mu);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kLdsLimit - 1024);
+  }
+  hipLaunchKernelGGL(kern, grid, block, lds, s, p, X, ldx, nb, Y, ldy);
   return hip_check(hipGetLastError(), "palette_mfma_kernel launch");
 }
 

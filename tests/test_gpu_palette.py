@@ -37,10 +37,24 @@ def _say(msg):
 _cache = {}
 
 
+def wide_exponents(rows, cols, seed):
+    # random sign and mantissa, exponents uniform over 64 values (2^-31 ..
+    # 2^32): every 64-weight group holds exponents outside any palette of 16,
+    # and no product overflows fp32 (random bit patterns would: their fp32
+    # sums can reach Inf where the fp64 reference stays finite)
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint32)
+    e = rng.integers(96, 160, size=(rows, cols), dtype=np.uint32)
+    return ((bits & 0x807F) | (e << 7)).astype(np.uint16)
+
+
 def pmatrix(name, rows=None, cols=None, seed=None):
     key = (name, rows, cols, seed)
     if key not in _cache:
-        wb = workloads.weights(name, rows=rows, cols=cols, seed=seed).numpy().view(np.uint16)
+        if name == "wide_exponents":
+            wb = wide_exponents(rows, cols, seed)
+        else:
+            wb = workloads.weights(name, rows=rows, cols=cols, seed=seed).numpy().view(np.uint16)
         _cache[key] = (wb, uw.PaletteMatrix.from_weights(wb, device="cuda:0"))
     return _cache[key]
 
@@ -123,11 +137,14 @@ def test_palette_argument_errors():
         uw.uw_palette_decompress(m.handle, out, 1028)  # ld not a multiple of 8
 
 
-# Matrix-core product over the palette form: 1, 2 and 4 blocks of 16 rows per
-# workgroup and 4 or 8 waves splitting K (both set by the row count), one to
-# four batch tiles per pass, several passes, ragged batches and row counts,
+# Matrix-core product over the palette form: from 8192 rows and 2 batch rows
+# the LDS-staged kernel (64 rows per workgroup, 1, 2 or 4 batch tiles), else
+# 1, 2 and 4 blocks of 16 rows per workgroup and 4 or 8 waves splitting K
+# (both set by the row count); several passes, ragged batches and row counts,
 # raw groups, every group raw.
 GEMM_CASES = [
+    ("down", 8192, 2048, 43, [2, 33]),          # staged, 8 % raw groups, a partial batch tile
+    ("wide_exponents", 8192, 1024, 44, [5]),   # staged, every group raw (64 exponents, all finite)
     ("gate", None, None, None, [16, 32, 64]),   # 4 row blocks per workgroup, 8 waves split K
     ("down", None, None, None, [4, 64, 100]),  # 1 row block per workgroup, 8 waves; 100 = two passes
     ("gate", 28672, 1024, 31, [3]),            # 4 row blocks per workgroup, 4 waves split K
