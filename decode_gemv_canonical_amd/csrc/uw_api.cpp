@@ -642,8 +642,8 @@ int uw_autotune(uw_matrix* m, int64_t batch, void* d_ws, size_t ws_bytes, void* 
   } else {
     // GEMM shape + 32 * waves splitting k (0 = the kernel's own pick)
     const std::vector<int> knobs = batch <= 16   ? std::vector<int>{1 + 32 * 4, 2, 15}
-                                   : batch <= 32 ? std::vector<int>{4 + 32 * 4, 8, 15}
-                                   : batch <= 64 ? std::vector<int>{4 + 32 * 4, 6, 15}
+                                   : batch <= 32 ? std::vector<int>{4 + 32 * 4, 8, 15, 17, 18}
+                                   : batch <= 64 ? std::vector<int>{4 + 32 * 4, 6, 15, 17, 18}
                                                  : std::vector<int>{16, 15, 14};
     for (int k : knobs) cands.push_back({UW_VARIANT_DECOMPRESS_GEMM, k});
   }

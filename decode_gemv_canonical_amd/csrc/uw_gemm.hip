@@ -290,7 +290,10 @@ int run_xlds_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, co
 // loads).  A 16-byte chunk c of staged row r sits at chunk c ^ (r % 16) of
 // its 256-byte row, so the 16 rows an operand read touches hit 16 different
 // bank groups.  Needs cols to be a multiple of 128 (no partial k-block to
-// zero).
+// zero).  With nsplit = 2 the grid holds two workgroups per tile, each taking
+// half of the k-blocks, and both add their partial sums into an fp32 Y that
+// was zeroed first: 0 + a + b and 0 + b + a are the same float, so the
+// result does not depend on their order.
 constexpr int kStages = 3;
 
 // 16 bytes per lane from the buffer resource at byte voff into LDS at m0 +
@@ -315,11 +318,13 @@ template <int RB, int TB, bool YBF16>
 __global__ __launch_bounds__(256) void bf16_mfma_stage_kernel(const uint16_t* __restrict__ W, int64_t rows, int64_t cols,
                                                               int64_t ldw, const uint16_t* __restrict__ X, int64_t ldx,
                                                               int64_t batch, void* __restrict__ Y, int64_t ldy,
-                                                              int n_groups, int ny) {
+                                                              int n_groups, int ny, int nsplit) {
   constexpr uint32_t kW = uint32_t(RB) * 64 * 256;  // weight part of a stage: 64 RB rows x 256 B
   constexpr uint32_t kX = uint32_t(TB) * 16 * 256;  // activation part: 16 TB rows x 256 B
   constexpr uint32_t kStage = kW + kX;
-  const int L = blockIdx.x;
+  const int per_split = int(gridDim.x) / nsplit;
+  const int split = int(blockIdx.x) / per_split;
+  const int L = int(blockIdx.x) % per_split;
   const int grp = (L / (kXcds * ny)) * kXcds + L % kXcds;
   const int y = (L / kXcds) % ny;
   if (grp >= n_groups) return;
@@ -346,8 +351,11 @@ __global__ __launch_bounds__(256) void bf16_mfma_stage_kernel(const uint16_t* __
     xvo[u] = uint32_t((b * ldx + 8 * (lchunk ^ (srow % 16))) * 2);
   }
   const uint32_t wdst = uint32_t(wave) * 16 * RB * 256;  // this wave's weight rows in a stage
+  // this workgroup's k-blocks [kb0, kb0 + nkb)
+  const int64_t nkb_all = cols / 128, half = (nkb_all + nsplit - 1) / nsplit;
+  const int64_t kb0 = split * half, nkb = std::max<int64_t>(0, std::min(nkb_all, kb0 + half) - kb0);
   auto issue = [&](int64_t kb, int st) {
-    const uint32_t kbytes = uint32_t(kb) * 256;
+    const uint32_t kbytes = uint32_t(kb0 + kb) * 256;
     const uint32_t base = uint32_t(st) * kStage;
 #pragma unroll
     for (int g = 0; g < 4 * RB; ++g) stage_load(rw, wvo[g] + kbytes, base + wdst + uint32_t(g) * 1024);
@@ -359,7 +367,6 @@ __global__ __launch_bounds__(256) void bf16_mfma_stage_kernel(const uint16_t* __
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int t = 0; t < TB; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int64_t nkb = cols / 128;
   // operand reads: row r of weight block i / of activation tile t, source
   // chunk 4 q + s at stored chunk (4 q + s) ^ r
   const uint32_t arow = wdst + uint32_t(r) * 256, xrow = kW + uint32_t(r) * 256;
@@ -402,24 +409,37 @@ __global__ __launch_bounds__(256) void bf16_mfma_stage_kernel(const uint16_t* __
       for (int e = 0; e < 4; ++e) {
         if (n + e < rows) {
           if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + n + e] = f32_to_bf16(vals[e]);
+          else if (nsplit > 1) unsafeAtomicAdd(static_cast<float*>(Y) + b * ldy + n + e, vals[e]);
           else static_cast<float*>(Y)[b * ldy + n + e] = vals[e];
         }
       }
     }
 }
 
+// Y[b][n] = 0 for b < batch, n < rows (fp32), ahead of a split product.
+__global__ void zero_rows_kernel(float* __restrict__ Y, int64_t batch, int64_t rows, int64_t ldy) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < batch * rows; i += int64_t(gridDim.x) * blockDim.x)
+    Y[(i / rows) * ldy + i % rows] = 0.f;
+}
+
 template <int RB, int TB>
 int run_stage_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, const uint16_t* X, int64_t batch,
-                   int64_t ldx, void* Y, int64_t ldy, int yt, void* stream) {
+                   int64_t ldx, void* Y, int64_t ldy, int yt, void* stream, int nsplit = 1) {
   const int n_groups = int((rows + 64 * RB - 1) / (64 * RB));
   const int ny = int((batch + 16 * TB - 1) / (16 * TB));
-  const int64_t grid = int64_t((n_groups + kXcds - 1) / kXcds) * kXcds * ny;
+  if (yt != UW_F32 || cols / 128 < 2 * kStages) nsplit = 1;  // the split adds fp32 partial sums in place
+  if (nsplit > 1) {
+    hipLaunchKernelGGL(zero_rows_kernel, dim3(unsigned(std::min<int64_t>(1024, (batch * rows + 255) / 256))), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<float*>(Y), batch, rows, ldy);
+    if (int rc = hip_check(hipGetLastError(), "zero_rows_kernel launch")) return rc;
+  }
+  const int64_t grid = int64_t((n_groups + kXcds - 1) / kXcds) * kXcds * ny * nsplit;
   const size_t lds = size_t(kStages) * (size_t(RB) * 64 * 256 + size_t(TB) * 16 * 256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto kern = yt == UW_BF16 ? bf16_mfma_stage_kernel<RB, TB, true> : bf16_mfma_stage_kernel<RB, TB, false>;
   allow_full_lds(kern);
   hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(256), lds, s, W, rows, cols, ldw, X, ldx, batch, Y, ldy, n_groups,
-                     ny);
+                     ny, nsplit);
   return hip_check(hipGetLastError(), "bf16_mfma_stage_kernel launch");
 }
 
@@ -447,7 +467,10 @@ int run_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, co
 // the activations staged in LDS, 4 waves of RB x 16 weight rows each (ks
 // does not apply).  Shapes 14..16: both operands staged through a ring of
 // LDS stages by direct loads (cols a multiple of 128 and each operand under
-// 2 GiB; else the LDS-activation kernel of the same tile runs).
+// 2 GiB; else the LDS-activation kernel of the same tile runs).  Shapes 17,
+// 18: the staged kernel with 64 x 64 and 64 x 32 tiles and two workgroups per
+// tile, each taking half of K and adding into Y (fp32 Y; with bf16 Y, or
+// under 6 k-blocks, one workgroup per tile).
 struct MfmaShape {
   int rb, tb, pipe, xlds;
 };
@@ -456,6 +479,7 @@ constexpr MfmaShape kMfmaShapes[] = {
     {1, 1, 1, 0}, {2, 1, 1, 0}, {1, 2, 1, 0}, {2, 2, 1, 0}, {1, 4, 1, 0}, {2, 4, 0, 0}, {4, 4, 0, 0}, {4, 2, 0, 0},
     {2, 4, 1, 0}, {1, 4, 1, 1}, {2, 4, 1, 1}, {2, 2, 1, 1}, {1, 8, 1, 1},
     {1, 8, 1, 2}, {1, 4, 1, 2}, {2, 4, 1, 2},  // 14..16: both operands staged in LDS, kStages deep (cols % 128 == 0)
+    {1, 4, 1, 3}, {1, 2, 1, 3},                // 17, 18: staged, two workgroups per tile splitting K (fp32 Y)
 };
 constexpr int kMfmaShapeCount = int(sizeof(kMfmaShapes) / sizeof(kMfmaShapes[0]));
 
@@ -484,17 +508,26 @@ int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
                      int64_t ldx, void* Y, int64_t ldy, int yt, int shape, int ks, void* stream) {
   if (shape <= 0 || shape >= kMfmaShapeCount) {
     // heuristic, from a sweep of every shape and ks on the MLP shapes and
-    // 8192^2 (8 rotated copies of W).  With at least 128 workgroups, both
-    // operands staged in LDS: 64 weight rows per workgroup and 64 batch rows
-    // (128 weight rows above 64 batch rows when that still gives 192); with
-    // fewer weight rows (down_proj's 4096 at 16 to 64 batch rows), operands
-    // straight from global memory with 4 waves splitting k.  Up to 8 batch
-    // rows (one tile of 16, partly padding): 32 weight rows per workgroup and
-    // 2 waves splitting k where that gives 384 workgroups (gate), else 16
-    // rows and 4 or 8 waves (down)
+    // 8192^2 (8 rotated copies of W).  9..64 batch rows: with at least 192
+    // workgroups of 64 x 64, both operands staged in LDS (gate); with fewer
+    // and more than 16 batch rows with fp32 Y, the staged kernel with two
+    // workgroups per tile splitting K (down_proj 4096 x 14336 at 32 / 64 rows:
+    // 38 / 42 us against 61 / 59; 8192^2: 38 / 45 against 52 / 53); else the
+    // staged kernel from 128 workgroups, below that operands straight from
+    // global memory with 4 waves splitting k.  Above 64 rows: 128 x 64 staged
+    // tiles when that gives 192 workgroups.  Up to 8 batch rows (one tile of
+    // 16, partly padding): 32 weight rows per workgroup and 2 waves splitting
+    // k where that gives 384 workgroups (gate), else 16 rows and 4 or 8 waves
+    // (down)
     const int64_t tiles64 = (batch + 63) / 64;
     const bool stage = stage_ok(rows, cols, ldw, batch, ldx);
-    if (batch > 8 && batch <= 64 && stage && (rows + 63) / 64 * tiles64 >= 128) {
+    const int64_t g64 = (rows + 63) / 64 * tiles64;  // workgroups of 64 x 64 tiles
+    if (batch > 8 && batch <= 64 && stage && g64 >= 192) {
+      shape = 15;
+    } else if (batch > 16 && batch <= 64 && stage && yt == UW_F32 && cols / 128 >= 6) {
+      // few weight rows (down_proj, 8192^2): two workgroups per tile split K
+      shape = g64 >= 96 && batch <= 32 ? 17 : 18;
+    } else if (batch > 8 && batch <= 64 && stage && g64 >= 128) {
       shape = 15;
     } else if (batch > 64 && stage) {
       shape = (rows + 127) / 128 * tiles64 >= 192 ? 16 : 15;
@@ -538,6 +571,14 @@ int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
     case 16:
       if (stage_ok(rows, cols, ldw, batch, ldx)) return run_stage_gemm<2, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
       return run_xlds_gemm<2, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+    case 17:
+      if (stage_ok(rows, cols, ldw, batch, ldx))
+        return run_stage_gemm<1, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream, 2);
+      return run_xlds_gemm<1, 4>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
+    case 18:
+      if (stage_ok(rows, cols, ldw, batch, ldx))
+        return run_stage_gemm<1, 2>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream, 2);
+      return run_xlds_gemm<2, 2>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
     default: return run_xlds_gemm<1, 8>(W, rows, cols, ldw, X, batch, ldx, Y, ldy, yt, stream);
   }
 }

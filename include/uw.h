@@ -342,7 +342,10 @@ int uw_plan_load(uw_matrix* m, const char* json);
  * and fp32 or unaligned X, which a GEMV-style kernel on the vector ALU takes
  * in passes of up to 8 rows.
  * 16, 32, 64 or 128 weight rows and 16 to 128 batch rows per workgroup; the
- * shapes 14..16 also need cols a multiple of 128 and each operand under 2 GiB.
+ * staged shapes 14..18 also need cols a multiple of 128 and each operand
+ * under 2 GiB.  Shapes 17 and 18 (fp32 Y) run two workgroups per tile, each
+ * over half of K, adding into Y after zeroing it; two addends keep the
+ * result independent of their order, so runs are reproducible.
  * Errors: UW_ERR_INVALID, UW_ERR_UNSUPPORTED, UW_ERR_HIP.
  */
 int uw_bf16_gemm(const uint16_t* d_W, int64_t rows, int64_t cols, int64_t ldw, const void* d_X,

@@ -366,10 +366,30 @@ def test_bf16_gemm_every_shape_ragged():
         X = workloads.activations(1024, batch, seed=540 + batch, dtype=torch.bfloat16)
         ref = products.gemm_f64(w2, X.float().numpy())
         for shape in range(1, uw.uw_bf16_gemm_shape_count()):
-            Y = torch.full((batch, 100), float("nan"), device=DEV)
-            uw.uw_bf16_gemm_shaped(W2, X.to(DEV), Y, shape, 0)
+            Y = torch.full((batch, 103), float("nan"), device=DEV)
+            uw.uw_bf16_gemm_shaped(W2, X.to(DEV), Y[:, :100], shape, 0)
             torch.cuda.synchronize()
-            check_f32(Y, ref, f"bf16 gemm 100x1024 shape={shape} b={batch}")
+            check_f32(Y[:, :100], ref, f"bf16 gemm 100x1024 shape={shape} b={batch}")
+            assert torch.isnan(Y[:, 100:]).all(), "wrote past the rows"
+    # the K-split shapes (17, 18): an odd number of k-blocks (9), fp32 and
+    # bf16 Y (bf16 runs one workgroup per tile), the same result twice
+    w3, _ = matrix("small", 200, 1152, 26)
+    W3 = torch.from_numpy(w3.view(np.int16)).to(DEV).view(torch.bfloat16)
+    for batch in (20, 64):
+        X = workloads.activations(1152, batch, seed=560 + batch, dtype=torch.bfloat16).to(DEV)
+        ref = products.gemm_f64(w3, X.float().cpu().numpy())
+        for shape in (17, 18):
+            Y = torch.full((batch, 205), float("nan"), device=DEV)
+            uw.uw_bf16_gemm_shaped(W3, X, Y[:, :200], shape, 0)
+            Y2 = torch.empty(batch, 200, device=DEV)
+            uw.uw_bf16_gemm_shaped(W3, X, Y2, shape, 0)
+            Yb = torch.empty(batch, 200, device=DEV, dtype=torch.bfloat16)
+            uw.uw_bf16_gemm_shaped(W3, X, Yb, shape, 0)
+            torch.cuda.synchronize()
+            check_f32(Y[:, :200], ref, f"bf16 gemm split shape={shape} b={batch}")
+            assert torch.isnan(Y[:, 200:]).all(), "wrote past the rows"
+            assert torch.equal(Y[:, :200], Y2), "split product differs between two runs"
+            check_bf16(Yb, ref, f"bf16 gemm split shape={shape} b={batch} bf16 out", 1152)
     # unaligned X (odd element offset): the VALU passes take it
     X = workloads.activations(cols + 1, 12, seed=530, dtype=torch.bfloat16).to(DEV)[:, 1:]
     Y = torch.empty(12, rows, device=DEV)
