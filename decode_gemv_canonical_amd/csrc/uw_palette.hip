@@ -20,7 +20,7 @@ namespace uw {
 namespace {
 
 constexpr int kPalThreads = 256;  // 4 waves
-constexpr int kPalChunk = 1;      // GEMV: tiles per register set (measured: 1 beats 2 and 4)
+constexpr int kPalChunk = 1;      // GEMV: tiles per register set
 constexpr int kPalDecChunk = 4;   // decompress: tiles whose loads a wave issues together
 
 struct DevPalette {
@@ -54,18 +54,40 @@ struct TileIn {
   uint4 rawe;      // this lane's 16 raw exponents when its group is raw
 };
 
-__device__ inline void load_tile(const DevPalette& p, int64_t T, int lane, TileIn& in) {
-  in.sm = *reinterpret_cast<const uint4*>(p.sm + T * 1024 + 16 * lane);
-  in.idx = *reinterpret_cast<const uint2*>(p.idx + T * 512 + 8 * lane);
-  in.rmask = (scalar_word(p.flags, T >> 1) >> (16 * (T & 1))) & 0xFFFFu;
-  in.rawe = uint4{0u, 0u, 0u, 0u};
-  if (in.rmask) {
-    const int g = lane >> 2;  // the lane's group within the tile
-    if ((in.rmask >> g) & 1u) {
-      const uint32_t slot = scalar_word(p.prefix, T) + uint32_t(__builtin_popcount(in.rmask & ((1u << g) - 1u)));
-      in.rawe = *reinterpret_cast<const uint4*>(p.raw + int64_t(slot) * 64 + 16 * (lane & 3));
-    }
+// Raw flags and first raw slot of the 64 tiles from `base`: lane i holds those
+// of tile base + i (tiles past the wave's last repeat the last).
+struct WaveFlags {
+  uint32_t flags, prefix;
+  int64_t base;
+};
+
+__device__ inline void load_flags(const DevPalette& p, int64_t T, int64_t T1, int lane, WaveFlags& f) {
+  const int64_t t = min(T + lane, T1 - 1);
+  f.flags = (p.flags[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+  f.prefix = p.prefix[t];
+  f.base = T;
+}
+
+// The loads of tile T (wave-uniform; tiles come in increasing order).  Every
+// call issues the same four loads: a lane whose group is not raw, and every
+// lane of a tile without raw groups, reads its own sign+mantissa bytes again
+// in place of raw exponents.  So the compiler's wait before the products of
+// one register set never waits for the loads of the other.
+__device__ inline void load_tile(const DevPalette& p, int64_t T, int64_t T1, int lane, WaveFlags& f, TileIn& in) {
+  if (T - f.base >= 64) {  // once per 64 tiles; the wait here keeps the paths after it alike
+    load_flags(p, T, T1, lane, f);
+    wait_vmcnt<0>();
   }
+  const int k = int(T - f.base);
+  in.rmask = __builtin_amdgcn_readlane(f.flags, k);
+  const uint32_t pre = __builtin_amdgcn_readlane(f.prefix, k);
+  const uint8_t* smp = p.sm + T * 1024 + 16 * lane;
+  in.sm = *reinterpret_cast<const uint4*>(smp);
+  in.idx = *reinterpret_cast<const uint2*>(p.idx + T * 512 + 8 * lane);
+  const int g = lane >> 2;  // the lane's group within the tile
+  const bool raw = (in.rmask >> g) & 1u;
+  const uint32_t slot = pre + uint32_t(__builtin_popcount(in.rmask & ((1u << g) - 1u)));
+  in.rawe = *reinterpret_cast<const uint4*>(raw ? p.raw + int64_t(slot) * 64 + 16 * (lane & 3) : smp);
 }
 
 __device__ inline uint32_t word_of(const uint4& v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; }
@@ -115,48 +137,70 @@ __device__ inline float tile_dot(const TileIn& in, const XTile<XF32>& x, const u
   return in.rmask ? tile_dot_as<XF32, true>(in, x, table, lane, acc) : tile_dot_as<XF32, false>(in, x, table, lane, acc);
 }
 
-// The loads of kPalChunk consecutive tiles of the wave's walk (row-major
-// tile order); tt = column tile of the first, advanced past the last.
+// A wave's tiles T0 .. T1 - 1 are whole rows (tpr tiles each, row-major).
+struct WaveTiles {
+  int64_t T0, T1, r0;
+  int tpr;
+};
+
+// The loads of tiles T .. T + kPalChunk - 1 (those past the wave's last load
+// the last again, so every call issues the same loads).
 template <bool XF32>
-__device__ __forceinline__ void issue_chunk(const DevPalette& p, const void* X, int64_t T, int64_t T1, int64_t& tt,
-                                            int lane, TileIn (&in)[kPalChunk], XTile<XF32> (&xs)[kPalChunk]) {
+__device__ __forceinline__ void issue_set(const DevPalette& p, const void* X, const WaveTiles& w, int64_t T, int lane,
+                                          WaveFlags& f, TileIn (&in)[kPalChunk], XTile<XF32> (&xs)[kPalChunk]) {
 #pragma unroll
   for (int i = 0; i < kPalChunk; ++i) {
-    if (T + i < T1) {
-      load_tile(p, T + i, lane, in[i]);
-      load_x<XF32>(X, tt, lane, xs[i]);
-    }
-    if (++tt == p.tpr) tt = 0;
+    const int64_t Ti = min(T + i, w.T1 - 1);
+    load_tile(p, Ti, w.T1, lane, f, in[i]);
+    load_x<XF32>(X, int(Ti - w.T0) % w.tpr, lane, xs[i]);
   }
 }
 
-// The products of a chunk; a row's sum is reduced and stored at its last tile.
-template <bool XF32, bool YBF16>
-__device__ __forceinline__ void consume_chunk(const DevPalette& p, int64_t T, int64_t T1, int64_t& t, int64_t& row,
-                                              float& acc, int lane, const uint32_t* table,
-                                              const TileIn (&in)[kPalChunk], const XTile<XF32> (&xs)[kPalChunk],
-                                              void* Y) {
+// The products of tiles T .. T + kPalChunk - 1 (T < T1, so the first is
+// always one of the wave's and runs without a branch that would leave its
+// loads possibly pending).  A row's sum is reduced at its last tile and kept
+// in lane (row - r0) of `res`: no store inside the loop (stores count with
+// the loads on this chip and would perturb the waits).
+template <bool XF32>
+__device__ __forceinline__ void consume_set(const WaveTiles& w, int64_t T, float& acc, float& res, int lane,
+                                            const uint32_t* table, const TileIn (&in)[kPalChunk],
+                                            const XTile<XF32> (&xs)[kPalChunk]) {
 #pragma unroll
   for (int i = 0; i < kPalChunk; ++i) {
-    if (T + i < T1) {
+    if (i == 0 || T + i < w.T1) {
+      // the raw exponents count as read on every path, so their load is
+      // waited for here and not, later, by the next load into these registers
+      asm volatile("" ::"v"(in[i].rawe.x), "v"(in[i].rawe.y), "v"(in[i].rawe.z), "v"(in[i].rawe.w));
       acc = tile_dot<XF32>(in[i], xs[i], table, lane, acc);
-      if (++t == p.tpr) {
+      const int rel = int(T + i - w.T0);
+      if (rel % w.tpr == w.tpr - 1) {
         const float s = wave_sum(acc);
-        if (lane == 0) {
-          if (YBF16) static_cast<uint16_t*>(Y)[row] = f32_to_bf16(s);
-          else static_cast<float*>(Y)[row] = s;
-        }
+        res = lane == rel / w.tpr ? s : res;
         acc = 0.f;
-        t = 0;
-        ++row;
       }
     }
   }
 }
 
+// The wave's rows: rows_per_wave consecutive rows (the last wave may have fewer).
+__device__ inline bool wave_tiles(const DevPalette& p, WaveTiles& w) {
+  const int64_t wave = int64_t(blockIdx.x) * (kPalThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r0 = wave * p.rows_per_wave;
+  if (r0 >= p.rows) return false;
+  const int64_t r1 = min(p.rows, r0 + p.rows_per_wave);
+  w.r0 = r0;
+  w.T0 = r0 * p.tpr;
+  w.T1 = r1 * p.tpr;
+  w.tpr = int(p.tpr);
+  return true;
+}
+
 // One wave per rows_per_wave consecutive rows.  The wave walks their tiles in
-// chunks of kPalChunk with two register sets: the loads of the next chunk are
-// in flight while the current one is multiplied.
+// sets of kPalChunk with two register sets: the loads of the next set are in
+// flight while the current one is multiplied.  Every path from the loads of
+// one set to the products of the other issues a fixed number of loads (the
+// next set's, or none after the last), so the compiler's wait before the
+// products leaves the next set's loads in flight.
 template <bool XF32, bool YBF16>
 __global__ __launch_bounds__(kPalThreads) void palette_gemv_kernel(DevPalette p, const void* __restrict__ X,
                                                                    void* __restrict__ Y) {
@@ -164,58 +208,70 @@ __global__ __launch_bounds__(kPalThreads) void palette_gemv_kernel(DevPalette p,
   build_pair_table(p, table);
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int64_t wave = int64_t(blockIdx.x) * (kPalThreads / 64) + (threadIdx.x >> 6);
-  const int64_t r0 = wave * p.rows_per_wave;
-  if (r0 >= p.rows) return;
-  const int64_t r1 = min(p.rows, r0 + p.rows_per_wave);
-  const int64_t T1 = r1 * p.tpr;
-  int64_t row = r0, t = 0, tt = 0;  // t, tt: column tile of the next tile to multiply / to load
-  float acc = 0.f;
+  WaveTiles w;
+  if (!wave_tiles(p, w)) return;
+  WaveFlags f;
+  load_flags(p, w.T0, w.T1, lane, f);
+  wait_vmcnt<0>();
+  float acc = 0.f, res = 0.f;
   TileIn a[kPalChunk], b[kPalChunk];
   XTile<XF32> xa[kPalChunk], xb[kPalChunk];
-  int64_t T = r0 * p.tpr;
-  issue_chunk<XF32>(p, X, T, T1, tt, lane, a, xa);
-  for (; T < T1; T += 2 * kPalChunk) {
-    issue_chunk<XF32>(p, X, T + kPalChunk, T1, tt, lane, b, xb);
-    consume_chunk<XF32, YBF16>(p, T, T1, t, row, acc, lane, table, a, xa, Y);
-    issue_chunk<XF32>(p, X, T + 2 * kPalChunk, T1, tt, lane, a, xa);
-    consume_chunk<XF32, YBF16>(p, T + kPalChunk, T1, t, row, acc, lane, table, b, xb, Y);
+  int64_t T = w.T0;
+  issue_set<XF32>(p, X, w, T, lane, f, a, xa);
+  while (true) {
+    if (T + kPalChunk >= w.T1) {
+      consume_set<XF32>(w, T, acc, res, lane, table, a, xa);
+      break;
+    }
+    issue_set<XF32>(p, X, w, T + kPalChunk, lane, f, b, xb);
+    consume_set<XF32>(w, T, acc, res, lane, table, a, xa);
+    T += kPalChunk;
+    if (T + kPalChunk >= w.T1) {
+      consume_set<XF32>(w, T, acc, res, lane, table, b, xb);
+      break;
+    }
+    issue_set<XF32>(p, X, w, T + kPalChunk, lane, f, a, xa);
+    consume_set<XF32>(w, T, acc, res, lane, table, b, xb);
+    T += kPalChunk;
+  }
+  if (lane < int(w.T1 - w.T0) / w.tpr) {
+    if (YBF16) static_cast<uint16_t*>(Y)[w.r0 + lane] = f32_to_bf16(res);
+    else static_cast<float*>(Y)[w.r0 + lane] = res;
   }
 }
 
 // bf16 weights to out[r * ld + c]: lane l writes its 16 weights as two
-// 16-byte stores.
+// 16-byte stores; a wave issues the loads of kPalDecChunk tiles together.
 __global__ __launch_bounds__(kPalThreads) void palette_decompress_kernel(DevPalette p, uint16_t* __restrict__ out,
                                                                          int64_t ld) {
   __shared__ uint32_t table[256];
   build_pair_table(p, table);
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int64_t wave = int64_t(blockIdx.x) * (kPalThreads / 64) + (threadIdx.x >> 6);
-  const int64_t r0 = wave * p.rows_per_wave;
-  if (r0 >= p.rows) return;
-  const int64_t r1 = min(p.rows, r0 + p.rows_per_wave);
-  for (int64_t row = r0; row < r1; ++row) {
-    for (int64_t t = 0; t < p.tpr; t += kPalDecChunk) {
-      TileIn in[kPalDecChunk];
+  WaveTiles w;
+  if (!wave_tiles(p, w)) return;
+  WaveFlags f;
+  load_flags(p, w.T0, w.T1, lane, f);
+  wait_vmcnt<0>();
+  for (int64_t T = w.T0; T < w.T1; T += kPalDecChunk) {
+    TileIn in[kPalDecChunk];
 #pragma unroll
-      for (int i = 0; i < kPalDecChunk; ++i)
-        if (t + i < p.tpr) load_tile(p, row * p.tpr + t + i, lane, in[i]);
+    for (int i = 0; i < kPalDecChunk; ++i) load_tile(p, min(T + i, w.T1 - 1), w.T1, lane, f, in[i]);
 #pragma unroll
-      for (int i = 0; i < kPalDecChunk; ++i) {
-        if (t + i < p.tpr) {
-          uint32_t w[8];
-          if (in[i].rmask) {
+    for (int i = 0; i < kPalDecChunk; ++i) {
+      if (T + i < w.T1) {
+        uint32_t v[8];
+        if (in[i].rmask) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) w[k] = pair_weights<true>(in[i], table, lane, k);
-          } else {
+          for (int k = 0; k < 8; ++k) v[k] = pair_weights<true>(in[i], table, lane, k);
+        } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) w[k] = pair_weights<false>(in[i], table, lane, k);
-          }
-          uint4* dst = reinterpret_cast<uint4*>(out + row * ld + (t + i) * 1024 + 16 * lane);
-          dst[0] = uint4{w[0], w[1], w[2], w[3]};
-          dst[1] = uint4{w[4], w[5], w[6], w[7]};
+          for (int k = 0; k < 8; ++k) v[k] = pair_weights<false>(in[i], table, lane, k);
         }
+        const int rel = int(T + i - w.T0);
+        uint4* dst = reinterpret_cast<uint4*>(out + (w.r0 + rel / w.tpr) * ld + int64_t(rel % w.tpr) * 1024 + 16 * lane);
+        dst[0] = uint4{v[0], v[1], v[2], v[3]};
+        dst[1] = uint4{v[4], v[5], v[6], v[7]};
       }
     }
   }
@@ -370,15 +426,31 @@ __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const u
     for (int tb = 0; tb < TB; ++tb) acc[i][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int64_t n_blocks = p.tpr * 8;  // 128-column blocks per row
   if constexpr (palette_two_sets<TB, RB>()) {
+    // Every path from the loads of one set to the products of the other
+    // issues a fixed number of loads (the next set's, or none at the last
+    // block), so the compiler's wait before the products leaves the next
+    // set's loads in flight; a load under a condition in between would make
+    // it wait for everything.
     BlockSet<TB, RB> sa, sb;
     int64_t kb = wave;
-    if (kb < n_blocks) load_set<TB, RB, true>(p, rflags, xr, row, r, kb, j, sa);
-    for (; kb < n_blocks; kb += 2 * ks) {
-      if (kb + ks < n_blocks) load_set<TB, RB, true>(p, rflags, xr, row, r, kb + ks, j, sb);
-      mfma_set<TB, RB>(sa, table, acc);
-      if (kb + ks >= n_blocks) break;
-      if (kb + 2 * ks < n_blocks) load_set<TB, RB, true>(p, rflags, xr, row, r, kb + 2 * ks, j, sa);
-      mfma_set<TB, RB>(sb, table, acc);
+    if (kb < n_blocks) {
+      load_set<TB, RB, true>(p, rflags, xr, row, r, kb, j, sa);
+      while (true) {
+        if (kb + ks >= n_blocks) {
+          mfma_set<TB, RB>(sa, table, acc);
+          break;
+        }
+        load_set<TB, RB, true>(p, rflags, xr, row, r, kb + ks, j, sb);
+        mfma_set<TB, RB>(sa, table, acc);
+        kb += ks;
+        if (kb + ks >= n_blocks) {
+          mfma_set<TB, RB>(sb, table, acc);
+          break;
+        }
+        load_set<TB, RB, true>(p, rflags, xr, row, r, kb + ks, j, sa);
+        mfma_set<TB, RB>(sb, table, acc);
+        kb += ks;
+      }
     }
   } else {
     for (int64_t kb = wave; kb < n_blocks; kb += ks) {

@@ -67,6 +67,7 @@ CASES = [
     ("gate", 37, 3072, 21),            # ragged: rows not a multiple of the rows per wave
     ("down", 1, 1024, 22),             # one row
     ("down", 5, 7168, 23),             # a row of 7 tiles (chunks of 4 cross rows)
+    ("down", 3, 67584, 24),            # 66 tiles per row: a wave re-reads its tile flags after 64
 ]
 
 
@@ -137,14 +138,14 @@ def test_palette_argument_errors():
         uw.uw_palette_decompress(m.handle, out, 1028)  # ld not a multiple of 8
 
 
-# Matrix-core product over the palette form: from 8192 rows and 2 batch rows
-# the LDS-staged kernel (64 rows per workgroup, 1, 2 or 4 batch tiles), else
-# 1, 2 and 4 blocks of 16 rows per workgroup and 4 or 8 waves splitting K
-# (both set by the row count); several passes, ragged batches and row counts,
-# raw groups, every group raw.
+# Matrix-core product over the palette form: 1, 2 and 4 blocks of 16 rows
+# per workgroup and 2 to 8 waves splitting K (both set by the row count), one
+# or two register sets (set by the batch tiles and row blocks); several
+# passes, ragged batches and row counts, raw groups, every group raw.
 GEMM_CASES = [
-    ("down", 8192, 2048, 43, [2, 33]),          # staged, 8 % raw groups, a partial batch tile
-    ("wide_exponents", 8192, 1024, 44, [5]),   # staged, every group raw (64 exponents, all finite)
+    ("down", 8192, 2048, 43, [2, 33]),          # 2 row blocks, 8 % raw groups, a partial batch tile
+    ("wide_exponents", 8192, 1024, 44, [5]),   # every group raw (64 exponents, all finite)
+    ("down", 3, 67584, 24, [3, 20]),           # 66 tiles per row
     ("gate", None, None, None, [16, 32, 64]),   # 4 row blocks per workgroup, 8 waves split K
     ("down", None, None, None, [4, 64, 100]),  # 1 row block per workgroup, 8 waves; 100 = two passes
     ("gate", 28672, 1024, 31, [3]),            # 4 row blocks per workgroup, 4 waves split K
