@@ -497,12 +497,14 @@ int heuristic_variant(const uw_matrix* m, const CallShape& c) {
   const bool ws_ok = runnable(m, UW_VARIANT_DECOMPRESS_GEMM, 0, c, nullptr);
   const bool pal_ok = runnable(m, UW_VARIANT_PALETTE, 0, c, nullptr);
   const int64_t batch = c.batch;
-  if (fused_ok && (batch == 1 || (batch == 2 && fused_rows_per_pass(m, batch, c.xt) >= 2))) return UW_VARIANT_FUSED;
-  // an attached direct-palette copy: its matrix-core product up to 64 batch
-  // rows (MLP shapes, 8 cold copies: gate 29-47 us at 3-64 rows against 40-87
-  // for the fused matrix-core product and 56-64 for decompress + GEMM; down
-  // 33-75 against 39-77 and 58-89)
+  // an attached direct-palette copy: its GEMV at one batch row and its
+  // matrix-core product up to 64 (MLP shapes, 8 cold copies: gate 20.4 /
+  // 25.2 us at 1 / 2 rows against 21.2 / 25.3 for the fused vector-ALU
+  // product, 26-45 at 16-64 against 40-87 for the fused matrix-core product
+  // and 56-65 for decompress + GEMM; down 20.5 / 22.3 against 23.8 / 30.9,
+  // 30-70 at 16-64 against 42-77 and 65-76)
   if (pal_ok && batch <= 64) return UW_VARIANT_PALETTE;
+  if (fused_ok && (batch == 1 || (batch == 2 && fused_rows_per_pass(m, batch, c.xt) >= 2))) return UW_VARIANT_FUSED;
   if (mfma_ok && (batch <= 32 || (batch <= 64 && !ws_ok))) return UW_VARIANT_FUSED_MFMA;
   if (ws_ok && (c.xt == UW_BF16 || !fused_ok)) return UW_VARIANT_DECOMPRESS_GEMM;
   if (mfma_ok) return UW_VARIANT_FUSED_MFMA;

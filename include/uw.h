@@ -222,11 +222,12 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
  *   d_Y  device, batch rows of rows elements of yt, row stride ldy >= rows.
  *   variant  a uw_variant; UW_VARIANT_AUTO uses the plan stored for this
  *            batch (uw_autotune, uw_set_plan, uw_plan_load) when that plan's
- *            variant can run this call, else a heuristic (batch 1, and batch
- *            2 when one VALU pass takes both rows: fused on VALU; up to 64
- *            with a direct-palette copy attached: the palette product; up to
- *            32: fused on the matrix cores where supported; above: decompress
- *            + GEMM when d_ws is large enough, else the matrix cores).  An
+ *            variant can run this call, else a heuristic (up to 64 with a
+ *            direct-palette copy attached: the palette product; else batch
+ *            1, and batch 2 when one VALU pass takes both rows: fused on
+ *            VALU; up to 32: fused on the matrix cores where supported;
+ *            above: decompress + GEMM when d_ws is large enough, else the
+ *            matrix cores).  An
  *            explicit variant runs with its default knob (uw_gemm_with_plan
  *            runs a given knob).
  *   d_ws/ws_bytes  caller-owned device workspace (uw_workspace_size bytes for
