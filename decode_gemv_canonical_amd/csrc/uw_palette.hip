@@ -396,16 +396,24 @@ constexpr bool palette_two_sets() {
   return 2 * (16 * TB + 21 * RB) + 4 * RB * TB <= 200;
 }
 
-template <int TB, int RB, bool YBF16>
+// SPLIT: two workgroups share each group of RB row blocks, each taking half
+// of the 128-column blocks and adding its partial sums into Y (zeroed first;
+// fp32 Y only).  Two partial sums added to zero give the same bits in either
+// order, so the result is deterministic.  Every workgroup reads the
+// activations of its part of K once, so the split lets a workgroup hold more
+// rows (fewer reads of X in all) while the chip stays full.
+template <int TB, int RB, bool YBF16, bool SPLIT>
 __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const uint16_t* __restrict__ X, int64_t ldx,
                                                            int nb, void* __restrict__ Y, int64_t ldy) {
+  static_assert(!(SPLIT && YBF16), "split partial sums are added in fp32");
   __shared__ uint32_t table[256];
   extern __shared__ float4 red[];  // [waves][TB][64] partial sums of one 16-row block, then the rows' tile flags
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ks = blockDim.x >> 6;
   const int r = lane & 15, j = lane >> 4;
   const int tpr = int(p.tpr);
   uint2* rflags = reinterpret_cast<uint2*>(red + ks * TB * 64);  // [16 RB rows][tpr]: (flags, prefix)
-  const int64_t base = int64_t(blockIdx.x) * 16 * RB;  // the workgroup's RB blocks of 16 rows
+  const int split = SPLIT ? int(blockIdx.x & 1) : 0;
+  const int64_t base = int64_t(SPLIT ? blockIdx.x >> 1 : blockIdx.x) * 16 * RB;  // the workgroup's RB blocks of 16 rows
   for (int b = threadIdx.x; b < 256; b += blockDim.x) table[b] = (pal_byte(p, b & 15) << 7) | (pal_byte(p, b >> 4) << 23);
   for (int i = threadIdx.x; i < 16 * RB * tpr; i += blockDim.x) {
     const int64_t row = std::min<int64_t>(p.rows - 1, base + i / tpr);
@@ -424,7 +432,8 @@ __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const u
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[i][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int64_t n_blocks = p.tpr * 8;  // 128-column blocks per row
+  const int64_t n_all = p.tpr * 8;  // 128-column blocks per row
+  const int64_t kb0 = SPLIT ? (split ? n_all / 2 : 0) : 0, n_blocks = SPLIT && !split ? n_all / 2 : n_all;  // its blocks
   if constexpr (palette_two_sets<TB, RB>()) {
     // Every path from the loads of one set to the products of the other
     // issues a fixed number of loads (the next set's, or none at the last
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const u
     // set's loads in flight; a load under a condition in between would make
     // it wait for everything.
     BlockSet<TB, RB> sa, sb;
-    int64_t kb = wave;
+    int64_t kb = kb0 + wave;
     if (kb < n_blocks) {
       load_set<TB, RB, true>(p, rflags, xr, row, r, kb, j, sa);
       while (true) {
@@ -453,7 +462,7 @@ __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const u
       }
     }
   } else {
-    for (int64_t kb = wave; kb < n_blocks; kb += ks) {
+    for (int64_t kb = kb0 + wave; kb < n_blocks; kb += ks) {
       BlockSet<TB, RB> sa;
       load_set<TB, RB, false>(p, rflags, xr, row, r, kb, j, sa);
       mfma_set<TB, RB>(sa, table, acc);
@@ -480,6 +489,7 @@ __global__ __launch_bounds__(512) void palette_mfma_kernel(DevPalette p, const u
       const int b = 16 * tb + bc;
       if (n < p.rows && b < nb) {
         if (YBF16) static_cast<uint16_t*>(Y)[b * ldy + n] = f32_to_bf16(sum);
+        else if (SPLIT) unsafeAtomicAdd(static_cast<float*>(Y) + b * ldy + n, sum);
         else static_cast<float*>(Y)[b * ldy + n] = sum;
       }
     }
@@ -578,32 +588,59 @@ extern "C" int uw_palette_decompress(const uw_palette* m, uint16_t* d_out, int64
 // re-reads of X from cache as the batch grows), and KS waves split K (at most
 // 8: a 1024-column multiple splits into 8 blocks of 128).  The largest RB
 // that still leaves about 1792 waves, then the fewest KS that reach it.
-void palette_mfma_shape(int64_t rows, int* rb, int* ks) {
+// Row blocks per workgroup (rb), waves splitting K within it (ks) and
+// workgroups splitting K (nsplit).  rb: the largest of 4, 2, 1 that still
+// gives about 224 workgroups of 8 waves.  Where that leaves one row block
+// per workgroup (few rows: down_proj 4096 x 14336), Y is fp32 and there are
+// two or more batch tiles, two row blocks and two workgroups per group
+// instead: as many workgroups, half the reads of X (down at 32 / 64 batch
+// rows: 42.7 / 69.7 -> 35.6 / 51.1 us; at 4 / 16 rows, where X is small,
+// 22.7 / 29.7 -> 26.5 / 31.4, so not there).
+void palette_mfma_shape(int64_t rows, int64_t kblocks, int tb, bool yf32, int* rb, int* ks, int* nsplit) {
   const int64_t blocks16 = (rows + 15) / 16;
   *rb = 1;
+  *nsplit = 1;
   for (int c : {4, 2})
     if ((blocks16 + c - 1) / c * 8 >= 1792) {
       *rb = c;
       break;
     }
-  const int64_t wgs = (blocks16 + *rb - 1) / *rb;
+  if (*rb == 1 && yf32 && tb >= 2 && blocks16 >= 128 && kblocks >= 32) {
+    *rb = 2;
+    *nsplit = 2;
+  }
+  const int64_t wgs = (blocks16 + *rb - 1) / *rb * *nsplit;
   *ks = 1;
   while (*ks < 8 && wgs * *ks < 1792) *ks *= 2;
 }
 
+__global__ void zero_f32_rows_kernel(float* __restrict__ Y, int nb, int64_t rows, int64_t ldy) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nb * rows; i += int64_t(gridDim.x) * blockDim.x)
+    Y[(i / rows) * ldy + i % rows] = 0.f;
+}
+
 template <int TB, int RB>
 int launch_palette_mfma_rb(const DevPalette& p, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt,
-                           int ks, hipStream_t s) {
+                           int ks, int nsplit, hipStream_t s) {
+  // the split kernel is instantiated for 2 row blocks and 2 or more batch tiles, fp32 Y
+  const bool split = RB == 2 && TB >= 2 && yt == UW_F32 && nsplit == 2;
   const size_t lds = size_t(ks) * TB * 64 * sizeof(float4) + size_t(16) * RB * size_t(p.tpr) * 8;
-  const dim3 grid(unsigned((p.rows + 16 * RB - 1) / (16 * RB))), block(64 * ks);
+  const dim3 grid(unsigned((p.rows + 16 * RB - 1) / (16 * RB) * (split ? 2 : 1))), block(64 * ks);
   // the kernel also holds a 1 KiB static table
   if (lds + 1024 > size_t(kLdsLimit)) return fail(UW_ERR_UNSUPPORTED, "uw_palette_gemm: too many tiles per row");
-  auto kern = yt == UW_BF16 ? palette_mfma_kernel<TB, RB, true> : palette_mfma_kernel<TB, RB, false>;
+  auto kern = yt == UW_BF16 ? palette_mfma_kernel<TB, RB, true, false> : palette_mfma_kernel<TB, RB, false, false>;
+  if constexpr (RB == 2 && TB >= 2)
+    if (split) kern = palette_mfma_kernel<TB, RB, false, true>;
   if (lds > 48 * 1024) {
     static std::mutex mu;
     std::lock_guard<std::mutex> lk(mu);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               kLdsLimit - 1024);
+  }
+  if (split) {  // the workgroups add their partial sums into Y
+    hipLaunchKernelGGL(zero_f32_rows_kernel, dim3(unsigned(std::min<int64_t>(1024, (nb * p.rows + 255) / 256))), dim3(256),
+                       0, s, static_cast<float*>(Y), nb, p.rows, ldy);
+    if (int rc = hip_check(hipGetLastError(), "zero_f32_rows_kernel launch")) return rc;
   }
   hipLaunchKernelGGL(kern, grid, block, lds, s, p, X, ldx, nb, Y, ldy);
   return hip_check(hipGetLastError(), "palette_mfma_kernel launch");
@@ -612,11 +649,11 @@ int launch_palette_mfma_rb(const DevPalette& p, const uint16_t* X, int64_t ldx, 
 template <int TB>
 int launch_palette_mfma(const DevPalette& p, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt,
                         hipStream_t s) {
-  int rb, ks;
-  palette_mfma_shape(p.rows, &rb, &ks);
-  if (rb == 4) return launch_palette_mfma_rb<TB, 4>(p, X, ldx, nb, Y, ldy, yt, ks, s);
-  if (rb == 2) return launch_palette_mfma_rb<TB, 2>(p, X, ldx, nb, Y, ldy, yt, ks, s);
-  return launch_palette_mfma_rb<TB, 1>(p, X, ldx, nb, Y, ldy, yt, ks, s);
+  int rb, ks, nsplit;
+  palette_mfma_shape(p.rows, p.tpr * 8, TB, yt == UW_F32, &rb, &ks, &nsplit);
+  if (rb == 4) return launch_palette_mfma_rb<TB, 4>(p, X, ldx, nb, Y, ldy, yt, ks, nsplit, s);
+  if (rb == 2) return launch_palette_mfma_rb<TB, 2>(p, X, ldx, nb, Y, ldy, yt, ks, nsplit, s);
+  return launch_palette_mfma_rb<TB, 1>(p, X, ldx, nb, Y, ldy, yt, ks, nsplit, s);
 }
 
 extern "C" int uw_palette_gemm(const uw_palette* m, const void* d_X, int64_t batch, int64_t ldx, int xt, void* d_Y,

@@ -146,6 +146,7 @@ GEMM_CASES = [
     ("down", 8192, 2048, 43, [2, 33]),          # 2 row blocks, 8 % raw groups, a partial batch tile
     ("wide_exponents", 8192, 1024, 44, [5]),   # every group raw (64 exponents, all finite)
     ("down", 3, 67584, 24, [3, 20]),           # 66 tiles per row
+    ("down", 2072, 4096, 45, [7, 40]),         # 40 rows: two workgroups per 32 rows split K, the last group partial
     ("gate", None, None, None, [16, 32, 64]),   # 4 row blocks per workgroup, 8 waves split K
     ("down", None, None, None, [4, 64, 100]),  # 1 row block per workgroup, 8 waves; 100 = two passes
     ("gate", 28672, 1024, 31, [3]),            # 4 row blocks per workgroup, 4 waves split K
@@ -170,6 +171,23 @@ def test_palette_gemm(case):
         torch.cuda.synchronize()
         check_f32(Y, ref, f"palette gemm {name} b={batch}")
         check_bf16(Yb, ref, f"palette gemm bf16 {name} b={batch}", wb.shape[1])
+
+
+def test_palette_gemm_split_is_deterministic():
+    # at 17..64 batch rows with fp32 Y, matrices with few row blocks run two
+    # workgroups per group of rows, each adding half of K into Y: two partial
+    # sums added to zero give the same bits in either order
+    wb, m = pmatrix("down", 2072, 4096, 45)
+    for batch in (17, 64):
+        X = workloads.activations(wb.shape[1], batch, seed=950 + batch, dtype=torch.bfloat16).to(DEV)
+        _say(f"palette gemm split determinism batch={batch}")
+        ys = [m.gemm(X) for _ in range(3)]
+        yb = m.gemm(X, out_dtype=torch.bfloat16)  # bf16 Y: one workgroup per group
+        torch.cuda.synchronize()
+        assert all(torch.equal(ys[0], y) for y in ys[1:])
+        ref = products.gemm_f64(wb, X.float().cpu().numpy())
+        check_f32(ys[0], ref, f"palette gemm split b={batch}")
+        check_bf16(yb, ref, f"palette gemm split bf16 b={batch}", wb.shape[1])
 
 
 def test_palette_gemm_strided_and_errors():
