@@ -417,9 +417,17 @@ __global__ __launch_bounds__(256) void bf16_mfma_stage_kernel(const uint16_t* __
 }
 
 // Y[b][n] = 0 for b < batch, n < rows (fp32), ahead of a split product.
-__global__ void zero_rows_kernel(float* __restrict__ Y, int64_t batch, int64_t rows, int64_t ldy) {
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < batch * rows; i += int64_t(gridDim.x) * blockDim.x)
-    Y[(i / rows) * ldy + i % rows] = 0.f;
+// Y[b][0 .. rows) = 0 for batch row b = blockIdx.y; 16-byte stores when every
+// row starts 16-byte aligned (VEC), else 4-byte ones.
+template <bool VEC>
+__global__ void zero_rows_kernel(float* __restrict__ Y, int64_t rows, int64_t ldy) {
+  float* y = Y + int64_t(blockIdx.y) * ldy;
+  const int64_t i = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (VEC && i + 4 <= rows) {
+    *reinterpret_cast<float4*>(y + i) = float4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    for (int64_t j = i; j < std::min<int64_t>(i + 4, rows); ++j) y[j] = 0.f;
+  }
 }
 
 template <int RB, int TB>
@@ -429,8 +437,13 @@ int run_stage_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw, c
   const int ny = int((batch + 16 * TB - 1) / (16 * TB));
   if (yt != UW_F32 || cols / 128 < 2 * kStages) nsplit = 1;  // the split adds fp32 partial sums in place
   if (nsplit > 1) {
-    hipLaunchKernelGGL(zero_rows_kernel, dim3(unsigned(std::min<int64_t>(1024, (batch * rows + 255) / 256))), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<float*>(Y), batch, rows, ldy);
+    const dim3 zgrid(unsigned((rows + 1023) / 1024), unsigned(batch));
+    if (reinterpret_cast<uintptr_t>(Y) % 16 == 0 && ldy % 4 == 0)
+      hipLaunchKernelGGL(zero_rows_kernel<true>, zgrid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                         static_cast<float*>(Y), rows, ldy);
+    else
+      hipLaunchKernelGGL(zero_rows_kernel<false>, zgrid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                         static_cast<float*>(Y), rows, ldy);
     if (int rc = hip_check(hipGetLastError(), "zero_rows_kernel launch")) return rc;
   }
   const int64_t grid = int64_t((n_groups + kXcds - 1) / kXcds) * kXcds * ny * nsplit;

@@ -614,9 +614,17 @@ void palette_mfma_shape(int64_t rows, int64_t kblocks, int tb, bool yf32, int* r
   while (*ks < 8 && wgs * *ks < 1792) *ks *= 2;
 }
 
-__global__ void zero_f32_rows_kernel(float* __restrict__ Y, int nb, int64_t rows, int64_t ldy) {
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nb * rows; i += int64_t(gridDim.x) * blockDim.x)
-    Y[(i / rows) * ldy + i % rows] = 0.f;
+// Y[b][0 .. rows) = 0 for batch row b = blockIdx.y; 16-byte stores when every
+// row starts 16-byte aligned (VEC), else 4-byte ones.
+template <bool VEC>
+__global__ void zero_f32_rows_kernel(float* __restrict__ Y, int64_t rows, int64_t ldy) {
+  float* y = Y + int64_t(blockIdx.y) * ldy;
+  const int64_t i = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (VEC && i + 4 <= rows) {
+    *reinterpret_cast<float4*>(y + i) = float4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    for (int64_t j = i; j < std::min<int64_t>(i + 4, rows); ++j) y[j] = 0.f;
+  }
 }
 
 template <int TB, int RB>
@@ -638,8 +646,11 @@ int launch_palette_mfma_rb(const DevPalette& p, const uint16_t* X, int64_t ldx, 
                               kLdsLimit - 1024);
   }
   if (split) {  // the workgroups add their partial sums into Y
-    hipLaunchKernelGGL(zero_f32_rows_kernel, dim3(unsigned(std::min<int64_t>(1024, (nb * p.rows + 255) / 256))), dim3(256),
-                       0, s, static_cast<float*>(Y), nb, p.rows, ldy);
+    const dim3 zgrid(unsigned((p.rows + 1023) / 1024), unsigned(nb));
+    if (aligned_to(Y, 16) && ldy % 4 == 0)
+      hipLaunchKernelGGL(zero_f32_rows_kernel<true>, zgrid, dim3(256), 0, s, static_cast<float*>(Y), p.rows, ldy);
+    else
+      hipLaunchKernelGGL(zero_f32_rows_kernel<false>, zgrid, dim3(256), 0, s, static_cast<float*>(Y), p.rows, ldy);
     if (int rc = hip_check(hipGetLastError(), "zero_f32_rows_kernel launch")) return rc;
   }
   hipLaunchKernelGGL(kern, grid, block, lds, s, p, X, ldx, nb, Y, ldy);
