@@ -1096,13 +1096,17 @@ struct ProductSink {
       rows_done[b] = lane == n_done ? s : rows_done[b];
       acc[b] = 0.f;
     }
-    ++n_done;  // a unit covers at most 64 rows (checked on the host)
+    // every lane holds a finished row: store them.  Only the block walk
+    // has units of more than 64 rows: on the flat walk (G <= 1024 and the
+    // groups per row a multiple of 16) a unit spans G / gcd(G, groups per
+    // row) <= 64 rows, and a split-row item at most 64 (checked on the host).
+    ++n_done;
+    if (!FLAT && n_done == kWave) store_done();
   }
   __device__ void to_row(int64_t row) {
-    const int r = int(row - first_row);  // a unit covers at most 64 rows
-    if (r != cur_row) {
+    if (int(row - first_row) != cur_row) {
       flush();
-      cur_row = r;
+      cur_row = int(row - first_row);
     }
   }
   __device__ void tile_raw(uint32_t) {}
@@ -1600,8 +1604,10 @@ int run_fused(const uw_matrix* m, const void* X, int64_t ldx, int nb, void* Y, i
   const size_t fixed = tables_bytes() + x_bytes(d, NBP, XF32);
   const int max_waves = fused_max_threads(NBP, XF32, d.flat) / kWave;
   // split rows: NBP partial sums per wave in LDS, and whole units per
-  // workgroup; where a unit's waves do not fit, one wave per unit
-  if (d.split && (d.unit_blocks > max_waves ||
+  // workgroup; where a unit's waves do not fit, or a block spans more rows
+  // than a wave's lanes can park (its first row waits for the previous
+  // wave's part), one wave per unit
+  if (d.split && (d.unit_blocks > max_waves || int64_t(d.G) > 62 * int64_t(d.gpr) ||
                   fixed + (ring_bytes(kRSLow, d.slot_bytes) + 4 * NBP) * d.unit_blocks > size_t(kLdsLimit))) {
     d.split = 0;
     d.n_items = d.n_units;
@@ -1803,10 +1809,6 @@ int fused_rows_per_pass(const uw_matrix* m, int64_t batch, int xt) {
 bool fused_supported(const uw_matrix* m, int xt, std::string* why) {
   if (m->h.plain()) return true;  // handled by the bf16 product
   const DevMatrix& d = m->dev;
-  if (int64_t(d.unit_blocks) * d.G > int64_t(kWave) * d.gpr) {
-    if (why) *why = "a work unit (lcm of G and the groups per row) spans more than 64 rows";
-    return false;
-  }
   if (tables_bytes() + x_bytes(d, 1, xt == UW_F32) + ring_bytes(d.flat ? kRSLow : kRS, d.slot_bytes) >
       size_t(kLdsLimit)) {
     if (why) *why = "x of this width does not fit in LDS next to the decode tables";

@@ -114,7 +114,22 @@ GEMV_CASES = [
     ("gate", 67, 4096, 16, {"G": 224}, torch.float32),
     ("down", 24, 14336, 17, {"G": 256}, torch.bfloat16),
     ("small", 50, 3072, 18, {"G": 80}, torch.float32),
+    # work units of more than 64 rows (the lcm of G and a groups-per-row
+    # count prime to it): the finished rows parked in lanes are stored every 64
+    ("small", 200, 320, 19, {"G": 1024}, torch.bfloat16),
+    ("down", 150, 448, 20, {"G": 512}, torch.float32),
 ]
+
+
+@pytest.mark.parametrize("batch", [3, 8])
+def test_gemm_fused_valu_long_units(batch):
+    wb, m = matrix("small", 200, 320, 19, G=1024)
+    X = workloads.activations(320, batch, seed=310 + batch, dtype=torch.bfloat16)
+    ref = products.gemm_f64(wb, X.float().numpy())
+    _say(f"gemm fused long units batch={batch}")
+    Y = m.gemm(X.to(DEV), variant=uw.UW_VARIANT_FUSED)
+    torch.cuda.synchronize()
+    check_f32(Y, ref, f"gemm fused long units b={batch}")
 
 
 @pytest.mark.parametrize("name,rows,cols,seed,opts,xdt", GEMV_CASES)

@@ -116,3 +116,67 @@ def special_values_bf16() -> list[int]:
     the largest finite value, +-Inf and NaNs with payloads."""
     return [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F, 0x0080, 0x7F7F, 0xFF7F,
             0x7F80, 0xFF80, 0x7FC0, 0x7FC1, 0xFFFF, 0x7F81, 0x3F80, 0xBF80]
+
+
+# Broad parity sweep: seeded random configurations over shape, weight recipe,
+# encoder options and batch size, so that every kernel meets ragged rows,
+# narrow and wide rows, every block size family and raw groups of every
+# density.  Recipes:
+#   gauss     N(0, sigma), sigma = 10^U(-4, 0.5)
+#   outliers  N(0, 0.02) with a Bernoulli(rate) mask replaced by N(0, 1),
+#             rate = 10^U(-3, -1)
+#   randbits  uniformly random 16-bit patterns (decompression only)
+#   finite    gauss with 1 % of entries replaced by finite special values
+#             (+-0, subnormal extremes, +-1)
+#   special   gauss with 1 % of entries replaced by any special value
+#             (NaN and Inf included: decompression only)
+SWEEP_SEED = 20261202
+_SWEEP_ROWS = (1, 2, 3, 7, 16, 17, 31, 64, 65, 100, 128, 129, 200, 257)
+_SWEEP_COLS64 = (1, 2, 3, 5, 8, 13, 16, 17, 31, 32, 48, 64, 80)
+_SWEEP_G = (0, 16, 32, 48, 64, 112, 128, 224, 256, 512, 1024)  # 0: the encoder's default
+_SWEEP_KL = ((0, 0), (16, 6), (8, 4), (1, 1), (32, 8), (24, 5), (12, 12), (4, 2))  # 0: default
+_SWEEP_BATCH = (1, 2, 3, 5, 8, 16, 17, 33, 64)
+_SWEEP_RECIPES = ("gauss", "outliers", "randbits", "finite", "special")
+
+
+def sweep_cases(n: int = 32, seed: int = SWEEP_SEED) -> list[dict]:
+    """n seeded random configurations for the parity sweep."""
+    g = _gen(seed)
+
+    def pick(seq):
+        return seq[int(torch.randint(0, len(seq), (1,), generator=g))]
+
+    cases = []
+    for i in range(n):
+        K, L = pick(_SWEEP_KL)
+        # the first cases pin one recipe each so every recipe is present
+        recipe = _SWEEP_RECIPES[i] if i < len(_SWEEP_RECIPES) else pick(_SWEEP_RECIPES)
+        cases.append({
+            "id": i, "rows": pick(_SWEEP_ROWS), "cols": 64 * pick(_SWEEP_COLS64), "recipe": recipe,
+            "K": K, "L": L, "G": pick(_SWEEP_G), "batch": pick(_SWEEP_BATCH),
+            "sigma": float(10.0 ** (torch.rand(1, generator=g) * 4.5 - 4.0)),
+            "rate": float(10.0 ** (torch.rand(1, generator=g) * 2.0 - 3.0)),
+            "seed": seed + 1 + i,
+        })
+    return cases
+
+
+def sweep_weights(case: dict) -> torch.Tensor:
+    """The weights (int16 bit view) of a sweep configuration."""
+    r, c, s = case["rows"], case["cols"], case["seed"]
+    rec = case["recipe"]
+    if rec == "randbits":
+        return random_bits_bf16(r, c, s)
+    if rec == "outliers":
+        return gaussian_with_outliers_bf16(r, c, SIGMA, case["rate"], s)
+    w = gaussian_bf16(r, c, case["sigma"], s)
+    if rec in ("finite", "special"):
+        g = _gen(s + 7)
+        vals = special_values_bf16()
+        if rec == "finite":
+            vals = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F, 0x0080, 0x3F80, 0xBF80]
+        table = torch.tensor([v - 65536 if v >= 32768 else v for v in vals], dtype=torch.int16)
+        mask = torch.rand(r, c, generator=g) < 0.01
+        pick = torch.randint(0, len(vals), (r, c), generator=g)
+        w = torch.where(mask, table[pick], w)
+    return w
