@@ -487,10 +487,13 @@ int run_variant(const uw_matrix* m, int variant, int knob, const void* d_X, int6
   }
 }
 
-// AUTO without a usable plan: one or two rows on VALU (when one pass takes
-// them); up to 32 rows on the matrix cores; beyond that decompress + GEMM
-// when the workspace is given (the measured crossovers on the MLP shapes: at
-// 64 rows decompress + GEMM is ahead on down_proj).
+// AUTO without a usable plan: on VALU one row, and up to 8 when one pass
+// takes them all with 16 waves per workgroup (gate_proj 24 / 29 / 39 us at 2
+// / 4 / 8 rows against 41 on the matrix cores; 8192 x 8192 33 us at 4
+// against 40; down_proj at 2 rows 31 against 39); up to 32 rows on the
+// matrix cores; beyond that decompress + GEMM when the workspace is given
+// (the measured crossovers on the MLP shapes: at 64 rows decompress + GEMM
+// is ahead on down_proj).
 int heuristic_variant(const uw_matrix* m, const CallShape& c) {
   const bool fused_ok = runnable(m, UW_VARIANT_FUSED, 0, c, nullptr);
   const bool mfma_ok = runnable(m, UW_VARIANT_FUSED_MFMA, 0, c, nullptr);
@@ -504,7 +507,9 @@ int heuristic_variant(const uw_matrix* m, const CallShape& c) {
   // and 56-65 for decompress + GEMM; down 20.5 / 22.3 against 23.8 / 30.9,
   // 30-70 at 16-64 against 42-77 and 65-76)
   if (pal_ok && batch <= 64) return UW_VARIANT_PALETTE;
-  if (fused_ok && (batch == 1 || (batch == 2 && fused_rows_per_pass(m, batch, c.xt) >= 2))) return UW_VARIANT_FUSED;
+  if (fused_ok && (batch == 1 || (batch == 2 && fused_rows_per_pass(m, batch, c.xt) >= 2) ||
+                   (batch <= 8 && fused_one_full_pass(m, batch, c.xt))))
+    return UW_VARIANT_FUSED;
   if (mfma_ok && (batch <= 32 || (batch <= 64 && !ws_ok))) return UW_VARIANT_FUSED_MFMA;
   if (ws_ok && (c.xt == UW_BF16 || !fused_ok)) return UW_VARIANT_DECOMPRESS_GEMM;
   if (mfma_ok) return UW_VARIANT_FUSED_MFMA;

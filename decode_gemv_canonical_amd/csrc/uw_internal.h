@@ -143,6 +143,7 @@ int launch_fused(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, 
 bool fused_supported(const uw_matrix* m, int xt, std::string* why);
 // Batch rows the VALU fused product takes per pass (its x copy fits in LDS).
 int fused_rows_per_pass(const uw_matrix* m, int64_t batch, int xt);
+bool fused_one_full_pass(const uw_matrix* m, int64_t batch, int xt);
 // nw: waves per workgroup (0 = chosen for the fewest idle waves, else 8..16).
 int launch_fused_mfma(const uw_matrix* m, const void* X, int64_t batch, int64_t ldx, void* Y, int64_t ldy, int yt,
                       void* stream, int nw = 0);

@@ -986,9 +986,22 @@ __global__ void palette_fill_kernel(uint8_t* __restrict__ out, PaletteFill f) {
 // X lives in LDS at kAreaAddr.  bf16 x as pairs: pair p at lane l holds
 // X[b][128p + l] | X[b][128p + 64 + l] << 16 (column groups 2p and 2p+1) in
 // word x_word(p, l)*NBP + b, where the 8 pairs of a 16-group tile are 8
-// consecutive words of the lane (two 16-byte reads per tile); fp32 x as word
-// k*NBP + b = X[b][k].
+// consecutive words of the lane (2 NBP 16-byte reads per tile); fp32 x as
+// word k*NBP + b = X[b][k].  With NBP >= 2 a lane's block of 8 NBP words
+// starts every 32 NBP bytes, so the lanes a read serves together would meet
+// on the same banks: 16-byte chunk j of lane l's block is stored at chunk
+// j ^ x_swz(l), which differs between lanes whose blocks start on the same
+// bank (x_slot gives the word for pair p, lane l, batch column b).
 __host__ __device__ inline uint32_t x_word(uint32_t p, uint32_t l) { return (((p >> 3) * 64 + l) << 3) + (p & 7); }
+template <int NBP>
+__host__ __device__ inline uint32_t x_swz(uint32_t l) {
+  return NBP >= 2 ? (l * 2u * NBP / 16u) & (2u * NBP - 1u) : 0u;
+}
+template <int NBP>
+__host__ __device__ inline uint32_t x_slot(uint32_t p, uint32_t l, uint32_t b) {
+  const uint32_t w = (p & 7) * NBP + b;  // word in the lane's block
+  return ((p >> 3) * 64 + l) * 8 * NBP + ((((w >> 2) ^ x_swz<NBP>(l)) << 2) | (w & 3));
+}
 template <int NBP, bool XF32>
 __device__ inline void load_x(const DevMatrix& d, const void* X, int64_t ldx, int nb_valid, uint32_t* xl) {
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -1013,7 +1026,7 @@ __device__ inline void load_x(const DevMatrix& d, const void* X, int64_t ldx, in
         v = x[b * ldx + k0];
         if (k1 < C) v |= uint32_t(x[b * ldx + k1]) << 16;
       }
-      xl[x_word(p, l) * NBP + b] = v;
+      xl[x_slot<NBP>(p, l, uint32_t(b))] = v;
     }
   }
 }
@@ -1119,9 +1132,10 @@ struct ProductSink {
       // c is a multiple of 16: the tile's 8 pairs are the 8 * NBP words at
       // x_word(c / 2, lane) * NBP = (c / 16 * 64 + lane) * 8 * NBP
       const uint32_t a = xlane + (uint32_t(c) >> 4) * (2048u * NBP);
+      const uint32_t swz = x_swz<NBP>(uint32_t(lane));
 #pragma unroll
       for (int j = 0; j < 2 * NBP; ++j) {
-        const uint4 v = ld128(a + 16 * j);
+        const uint4 v = ld128(a + 16 * (uint32_t(j) ^ swz));
         xw[4 * j] = v.x;
         xw[4 * j + 1] = v.y;
         xw[4 * j + 2] = v.z;
@@ -1132,7 +1146,7 @@ struct ProductSink {
   // x of column group cg at this lane
   __device__ float x_at(int cg, int b) const {
     if (XF32) return bits_f32(ld32(xaddr + ((uint32_t(cg) * 64 + lane) * NBP + b) * 4));
-    const uint32_t v = ld32(xaddr + (x_word(uint32_t(cg) >> 1, uint32_t(lane)) * NBP + b) * 4);
+    const uint32_t v = ld32(xaddr + x_slot<NBP>(uint32_t(cg) >> 1, uint32_t(lane), uint32_t(b)) * 4);
     return bits_f32((cg & 1) ? (v & 0xFFFF0000u) : (v << 16));
   }
   // tile_begin() guarantees an even c0: pair k is x pair c0/2 + k
@@ -1149,9 +1163,9 @@ struct ProductSink {
 #pragma unroll
       for (int b = 0; b < NBP; ++b) acc[b] = dot2_bf16(D, xw[k * NBP + b], acc[b]);
     } else {
-      const uint32_t a = xaddr + x_word((uint32_t(c0) >> 1) + uint32_t(k), uint32_t(lane)) * NBP * 4;
+      const uint32_t pk = (uint32_t(c0) >> 1) + uint32_t(k);
 #pragma unroll
-      for (int b = 0; b < NBP; ++b) acc[b] = dot2_bf16(D, ld32(a + 4 * b), acc[b]);
+      for (int b = 0; b < NBP; ++b) acc[b] = dot2_bf16(D, ld32(xaddr + x_slot<NBP>(pk, uint32_t(lane), uint32_t(b)) * 4), acc[b]);
     }
   }
   __device__ void single(int, int64_t row, int cg, uint32_t w) {
@@ -1804,6 +1818,19 @@ int launch_palette_transcode(const uw_matrix* m, uint8_t* out, void* stream) {
 
 int fused_rows_per_pass(const uw_matrix* m, int64_t batch, int xt) {
   return m->h.plain() ? int(std::min<int64_t>(batch, 8)) : fused_chunk(m->dev, batch, xt == UW_F32);
+}
+
+// Whether one pass of the vector-ALU product takes all `batch` rows with
+// a full workgroup of 16 waves: x of every row next to the decode tables and
+// 16 rings of the short depth.
+bool fused_one_full_pass(const uw_matrix* m, int64_t batch, int xt) {
+  if (m->h.plain()) return false;
+  const DevMatrix& d = m->dev;
+  const bool xf32 = xt == UW_F32;
+  const int nbp = fused_chunk(d, batch, xf32);
+  if (nbp < batch || fused_max_threads(nbp, xf32, d.flat) / kWave < 16) return false;
+  const size_t per_wave = ring_bytes(d.flat ? kRSLow : kRS, d.slot_bytes) + 4 * size_t(nbp);
+  return tables_bytes() + x_bytes(d, nbp, xf32) + 16 * per_wave <= size_t(kLdsLimit);
 }
 
 bool fused_supported(const uw_matrix* m, int xt, std::string* why) {

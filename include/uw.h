@@ -224,8 +224,9 @@ int uw_gemv_fused(const uw_matrix* m, const void* d_x, int xt, void* d_y, int yt
  *            batch (uw_autotune, uw_set_plan, uw_plan_load) when that plan's
  *            variant can run this call, else a heuristic (up to 64 with a
  *            direct-palette copy attached: the palette product; else batch
- *            1, and batch 2 when one VALU pass takes both rows: fused on
- *            VALU; up to 32: fused on the matrix cores where supported;
+ *            1, batch 2 when one VALU pass takes both rows, and up to 8
+ *            when one VALU pass takes them all with 16 waves per workgroup:
+ *            fused on VALU; up to 32: fused on the matrix cores where supported;
  *            above: decompress + GEMM when d_ws is large enough, else the
  *            matrix cores).  An
  *            explicit variant runs with its default knob (uw_gemm_with_plan

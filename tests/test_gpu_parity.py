@@ -302,10 +302,10 @@ def test_gemm_fused_valu_fp32_split_rows(batch):
     check_f32(Y, ref, f"gemm fused fp32 split b={batch}")
 
 
-@pytest.mark.parametrize("batch", [2, 3, 40, 64])
+@pytest.mark.parametrize("batch", [2, 3, 8, 16, 40, 64])
 def test_gemm_auto_without_plan(batch):
-    # every heuristic branch of AUTO (VALU, matrix cores, decompress + GEMM with
-    # a workspace, matrix cores without one) against the fp64 product
+    # every heuristic branch of AUTO (VALU up to 8 rows, matrix cores, decompress
+    # + GEMM with a workspace, matrix cores without one) against the fp64 product
     wb, m = matrix("gate", 70, 4096, 15, G=224)
     X = workloads.activations(4096, batch, seed=330 + batch, dtype=torch.bfloat16)
     ref = products.gemm_f64(wb, X.float().numpy())

@@ -135,15 +135,16 @@ def test_gate_b32_autotune_with_palette_and_plan_file(tmp_path):
 def test_auto_without_a_plan_takes_the_attached_palette_copy():
     # with no plan stored, AUTO's heuristic runs the palette product for 1..64
     # batch rows once a palette copy is attached (bit-identical to the explicit
-    # variant); with none, the fused vector-ALU product at 1 and 2 rows and the
-    # fused matrix-core product above
+    # variant); with none, the fused vector-ALU product up to 8 rows (at 4096
+    # columns one pass takes 8 rows with 16 waves per workgroup) and the fused
+    # matrix-core product above
     w = workloads.weights("gate", rows=256, cols=4096, seed=91)
     wb = w.numpy().view(np.uint16)
     m = uw.CompressedMatrix.from_weights(w, device="cuda:0")
     for batch in (1, 2, 3, 16, 64):
         X = workloads.activations(4096, batch, seed=700 + batch, dtype=torch.bfloat16).to(DEV)
         ref = products.gemm_f64(wb, X.float().cpu().numpy())
-        y_mfma = m.gemm(X, variant=uw.UW_VARIANT_FUSED if batch <= 2 else uw.UW_VARIANT_FUSED_MFMA)
+        y_mfma = m.gemm(X, variant=uw.UW_VARIANT_FUSED if batch <= 8 else uw.UW_VARIANT_FUSED_MFMA)
         y_auto0 = m.gemm(X, variant=uw.UW_VARIANT_AUTO)
         p = m.transcode_palette()
         y_pal = m.gemm(X, variant=uw.UW_VARIANT_PALETTE)
