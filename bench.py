@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--workload", default="gate", choices=["gate", "down", "big", "small"])
     p.add_argument("--no-extras", action="store_true", help="skip comparators, GEMM sweep and CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle timing (profiler passes: its worker processes would each load the profiler)")
     p.add_argument("--skip-gemm", action="store_true", help="skip the batched-product sweep")
     p.add_argument("--gemm-only", action="store_true", help="run only the batched-product sweep (prints its JSON)")
     p.add_argument("--stack", action="store_true",
@@ -708,8 +710,11 @@ def main():
             log("gemm sweep")
             extras["gemm"] = gemm_sweep(uw, workloads, torch, dev, 48)
         out["extras"] = extras
-        log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
+        if args.no_cpu_baseline:
+            out["cpu_baseline"] = None
+        else:
+            log("cpu baseline (oracle)")
+            out["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
     for m in mats:
         m.close()
     print(json.dumps(out), flush=True)
