@@ -132,6 +132,24 @@ def test_gate_b32_autotune_with_palette_and_plan_file(tmp_path):
         h.close()
 
 
+def test_auto_without_a_plan_picks_valu_only_when_one_pass_has_16_waves():
+    # 4096 columns: one pass of 4 rows keeps 16 waves per CU, so AUTO runs the
+    # vector-ALU product; 14336 columns: 4 rows of x leave room for few waves,
+    # so AUTO runs the matrix-core product (bit-identical to the explicit variant)
+    for cols, want in ((4096, uw.UW_VARIANT_FUSED), (14336, uw.UW_VARIANT_FUSED_MFMA)):
+        w = workloads.weights("down", rows=64, cols=cols, seed=95)
+        wb = w.numpy().view(np.uint16)
+        m = uw.CompressedMatrix.from_weights(w, device="cuda:0")
+        X = workloads.activations(cols, 4, seed=705, dtype=torch.bfloat16).to(DEV)
+        y_want = m.gemm(X, variant=want)
+        y_auto = m.gemm(X, variant=uw.UW_VARIANT_AUTO)
+        torch.cuda.synchronize()
+        _say(f"auto small batch cols={cols}")
+        assert torch.equal(y_auto, y_want)
+        check_f32(y_auto, products.gemm_f64(wb, X.float().cpu().numpy()), f"auto b=4 cols={cols}")
+        m.close()
+
+
 def test_auto_without_a_plan_takes_the_attached_palette_copy():
     # with no plan stored, AUTO's heuristic runs the palette product for 1..64
     # batch rows once a palette copy is attached (bit-identical to the explicit
