@@ -612,6 +612,10 @@ void palette_mfma_shape(int64_t rows, int64_t kblocks, int tb, bool yf32, int* r
   const int64_t wgs = (blocks16 + *rb - 1) / *rb * *nsplit;
   *ks = 1;
   while (*ks < 8 && wgs * *ks < 1792) *ks *= 2;
+  // one batch tile over 4 row blocks: 4 waves splitting K are ahead of 8
+  // (gate_proj at 1 / 4 / 16 rows, interleaved, 8 cold copies: 24.4 / 24.6 /
+  // 25.5 us against 25.0 / 25.1 / 26.1); with more batch tiles 8 stay ahead
+  if (tb == 1 && *rb == 4) *ks = std::min(*ks, 4);
 }
 
 // Y[b][0 .. rows) = 0 for batch row b = blockIdx.y; 16-byte stores when every
