@@ -596,7 +596,7 @@ extern "C" int uw_palette_decompress(const uw_palette* m, uint16_t* d_out, int64
 // instead: as many workgroups, half the reads of X (down at 32 / 64 batch
 // rows: 42.7 / 69.7 -> 35.6 / 51.1 us; at 4 / 16 rows, where X is small,
 // 22.7 / 29.7 -> 26.5 / 31.4, so not there).
-void palette_mfma_shape(int64_t rows, int64_t kblocks, int tb, bool yf32, int* rb, int* ks, int* nsplit) {
+void palette_mfma_shape(int64_t rows, int64_t kblocks, int tb, int nb, bool yf32, int* rb, int* ks, int* nsplit) {
   const int64_t blocks16 = (rows + 15) / 16;
   *rb = 1;
   *nsplit = 1;
@@ -614,8 +614,13 @@ void palette_mfma_shape(int64_t rows, int64_t kblocks, int tb, bool yf32, int* r
   while (*ks < 8 && wgs * *ks < 1792) *ks *= 2;
   // one batch tile over 4 row blocks: 4 waves splitting K are ahead of 8
   // (gate_proj at 1 / 4 / 16 rows, interleaved, 8 cold copies: 24.4 / 24.6 /
-  // 25.5 us against 25.0 / 25.1 / 26.1); with more batch tiles 8 stay ahead
-  if (tb == 1 && *rb == 4) *ks = std::min(*ks, 4);
+  // 25.5 us against 25.0 / 25.1 / 26.1); with more batch tiles 8 stay ahead.
+  // Up to 4 batch rows, 2 row blocks (two register sets) with 4 waves are
+  // ahead again (23.5 / 23.7 / 24.2 us at 1 / 2 / 4 rows; 29.6 at 16).
+  if (tb == 1 && *rb == 4) {
+    *ks = std::min(*ks, 4);
+    if (nb <= 4) *rb = 2;
+  }
 }
 
 // Y[b][0 .. rows) = 0 for batch row b = blockIdx.y; 16-byte stores when every
@@ -665,7 +670,7 @@ template <int TB>
 int launch_palette_mfma(const DevPalette& p, const uint16_t* X, int64_t ldx, int nb, void* Y, int64_t ldy, int yt,
                         hipStream_t s) {
   int rb, ks, nsplit;
-  palette_mfma_shape(p.rows, p.tpr * 8, TB, yt == UW_F32, &rb, &ks, &nsplit);
+  palette_mfma_shape(p.rows, p.tpr * 8, TB, nb, yt == UW_F32, &rb, &ks, &nsplit);
   if (rb == 4) return launch_palette_mfma_rb<TB, 4>(p, X, ldx, nb, Y, ldy, yt, ks, nsplit, s);
   if (rb == 2) return launch_palette_mfma_rb<TB, 2>(p, X, ldx, nb, Y, ldy, yt, ks, nsplit, s);
   return launch_palette_mfma_rb<TB, 1>(p, X, ldx, nb, Y, ldy, yt, ks, nsplit, s);
