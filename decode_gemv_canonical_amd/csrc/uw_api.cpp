@@ -501,9 +501,9 @@ int heuristic_variant(const uw_matrix* m, const CallShape& c) {
   const bool pal_ok = runnable(m, UW_VARIANT_PALETTE, 0, c, nullptr);
   const int64_t batch = c.batch;
   // an attached direct-palette copy: its GEMV at one batch row and its
-  // matrix-core product up to 64 (MLP shapes, 8 cold copies: gate 20.4 /
-  // 25.2 us at 1 / 2 rows against 21.2 / 25.3 for the fused vector-ALU
-  // product, 26-45 at 16-64 against 40-87 for the fused matrix-core product
+  // matrix-core product up to 64 (MLP shapes, 8 cold copies: gate 20.3 /
+  // 23.8 / 24.3 us at 1 / 2 / 4 rows against 21.0 / 24.2 / 28.2 for the fused
+  // vector-ALU product, 25-45 at 8-64 against 38-87 for the fused products
   // and 56-65 for decompress + GEMM; down 20.5 / 22.3 against 23.8 / 30.9,
   // 30-70 at 16-64 against 42-77 and 65-76)
   if (pal_ok && batch <= 64) return UW_VARIANT_PALETTE;
