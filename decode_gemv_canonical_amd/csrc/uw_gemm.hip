@@ -542,6 +542,11 @@ int launch_mfma_gemm(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
       shape = g64 >= 96 && batch <= 32 ? 17 : 18;
     } else if (batch > 8 && batch <= 64 && stage && g64 >= 128) {
       shape = 15;
+    } else if (batch > 64 && cols <= 4096 && rows >= 12288 && (batch > 128 || rows >= 24576)) {
+      // tall matrices with short rows: 64 x 128 tiles with the activations in
+      // LDS (14336 x 4096 at 256 rows: 75 us against 89; 28672 x 4096 at
+      // 96-256 rows: 80-146 against 90-174)
+      shape = 13;
     } else if (batch > 64 && stage) {
       shape = (rows + 127) / 128 * tiles64 >= 192 ? 16 : 15;
     } else if (batch <= 8 && (rows + 31) / 32 >= 384) {
