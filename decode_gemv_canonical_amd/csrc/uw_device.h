@@ -100,6 +100,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ inline void load_lds16(const void* src, uint32_t dst) {
   __builtin_amdgcn_global_load_lds((global_void*)(const_cast<void*>(src)), (lds_void*)(size_t(dst)), 16, 0, 0);
 }
+// The same, non-temporal (cache policy bit 2, nt), for bytes read once that
+// share no cache line with later loads.
+__device__ inline void load_lds16_stream(const void* src, uint32_t dst) {
+  __builtin_amdgcn_global_load_lds((global_void*)(const_cast<void*>(src)), (lds_void*)(size_t(dst)), 16, 0, 2);
+}
 
 // Words read by the whole wave go through the constant address space so they
 // become scalar loads.
