@@ -339,10 +339,11 @@ __device__ inline uint32_t seg_end(const BlockRef& r, int t) {
 // floor (the slot then starts (address & 15) bytes before the segment) by NQ
 // 1 KB direct loads, each with at least one active lane, so every step issues
 // exactly 1 + NQ loads.
-template <int NQ>
+template <int NQ, bool NT = true>
 __device__ inline void issue_step(const uint8_t* sm_tile, const uint8_t* q, uint32_t lo, uint32_t hi, uint32_t sm_slot,
                                   uint32_t q_slot, int lane) {
-  load_lds16_stream(sm_tile + 16 * lane, sm_slot);
+  if constexpr (NT) load_lds16_stream(sm_tile + 16 * lane, sm_slot);
+  else load_lds16(sm_tile + 16 * lane, sm_slot);
   const uint8_t* a = q + lo;
   const uint32_t delta = uint32_t(reinterpret_cast<uintptr_t>(a)) & 15u;
   const uint8_t* base = a - delta;
@@ -377,7 +378,7 @@ __device__ inline void wait_tables(int issued) {
 // ahead of the consumer; past the end the last step is loaded again so the
 // count of loads stays fixed.  The end of the next tile's segment is read one
 // step early so its scalar load is back when it is needed.
-template <int RS, int NQ>
+template <int RS, int NQ, bool NT = true>
 struct Feeder {
   BlockRef r;
   int blk, b_end, t;
@@ -395,7 +396,7 @@ struct Feeder {
     for (int i = 0; i < RS; ++i) feed(d, sm_ring + 1024u * i, q_ring + uint32_t(d.slot_bytes) * i, lane);
   }
   __device__ void feed(const DevMatrix& d, uint32_t sm_slot, uint32_t q_slot, int lane) {
-    issue_step<NQ>(sm_tile, r.q, lo, next_hi, sm_slot, q_slot, lane);
+    issue_step<NQ, NT>(sm_tile, r.q, lo, next_hi, sm_slot, q_slot, lane);
     hi = next_hi;
     if (blk >= b_end) return;  // past the end: repeat the last step
     if (++t < r.nt) {
@@ -419,10 +420,10 @@ struct Feeder {
 // waits for its slot, decodes the tile into the sink and refills the slot RS
 // steps ahead.  Sink hooks: block_begin(blk), tile_end(t, nt), plus the
 // per-weight calls of decode_tile.
-template <int RS, int NQ, int XTRA, bool PAIR, class Sink>
+template <int RS, int NQ, int XTRA, bool PAIR, bool NT = true, class Sink>
 __device__ __forceinline__ void run_blocks(const DevMatrix& d, int b0, int b1, uint32_t sm_ring, uint32_t q_ring,
                                            int lane, Sink& sink) {
-  Feeder<RS, NQ> fd;
+  Feeder<RS, NQ, NT> fd;
   fd.init(d, b0, b1, sm_ring, q_ring, lane);
   const int slot_bytes = d.slot_bytes, gpr = d.gpr;
   LaneDec s{};
@@ -487,55 +488,59 @@ __device__ __forceinline__ void run_blocks(const DevMatrix& d, int b0, int b1, u
 // GEMV 21.2 -> 18.9 us on one box, down 23.4 -> 22.7).  The queue loads stay
 // cached: marked nt too, the line two segments share is fetched twice
 // (2 % more traffic, no faster).
-template <int NQ>
+// The instructions of one step.  SMPOL is the cache policy of the
+// sign+mantissa load ("nt " or ""); the s_lshr_b32 after the M0 write is also
+// the wait state that write needs.  With NQ = 4, loads 2 and 3 run from M0 =
+// slot + 2 KB and the floor + 2 KB (the immediate offset has 12 bits).
+#define UW_STEP_HEAD(SMPOL)                                           \
+  "s_nop 4\n"                                                         \
+  "s_mov_b32 m0, %[slot]\n"                                           \
+  "s_lshr_b32 %[t], %[sh], 8\n"                                       \
+  "buffer_load_dwordx4 %[l16], %[rsm], %[smo] offen " SMPOL "lds\n"   \
+  "s_lshr_b64 exec, -1, %[sh]\n"                                      \
+  "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:1024 lds\n"  \
+  "s_lshr_b64 exec, -1, %[t]\n"                                       \
+  "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:2048 lds\n"
+#define UW_STEP_TAIL4                                                 \
+  "s_add_u32 m0, %[slot], 0x800\n"                                    \
+  "s_lshr_b32 %[t], %[sh], 16\n"                                      \
+  "s_add_u32 %[f2], %[fl], 0x800\n"                                   \
+  "s_lshr_b64 exec, -1, %[t]\n"                                       \
+  "buffer_load_dwordx4 %[l16], %[rq], %[f2] offen offset:1024 lds\n"  \
+  "s_lshr_b32 %[t], %[sh], 24\n"                                      \
+  "s_lshr_b64 exec, -1, %[t]\n"                                       \
+  "buffer_load_dwordx4 %[l16], %[rq], %[f2] offen offset:2048 lds\n"
+#define UW_STEP_IN                                                                                          \
+  [slot] "s"(slot), [l16] "v"(lane16), [rsm] "s"(rsm), [smo] "s"(sm_off), [rq] "s"(rq), [fl] "s"(floor16), \
+      [sh] "s"(shifts)
+// NT: the sign+mantissa load is non-temporal.  A caller whose next kernel
+// reads the same sign+mantissa bytes again (the exponent-plane decode) keeps
+// them cached.
+template <int NQ, bool NT = true>
 __device__ __forceinline__ void issue_flat(__amdgpu_buffer_rsrc_t rsm, __amdgpu_buffer_rsrc_t rq, int v,
                                            uint32_t floor16, uint32_t shifts, uint32_t slot, uint32_t lane16) {
   static_assert(NQ == 2 || NQ == 4, "queue loads per step");
   const uint32_t sm_off = uint32_t(v) * 1024u;
   uint32_t t, f2;
-  if constexpr (NQ == 2) {
-    asm volatile(
-        "s_nop 4\n"
-        "s_mov_b32 m0, %[slot]\n"
-        "s_lshr_b32 %[t], %[sh], 8\n"  // also the wait state after the M0 write
-        "buffer_load_dwordx4 %[l16], %[rsm], %[smo] offen nt lds\n"
-        "s_lshr_b64 exec, -1, %[sh]\n"
-        "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:1024 lds\n"
-        "s_lshr_b64 exec, -1, %[t]\n"
-        "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:2048 lds\n"
-        "s_mov_b64 exec, -1"
-        : [t] "=&s"(t)
-        : [slot] "s"(slot), [l16] "v"(lane16), [rsm] "s"(rsm), [smo] "s"(sm_off), [rq] "s"(rq), [fl] "s"(floor16),
-          [sh] "s"(shifts)
-        : "memory", "m0", "exec");
-  } else {
-    asm volatile(
-        "s_nop 4\n"
-        "s_mov_b32 m0, %[slot]\n"
-        "s_lshr_b32 %[t], %[sh], 8\n"  // also the wait state after the M0 write
-        "buffer_load_dwordx4 %[l16], %[rsm], %[smo] offen nt lds\n"
-        "s_lshr_b64 exec, -1, %[sh]\n"
-        "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:1024 lds\n"
-        "s_lshr_b64 exec, -1, %[t]\n"
-        "buffer_load_dwordx4 %[l16], %[rq], %[fl] offen offset:2048 lds\n"
-        // loads 2 and 3 from M0 = slot + 2 KB and the floor + 2 KB (the
-        // immediate offset has 12 bits)
-        "s_add_u32 m0, %[slot], 0x800\n"
-        "s_lshr_b32 %[t], %[sh], 16\n"
-        "s_add_u32 %[f2], %[fl], 0x800\n"
-        "s_lshr_b64 exec, -1, %[t]\n"
-        "buffer_load_dwordx4 %[l16], %[rq], %[f2] offen offset:1024 lds\n"
-        "s_lshr_b32 %[t], %[sh], 24\n"
-        "s_lshr_b64 exec, -1, %[t]\n"
-        "buffer_load_dwordx4 %[l16], %[rq], %[f2] offen offset:2048 lds\n"
-        "s_mov_b64 exec, -1"
-        : [t] "=&s"(t), [f2] "=&s"(f2)
-        : [slot] "s"(slot), [l16] "v"(lane16), [rsm] "s"(rsm), [smo] "s"(sm_off), [rq] "s"(rq), [fl] "s"(floor16),
-          [sh] "s"(shifts)
-        : "memory", "m0", "exec");
-  }
+  if constexpr (NQ == 2 && NT)
+    asm volatile(UW_STEP_HEAD("nt ") "s_mov_b64 exec, -1" : [t] "=&s"(t) : UW_STEP_IN : "memory", "m0", "exec");
+  else if constexpr (NQ == 2)
+    asm volatile(UW_STEP_HEAD("") "s_mov_b64 exec, -1" : [t] "=&s"(t) : UW_STEP_IN : "memory", "m0", "exec");
+  else if constexpr (NT)
+    asm volatile(UW_STEP_HEAD("nt ") UW_STEP_TAIL4 "s_mov_b64 exec, -1"
+                 : [t] "=&s"(t), [f2] "=&s"(f2)
+                 : UW_STEP_IN
+                 : "memory", "m0", "exec");
+  else
+    asm volatile(UW_STEP_HEAD("") UW_STEP_TAIL4 "s_mov_b64 exec, -1"
+                 : [t] "=&s"(t), [f2] "=&s"(f2)
+                 : UW_STEP_IN
+                 : "memory", "m0", "exec");
   (void)f2;
 }
+#undef UW_STEP_HEAD
+#undef UW_STEP_TAIL4
+#undef UW_STEP_IN
 
 // N loads of 16 bytes on lane 0 only (from the start of the resource) into
 // the 16 bytes at dst: they keep a step's count of loads where there is
@@ -610,7 +615,7 @@ __device__ __forceinline__ bool item_ends_mid_row(const DevMatrix& d, const Walk
 
 // Issue the first RS steps of the tiles of blocks [b0, b1) into the ring;
 // returns the next step to issue.
-template <int RS, int NQ>
+template <int RS, int NQ, bool NT = true>
 __device__ __forceinline__ int flat_start(const DevMatrix& d, int b0, int b1, uint32_t ring, int lane) {
   const uint32_t lane16 = 16u * uint32_t(lane);
   const uint32_t stride = 1024u + uint32_t(d.slot_bytes);
@@ -622,7 +627,7 @@ __device__ __forceinline__ int flat_start(const DevMatrix& d, int b0, int b1, ui
 #pragma unroll
   for (int i = 0; i < RS; ++i) {
     if (fv < u1) {
-      issue_flat<NQ>(rsm, rq, fv, fstep[0], fstep[1], slot, lane16);
+      issue_flat<NQ, NT>(rsm, rq, fv, fstep[0], fstep[1], slot, lane16);
       ++fv;
       fstep += 2;
       slot += stride;
@@ -647,7 +652,7 @@ __device__ __forceinline__ void set_priority(int p) {
 // Tiles of blocks [b0, b1), whose first tile is at row row_base, column
 // group c_start (0 unless blocks split rows); flat_start has issued the
 // steps before fv0.
-template <int RS, int NQ, int XTRA, bool PAIR, class Sink>
+template <int RS, int NQ, int XTRA, bool PAIR, bool NT = true, class Sink>
 __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, int b1, int64_t row_base, int c_start,
                                          uint32_t ring, int lane, Sink& sink) {
   const uint32_t lane16 = 16u * uint32_t(lane);
@@ -696,7 +701,7 @@ __device__ __forceinline__ void run_flat(const DevMatrix& d, int fv0, int b0, in
       // every LDS read of the slot is done before it is refilled (the
       // builtin form, so the compiler knows the reads have completed)
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      issue_flat<NQ>(rsm, rq, fv, f_floor, f_shifts, slot, lane16);
+      issue_flat<NQ, NT>(rsm, rq, fv, f_floor, f_shifts, slot, lane16);
       ++fv;
       fstep += 2;
       f_floor = fstep[0];
@@ -908,13 +913,16 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
   const int u_first = item0 + blockIdx.x * waves + wave;
   const int n_items = item1;
   int fv = 0;
+  // the exponent plane's product reads the sign+mantissa bytes next, so this
+  // decode leaves them cached
+  constexpr bool kNT = SINK != 1;
   // the decode tables, then the first unit's loads; the tables have landed
   // once only the ring's loads may be younger
   const int n_tab = issue_tables(d, wave, waves, lane);
   int issued = 0;
   if (FLAT && u_first < n_items) {
     const WalkItem it = walk_item(d, u_first);
-    fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
+    fv = flat_start<RS, NQ, kNT>(d, it.b0, it.b1, sm_ring, lane);
     issued = fv - it.b0 * d.T;
   }
   if (n_tab) wait_tables<RS, NQ>(issued);
@@ -926,11 +934,11 @@ __global__ __launch_bounds__(1024) void decompress_kernel(DevMatrix d, uint16_t*
     // the two 16-byte stores per tile only make the ring waits stricter
     if (FLAT) {
       const WalkItem it = walk_item(d, u);
-      if (u != u_first) fv = flat_start<RS, NQ>(d, it.b0, it.b1, sm_ring, lane);
-      run_flat<RS, NQ, 0, PAIR>(d, fv, it.b0, it.b1, it.row, it.c0, sm_ring, lane, sink);
+      if (u != u_first) fv = flat_start<RS, NQ, kNT>(d, it.b0, it.b1, sm_ring, lane);
+      run_flat<RS, NQ, 0, PAIR, kNT>(d, fv, it.b0, it.b1, it.row, it.c0, sm_ring, lane, sink);
     } else {
       const int b0 = u * d.unit_blocks, b1 = std::min(d.n_blocks, b0 + d.unit_blocks);
-      run_blocks<RS, NQ, 0, PAIR>(d, b0, b1, sm_ring, q_ring, lane, sink);
+      run_blocks<RS, NQ, 0, PAIR, kNT>(d, b0, b1, sm_ring, q_ring, lane, sink);
     }
   }
 }
